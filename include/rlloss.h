@@ -1,0 +1,289 @@
+/*
+ * rlloss.h -- C ABI of the fused LM-head + RL policy loss library (gfx950).
+ *
+ * The method (prime-rl pull request 4233, PR description):
+ *   z_t     = W h_t / tau                        (LM head, vocabulary V)
+ *   log p_t = log_softmax(z_t)                   (full vocabulary)
+ *   loss_t  = -adv_tau * A_t * ( w(a_t) * log p_t(a_t)
+ *                                - sum_e sg[u_e * w_e] * log p_t(v_e) )
+ *             + beta * KL(q || p)
+ *   L       = sum_t loss_t / D
+ * with w the importance weight of the loss type ("What changes": ipo
+ * 1(|p-q| <= eps) * min(p/q, max_importance_ratio); icepop
+ * 1(low <= p/q <= high) * p/q; reinforce 1), e = (v_e, u_e) the entries of a
+ * ragged per-token support in CSR form (int32 ids, host int64 offsets:
+ * "TokenSupport" bullet), and KL(q || p) = sum_e u_e (log q(v_e) - log p(v_e))
+ * over the same support (KL bullet; exact estimator on a replayed support
+ * with u = q, k1 on sampler draws with u = 1/K).  Importance weights are
+ * held constant in the gradient.
+ *
+ * Conventions for every entry point:
+ *  - Array arguments are device pointers unless the name ends in _host.
+ *  - The caller owns every buffer.  The library allocates no device memory:
+ *    temporary storage comes from the caller's workspace.
+ *  - `stream` is a hipStream_t passed as void* (NULL = the default stream).
+ *    All device work is enqueued asynchronously on it; the call returns
+ *    without synchronising (except rl_validate_support_sync).
+ *  - Argument, configuration and CSR-structure errors are detected on the
+ *    host and returned before anything is enqueued.  Malformed data that only
+ *    the device can see (ids out of range, non-finite values) is reported by
+ *    rl_validate_support, not by the compute calls.
+ *  - Row-major layouts throughout; bf16 values are stored as raw 16-bit
+ *    words (IEEE bfloat16).
+ *  - Results are deterministic: the same inputs and configuration on the same
+ *    device give bitwise identical outputs (no floating-point atomics).
+ */
+#ifndef RLLOSS_H
+#define RLLOSS_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum rl_status {
+  RL_OK = 0,
+  RL_E_ARG = 1,           /* null pointer, bad size or dtype, size overflow */
+  RL_E_CFG = 2,           /* inconsistent or out-of-range configuration     */
+  RL_E_CSR = 3,           /* host offsets are not a valid CSR               */
+  RL_E_WORKSPACE = 4,     /* workspace missing or smaller than required     */
+  RL_E_HIP = 5,           /* a HIP runtime call or kernel launch failed     */
+  RL_E_INVALID_INPUT = 6  /* rl_validate_support_sync found bad data        */
+} rl_status;
+
+typedef enum rl_dtype { RL_DTYPE_FP32 = 0, RL_DTYPE_BF16 = 1 } rl_dtype;
+
+typedef enum rl_loss_type {
+  RL_LOSS_IPO = 0,       /* w = 1(|p-q| <= ipo_eps) * min(p/q, max_ratio) */
+  RL_LOSS_ICEPOP = 1,    /* w = 1(icepop_lo <= p/q <= icepop_hi) * p/q    */
+  RL_LOSS_REINFORCE = 2  /* w = 1                                         */
+} rl_loss_type;
+
+typedef enum rl_kl_estimator {
+  RL_KL_NONE = 0,
+  RL_KL_EXACT = 1,  /* replayed support, u = q: the KL is exact           */
+  RL_KL_K1 = 2      /* sampler draws, u = 1/K: the k1 estimate            */
+} rl_kl_estimator;
+
+typedef enum rl_backward {
+  RL_BWD_AUTO = 0,    /* SPARSE for reinforce without KL on a support, else DENSE */
+  RL_BWD_DENSE = 1,   /* full softmax backward through the LM head                */
+  RL_BWD_SPARSE = 2,  /* gradient only on label + support entries (requires
+                         reinforce, no KL, a support)                              */
+  RL_BWD_NONE = 3     /* forward only: no dh, no dW                                */
+} rl_backward;
+
+/* Indices into rl_loss_out.metrics (prime-rl PR 4233, "Metrics" bullet). */
+enum {
+  RL_METRIC_MASKED_FRACTION = 0, /* fraction of tokens whose label weight indicator is 0   */
+  RL_METRIC_SUPPORT_MASS = 1,    /* mean over tokens with a support of sum_e u_e p/q      */
+  RL_METRIC_MASK_TV = 2,         /* fraction of tokens with |p - q| > ipo_eps (label)     */
+  RL_METRIC_KL = 3,              /* mean KL_t (0 without KL)                              */
+  RL_METRIC_KL_BETA = 4,         /* beta                                                  */
+  RL_METRIC_MAX_ABS_KAPPA = 5,   /* max_t |kappa_t|, the net softmax coefficient          */
+  RL_METRIC_ENTROPY_MEAN = 6,    /* mean entropy of the training softmax                  */
+  RL_METRIC_COUNT = 7
+};
+
+typedef struct rl_loss_cfg {
+  int64_t N;            /* tokens, >= 1                                         */
+  int64_t H;            /* hidden size, >= 8 and a multiple of 8                */
+  int64_t V;            /* vocabulary, 1 .. 2^31-1                              */
+  int64_t nnz;          /* support entries (0 without a support)                */
+  int64_t token_chunk;  /* tokens per pass through the head; 0 = default 16384  */
+  int32_t dtype;        /* rl_dtype of h and W                                  */
+  int32_t grad_dtype;   /* rl_dtype of dh (dW is always fp32)                   */
+  int32_t loss_type;    /* rl_loss_type                                         */
+  int32_t kl_estimator; /* rl_kl_estimator                                      */
+  int32_t backward;     /* rl_backward                                          */
+  int32_t replayed;     /* 1: the support is a replayed truncated set, u = q    */
+  int32_t accumulate_dW;/* 1: dW += gradient, 0: dW = gradient                  */
+  int32_t reserved0;    /* must be 0                                            */
+  float ipo_eps;        /* IPO threshold on |p - q|, >= 0                       */
+  float max_ratio;      /* IPO cap on p/q, > 0                                  */
+  float icepop_lo;      /* IcePop band, 0 <= lo <= hi                           */
+  float icepop_hi;
+  float adv_tau;        /* advantage scale                                      */
+  float kl_coeff;       /* beta, >= 0                                           */
+  float inv_temperature;/* 1/tau, > 0                                           */
+  float loss_norm;      /* D, > 0 (the caller passes e.g. the token count)      */
+} rl_loss_cfg;
+
+typedef struct rl_loss_out {
+  float* loss;              /* [1]            required                          */
+  float* token_loss;        /* [N]            nullable                          */
+  float* logprobs;          /* [N]            nullable, log p_t(a_t)            */
+  float* entropy;           /* [N]            nullable                          */
+  float* weight;            /* [N]            nullable, w(a_t)                  */
+  uint8_t* keep;            /* [N]            nullable, 1 = weight indicator on */
+  float* support_logprobs;  /* [nnz]          nullable, log p_t(v_e)            */
+  void* dh;                 /* [N,H]          nullable, grad_dtype              */
+  float* dW;                /* [V,H] fp32     nullable                          */
+  float* metrics;           /* [RL_METRIC_COUNT] nullable                       */
+} rl_loss_out;
+
+/*
+ * rl_loss_workspace_size -- bytes of device workspace rl_loss_fwd_bwd needs
+ * for `cfg` (with `has_support` = 1 when a CSR support will be passed and
+ * `want_dh`/`want_dW` = 1 when those outputs will be non-null).
+ * Errors: RL_E_ARG (null, bad sizes, overflow), RL_E_CFG.
+ */
+rl_status rl_loss_workspace_size(const rl_loss_cfg* cfg, int32_t has_support,
+                                 int32_t want_dh, int32_t want_dW, size_t* bytes);
+
+/*
+ * rl_loss_fwd_bwd -- the fused LM head + RLLoss forward and backward.
+ *
+ *  h                 [N,H] dtype     hidden states
+ *  W                 [V,H] dtype     head weights (nn.Linear [out,in] layout)
+ *  labels            [N] int32       sampled token ids, in [0, V)
+ *  infer_logprobs    [N] fp32        sampler log q(label), finite, <= 0
+ *  adv               [N] fp32        advantages A_t
+ *  csr_offsets_host  [N+1] int64     host; NULL = no support (then nnz = 0)
+ *  csr_offsets_dev   [N+1] int64     device copy of the same offsets
+ *  csr_ids           [nnz] int32     support ids in [0, V); repeats allowed
+ *  csr_u             [nnz] fp32      estimator weights u_e >= 0
+ *  csr_logq          [nnz] fp32      sampler log q(v_e); NULL = log(u_e)
+ *  workspace         device, >= rl_loss_workspace_size() bytes, any contents
+ *
+ * Backward: dh = (dL/dz) W / tau, dW = (dL/dz)^T h / tau with
+ *   dL/dz_t = (kappa_t p_t - s_t w_t e_a + sum_e (s_t u_e w_e - beta u_e) e_{v_e}) / D,
+ *   kappa_t = s_t (w_t - sum_e u_e w_e) + beta sum_e u_e,  s_t = adv_tau A_t.
+ * The sparse backward drops the kappa_t p_t term (exact when kappa_t = 0,
+ * e.g. reinforce without KL with sum_e u_e = 1 per row; the
+ * RL_METRIC_MAX_ABS_KAPPA metric reports the dropped coefficient).
+ * Errors: RL_E_ARG, RL_E_CFG, RL_E_CSR, RL_E_WORKSPACE, RL_E_HIP.
+ */
+rl_status rl_loss_fwd_bwd(const void* h, const void* W, const int32_t* labels,
+                          const float* infer_logprobs, const float* adv,
+                          const int64_t* csr_offsets_host, const int64_t* csr_offsets_dev,
+                          const int32_t* csr_ids, const float* csr_u, const float* csr_logq,
+                          const rl_loss_cfg* cfg, const rl_loss_out* out,
+                          void* workspace, size_t workspace_bytes, void* stream);
+
+/* ---------------------------------------------------------------------------
+ * Loss-only mismatch replay over (log p_train, log q_infer, A) triples.
+ * Sources: IPO documentation page ("Masking by Probability, Not Ratio");
+ * Rollout Correction Methods page ("Bypassing PPO importance sampling",
+ * "Decoupled, 3-policy PPO Importance Sampling", "Importance Sampling",
+ * token level); the Tencent article on KL/clip/entropy, section 2 (dual clip,
+ * defaults 0.2 / 0.2 / 3.0); prime-rl PR 4233 (weights, loss form).
+ * Per token: P = e^lp, Q = e^lq, r = e^(lp-lq);
+ *   IPO[i]:   masked iff |P-Q| > eps[i];  w = kept * min(r, max_ratio);  l = -A w lp
+ *   IcePop:   low iff r < lo, high iff r > hi; w = kept * r;               l = -A w lp
+ *   REINFORCE: l = -A lp
+ *   PPO-bypass with dual clip: J = min(rA, clip(r, 1-clip_low, 1+clip_high) A),
+ *             for A < 0 J = max(J, clip_c A); l = -J.  clip bit: clipped term
+ *             smaller; dual bit: A < 0 and clip_c A > min(...)
+ *   Decoupled token TIS, truncate, pi_old := pi_train: rho = r,
+ *             w = min(rho, tis_upper); l = -w A.  trunc bit: rho > tis_upper
+ * ------------------------------------------------------------------------ */
+#define RL_ELEM_MAX_EPS 8
+
+typedef struct rl_elem_cfg {
+  int32_t n_eps;              /* 1 .. RL_ELEM_MAX_EPS                         */
+  int32_t primary_eps_index;  /* which eps gives out->w_primary               */
+  float eps[RL_ELEM_MAX_EPS]; /* IPO thresholds, >= 0                         */
+  float max_ratio;            /* > 0                                          */
+  float icepop_lo, icepop_hi; /* 0 <= lo <= hi                                */
+  float clip_low, clip_high;  /* PPO clip, in [0, 1) and >= 0                 */
+  float clip_c;               /* dual-clip constant, > 1                      */
+  float tis_upper;            /* TIS truncation bound, > 0                    */
+} rl_elem_cfg;
+
+/* Mask-word bits (uint16 per token). */
+#define RL_ELEM_BIT_IPO0 0          /* bits 0..7: IPO eps[i] masked */
+#define RL_ELEM_BIT_ICEPOP_LOW 8
+#define RL_ELEM_BIT_ICEPOP_HIGH 9
+#define RL_ELEM_BIT_PPO_CLIP 10
+#define RL_ELEM_BIT_DUAL_CLIP 11
+#define RL_ELEM_BIT_TIS_TRUNC 12
+
+/* Indices into rl_elem_out.sums (fp64; counts are exact integers). */
+enum {
+  RL_ELEM_IPO_KEPT = 0,        /* + 3*i for eps[i]: kept count        */
+  RL_ELEM_IPO_LOSS = 1,        /* + 3*i: sum of l                     */
+  RL_ELEM_IPO_WEIGHT = 2,      /* + 3*i: sum of w                     */
+  RL_ELEM_ICEPOP_KEPT = 24,
+  RL_ELEM_ICEPOP_LOW = 25,
+  RL_ELEM_ICEPOP_HIGH = 26,
+  RL_ELEM_ICEPOP_LOSS = 27,
+  RL_ELEM_ICEPOP_WEIGHT = 28,
+  RL_ELEM_REINFORCE_LOSS = 29,
+  RL_ELEM_PPO_LOSS = 30,
+  RL_ELEM_PPO_CLIP = 31,
+  RL_ELEM_PPO_CLIP_LOWER = 32,
+  RL_ELEM_PPO_KL = 33,         /* sum of lq - lp                      */
+  RL_ELEM_TIS_LOSS = 34,
+  RL_ELEM_TIS_TRUNC = 35,
+  RL_ELEM_TIS_WEIGHT = 36,
+  RL_ELEM_SUM_COUNT = 37
+};
+
+typedef struct rl_elem_out {
+  uint16_t* mask_word;  /* [N] nullable */
+  float* w_primary;     /* [N] nullable: IPO weight at eps[primary_eps_index] */
+  double* sums;         /* [RL_ELEM_SUM_COUNT] required */
+} rl_elem_out;
+
+/* Workspace bytes for rl_loss_elementwise with N tokens. */
+rl_status rl_elementwise_workspace_size(int64_t N, size_t* bytes);
+
+/*
+ * rl_loss_elementwise -- one pass over lp, lq, A [N] fp32 (device).
+ * Errors: RL_E_ARG, RL_E_CFG, RL_E_WORKSPACE, RL_E_HIP.
+ */
+rl_status rl_loss_elementwise(const float* lp, const float* lq, const float* adv, int64_t N,
+                              const rl_elem_cfg* cfg, const rl_elem_out* out,
+                              void* workspace, size_t workspace_bytes, void* stream);
+
+/* ---------------------------------------------------------------------------
+ * Sampler-evidence validation of a CSR support (prime-rl PR 4233, "What
+ * changes": checked on the GPU on the CSR entries once per step, before the
+ * optimizer).  Flag bits written to *flags_dev (bitwise OR over all items):
+ * ------------------------------------------------------------------------ */
+#define RL_BAD_LABEL 0x001          /* a label outside [0, V)                    */
+#define RL_BAD_ID 0x002             /* a support id outside [0, V)               */
+#define RL_BAD_U 0x004              /* a u_e < 0 or not finite                   */
+#define RL_BAD_LOGQ 0x008           /* a csr_logq value not finite or > 0        */
+#define RL_BAD_INFER_LOGPROB 0x010  /* an infer_logprobs value not finite or > 0 */
+#define RL_BAD_REPLAY_MASS 0x020    /* replayed: |sum_e u_e - 1| > 1e-3 in a row */
+#define RL_BAD_REPLAY_LABEL 0x040   /* replayed: a row without its own label     */
+#define RL_BAD_ADV 0x080            /* an advantage not finite                   */
+#define RL_BAD_OFFSETS 0x100        /* device offsets not a CSR of nnz entries   */
+
+/*
+ * rl_validate_support -- enqueue the checks; writes one int32 to flags_dev.
+ * Any of the csr_* pointers may be NULL when csr_offsets_host is NULL.
+ * Errors: RL_E_ARG, RL_E_CSR (host offsets), RL_E_HIP.
+ */
+rl_status rl_validate_support(int64_t N, int64_t V, int64_t nnz, const int32_t* labels,
+                              const float* infer_logprobs, const float* adv,
+                              const int64_t* csr_offsets_host, const int64_t* csr_offsets_dev,
+                              const int32_t* csr_ids, const float* csr_u, const float* csr_logq,
+                              int32_t replayed, int32_t* flags_dev, void* stream);
+
+/*
+ * rl_validate_support_sync -- rl_validate_support, then synchronise `stream`
+ * and copy the flag word to *flags_host.  Returns RL_E_INVALID_INPUT when
+ * any flag is set.  This is the one call that waits for the device.
+ */
+rl_status rl_validate_support_sync(int64_t N, int64_t V, int64_t nnz, const int32_t* labels,
+                                   const float* infer_logprobs, const float* adv,
+                                   const int64_t* csr_offsets_host,
+                                   const int64_t* csr_offsets_dev, const int32_t* csr_ids,
+                                   const float* csr_u, const float* csr_logq, int32_t replayed,
+                                   int32_t* flags_dev, int32_t* flags_host, void* stream);
+
+/* Static description of a status code; never NULL. */
+const char* rl_status_string(rl_status s);
+
+/* Library version string, e.g. "rlloss 0.1.0 gfx950". */
+const char* rl_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* RLLOSS_H */

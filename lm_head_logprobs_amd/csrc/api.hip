@@ -1,0 +1,412 @@
+// C ABI of librlloss: argument checks, planning, workspace layout, launches.
+//
+// Fused head + RLLoss (prime-rl PR 4233).  Tokens are processed in chunks of
+// Tc rows sliced from the batch with host offsets, so no device value is read
+// back.  Per chunk:
+//   1. forward GEMM  S^T = W h_c^T  (MFMA) with an online-softmax epilogue:
+//      per (token, 128-row vocabulary tile) the max m, sum e^(z-m) and
+//      sum e^(z-m)(z-m); and, for a dense backward, Pt = e^(z-m) [V, Tc]
+//   2. combine: per token LSE and entropy from the partials, label and
+//      support logits by fp32 dot products, weights, KL, loss, kappa and the
+//      per-entry gradient coefficients
+//   3. dense backward only: form G (= kappa/D p) from Pt in both layouts,
+//      dh partials = G (W^T)^T split over V, dW (+)= G^T (h_c^T)^T
+//   4. dh = partials + label/support rows of W scaled by their coefficients
+// After the chunks: the label/support terms of dW via vocabulary buckets, then
+// the fixed-order loss and metric reduction.
+#include <cmath>
+#include <cstring>
+
+#include "kernels.h"
+
+namespace {
+
+using namespace rl;
+
+constexpr size_t WS_ALIGN = 256;
+constexpr int64_t DEFAULT_CHUNK = 16384;
+
+bool mul_ok(int64_t a, int64_t b, int64_t* out) {
+  if (a < 0 || b < 0) return false;
+  return !__builtin_mul_overflow(a, b, out);
+}
+
+struct Layout {
+  size_t off = 0;
+  bool ok = true;
+  size_t take(int64_t n, int64_t elem) {
+    int64_t bytes;
+    if (!mul_ok(n, elem, &bytes) || bytes > ((int64_t)1 << 56)) {
+      ok = false;
+      return 0;
+    }
+    const size_t o = off;
+    off = (off + (size_t)bytes + WS_ALIGN - 1) / WS_ALIGN * WS_ALIGN;
+    return o;
+  }
+};
+
+struct Plan {
+  int64_t N, H, V, nnz, E, Tc, Tcpad, Vpad, J;
+  int dtype, gdtype;
+  int64_t esz;
+  int mode;  // resolved rl_backward
+  bool has_support, want_dh, want_dW, dense, kl_active;
+  float beta;
+  int splits;
+  int64_t k_split;
+  size_t o_pm, o_ps, o_pt, o_lse, o_kap, o_stats, o_coef;
+  size_t o_Pt, o_G, o_Wt, o_ht, o_dhp;
+  size_t o_ka, o_kb, o_ia, o_ib, o_hist, o_start, o_rows;
+  size_t total;
+};
+
+bool finite(float x) { return std::isfinite(x); }
+
+rl_status check_cfg(const rl_loss_cfg* c, bool has_support) {
+  if (c->N < 1 || c->H < 8 || (c->H % 8) != 0 || c->V < 1 || c->nnz < 0) return RL_E_ARG;
+  if (c->V > (int64_t)INT32_MAX - 2 || c->N > (int64_t)INT32_MAX) return RL_E_ARG;
+  if (c->N + c->nnz > (int64_t)INT32_MAX) return RL_E_ARG;
+  if (!has_support && c->nnz != 0) return RL_E_ARG;
+  if (c->token_chunk < 0 || c->reserved0 != 0) return RL_E_ARG;
+  if ((c->dtype != RL_DTYPE_FP32 && c->dtype != RL_DTYPE_BF16) ||
+      (c->grad_dtype != RL_DTYPE_FP32 && c->grad_dtype != RL_DTYPE_BF16))
+    return RL_E_ARG;
+  if (c->loss_type < RL_LOSS_IPO || c->loss_type > RL_LOSS_REINFORCE) return RL_E_CFG;
+  if (!(c->ipo_eps >= 0.0f) || !(c->max_ratio > 0.0f)) return RL_E_CFG;
+  if (!(c->icepop_lo >= 0.0f) || !(c->icepop_lo <= c->icepop_hi)) return RL_E_CFG;
+  if (!finite(c->adv_tau)) return RL_E_CFG;
+  if (!(c->inv_temperature > 0.0f) || !finite(c->inv_temperature)) return RL_E_CFG;
+  if (!(c->loss_norm > 0.0f) || !finite(c->loss_norm)) return RL_E_CFG;
+  if (c->kl_estimator < RL_KL_NONE || c->kl_estimator > RL_KL_K1) return RL_E_CFG;
+  if (!(c->kl_coeff >= 0.0f) || !finite(c->kl_coeff)) return RL_E_CFG;
+  const bool kl_active = c->kl_estimator != RL_KL_NONE && c->kl_coeff > 0.0f;
+  if (kl_active && !has_support) return RL_E_CFG;
+  if (c->kl_estimator == RL_KL_EXACT && !c->replayed) return RL_E_CFG;
+  if (c->replayed != 0 && c->replayed != 1) return RL_E_CFG;
+  if (c->replayed && !has_support) return RL_E_CFG;
+  if (c->accumulate_dW != 0 && c->accumulate_dW != 1) return RL_E_CFG;
+  if (c->backward < RL_BWD_AUTO || c->backward > RL_BWD_NONE) return RL_E_CFG;
+  const bool sparse_ok = c->loss_type == RL_LOSS_REINFORCE && !kl_active && has_support;
+  if (c->backward == RL_BWD_SPARSE && !sparse_ok) return RL_E_CFG;
+  return RL_OK;
+}
+
+rl_status make_plan(const rl_loss_cfg* c, bool has_support, bool want_dh, bool want_dW,
+                    Plan* p) {
+  const rl_status st = check_cfg(c, has_support);
+  if (st != RL_OK) return st;
+  p->N = c->N;
+  p->H = c->H;
+  p->V = c->V;
+  p->nnz = c->nnz;
+  p->E = c->N + c->nnz;
+  p->has_support = has_support;
+  p->dtype = c->dtype;
+  p->gdtype = c->grad_dtype;
+  p->esz = c->dtype == RL_DTYPE_BF16 ? 2 : 4;
+  p->kl_active = c->kl_estimator != RL_KL_NONE && c->kl_coeff > 0.0f;
+  p->beta = p->kl_active ? c->kl_coeff : 0.0f;
+  int mode = c->backward;
+  if (mode == RL_BWD_AUTO)
+    mode = (c->loss_type == RL_LOSS_REINFORCE && !p->kl_active && has_support) ? RL_BWD_SPARSE
+                                                                               : RL_BWD_DENSE;
+  p->mode = mode;
+  p->want_dh = want_dh && mode != RL_BWD_NONE;
+  p->want_dW = want_dW && mode != RL_BWD_NONE;
+  p->dense = mode == RL_BWD_DENSE && (p->want_dh || p->want_dW);
+  p->Tc = c->token_chunk > 0 ? std::min(c->token_chunk, c->N) : std::min(DEFAULT_CHUNK, c->N);
+  p->Tcpad = round_up(p->Tc, 64);
+  p->Vpad = round_up(p->V, 64);
+  p->J = ceil_div(p->V, FWD_VTILE);
+  const int bk = gemm_k_tile(p->dtype);
+  {
+    const int64_t tiles = ceil_div(p->Tc, 128) * ceil_div(p->H, 128);
+    int64_t sp = std::max<int64_t>(1, std::min<int64_t>(16, ceil_div(1024, tiles)));
+    p->k_split = round_up(ceil_div(p->Vpad, sp), bk);
+    p->splits = (int)ceil_div(p->Vpad, p->k_split);
+  }
+  Layout L;
+  const int64_t TJ = p->Tc * p->J;
+  p->o_pm = L.take(TJ, 4);
+  p->o_ps = L.take(TJ, 4);
+  p->o_pt = L.take(TJ, 4);
+  p->o_lse = L.take(p->N, 4);
+  p->o_kap = L.take(p->N, 4);
+  p->o_stats = L.take(p->N, 4 * STAT_N);
+  p->o_coef = L.take(p->E, 4);
+  p->o_Pt = p->o_G = p->o_Wt = p->o_ht = p->o_dhp = 0;
+  if (p->dense) {
+    int64_t vt;
+    if (!mul_ok(p->V, p->Tcpad, &vt)) return RL_E_ARG;
+    p->o_Pt = L.take(vt, p->esz);
+    if (p->want_dh) {
+      int64_t tv, hv, sth;
+      if (!mul_ok(p->Tc, p->Vpad, &tv) || !mul_ok(p->H, p->Vpad, &hv) ||
+          !mul_ok((int64_t)p->splits * p->Tc, p->H, &sth))
+        return RL_E_ARG;
+      p->o_G = L.take(tv, p->esz);
+      p->o_Wt = L.take(hv, p->esz);
+      p->o_dhp = L.take(sth, 4);
+    }
+    if (p->want_dW) p->o_ht = L.take(p->H * p->Tcpad, p->esz);
+  }
+  p->o_ka = p->o_kb = p->o_ia = p->o_ib = p->o_hist = p->o_start = p->o_rows = 0;
+  if (p->want_dW) {
+    p->o_ka = L.take(p->E, 4);
+    p->o_kb = L.take(p->E, 4);
+    p->o_ia = L.take(p->E, 4);
+    p->o_ib = L.take(p->E, 4);
+    p->o_hist = L.take(csc_hist_len(p->E), 4);
+    p->o_start = L.take(p->V + 2, 4);
+  }
+  if ((p->want_dW) && has_support) p->o_rows = L.take(p->nnz, 4);
+  if (!L.ok) return RL_E_ARG;
+  p->total = L.off;
+  return RL_OK;
+}
+
+rl_status check_host_csr(const int64_t* off, int64_t N, int64_t nnz) {
+  if (off[0] != 0) return RL_E_CSR;
+  for (int64_t t = 0; t < N; ++t)
+    if (off[t + 1] < off[t]) return RL_E_CSR;
+  if (off[N] != nnz) return RL_E_CSR;
+  return RL_OK;
+}
+
+bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
+
+#define RL_TRY(expr)                              \
+  do {                                            \
+    if ((expr) != hipSuccess) return RL_E_HIP;    \
+  } while (0)
+
+}  // namespace
+
+extern "C" {
+
+const char* rl_status_string(rl_status s) {
+  switch (s) {
+    case RL_OK: return "ok";
+    case RL_E_ARG: return "invalid argument (null pointer, size, dtype, alignment or overflow)";
+    case RL_E_CFG: return "invalid or inconsistent loss configuration";
+    case RL_E_CSR: return "host CSR offsets are not a valid support (off[0]=0, monotone, off[N]=nnz)";
+    case RL_E_WORKSPACE: return "workspace missing, misaligned or smaller than required";
+    case RL_E_HIP: return "HIP runtime error or kernel launch failure";
+    case RL_E_INVALID_INPUT: return "validation found malformed support or label data";
+  }
+  return "unknown status";
+}
+
+const char* rl_version(void) { return "rlloss 0.1.0 gfx950"; }
+
+rl_status rl_loss_workspace_size(const rl_loss_cfg* cfg, int32_t has_support, int32_t want_dh,
+                                 int32_t want_dW, size_t* bytes) {
+  if (cfg == nullptr || bytes == nullptr) return RL_E_ARG;
+  Plan p;
+  const rl_status st = make_plan(cfg, has_support != 0, want_dh != 0, want_dW != 0, &p);
+  if (st != RL_OK) return st;
+  *bytes = p.total;
+  return RL_OK;
+}
+
+rl_status rl_loss_fwd_bwd(const void* h, const void* W, const int32_t* labels,
+                          const float* infer_logprobs, const float* adv,
+                          const int64_t* csr_offsets_host, const int64_t* csr_offsets_dev,
+                          const int32_t* csr_ids, const float* csr_u, const float* csr_logq,
+                          const rl_loss_cfg* cfg, const rl_loss_out* out, void* workspace,
+                          size_t workspace_bytes, void* stream) {
+  if (cfg == nullptr || out == nullptr || out->loss == nullptr) return RL_E_ARG;
+  if (h == nullptr || W == nullptr || labels == nullptr || infer_logprobs == nullptr ||
+      adv == nullptr)
+    return RL_E_ARG;
+  const bool has_support = csr_offsets_host != nullptr;
+  if (has_support && (csr_offsets_dev == nullptr || csr_ids == nullptr || csr_u == nullptr))
+    return RL_E_ARG;
+  if (!has_support && (csr_offsets_dev != nullptr || csr_ids != nullptr || csr_u != nullptr ||
+                       csr_logq != nullptr))
+    return RL_E_ARG;
+  if (!aligned(h, 16) || !aligned(W, 16) || (out->dh && !aligned(out->dh, 16)) ||
+      (out->dW && !aligned(out->dW, 16)))
+    return RL_E_ARG;
+  Plan p;
+  rl_status st = make_plan(cfg, has_support, out->dh != nullptr, out->dW != nullptr, &p);
+  if (st != RL_OK) return st;
+  if (has_support) {
+    st = check_host_csr(csr_offsets_host, p.N, p.nnz);
+    if (st != RL_OK) return st;
+  }
+  if (p.total > 0 && (workspace == nullptr || workspace_bytes < p.total ||
+                      !aligned(workspace, WS_ALIGN)))
+    return RL_E_WORKSPACE;
+
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  char* ws = static_cast<char*>(workspace);
+  auto F = [&](size_t o) { return reinterpret_cast<float*>(ws + o); };
+  auto I = [&](size_t o) { return reinterpret_cast<int32_t*>(ws + o); };
+  float *pm = F(p.o_pm), *ps = F(p.o_ps), *pt = F(p.o_pt);
+  float *lse = F(p.o_lse), *kap = F(p.o_kap), *stats = F(p.o_stats), *coef = F(p.o_coef);
+  void* Pt = p.dense ? ws + p.o_Pt : nullptr;
+  void* G = (p.dense && p.want_dh) ? ws + p.o_G : nullptr;
+  void* Wt = (p.dense && p.want_dh) ? ws + p.o_Wt : nullptr;
+  void* ht = (p.dense && p.want_dW) ? ws + p.o_ht : nullptr;
+  float* dhp = (p.dense && p.want_dh) ? F(p.o_dhp) : nullptr;
+  const char* hb = static_cast<const char*>(h);
+
+  const WeightParams wp{cfg->loss_type, cfg->ipo_eps, cfg->max_ratio, cfg->icepop_lo,
+                        cfg->icepop_hi};
+  const float inv_D = 1.0f / cfg->loss_norm;
+
+  if (p.dense && p.want_dh) RL_TRY(transpose_pad(p.dtype, W, p.H, p.V, p.H, Wt, p.Vpad, s));
+
+  for (int64_t c0 = 0; c0 < p.N; c0 += p.Tc) {
+    const int64_t tc = std::min(p.Tc, p.N - c0);
+    const int64_t tck = round_up(tc, 64);
+    const void* hc = hb + c0 * p.H * p.esz;
+    FwdEpiArgs fa{cfg->inv_temperature, p.V, tc, p.J, pm, ps, pt, Pt, p.Tcpad};
+    RL_TRY(gemm_fwd(p.dtype, W, hc, p.V, tc, p.H, fa, s));
+    CombineArgs ca{};
+    ca.h = h;
+    ca.W = W;
+    ca.labels = labels;
+    ca.infer_lp = infer_logprobs;
+    ca.adv = adv;
+    ca.off = has_support ? csr_offsets_dev : nullptr;
+    ca.ids = csr_ids;
+    ca.u = csr_u;
+    ca.logq = csr_logq;
+    ca.part_m = pm;
+    ca.part_s = ps;
+    ca.part_t = pt;
+    ca.t0 = c0;
+    ca.Tc = tc;
+    ca.N = p.N;
+    ca.H = p.H;
+    ca.V = p.V;
+    ca.J = p.J;
+    ca.nnz = p.nnz;
+    ca.wp = wp;
+    ca.adv_tau = cfg->adv_tau;
+    ca.beta = p.beta;
+    ca.inv_t = cfg->inv_temperature;
+    ca.inv_D = inv_D;
+    ca.lse = lse;
+    ca.kappa_s = kap;
+    ca.stats = stats;
+    ca.coef = coef;
+    ca.o_logprobs = out->logprobs;
+    ca.o_entropy = out->entropy;
+    ca.o_weight = out->weight;
+    ca.o_keep = out->keep;
+    ca.o_token_loss = out->token_loss;
+    ca.o_support_lp = has_support ? out->support_logprobs : nullptr;
+    RL_TRY(combine(p.dtype, ca, s));
+    if (p.dense) {
+      RL_TRY(form_g(p.dtype, Pt, p.Tcpad, G, p.Vpad, pm, p.J, lse + c0, kap + c0, p.V, p.Vpad, tc,
+                    tck, s));
+      if (p.want_dh)
+        RL_TRY(gemm_store(p.dtype, G, p.Vpad, Wt, p.Vpad, tc, p.H, p.Vpad, p.splits, p.k_split,
+                          dhp, p.H, p.Tc * p.H, s));
+      if (p.want_dW) {
+        RL_TRY(transpose_pad(p.dtype, hc, p.H, tc, p.H, ht, tck, s));
+        const int acc = (c0 > 0 || cfg->accumulate_dW) ? 1 : 0;
+        RL_TRY(gemm_dw(p.dtype, Pt, p.Tcpad, ht, tck, p.V, p.H, tck, out->dW, p.H, acc, s));
+      }
+    }
+    if (p.want_dh)
+      RL_TRY(finalize_dh(p.dtype, p.gdtype, dhp, p.dense ? p.splits : 0, p.Tc * p.H, W, labels,
+                         has_support ? csr_offsets_dev : nullptr, csr_ids, coef, c0, tc, p.N,
+                         p.nnz, p.V, p.H, out->dh, s));
+  }
+  if (p.want_dW) {
+    CscWork cw{I(p.o_ka), I(p.o_kb), I(p.o_ia), I(p.o_ib), I(p.o_hist), I(p.o_start),
+               csc_hist_len(p.E)};
+    int32_t* rows = has_support ? I(p.o_rows) : nullptr;
+    if (has_support) RL_TRY(csr_rows(csr_offsets_dev, p.N, p.nnz, rows, s));
+    const int32_t* perm = nullptr;
+    RL_TRY(csc_build(labels, csr_ids, p.N, p.nnz, p.V, cw, &perm, s));
+    const int overwrite = (!p.dense && !cfg->accumulate_dW) ? 1 : 0;
+    RL_TRY(sparse_dw(p.dtype, h, p.H, p.N, p.V, cw.start, perm, rows, coef, out->dW, overwrite,
+                     s));
+  }
+  RL_TRY(reduce_final(stats, p.N, inv_D, p.beta, out->loss, out->metrics, s));
+  return RL_OK;
+}
+
+rl_status rl_elementwise_workspace_size(int64_t N, size_t* bytes) {
+  if (bytes == nullptr || N < 1) return RL_E_ARG;
+  int64_t b;
+  if (!mul_ok(elem_num_blocks(N), (int64_t)RL_ELEM_SUM_COUNT * 8, &b)) return RL_E_ARG;
+  *bytes = (size_t)b;
+  return RL_OK;
+}
+
+rl_status rl_loss_elementwise(const float* lp, const float* lq, const float* adv, int64_t N,
+                              const rl_elem_cfg* cfg, const rl_elem_out* out, void* workspace,
+                              size_t workspace_bytes, void* stream) {
+  if (lp == nullptr || lq == nullptr || adv == nullptr || cfg == nullptr || out == nullptr ||
+      out->sums == nullptr || N < 1)
+    return RL_E_ARG;
+  if (!aligned(lp, 16) || !aligned(lq, 16) || !aligned(adv, 16) ||
+      (out->mask_word && !aligned(out->mask_word, 16)) ||
+      (out->w_primary && !aligned(out->w_primary, 16)))
+    return RL_E_ARG;
+  if (cfg->n_eps < 1 || cfg->n_eps > RL_ELEM_MAX_EPS || cfg->primary_eps_index < 0 ||
+      cfg->primary_eps_index >= cfg->n_eps)
+    return RL_E_CFG;
+  for (int i = 0; i < cfg->n_eps; ++i)
+    if (!(cfg->eps[i] >= 0.0f)) return RL_E_CFG;
+  if (!(cfg->max_ratio > 0.0f) || !(cfg->icepop_lo >= 0.0f) ||
+      !(cfg->icepop_lo <= cfg->icepop_hi) || !(cfg->clip_low >= 0.0f && cfg->clip_low < 1.0f) ||
+      !(cfg->clip_high >= 0.0f) || !(cfg->clip_c > 1.0f) || !(cfg->tis_upper > 0.0f))
+    return RL_E_CFG;
+  size_t need;
+  rl_elementwise_workspace_size(N, &need);
+  if (workspace == nullptr || workspace_bytes < need || !aligned(workspace, 16))
+    return RL_E_WORKSPACE;
+  RL_TRY(rl::elementwise(lp, lq, adv, N, *cfg, out->mask_word, out->w_primary,
+                         static_cast<double*>(workspace), out->sums,
+                         static_cast<hipStream_t>(stream)));
+  return RL_OK;
+}
+
+rl_status rl_validate_support(int64_t N, int64_t V, int64_t nnz, const int32_t* labels,
+                              const float* infer_logprobs, const float* adv,
+                              const int64_t* csr_offsets_host, const int64_t* csr_offsets_dev,
+                              const int32_t* csr_ids, const float* csr_u, const float* csr_logq,
+                              int32_t replayed, int32_t* flags_dev, void* stream) {
+  if (N < 1 || V < 1 || nnz < 0 || labels == nullptr || infer_logprobs == nullptr ||
+      adv == nullptr || flags_dev == nullptr)
+    return RL_E_ARG;
+  const bool has_support = csr_offsets_host != nullptr;
+  if (has_support) {
+    if (csr_offsets_dev == nullptr || csr_ids == nullptr || csr_u == nullptr) return RL_E_ARG;
+    const rl_status st = check_host_csr(csr_offsets_host, N, nnz);
+    if (st != RL_OK) return st;
+  } else if (nnz != 0) {
+    return RL_E_ARG;
+  }
+  RL_TRY(rl::validate(N, V, nnz, labels, infer_logprobs, adv,
+                      has_support ? csr_offsets_dev : nullptr, csr_ids, csr_u, csr_logq,
+                      replayed ? 1 : 0, flags_dev, static_cast<hipStream_t>(stream)));
+  return RL_OK;
+}
+
+rl_status rl_validate_support_sync(int64_t N, int64_t V, int64_t nnz, const int32_t* labels,
+                                   const float* infer_logprobs, const float* adv,
+                                   const int64_t* csr_offsets_host,
+                                   const int64_t* csr_offsets_dev, const int32_t* csr_ids,
+                                   const float* csr_u, const float* csr_logq, int32_t replayed,
+                                   int32_t* flags_dev, int32_t* flags_host, void* stream) {
+  if (flags_host == nullptr) return RL_E_ARG;
+  rl_status st = rl_validate_support(N, V, nnz, labels, infer_logprobs, adv, csr_offsets_host,
+                                     csr_offsets_dev, csr_ids, csr_u, csr_logq, replayed,
+                                     flags_dev, stream);
+  if (st != RL_OK) return st;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  RL_TRY(hipMemcpyAsync(flags_host, flags_dev, sizeof(int32_t), hipMemcpyDeviceToHost, s));
+  RL_TRY(hipStreamSynchronize(s));
+  return *flags_host ? RL_E_INVALID_INPUT : RL_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,116 @@
+// Internal definitions shared by the HIP translation units of librlloss.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include <algorithm>
+
+#include "../../include/rlloss.h"
+
+typedef uint16_t bf16_t;  // raw IEEE bfloat16 bits
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+#define RL_WAVE 64
+
+__device__ __forceinline__ float bf16_bits_to_f32(uint32_t bits16) {
+  return __uint_as_float(bits16 << 16);
+}
+
+// Round to nearest even; NaN stays NaN.
+__device__ __forceinline__ uint32_t f32_to_bf16_bits(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return (u >> 16) | 0x40u;
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return u >> 16;
+}
+
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  return f32_to_bf16_bits(lo) | (f32_to_bf16_bits(hi) << 16);
+}
+
+// Element access for the two storage types (bf16 bits or fp32).
+template <typename T> struct Elem;
+template <> struct Elem<bf16_t> {
+  static constexpr int VEC = 8;  // elements per 16-byte vector
+  __device__ __forceinline__ static float to_f32(bf16_t x) { return bf16_bits_to_f32(x); }
+  __device__ __forceinline__ static bf16_t from_f32(float f) { return (bf16_t)f32_to_bf16_bits(f); }
+  // Unpack one 16-byte vector to 8 floats.
+  __device__ __forceinline__ static void unpack(const u32x4& v, float* out) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      out[2 * i] = __uint_as_float(v[i] << 16);
+      out[2 * i + 1] = __uint_as_float(v[i] & 0xffff0000u);
+    }
+  }
+  __device__ __forceinline__ static u32x4 pack(const float* in) {
+    u32x4 v;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) v[i] = pack_bf16x2(in[2 * i], in[2 * i + 1]);
+    return v;
+  }
+};
+template <> struct Elem<float> {
+  static constexpr int VEC = 4;
+  __device__ __forceinline__ static float to_f32(float x) { return x; }
+  __device__ __forceinline__ static float from_f32(float f) { return f; }
+  __device__ __forceinline__ static void unpack(const u32x4& v, float* out) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) out[i] = __uint_as_float(v[i]);
+  }
+  __device__ __forceinline__ static u32x4 pack(const float* in) {
+    u32x4 v;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) v[i] = __float_as_uint(in[i]);
+    return v;
+  }
+};
+
+// Importance weight of the three loss types (prime-rl PR 4233, "What
+// changes"): ipo 1(|p-q| <= eps) * min(p/q, max_ratio); icepop
+// 1(lo <= p/q <= hi) * p/q; reinforce 1.  Inputs are log-probabilities.
+struct WeightParams {
+  int type;
+  float eps, max_ratio, lo, hi;
+};
+
+__device__ __forceinline__ float rl_weight(float lp, float lq, const WeightParams& wp,
+                                           bool* keep) {
+  if (wp.type == RL_LOSS_REINFORCE) {
+    *keep = true;
+    return 1.0f;
+  }
+  float r = expf(lp - lq);
+  if (wp.type == RL_LOSS_IPO) {
+    float P = expf(lp), Q = expf(lq);
+    bool k = fabsf(P - Q) <= wp.eps;
+    *keep = k;
+    return k ? fminf(r, wp.max_ratio) : 0.0f;
+  }
+  bool k = (wp.lo <= r) && (r <= wp.hi);
+  *keep = k;
+  return k ? r : 0.0f;
+}
+
+// Wave-level reductions (64 lanes), fixed butterfly order.
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
+  return v;
+}
+__device__ __forceinline__ double wave_sum_d(double v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
+  return v;
+}
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
+  return v;
+}
+
+__host__ __device__ static inline int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
+__host__ __device__ static inline int64_t round_up(int64_t a, int64_t b) { return ceil_div(a, b) * b; }

@@ -1,0 +1,440 @@
+// Per-token kernels of the fused head: log-sum-exp merge, label/support logit
+// gathers, weights and loss (combine), the dense softmax-gradient operand
+// (form_g), dh finalisation and the deterministic loss/metric reduction.
+//
+// Method: prime-rl pull request 4233, PR description (RLLoss formula, the
+// estimator sum_v u_v f(v) of E_q[f], weights per loss type, KL over the same
+// support).  The gradient treats every importance weight as a constant:
+//   dL/dz_t = (kappa_t p_t - s_t w_t e_a + sum_e (s_t c_e - beta u_e) e_{v_e}) / D
+//   kappa_t = s_t (w_t - sum_e c_e) + beta sum_e u_e,   c_e = u_e w_e.
+// The kappa_t p_t part is the dense operand G; the label and entry parts are
+// per-entry coefficients applied by gathers (dh) and a bucketed scatter (dW).
+#include "kernels.h"
+
+namespace rl {
+namespace {
+
+constexpr int NT = 256;
+
+// Fixed-order block reduction over 256 threads (4 waves): butterfly inside
+// each wave, then the 4 wave results summed in wave order.
+__device__ __forceinline__ float block_sum(float v, float* sh) {
+  v = wave_sum(v);
+  const int w = threadIdx.x >> 6;
+  __syncthreads();
+  if ((threadIdx.x & 63) == 0) sh[w] = v;
+  __syncthreads();
+  return ((sh[0] + sh[1]) + sh[2]) + sh[3];
+}
+__device__ __forceinline__ float block_max(float v, float* sh) {
+  v = wave_max(v);
+  const int w = threadIdx.x >> 6;
+  __syncthreads();
+  if ((threadIdx.x & 63) == 0) sh[w] = v;
+  __syncthreads();
+  return fmaxf(fmaxf(sh[0], sh[1]), fmaxf(sh[2], sh[3]));
+}
+
+template <typename T>
+__device__ __forceinline__ float dot_row_part(const T* __restrict__ x, const T* __restrict__ y,
+                                              int64_t H, int start, int stride) {
+  constexpr int VEC = Elem<T>::VEC;
+  float acc = 0.0f;
+  for (int64_t c = (int64_t)start * VEC; c < H; c += (int64_t)stride * VEC) {
+    const u32x4 a = *reinterpret_cast<const u32x4*>(x + c);
+    const u32x4 b = *reinterpret_cast<const u32x4*>(y + c);
+    float fa[VEC], fb[VEC];
+    Elem<T>::unpack(a, fa);
+    Elem<T>::unpack(b, fb);
+#pragma unroll
+    for (int i = 0; i < VEC; ++i) acc = fmaf(fa[i], fb[i], acc);
+  }
+  return acc;
+}
+
+// dst[c][r] = src[r][c]; zero for R <= r < Rpad.  64 x 64 tiles through LDS.
+template <typename T>
+__global__ void __launch_bounds__(NT) transpose_kernel(const T* __restrict__ src, int64_t ld_src,
+                                                       int64_t R, int64_t C, T* __restrict__ dst,
+                                                       int64_t Rpad) {
+  __shared__ T tile[64][65];
+  const int64_t r0 = (int64_t)blockIdx.x * 64, c0 = (int64_t)blockIdx.y * 64;
+  const int tr = threadIdx.x >> 2, tc = (threadIdx.x & 3) * 16;
+  {
+    const int64_t r = r0 + tr;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const int64_t c = c0 + tc + i;
+      tile[tr][tc + i] = (r < R && c < C) ? src[r * ld_src + c] : Elem<T>::from_f32(0.0f);
+    }
+  }
+  __syncthreads();
+  {
+    const int64_t c = c0 + tr;
+    if (c < C) {
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const int64_t r = r0 + tc + i;
+        if (r < Rpad) dst[c * Rpad + r] = tile[tc + i][tr];
+      }
+    }
+  }
+}
+
+template <typename T>
+__global__ void __launch_bounds__(NT) combine_kernel(CombineArgs a) {
+  __shared__ float sh[8];
+  __shared__ float wsum[4][6];
+  const int tid = threadIdx.x;
+  const int64_t tl = blockIdx.x;
+  const int64_t t = a.t0 + tl;
+  const T* h = static_cast<const T*>(a.h) + t * a.H;
+  const T* W = static_cast<const T*>(a.W);
+
+  // Merge the per-tile online-softmax partials: LSE and entropy.
+  const float* pm = a.part_m + tl * a.J;
+  const float* ps = a.part_s + tl * a.J;
+  const float* pt = a.part_t + tl * a.J;
+  float mx = -INFINITY;
+  for (int64_t j = tid; j < a.J; j += NT) mx = fmaxf(mx, pm[j]);
+  const float M = block_max(mx, sh);
+  float S = 0.0f, Tq = 0.0f;
+  for (int64_t j = tid; j < a.J; j += NT) {
+    const float dm = pm[j] - M;
+    const float e = __expf(dm);
+    S += ps[j] * e;
+    Tq += e * (pt[j] + dm * ps[j]);
+  }
+  S = block_sum(S, sh);
+  Tq = block_sum(Tq, sh);
+  const float logS = logf(S);
+  const float lse = M + logS;
+  const float ent = logS - Tq / S;
+
+  // Label logit and log-probability.  An id outside [0, V) reads nothing and
+  // yields NaN (such inputs are reported by the validation call).
+  const int32_t lab = a.labels[t];
+  const bool lab_ok = lab >= 0 && lab < a.V;
+  float za = a.inv_t * block_sum(lab_ok ? dot_row_part<T>(h, W + (int64_t)lab * a.H, a.H, tid, NT)
+                                        : 0.0f, sh);
+  if (!lab_ok) za = NAN;
+  const float lp = za - lse;
+  const float lq = a.infer_lp[t];
+  bool keep;
+  const float w = rl_weight(lp, lq, a.wp, &keep);
+  const float s = a.adv_tau * a.adv[t];
+
+  // Support entries: one wave per entry, entries strided over the 4 waves;
+  // each wave keeps its own running sums, combined in wave order.
+  const int wave = tid >> 6, lane = tid & 63;
+  float sc = 0.0f, cent = 0.0f, su = 0.0f, kl = 0.0f, sm = 0.0f;
+  int64_t e0 = 0, e1 = 0;
+  if (a.off != nullptr) {
+    // Device offsets are clamped into [0, nnz] so a corrupted copy cannot
+    // send a read out of bounds.
+    e0 = min(max(a.off[t], (int64_t)0), a.nnz);
+    e1 = min(max(a.off[t + 1], e0), a.nnz);
+    for (int64_t e = e0 + wave; e < e1; e += 4) {
+      const int32_t v = a.ids[e];
+      const bool v_ok = v >= 0 && v < a.V;
+      float ze = a.inv_t * wave_sum(v_ok ? dot_row_part<T>(h, W + (int64_t)v * a.H, a.H, lane, 64)
+                                         : 0.0f);
+      if (!v_ok) ze = NAN;
+      const float lpe = ze - lse;
+      const float ue = a.u[e];
+      const float lqe = a.logq != nullptr ? a.logq[e] : logf(ue);
+      bool ke;
+      const float we = rl_weight(lpe, lqe, a.wp, &ke);
+      const float ce = ue * we;
+      sc += ce;
+      cent += ce * lpe;
+      su += ue;
+      kl += ue * (lqe - lpe);
+      sm += ue * __expf(lpe - lqe);
+      if (lane == 0) {
+        a.coef[a.N + e] = (s * ce - a.beta * ue) * a.inv_t * a.inv_D;
+        if (a.o_support_lp != nullptr) a.o_support_lp[e] = lpe;
+      }
+    }
+  }
+  __syncthreads();
+  if (lane == 0) {
+    wsum[wave][0] = sc;
+    wsum[wave][1] = cent;
+    wsum[wave][2] = su;
+    wsum[wave][3] = kl;
+    wsum[wave][4] = sm;
+  }
+  __syncthreads();
+  if (tid == 0) {
+    float acc[5];
+#pragma unroll
+    for (int k = 0; k < 5; ++k) acc[k] = ((wsum[0][k] + wsum[1][k]) + wsum[2][k]) + wsum[3][k];
+    sc = acc[0];
+    cent = acc[1];
+    su = acc[2];
+    kl = acc[3];
+    sm = acc[4];
+    const float klt = a.beta != 0.0f ? kl : 0.0f;
+    const float loss = -s * (w * lp - cent) + a.beta * klt;
+    const float kappa = s * (w - sc) + a.beta * su;
+    a.lse[t] = lse;
+    a.kappa_s[t] = kappa * a.inv_t * a.inv_D;
+    a.coef[t] = -s * w * a.inv_t * a.inv_D;
+    float* st = a.stats + t * STAT_N;
+    st[STAT_LOSS] = loss;
+    st[STAT_MASKED] = keep ? 0.0f : 1.0f;
+    st[STAT_SMASS] = sm;
+    st[STAT_HAS_SUPPORT] = (e1 > e0) ? 1.0f : 0.0f;
+    st[STAT_TVFAIL] = fabsf(expf(lp) - expf(lq)) > a.wp.eps ? 1.0f : 0.0f;
+    st[STAT_KL] = klt;
+    st[STAT_ABS_KAPPA] = fabsf(kappa);
+    st[STAT_ENTROPY] = ent;
+    if (a.o_logprobs) a.o_logprobs[t] = lp;
+    if (a.o_entropy) a.o_entropy[t] = ent;
+    if (a.o_weight) a.o_weight[t] = w;
+    if (a.o_keep) a.o_keep[t] = keep ? 1 : 0;
+    if (a.o_token_loss) a.o_token_loss[t] = loss;
+  }
+}
+
+// Gt (in place over Pt) and G from Pt = e^(z - m_tile).  64 (vocab) x 64
+// (token) tiles.  Columns Tc..Tcpad of Gt and Vpad padding of G are zeroed.
+template <typename T>
+__global__ void __launch_bounds__(NT) form_g_kernel(T* __restrict__ Pt, int64_t ldp,
+                                                    T* __restrict__ G, int64_t ldg,
+                                                    const float* __restrict__ part_m, int64_t J,
+                                                    const float* __restrict__ lse,
+                                                    const float* __restrict__ kap, int64_t V,
+                                                    int64_t Tc) {
+  __shared__ float scale[64];
+  __shared__ T tile[64][65];
+  const int64_t t0 = (int64_t)blockIdx.x * 64, v0 = (int64_t)blockIdx.y * 64;
+  const int tid = threadIdx.x;
+  if (tid < 64) {
+    const int64_t t = t0 + tid;
+    scale[tid] = (t < Tc) ? kap[t] * __expf(part_m[t * J + v0 / FWD_VTILE] - lse[t]) : 0.0f;
+  }
+  __syncthreads();
+  const int r = tid >> 2, cc = (tid & 3) * 16;
+  {
+    const int64_t v = v0 + r;
+    if (v < V) {
+      T* row = Pt + v * ldp + t0 + cc;
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const int64_t t = t0 + cc + i;
+        const float g = (t < Tc) ? scale[cc + i] * Elem<T>::to_f32(row[i]) : 0.0f;
+        const T gv = Elem<T>::from_f32(g);
+        row[i] = gv;
+        tile[cc + i][r] = gv;
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < 16; ++i) tile[cc + i][r] = Elem<T>::from_f32(0.0f);
+    }
+  }
+  if (G == nullptr) return;
+  __syncthreads();
+  {
+    const int64_t t = t0 + r;
+    if (t < Tc) {
+      T* grow = G + t * ldg + v0 + cc;
+#pragma unroll
+      for (int i = 0; i < 16; ++i) grow[i] = tile[r][cc + i];
+    }
+  }
+}
+
+template <typename T, typename GT>
+__global__ void __launch_bounds__(NT) finalize_dh_kernel(
+    const float* __restrict__ part, int splits, int64_t split_stride, const T* __restrict__ W,
+    const int32_t* __restrict__ labels, const int64_t* __restrict__ off,
+    const int32_t* __restrict__ ids, const float* __restrict__ coef, int64_t t0, int64_t N,
+    int64_t nnz, int64_t V, int64_t H, GT* __restrict__ dh) {
+  constexpr int VEC = 8;  // columns per thread per step
+  const int64_t tl = blockIdx.x;
+  const int64_t t = t0 + tl;
+  const int64_t e0 = off ? min(max(off[t], (int64_t)0), nnz) : 0;
+  const int64_t e1 = off ? min(max(off[t + 1], e0), nnz) : 0;
+  const int32_t lab = labels[t];
+  const bool lab_ok = lab >= 0 && lab < V;
+  const float cl = coef[t];
+  for (int64_t c = (int64_t)threadIdx.x * VEC; c < H; c += (int64_t)NT * VEC) {
+    float acc[VEC];
+#pragma unroll
+    for (int i = 0; i < VEC; ++i) acc[i] = 0.0f;
+    for (int sp = 0; sp < splits; ++sp) {
+      const float* p = part + sp * split_stride + tl * H + c;
+#pragma unroll
+      for (int i = 0; i < VEC; ++i) acc[i] += p[i];
+    }
+    if (lab_ok) {
+      const T* wr = W + (int64_t)lab * H + c;
+#pragma unroll
+      for (int i = 0; i < VEC; ++i) acc[i] = fmaf(cl, Elem<T>::to_f32(wr[i]), acc[i]);
+    }
+    for (int64_t e = e0; e < e1; ++e) {
+      const float ce = coef[N + e];
+      const int32_t v = ids[e];
+      if (v < 0 || v >= V) continue;
+      const T* wr = W + (int64_t)v * H + c;
+#pragma unroll
+      for (int i = 0; i < VEC; ++i) acc[i] = fmaf(ce, Elem<T>::to_f32(wr[i]), acc[i]);
+    }
+    GT* o = dh + t * H + c;
+#pragma unroll
+    for (int i = 0; i < VEC; ++i) o[i] = Elem<GT>::from_f32(acc[i]);
+  }
+}
+
+__global__ void __launch_bounds__(1024) reduce_final_kernel(const float* __restrict__ stats,
+                                                            int64_t N, float inv_D, float beta,
+                                                            float* loss, float* metrics) {
+  __shared__ double sh[STAT_N][16];
+  double acc[STAT_N];
+#pragma unroll
+  for (int k = 0; k < STAT_N; ++k) acc[k] = 0.0;
+  for (int64_t t = threadIdx.x; t < N; t += 1024) {
+    const float* st = stats + t * STAT_N;
+#pragma unroll
+    for (int k = 0; k < STAT_N; ++k) {
+      if (k == STAT_ABS_KAPPA)
+        acc[k] = fmax(acc[k], (double)st[k]);
+      else
+        acc[k] += (double)st[k];
+    }
+  }
+  const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
+#pragma unroll
+  for (int k = 0; k < STAT_N; ++k) {
+    double v = acc[k];
+    if (k == STAT_ABS_KAPPA) {
+#pragma unroll
+      for (int o = 32; o > 0; o >>= 1) v = fmax(v, __shfl_xor(v, o, 64));
+    } else {
+      v = wave_sum_d(v);
+    }
+    if (lane == 0) sh[k][w] = v;
+  }
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    double r[STAT_N];
+#pragma unroll
+    for (int k = 0; k < STAT_N; ++k) {
+      double v = sh[k][0];
+      for (int i = 1; i < 16; ++i) v = (k == STAT_ABS_KAPPA) ? fmax(v, sh[k][i]) : v + sh[k][i];
+      r[k] = v;
+    }
+    const double n = (double)N;
+    *loss = (float)(r[STAT_LOSS] * (double)inv_D);
+    if (metrics) {
+      metrics[RL_METRIC_MASKED_FRACTION] = (float)(r[STAT_MASKED] / n);
+      metrics[RL_METRIC_SUPPORT_MASS] =
+          r[STAT_HAS_SUPPORT] > 0 ? (float)(r[STAT_SMASS] / r[STAT_HAS_SUPPORT]) : 0.0f;
+      metrics[RL_METRIC_MASK_TV] = (float)(r[STAT_TVFAIL] / n);
+      metrics[RL_METRIC_KL] = (float)(r[STAT_KL] / n);
+      metrics[RL_METRIC_KL_BETA] = beta;
+      metrics[RL_METRIC_MAX_ABS_KAPPA] = (float)r[STAT_ABS_KAPPA];
+      metrics[RL_METRIC_ENTROPY_MEAN] = (float)(r[STAT_ENTROPY] / n);
+    }
+  }
+}
+
+__global__ void csr_rows_kernel(const int64_t* __restrict__ off, int64_t N, int64_t nnz,
+                                int32_t* __restrict__ row_of) {
+  const int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (t >= N) return;
+  if (t == 0)  // entries before the first row keep a marker no bucket reads
+    for (int64_t e = 0; e < min(max(off[0], (int64_t)0), nnz); ++e) row_of[e] = -1;
+  const int64_t e0 = min(max(off[t], (int64_t)0), nnz);
+  const int64_t e1 = min(max(off[t + 1], e0), nnz);
+  for (int64_t e = e0; e < e1; ++e) row_of[e] = (int32_t)t;
+}
+
+__global__ void fill_f32_kernel(float* p, int64_t n, float v) {
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n;
+       i += (int64_t)gridDim.x * blockDim.x)
+    p[i] = v;
+}
+
+}  // namespace
+
+hipError_t transpose_pad(int dtype, const void* src, int64_t ld_src, int64_t R, int64_t C,
+                         void* dst, int64_t Rpad, hipStream_t s) {
+  const dim3 grid((unsigned)ceil_div(Rpad, 64), (unsigned)ceil_div(C, 64));
+  if (dtype == RL_DTYPE_BF16)
+    hipLaunchKernelGGL(transpose_kernel<bf16_t>, grid, dim3(NT), 0, s,
+                       static_cast<const bf16_t*>(src), ld_src, R, C, static_cast<bf16_t*>(dst),
+                       Rpad);
+  else
+    hipLaunchKernelGGL(transpose_kernel<float>, grid, dim3(NT), 0, s,
+                       static_cast<const float*>(src), ld_src, R, C, static_cast<float*>(dst),
+                       Rpad);
+  return hipGetLastError();
+}
+
+hipError_t combine(int dtype, const CombineArgs& a, hipStream_t s) {
+  if (a.Tc <= 0) return hipSuccess;
+  if (dtype == RL_DTYPE_BF16)
+    hipLaunchKernelGGL(combine_kernel<bf16_t>, dim3((unsigned)a.Tc), dim3(NT), 0, s, a);
+  else
+    hipLaunchKernelGGL(combine_kernel<float>, dim3((unsigned)a.Tc), dim3(NT), 0, s, a);
+  return hipGetLastError();
+}
+
+hipError_t form_g(int dtype, void* Pt, int64_t ldp, void* G, int64_t ldg, const float* part_m,
+                  int64_t J, const float* lse_c, const float* kappa_c, int64_t V, int64_t Vpad,
+                  int64_t Tc, int64_t Tcpad, hipStream_t s) {
+  (void)Vpad;
+  const dim3 grid((unsigned)ceil_div(Tcpad, 64), (unsigned)ceil_div(V, 64));
+  if (dtype == RL_DTYPE_BF16)
+    hipLaunchKernelGGL(form_g_kernel<bf16_t>, grid, dim3(NT), 0, s, static_cast<bf16_t*>(Pt), ldp,
+                       static_cast<bf16_t*>(G), ldg, part_m, J, lse_c, kappa_c, V, Tc);
+  else
+    hipLaunchKernelGGL(form_g_kernel<float>, grid, dim3(NT), 0, s, static_cast<float*>(Pt), ldp,
+                       static_cast<float*>(G), ldg, part_m, J, lse_c, kappa_c, V, Tc);
+  return hipGetLastError();
+}
+
+hipError_t finalize_dh(int dtype, int grad_dtype, const float* part, int splits,
+                       int64_t split_stride, const void* W, const int32_t* labels,
+                       const int64_t* off, const int32_t* ids, const float* coef, int64_t t0,
+                       int64_t Tc, int64_t N, int64_t nnz, int64_t V, int64_t H, void* dh,
+                       hipStream_t s) {
+  if (Tc <= 0) return hipSuccess;
+  const dim3 grid((unsigned)Tc);
+#define RL_FIN(T, GT)                                                                           \
+  hipLaunchKernelGGL((finalize_dh_kernel<T, GT>), grid, dim3(NT), 0, s, part, splits,          \
+                     split_stride, static_cast<const T*>(W), labels, off, ids, coef, t0, N, nnz, \
+                     V, H, static_cast<GT*>(dh))
+  if (dtype == RL_DTYPE_BF16) {
+    if (grad_dtype == RL_DTYPE_BF16) RL_FIN(bf16_t, bf16_t); else RL_FIN(bf16_t, float);
+  } else {
+    if (grad_dtype == RL_DTYPE_BF16) RL_FIN(float, bf16_t); else RL_FIN(float, float);
+  }
+#undef RL_FIN
+  return hipGetLastError();
+}
+
+hipError_t reduce_final(const float* stats, int64_t N, float inv_D, float beta, float* loss,
+                        float* metrics, hipStream_t s) {
+  hipLaunchKernelGGL(reduce_final_kernel, dim3(1), dim3(1024), 0, s, stats, N, inv_D, beta, loss,
+                     metrics);
+  return hipGetLastError();
+}
+
+hipError_t csr_rows(const int64_t* off, int64_t N, int64_t nnz, int32_t* row_of, hipStream_t s) {
+  hipLaunchKernelGGL(csr_rows_kernel, dim3((unsigned)ceil_div(N, 256)), dim3(256), 0, s, off, N,
+                     nnz, row_of);
+  return hipGetLastError();
+}
+
+hipError_t fill_f32(float* p, int64_t n, float v, hipStream_t s) {
+  if (n <= 0) return hipSuccess;
+  const int64_t blocks = std::min<int64_t>(ceil_div(n, 256), 8192);
+  hipLaunchKernelGGL(fill_f32_kernel, dim3((unsigned)blocks), dim3(256), 0, s, p, n, v);
+  return hipGetLastError();
+}
+
+}  // namespace rl

@@ -1,0 +1,122 @@
+// Launchers of the device kernels (internal to librlloss).
+#pragma once
+
+#include "common.h"
+
+namespace rl {
+
+// Forward GEMM tile extent along the vocabulary: the online-softmax partials
+// are kept per (token, block of FWD_VTILE vocabulary rows).
+constexpr int FWD_VTILE = 128;
+
+struct FwdEpiArgs {
+  float inv_t;
+  int64_t V, Tc, J;      // vocabulary, tokens in the chunk, vocab tiles
+  float* part_m;         // [Tc, J] tile max of z
+  float* part_s;         // [Tc, J] sum exp(z - m)
+  float* part_t;         // [Tc, J] sum exp(z - m) (z - m)
+  void* Pt;              // [V, ldp] exp(z - m) per element (dtype of h/W), or null
+  int64_t ldp;
+};
+
+// S^T = W h_c^T with the online-softmax epilogue.  W [V,H], h_c [Tc,H].
+hipError_t gemm_fwd(int dtype, const void* W, const void* hc, int64_t V, int64_t Tc, int64_t H,
+                    const FwdEpiArgs& a, hipStream_t s);
+
+// C[split] = A[:, ks] B[:, ks]^T (fp32 out), split-K over K in `splits` slices
+// of k_split elements (a multiple of the K tile).  A [M,K] lda, B [N,K] ldb.
+hipError_t gemm_store(int dtype, const void* A, int64_t lda, const void* B, int64_t ldb,
+                      int64_t M, int64_t N, int64_t K, int splits, int64_t k_split, float* C,
+                      int64_t ldc, int64_t split_stride, hipStream_t s);
+
+// dW (=|+=) A B^T in fp32.
+hipError_t gemm_dw(int dtype, const void* A, int64_t lda, const void* B, int64_t ldb, int64_t M,
+                   int64_t N, int64_t K, float* C, int64_t ldc, int accumulate, hipStream_t s);
+
+int gemm_k_tile(int dtype);
+
+// dst[c][r] = src[r][c] for r < R, 0 for R <= r < Rpad; c < C.
+hipError_t transpose_pad(int dtype, const void* src, int64_t ld_src, int64_t R, int64_t C,
+                         void* dst, int64_t Rpad, hipStream_t s);
+
+struct CombineArgs {
+  // inputs
+  const void* h;  // [N,H] full batch
+  const void* W;  // [V,H]
+  const int32_t* labels;
+  const float* infer_lp;
+  const float* adv;
+  const int64_t* off;  // device offsets [N+1] or null
+  const int32_t* ids;
+  const float* u;
+  const float* logq;  // may be null
+  const float *part_m, *part_s, *part_t;  // [Tc, J]
+  int64_t t0, Tc, N, H, V, J, nnz;
+  WeightParams wp;
+  float adv_tau, beta, inv_t, inv_D;
+  // outputs (global token index)
+  float* lse;         // [N]
+  float* kappa_s;     // [N] kappa_t * inv_t / D
+  float* stats;       // [N, 8] per-token reduction inputs
+  float* coef;        // [N + nnz] gradient coefficient of label / entry (times inv_t / D)
+  float* o_logprobs;  // nullable
+  float* o_entropy;
+  float* o_weight;
+  uint8_t* o_keep;
+  float* o_token_loss;
+  float* o_support_lp;  // [nnz] nullable
+};
+constexpr int STAT_LOSS = 0, STAT_MASKED = 1, STAT_SMASS = 2, STAT_HAS_SUPPORT = 3,
+              STAT_TVFAIL = 4, STAT_KL = 5, STAT_ABS_KAPPA = 6, STAT_ENTROPY = 7, STAT_N = 8;
+hipError_t combine(int dtype, const CombineArgs& a, hipStream_t s);
+
+// G^T (in place over Pt) and G from Pt = exp(z - m_tile):
+// g = kappa_s[t] * exp(m[t, v / FWD_VTILE] - lse[t]) * Pt[v, t].
+hipError_t form_g(int dtype, void* Pt, int64_t ldp, void* G, int64_t ldg, const float* part_m,
+                  int64_t J, const float* lse_c, const float* kappa_c, int64_t V, int64_t Vpad,
+                  int64_t Tc, int64_t Tcpad, hipStream_t s);
+
+// dh[t] = sum_s part[s][t] + sum over label/entries of coef * W[v] ; grad dtype.
+hipError_t finalize_dh(int dtype, int grad_dtype, const float* part, int splits,
+                       int64_t split_stride, const void* W, const int32_t* labels,
+                       const int64_t* off, const int32_t* ids, const float* coef, int64_t t0,
+                       int64_t Tc, int64_t N, int64_t nnz, int64_t V, int64_t H, void* dh,
+                       hipStream_t s);
+
+hipError_t reduce_final(const float* stats, int64_t N, float inv_D, float beta, float* loss,
+                        float* metrics, hipStream_t s);
+
+// CSR entry -> row index.
+hipError_t csr_rows(const int64_t* off, int64_t N, int64_t nnz, int32_t* row_of, hipStream_t s);
+
+// Vocab-major bucketing of the N + nnz gradient entries (labels first, then
+// support entries), stable in entry order.  Writes start[V+2] (bucket V holds
+// out-of-range ids) and the sorted entry permutation.
+struct CscWork {
+  int32_t *keys_a, *keys_b, *idx_a, *idx_b, *hist, *start;
+  int64_t hist_len;
+};
+int64_t csc_hist_len(int64_t E);
+hipError_t csc_build(const int32_t* labels, const int32_t* ids, int64_t N, int64_t nnz,
+                     int64_t V, const CscWork& w, const int32_t** perm_out, hipStream_t s);
+
+// dW[v] (=|+=) sum over entries in bucket v of coef * h[tok].
+hipError_t sparse_dw(int dtype, const void* h, int64_t H, int64_t N, int64_t V,
+                     const int32_t* start, const int32_t* perm, const int32_t* row_of,
+                     const float* coef, float* dW, int overwrite, hipStream_t s);
+
+hipError_t fill_f32(float* p, int64_t n, float v, hipStream_t s);
+
+// Loss-only replay.
+int64_t elem_num_blocks(int64_t N);
+hipError_t elementwise(const float* lp, const float* lq, const float* adv, int64_t N,
+                       const rl_elem_cfg& c, uint16_t* word, float* w_primary, double* partials,
+                       double* sums, hipStream_t s);
+
+// Validation.
+hipError_t validate(int64_t N, int64_t V, int64_t nnz, const int32_t* labels,
+                    const float* infer_lp, const float* adv, const int64_t* off,
+                    const int32_t* ids, const float* u, const float* logq, int replayed,
+                    int32_t* flags, hipStream_t s);
+
+}  // namespace rl

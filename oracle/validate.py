@@ -16,7 +16,10 @@ the ones below follow from what the loss needs of its inputs:
   bit 6  replayed: a row that does not hold its own label
   bit 7  an advantage not finite
   bit 8  device offsets not a valid CSR (off[0] != 0, decreasing,
-         off[N] != nnz)
+         off[N] != nnz, or a row outside [0, nnz])
+
+Entry checks (bits 1-3) do not depend on the offsets and always run; the
+replayed-row checks (bits 5-6) run on every row whose own offsets are sane.
 """
 
 import numpy as np
@@ -52,8 +55,19 @@ def validate_reference(V, labels, infer_logprobs, adv, offsets=None, ids=None, u
     off = np.asarray(offsets, np.int64)
     ids = np.asarray(ids, np.int64)
     nnz = len(ids)
-    if off[0] != 0 or np.any(np.diff(off) < 0) or off[N] != nnz:
-        return flags | BAD_OFFSETS
+
+    def row_sane(t):
+        e0, e1 = off[t], off[t + 1]
+        ok = 0 <= e0 <= e1 <= nnz
+        if t == 0 and e0 != 0:
+            ok = False
+        if t == N - 1 and e1 != nnz:
+            ok = False
+        return ok
+
+    sane = [row_sane(t) for t in range(N)]
+    if not all(sane):
+        flags |= BAD_OFFSETS
     if np.any((ids < 0) | (ids >= V)):
         flags |= BAD_ID
     uu = np.asarray(u, np.float32).astype(np.float64)
@@ -65,6 +79,8 @@ def validate_reference(V, labels, infer_logprobs, adv, offsets=None, ids=None, u
             flags |= BAD_LOGQ
     if replayed:
         for t in range(N):
+            if not sane[t]:
+                continue
             e0, e1 = off[t], off[t + 1]
             s = uu[e0:e1].sum()
             if not abs(s - 1.0) <= REPLAY_MASS_TOL:

@@ -37,7 +37,7 @@ def test_clean_support_has_no_flags():
     (lambda d: d["u"].__setitem__(0, 0.4), ov.BAD_REPLAY_MASS),
     (lambda d: d["labels"].__setitem__(2, 8), ov.BAD_REPLAY_LABEL),
     (lambda d: d["adv"].__setitem__(0, np.inf), ov.BAD_ADV),
-    (lambda d: d["offsets"].__setitem__(1, 5), ov.BAD_OFFSETS),
+    (lambda d: d["offsets"].__setitem__(1, 5), ov.BAD_OFFSETS | ov.BAD_REPLAY_MASS),
     (lambda d: d["offsets"].__setitem__(3, 4), ov.BAD_OFFSETS),
 ])
 def test_each_violation_sets_its_bit(mutate, bit):
