@@ -1,0 +1,263 @@
+#!/usr/bin/env python3
+"""Benchmark of the fused LM head + RLLoss forward and backward on one MI355X.
+
+One step = one pass of the hot path over one batch of synthetic input that is
+already resident in HBM: the sampler-evidence validation of the batch, then
+rl_loss_fwd_bwd (LM-head GEMM with online log-sum-exp, per-token log-probs,
+entropy, weights, loss, dense backward dh and dW).  Default workload: 16384
+tokens, H=2048, V=152064, bf16, IPO eps 0.3, no support.
+
+Prints ONE JSON line (rank 0).  `roofline` is for the kernel with the largest
+summed time, timed with HIP events around each of its launches on the launch
+stream inside the timed region (rl_profile_begin / rl_profile_end).
+`cpu_baseline` times the fp64 oracle on a bounded token sample of the same
+workload on the host cores.
+"""
+
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "tokens/s fused LM-head+RLLoss fwd+bwd (H=2048,V=152k) + % bf16 MFMA peak"
+PEAK_BF16_TFLOPS = 2500.0  # MI355X dense bf16 MFMA
+PEAK_FP32_TFLOPS = 157.3
+PEAK_HBM_GBS = 8000.0
+GEMMS = ("gemm_fwd", "gemm_dh", "gemm_dw")
+KERNEL_SOURCES = ("gemm.hip", "common.h", "kernels.h")
+
+
+def kernel_src_sha() -> str:
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, "lm_head_logprobs_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def read_traffic(kernel: str, workload: str):
+    """HBM bytes per launch from the committed rocprofv3 counter summary, if it
+    was taken on the current kernel sources; else None."""
+    path = os.path.join(ROOT, "profiles", f"{kernel}_{workload}_traffic.txt")
+    if not os.path.exists(path):
+        return None
+    vals = {}
+    with open(path) as f:
+        for line in f:
+            if ":" in line and not line.startswith("#"):
+                k, v = line.split(":", 1)
+                vals[k.strip()] = v.strip()
+    if vals.get("kernel_src_sha") != kernel_src_sha():
+        return None
+    try:
+        return float(vals["hbm_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
+def cpu_baseline(wl, target_s: float, seed: int = 0):
+    import numpy as np
+    from threadpoolctl import threadpool_info, threadpool_limits
+
+    from oracle import head as ohead
+
+    cores = len(os.sched_getaffinity(0))
+    d = wl.to_host_numpy()
+    h64 = d["h"].astype(np.float64)
+    W64 = d["W"].astype(np.float64)
+    rng = np.random.default_rng(seed)
+    args = (d["labels"], d["infer_logprobs"], d["adv"], wl.params)
+    kw = dict(offsets=d["offsets"], ids=d["ids"], u=d["u"], logq=d["logq"], want_grads=True,
+              chunk=64)
+    with threadpool_limits(limits=cores):
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+        n0 = 16
+        tok = np.sort(rng.choice(wl.N, n0, replace=False))
+        t0 = time.perf_counter()
+        ohead.head_reference(h64, W64, *args, tokens=tok, **kw)
+        dt0 = time.perf_counter() - t0
+        n = int(min(max(16, round(n0 * target_s / max(dt0, 1e-3))), wl.N, 2048))
+        tok = np.sort(rng.choice(wl.N, n, replace=False))
+        t0 = time.perf_counter()
+        ohead.head_reference(h64, W64, *args, tokens=tok, **kw)
+        dt = time.perf_counter() - t0
+    return {
+        "value": n / dt,
+        "unit": "tokens/s",
+        "cores": int(threads),
+        "kind": "oracle",
+        "sample": (f"{n} of {wl.N} tokens of the same workload (full H={wl.H}, V={wl.V}), "
+                   f"fp64 forward + dense backward (dh rows, dW from those tokens), "
+                   f"{dt:.1f} s on {cores} host cores"),
+    }
+
+
+def bench_head(args, torch):
+    from lm_head_logprobs_amd import _lib as L
+    from lm_head_logprobs_amd import ops
+    from synth import make_head
+
+    dev = torch.device("cuda:0")
+    wl = make_head(args.workload, device=dev)
+    fh = ops.FusedHead(wl.h, wl.W, wl.labels, wl.infer_logprobs, wl.adv, wl.params, wl.offsets,
+                       wl.ids, wl.u, wl.logq, token_chunk=args.token_chunk)
+    flags = torch.zeros(1, device=dev, dtype=torch.int32)
+
+    def step():
+        L.rl_validate_support(wl.N, wl.V, wl.nnz, wl.labels, wl.infer_logprobs, wl.adv,
+                              fh.offsets_host, fh.offsets_dev, wl.ids, wl.u, wl.logq,
+                              wl.params["replayed"], flags)
+        fh()
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    if int(flags.item()) != 0:
+        raise RuntimeError(f"validation flags {int(flags.item()):#x} on the synthetic batch")
+    L.rl_profile_begin()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    e0.record()
+    for _ in range(args.steps):
+        step()
+    e1.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    prof = L.rl_profile_end()
+    ms = e0.elapsed_time(e1) / args.steps
+    N, H, V = wl.N, wl.H, wl.V
+    value = N / (ms * 1e-3)
+    flops_6nhv = 6.0 * N * H * V
+    peak = PEAK_BF16_TFLOPS if wl.dtype == "bf16" else PEAK_FP32_TFLOPS
+    kernels = {k: {"launches": n, "avg_ms": t / n, "ms_per_step": t / args.steps}
+               for k, (n, t) in sorted(prof.items(), key=lambda kv: -kv[1][1])}
+    dom = max(prof, key=lambda k: prof[k][1])
+    n_launch, tot_ms = prof[dom]
+    avg_ms = tot_ms / n_launch
+    roof = None
+    if dom in GEMMS:
+        work = 2.0 * N * H * V * args.steps  # each GEMM contracts N x H x V once per step
+        achieved = work / (tot_ms * 1e-3) / 1e12
+        traffic = read_traffic(dom, args.workload)
+        roof = {"bound": "mfma", "achieved": achieved, "peak": peak, "unit": "TFLOP/s",
+                "frac": achieved / peak, "traffic": traffic, "kernel": dom,
+                "avg_launch_ms": avg_ms, "algorithmic_tflop_per_launch": 2.0 * N * H * V /
+                n_launch * args.steps / 1e12}
+    out = {
+        "metric": METRIC,
+        "value": value,
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": wl.dtype,
+        "data": "synthetic",
+        "config": {"workload": args.workload, "tokens": N, "H": H, "V": V,
+                   "loss": wl.params["loss_type"], "support_nnz": wl.nnz,
+                   "kl": wl.params["kl_estimator"], "backward": wl.params["backward"],
+                   "token_chunk": fh.cfg.token_chunk or min(N, 16384)},
+        "mfma_frac_6nhv": flops_6nhv / (ms * 1e-3) / 1e12 / peak,
+        "roofline": roof,
+        "kernels": kernels,
+        "wall_s_timed": wall,
+    }
+    return out, wl
+
+
+def bench_replay(args, torch):
+    from lm_head_logprobs_amd import _lib as L
+    from lm_head_logprobs_amd import ops
+    from synth import make_replay
+
+    r = make_replay(device="cuda:0")
+    # Rotate over independent copies (> 620 MB) so every pass reads HBM, not the
+    # 256 MB Infinity Cache.
+    copies = [ops.Replay(r.lp.clone(), r.lq.clone(), r.adv.clone(), r.params) for _ in range(16)]
+    for i in range(args.warmup):
+        copies[i % 16]()
+    torch.cuda.synchronize()
+    L.rl_profile_begin()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for i in range(args.steps):
+        copies[i % 16]()
+    e1.record()
+    torch.cuda.synchronize()
+    prof = L.rl_profile_end()
+    ms = e0.elapsed_time(e1) / args.steps
+    n, tot = prof["elementwise"]
+    avg = tot / n
+    byt = 18.0 * r.N
+    achieved = byt / (avg * 1e-3) / 1e9
+    return {
+        "metric": "tokens/s loss-only mismatch replay (fp32 elementwise)",
+        "value": r.N / (ms * 1e-3), "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": ms, "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "fp32", "data": "synthetic",
+        "config": {"workload": "c2_replay", "tokens": r.N},
+        "roofline": {"bound": "hbm", "achieved": achieved, "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                     "frac": achieved / PEAK_HBM_GBS,
+                     "traffic": read_traffic("elementwise", "c2_replay"),
+                     "kernel": "elementwise (main + final reduction)", "avg_launch_ms": avg},
+        "cpu_baseline": None,
+    }, None
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="c3_head16k_ipo",
+                    help="c3_head16k_ipo (default), c4_head16k_ipo_topp_replay, "
+                         "c5a_head64k_draws_ipo_k1, c5b_head64k_draws_reinforce, c2_replay")
+    ap.add_argument("--token-chunk", type=int, default=0)
+    ap.add_argument("--cpu-seconds", type=float, default=15.0,
+                    help="target length of the oracle CPU baseline sample")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="also run a plain 1 GiB device copy (counter calibration)")
+    args = ap.parse_args()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py: this build runs on one GPU only; --gpus N > 1 is not supported "
+              "(how the path would shard across GPUs is described in DESIGN.md)",
+              file=sys.stderr)
+        sys.exit(2)
+    import torch
+
+    if not torch.cuda.is_available():
+        print("bench.py: no GPU visible", file=sys.stderr)
+        sys.exit(1)
+    if args.workload == "c2_replay":
+        out, wl = bench_replay(args, torch)
+    else:
+        out, wl = bench_head(args, torch)
+    if args.copy_calibration:
+        a = torch.empty(1 << 28, device="cuda:0", dtype=torch.float32)
+        b = torch.empty_like(a)
+        b.copy_(a)
+        torch.cuda.synchronize()
+    if wl is not None:
+        out["cpu_baseline"] = (None if args.no_cpu_baseline
+                               else cpu_baseline(wl, args.cpu_seconds))
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -277,6 +277,24 @@ rl_status rl_validate_support_sync(int64_t N, int64_t V, int64_t nnz, const int3
                                    const float* csr_u, const float* csr_logq, int32_t replayed,
                                    int32_t* flags_dev, int32_t* flags_host, void* stream);
 
+/* ---------------------------------------------------------------------------
+ * Opt-in kernel timing.  Between rl_profile_begin and rl_profile_end every
+ * kernel the library enqueues is bracketed by two hipEvents on the caller's
+ * stream; rl_profile_end waits for those events and reports, per kernel name,
+ * the number of launches and the summed event-to-event time.  Off by default;
+ * when off no event is recorded.  Process-wide; calls are serialised.
+ * ------------------------------------------------------------------------ */
+typedef struct rl_profile_entry {
+  char name[32];      /* kernel (launch site) name, NUL-terminated */
+  int64_t launches;
+  double total_ms;
+} rl_profile_entry;
+
+rl_status rl_profile_begin(void);
+/* Writes at most max_entries entries; *n_entries receives the number of
+ * kernel names seen.  Errors: RL_E_ARG (null), RL_E_HIP. */
+rl_status rl_profile_end(rl_profile_entry* out, int32_t max_entries, int32_t* n_entries);
+
 /* Static description of a status code; never NULL. */
 const char* rl_status_string(rl_status s);
 

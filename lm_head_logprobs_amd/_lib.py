@@ -33,6 +33,8 @@ EXPORTED = (
     "rl_loss_elementwise",
     "rl_validate_support",
     "rl_validate_support_sync",
+    "rl_profile_begin",
+    "rl_profile_end",
     "rl_status_string",
     "rl_version",
 )
@@ -72,6 +74,11 @@ class RlElemCfg(ctypes.Structure):
 class RlElemOut(ctypes.Structure):
     _fields_ = [("mask_word", ctypes.c_void_p), ("w_primary", ctypes.c_void_p),
                 ("sums", ctypes.c_void_p)]
+
+
+class RlProfileEntry(ctypes.Structure):
+    _fields_ = [("name", ctypes.c_char * 32), ("launches", ctypes.c_int64),
+                ("total_ms", ctypes.c_double)]
 
 
 class RlError(RuntimeError):
@@ -115,6 +122,11 @@ def lib() -> ctypes.CDLL:
         L.rl_status_string.restype = ctypes.c_char_p
         L.rl_version.argtypes = []
         L.rl_version.restype = ctypes.c_char_p
+        L.rl_profile_begin.argtypes = []
+        L.rl_profile_begin.restype = ctypes.c_int
+        L.rl_profile_end.argtypes = [ctypes.POINTER(RlProfileEntry), i32,
+                                     ctypes.POINTER(ctypes.c_int32)]
+        L.rl_profile_end.restype = ctypes.c_int
         _lib = L
     return _lib
 
@@ -209,3 +221,20 @@ def rl_validate_support_sync(N, V, nnz, labels, infer_logprobs, adv, csr_offsets
     if st not in (RL_OK, RL_E_INVALID_INPUT):
         raise RlError(st, "rl_validate_support_sync")
     return st, f.value
+
+
+def rl_profile_begin() -> None:
+    st = lib().rl_profile_begin()
+    if st != RL_OK:
+        raise RlError(st, "rl_profile_begin")
+
+
+def rl_profile_end() -> dict:
+    """{kernel name: (launches, total_ms)} since rl_profile_begin."""
+    arr = (RlProfileEntry * 64)()
+    n = ctypes.c_int32(0)
+    st = lib().rl_profile_end(arr, 64, ctypes.byref(n))
+    if st != RL_OK:
+        raise RlError(st, "rl_profile_end")
+    return {arr[i].name.decode(): (int(arr[i].launches), float(arr[i].total_ms))
+            for i in range(min(n.value, 64))}

@@ -16,12 +16,60 @@
 // the fixed-order loss and metric reduction.
 #include <cmath>
 #include <cstring>
+#include <mutex>
+#include <vector>
 
 #include "kernels.h"
 
 namespace {
 
 using namespace rl;
+
+// ---- opt-in event timing of every launch site --------------------------------
+enum ProfKind {
+  K_GEMM_FWD, K_COMBINE, K_FORM_G, K_GEMM_DH, K_TRANSPOSE_H, K_GEMM_DW, K_FINALIZE_DH,
+  K_TRANSPOSE_W, K_CSR_ROWS, K_CSC_BUILD, K_SPARSE_DW, K_REDUCE, K_ELEMENTWISE, K_VALIDATE,
+  K_COUNT
+};
+const char* const kProfNames[K_COUNT] = {
+    "gemm_fwd",   "combine",   "form_g",   "gemm_dh",   "transpose_h",
+    "gemm_dw",    "finalize_dh", "transpose_w", "csr_rows", "csc_build",
+    "sparse_dw",  "reduce",    "elementwise", "validate"};
+
+struct ProfRec {
+  int kind;
+  hipEvent_t a, b;
+};
+std::mutex g_prof_mu;
+bool g_prof_on = false;
+std::vector<ProfRec> g_prof_recs;
+std::vector<hipEvent_t> g_prof_pool;
+
+hipEvent_t prof_event() {
+  if (!g_prof_pool.empty()) {
+    hipEvent_t e = g_prof_pool.back();
+    g_prof_pool.pop_back();
+    return e;
+  }
+  hipEvent_t e = nullptr;
+  if (hipEventCreate(&e) != hipSuccess) return nullptr;
+  return e;
+}
+
+template <class F>
+hipError_t timed(int kind, hipStream_t s, F&& f) {
+  if (!g_prof_on) return f();
+  std::lock_guard<std::mutex> lk(g_prof_mu);
+  hipEvent_t a = prof_event(), b = prof_event();
+  if (a == nullptr || b == nullptr) return hipErrorOutOfMemory;
+  hipError_t e = hipEventRecord(a, s);
+  if (e != hipSuccess) return e;
+  e = f();
+  if (e != hipSuccess) return e;
+  e = hipEventRecord(b, s);
+  g_prof_recs.push_back({kind, a, b});
+  return e;
+}
 
 constexpr size_t WS_ALIGN = 256;
 constexpr int64_t DEFAULT_CHUNK = 16384;
@@ -200,6 +248,49 @@ const char* rl_status_string(rl_status s) {
 
 const char* rl_version(void) { return "rlloss 0.1.0 gfx950"; }
 
+rl_status rl_profile_begin(void) {
+  std::lock_guard<std::mutex> lk(g_prof_mu);
+  for (auto& r : g_prof_recs) {
+    g_prof_pool.push_back(r.a);
+    g_prof_pool.push_back(r.b);
+  }
+  g_prof_recs.clear();
+  g_prof_on = true;
+  return RL_OK;
+}
+
+rl_status rl_profile_end(rl_profile_entry* out, int32_t max_entries, int32_t* n_entries) {
+  if (n_entries == nullptr || (out == nullptr && max_entries > 0)) return RL_E_ARG;
+  std::lock_guard<std::mutex> lk(g_prof_mu);
+  g_prof_on = false;
+  int64_t cnt[K_COUNT] = {};
+  double ms[K_COUNT] = {};
+  rl_status st = RL_OK;
+  for (auto& r : g_prof_recs) {
+    float t = 0.0f;
+    if (hipEventSynchronize(r.b) != hipSuccess || hipEventElapsedTime(&t, r.a, r.b) != hipSuccess)
+      st = RL_E_HIP;
+    cnt[r.kind] += 1;
+    ms[r.kind] += t;
+    g_prof_pool.push_back(r.a);
+    g_prof_pool.push_back(r.b);
+  }
+  g_prof_recs.clear();
+  int32_t n = 0;
+  for (int k = 0; k < K_COUNT; ++k) {
+    if (cnt[k] == 0) continue;
+    if (n < max_entries) {
+      std::memset(out[n].name, 0, sizeof(out[n].name));
+      std::strncpy(out[n].name, kProfNames[k], sizeof(out[n].name) - 1);
+      out[n].launches = cnt[k];
+      out[n].total_ms = ms[k];
+    }
+    ++n;
+  }
+  *n_entries = n;
+  return st;
+}
+
 rl_status rl_loss_workspace_size(const rl_loss_cfg* cfg, int32_t has_support, int32_t want_dh,
                                  int32_t want_dW, size_t* bytes) {
   if (cfg == nullptr || bytes == nullptr) return RL_E_ARG;
@@ -257,14 +348,14 @@ rl_status rl_loss_fwd_bwd(const void* h, const void* W, const int32_t* labels,
                         cfg->icepop_hi};
   const float inv_D = 1.0f / cfg->loss_norm;
 
-  if (p.dense && p.want_dh) RL_TRY(transpose_pad(p.dtype, W, p.H, p.V, p.H, Wt, p.Vpad, s));
+  if (p.dense && p.want_dh) RL_TRY(timed(K_TRANSPOSE_W, s, [&] { return transpose_pad(p.dtype, W, p.H, p.V, p.H, Wt, p.Vpad, s); }));
 
   for (int64_t c0 = 0; c0 < p.N; c0 += p.Tc) {
     const int64_t tc = std::min(p.Tc, p.N - c0);
     const int64_t tck = round_up(tc, 64);
     const void* hc = hb + c0 * p.H * p.esz;
     FwdEpiArgs fa{cfg->inv_temperature, p.V, tc, p.J, pm, ps, pt, Pt, p.Tcpad};
-    RL_TRY(gemm_fwd(p.dtype, W, hc, p.V, tc, p.H, fa, s));
+    RL_TRY(timed(K_GEMM_FWD, s, [&] { return gemm_fwd(p.dtype, W, hc, p.V, tc, p.H, fa, s); }));
     CombineArgs ca{};
     ca.h = h;
     ca.W = W;
@@ -300,36 +391,51 @@ rl_status rl_loss_fwd_bwd(const void* h, const void* W, const int32_t* labels,
     ca.o_keep = out->keep;
     ca.o_token_loss = out->token_loss;
     ca.o_support_lp = has_support ? out->support_logprobs : nullptr;
-    RL_TRY(combine(p.dtype, ca, s));
+    RL_TRY(timed(K_COMBINE, s, [&] { return combine(p.dtype, ca, s); }));
     if (p.dense) {
-      RL_TRY(form_g(p.dtype, Pt, p.Tcpad, G, p.Vpad, pm, p.J, lse + c0, kap + c0, p.V, p.Vpad, tc,
-                    tck, s));
+      RL_TRY(timed(K_FORM_G, s, [&] {
+        return form_g(p.dtype, Pt, p.Tcpad, G, p.Vpad, pm, p.J, lse + c0, kap + c0, p.V, p.Vpad,
+                      tc, tck, s);
+      }));
       if (p.want_dh)
-        RL_TRY(gemm_store(p.dtype, G, p.Vpad, Wt, p.Vpad, tc, p.H, p.Vpad, p.splits, p.k_split,
-                          dhp, p.H, p.Tc * p.H, s));
+        RL_TRY(timed(K_GEMM_DH, s, [&] {
+          return gemm_store(p.dtype, G, p.Vpad, Wt, p.Vpad, tc, p.H, p.Vpad, p.splits, p.k_split,
+                            dhp, p.H, p.Tc * p.H, s);
+        }));
       if (p.want_dW) {
-        RL_TRY(transpose_pad(p.dtype, hc, p.H, tc, p.H, ht, tck, s));
+        RL_TRY(timed(K_TRANSPOSE_H, s,
+                     [&] { return transpose_pad(p.dtype, hc, p.H, tc, p.H, ht, tck, s); }));
         const int acc = (c0 > 0 || cfg->accumulate_dW) ? 1 : 0;
-        RL_TRY(gemm_dw(p.dtype, Pt, p.Tcpad, ht, tck, p.V, p.H, tck, out->dW, p.H, acc, s));
+        RL_TRY(timed(K_GEMM_DW, s, [&] {
+          return gemm_dw(p.dtype, Pt, p.Tcpad, ht, tck, p.V, p.H, tck, out->dW, p.H, acc, s);
+        }));
       }
     }
     if (p.want_dh)
-      RL_TRY(finalize_dh(p.dtype, p.gdtype, dhp, p.dense ? p.splits : 0, p.Tc * p.H, W, labels,
-                         has_support ? csr_offsets_dev : nullptr, csr_ids, coef, c0, tc, p.N,
-                         p.nnz, p.V, p.H, out->dh, s));
+      RL_TRY(timed(K_FINALIZE_DH, s, [&] {
+        return finalize_dh(p.dtype, p.gdtype, dhp, p.dense ? p.splits : 0, p.Tc * p.H, W, labels,
+                           has_support ? csr_offsets_dev : nullptr, csr_ids, coef, c0, tc, p.N,
+                           p.nnz, p.V, p.H, out->dh, s);
+      }));
   }
   if (p.want_dW) {
     CscWork cw{I(p.o_ka), I(p.o_kb), I(p.o_ia), I(p.o_ib), I(p.o_hist), I(p.o_start),
                csc_hist_len(p.E)};
     int32_t* rows = has_support ? I(p.o_rows) : nullptr;
-    if (has_support) RL_TRY(csr_rows(csr_offsets_dev, p.N, p.nnz, rows, s));
+    if (has_support)
+      RL_TRY(timed(K_CSR_ROWS, s, [&] { return csr_rows(csr_offsets_dev, p.N, p.nnz, rows, s); }));
     const int32_t* perm = nullptr;
-    RL_TRY(csc_build(labels, csr_ids, p.N, p.nnz, p.V, cw, &perm, s));
+    RL_TRY(timed(K_CSC_BUILD, s,
+                 [&] { return csc_build(labels, csr_ids, p.N, p.nnz, p.V, cw, &perm, s); }));
     const int overwrite = (!p.dense && !cfg->accumulate_dW) ? 1 : 0;
-    RL_TRY(sparse_dw(p.dtype, h, p.H, p.N, p.V, cw.start, perm, rows, coef, out->dW, overwrite,
-                     s));
+    RL_TRY(timed(K_SPARSE_DW, s, [&] {
+      return sparse_dw(p.dtype, h, p.H, p.N, p.V, cw.start, perm, rows, coef, out->dW, overwrite,
+                       s);
+    }));
   }
-  RL_TRY(reduce_final(stats, p.N, inv_D, p.beta, out->loss, out->metrics, s));
+  RL_TRY(timed(K_REDUCE, s, [&] {
+    return reduce_final(stats, p.N, inv_D, p.beta, out->loss, out->metrics, s);
+  }));
   return RL_OK;
 }
 
@@ -364,9 +470,11 @@ rl_status rl_loss_elementwise(const float* lp, const float* lq, const float* adv
   rl_elementwise_workspace_size(N, &need);
   if (workspace == nullptr || workspace_bytes < need || !aligned(workspace, 16))
     return RL_E_WORKSPACE;
-  RL_TRY(rl::elementwise(lp, lq, adv, N, *cfg, out->mask_word, out->w_primary,
-                         static_cast<double*>(workspace), out->sums,
-                         static_cast<hipStream_t>(stream)));
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  RL_TRY(timed(K_ELEMENTWISE, s, [&] {
+    return rl::elementwise(lp, lq, adv, N, *cfg, out->mask_word, out->w_primary,
+                           static_cast<double*>(workspace), out->sums, s);
+  }));
   return RL_OK;
 }
 
@@ -386,9 +494,12 @@ rl_status rl_validate_support(int64_t N, int64_t V, int64_t nnz, const int32_t* 
   } else if (nnz != 0) {
     return RL_E_ARG;
   }
-  RL_TRY(rl::validate(N, V, nnz, labels, infer_logprobs, adv,
-                      has_support ? csr_offsets_dev : nullptr, csr_ids, csr_u, csr_logq,
-                      replayed ? 1 : 0, flags_dev, static_cast<hipStream_t>(stream)));
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  RL_TRY(timed(K_VALIDATE, s, [&] {
+    return rl::validate(N, V, nnz, labels, infer_logprobs, adv,
+                        has_support ? csr_offsets_dev : nullptr, csr_ids, csr_u, csr_logq,
+                        replayed ? 1 : 0, flags_dev, s);
+  }));
   return RL_OK;
 }
 

@@ -27,7 +27,7 @@ def _declared():
 
 def test_every_declared_symbol_is_exported():
     names = _declared()
-    assert len(names) == 8
+    assert len(names) == 10
     out = subprocess.run(["nm", "-D", "--defined-only", L.LIB_PATH], capture_output=True,
                          text=True, check=True).stdout
     exported = {ln.split()[-1] for ln in out.splitlines() if " T " in ln}
@@ -42,6 +42,13 @@ def test_status_strings_and_version():
         assert len(L.status_string(s)) >= 2
     assert "unknown" in L.status_string(99)
     assert "gfx950" in L.rl_version()
+
+
+def test_profile_calls_without_launches():
+    L.rl_profile_begin()
+    assert L.rl_profile_end() == {}
+    n = ctypes.c_int32(0)
+    assert L.lib().rl_profile_end(None, 4, ctypes.byref(n)) == L.RL_E_ARG
 
 
 def test_struct_layout_matches_header():
