@@ -4,12 +4,12 @@
 // Tc rows sliced from the batch with host offsets, so no device value is read
 // back.  Per chunk:
 //   1. forward GEMM  S^T = W h_c^T  (MFMA) with an online-softmax epilogue:
-//      per (token, 128-row vocabulary tile) the max m, sum e^(z-m) and
-//      sum e^(z-m)(z-m); and, for a dense backward, Pt = e^(z-m) [V, Tc]
+//      per (token, 256-row vocabulary tile) the max m, sum e^(z-m) and
+//      sum e^(z-m)(z-m); and, for a dense backward, P = e^(z-m) [Tc, V]
 //   2. combine: per token LSE and entropy from the partials, label and
 //      support logits by fp32 dot products, weights, KL, loss, kappa and the
 //      per-entry gradient coefficients
-//   3. dense backward only: form G (= kappa/D p) from Pt in both layouts,
+//   3. dense backward only: form G (= kappa/D p) from P in both layouts,
 //      dh partials = G (W^T)^T split over V, dW (+)= G^T (h_c^T)^T
 //   4. dh = partials + label/support rows of W scaled by their coefficients
 // After the chunks: the label/support terms of dW via vocabulary buckets, then
@@ -104,7 +104,8 @@ struct Plan {
   int splits;
   int64_t k_split;
   size_t o_pm, o_ps, o_pt, o_lse, o_kap, o_stats, o_coef;
-  size_t o_Pt, o_G, o_Wt, o_ht, o_dhp;
+  size_t o_P, o_Gt, o_Wt, o_ht, o_dhp;
+  int vtile;
   size_t o_ka, o_kb, o_ia, o_ib, o_hist, o_start, o_rows;
   size_t total;
 };
@@ -165,8 +166,9 @@ rl_status make_plan(const rl_loss_cfg* c, bool has_support, bool want_dh, bool w
   p->dense = mode == RL_BWD_DENSE && (p->want_dh || p->want_dW);
   p->Tc = c->token_chunk > 0 ? std::min(c->token_chunk, c->N) : std::min(DEFAULT_CHUNK, c->N);
   p->Tcpad = round_up(p->Tc, 64);
-  p->Vpad = round_up(p->V, 64);
-  p->J = ceil_div(p->V, FWD_VTILE);
+  p->Vpad = round_up(p->V, 256);
+  p->vtile = fwd_vtile(p->dtype);
+  p->J = ceil_div(p->V, p->vtile);
   const int bk = gemm_k_tile(p->dtype);
   {
     const int64_t tiles = ceil_div(p->Tc, 128) * ceil_div(p->H, 128);
@@ -183,21 +185,22 @@ rl_status make_plan(const rl_loss_cfg* c, bool has_support, bool want_dh, bool w
   p->o_kap = L.take(p->N, 4);
   p->o_stats = L.take(p->N, 4 * STAT_N);
   p->o_coef = L.take(p->E, 4);
-  p->o_Pt = p->o_G = p->o_Wt = p->o_ht = p->o_dhp = 0;
+  p->o_P = p->o_Gt = p->o_Wt = p->o_ht = p->o_dhp = 0;
   if (p->dense) {
-    int64_t vt;
-    if (!mul_ok(p->V, p->Tcpad, &vt)) return RL_E_ARG;
-    p->o_Pt = L.take(vt, p->esz);
+    int64_t vt, tv;
+    if (!mul_ok(p->V, p->Tcpad, &vt) || !mul_ok(p->Tc, p->Vpad, &tv)) return RL_E_ARG;
+    p->o_P = L.take(tv, p->esz);  // e^(z - m) token-major, then G in place
+    if (p->want_dW) {
+      p->o_Gt = L.take(vt, p->esz);
+      p->o_ht = L.take(p->H * p->Tcpad, p->esz);
+    }
     if (p->want_dh) {
-      int64_t tv, hv, sth;
-      if (!mul_ok(p->Tc, p->Vpad, &tv) || !mul_ok(p->H, p->Vpad, &hv) ||
-          !mul_ok((int64_t)p->splits * p->Tc, p->H, &sth))
+      int64_t hv, sth;
+      if (!mul_ok(p->H, p->Vpad, &hv) || !mul_ok((int64_t)p->splits * p->Tc, p->H, &sth))
         return RL_E_ARG;
-      p->o_G = L.take(tv, p->esz);
       p->o_Wt = L.take(hv, p->esz);
       p->o_dhp = L.take(sth, 4);
     }
-    if (p->want_dW) p->o_ht = L.take(p->H * p->Tcpad, p->esz);
   }
   p->o_ka = p->o_kb = p->o_ia = p->o_ib = p->o_hist = p->o_start = p->o_rows = 0;
   if (p->want_dW) {
@@ -337,8 +340,8 @@ rl_status rl_loss_fwd_bwd(const void* h, const void* W, const int32_t* labels,
   auto I = [&](size_t o) { return reinterpret_cast<int32_t*>(ws + o); };
   float *pm = F(p.o_pm), *ps = F(p.o_ps), *pt = F(p.o_pt);
   float *lse = F(p.o_lse), *kap = F(p.o_kap), *stats = F(p.o_stats), *coef = F(p.o_coef);
-  void* Pt = p.dense ? ws + p.o_Pt : nullptr;
-  void* G = (p.dense && p.want_dh) ? ws + p.o_G : nullptr;
+  void* P = p.dense ? ws + p.o_P : nullptr;
+  void* Gt = (p.dense && p.want_dW) ? ws + p.o_Gt : nullptr;
   void* Wt = (p.dense && p.want_dh) ? ws + p.o_Wt : nullptr;
   void* ht = (p.dense && p.want_dW) ? ws + p.o_ht : nullptr;
   float* dhp = (p.dense && p.want_dh) ? F(p.o_dhp) : nullptr;
@@ -354,7 +357,7 @@ rl_status rl_loss_fwd_bwd(const void* h, const void* W, const int32_t* labels,
     const int64_t tc = std::min(p.Tc, p.N - c0);
     const int64_t tck = round_up(tc, 64);
     const void* hc = hb + c0 * p.H * p.esz;
-    FwdEpiArgs fa{cfg->inv_temperature, p.V, tc, p.J, pm, ps, pt, Pt, p.Tcpad};
+    FwdEpiArgs fa{cfg->inv_temperature, p.V, tc, p.J, pm, ps, pt, P, p.Vpad};
     RL_TRY(timed(K_GEMM_FWD, s, [&] { return gemm_fwd(p.dtype, W, hc, p.V, tc, p.H, fa, s); }));
     CombineArgs ca{};
     ca.h = h;
@@ -394,12 +397,12 @@ rl_status rl_loss_fwd_bwd(const void* h, const void* W, const int32_t* labels,
     RL_TRY(timed(K_COMBINE, s, [&] { return combine(p.dtype, ca, s); }));
     if (p.dense) {
       RL_TRY(timed(K_FORM_G, s, [&] {
-        return form_g(p.dtype, Pt, p.Tcpad, G, p.Vpad, pm, p.J, lse + c0, kap + c0, p.V, p.Vpad,
-                      tc, tck, s);
+        return form_g(p.dtype, P, p.Vpad, Gt, p.Tcpad, pm, p.J, p.vtile, lse + c0, kap + c0, p.V,
+                      tc, tck, p.want_dh ? 1 : 0, s);
       }));
       if (p.want_dh)
         RL_TRY(timed(K_GEMM_DH, s, [&] {
-          return gemm_store(p.dtype, G, p.Vpad, Wt, p.Vpad, tc, p.H, p.Vpad, p.splits, p.k_split,
+          return gemm_store(p.dtype, P, p.Vpad, Wt, p.Vpad, tc, p.H, p.Vpad, p.splits, p.k_split,
                             dhp, p.H, p.Tc * p.H, s);
         }));
       if (p.want_dW) {
@@ -407,7 +410,7 @@ rl_status rl_loss_fwd_bwd(const void* h, const void* W, const int32_t* labels,
                      [&] { return transpose_pad(p.dtype, hc, p.H, tc, p.H, ht, tck, s); }));
         const int acc = (c0 > 0 || cfg->accumulate_dW) ? 1 : 0;
         RL_TRY(timed(K_GEMM_DW, s, [&] {
-          return gemm_dw(p.dtype, Pt, p.Tcpad, ht, tck, p.V, p.H, tck, out->dW, p.H, acc, s);
+          return gemm_dw(p.dtype, Gt, p.Tcpad, ht, tck, p.V, p.H, tck, out->dW, p.H, acc, s);
         }));
       }
     }

@@ -13,6 +13,7 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef int32_t i32x4 __attribute__((ext_vector_type(4)));
 
 #define RL_WAVE 64
 
@@ -28,8 +29,14 @@ __device__ __forceinline__ uint32_t f32_to_bf16_bits(float f) {
   return u >> 16;
 }
 
+// Two floats to packed bf16 with v_cvt_pk_bf16_f32 (round to nearest even,
+// NaN kept; checked bit for bit against the definition above).
 __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
-  return f32_to_bf16_bits(lo) | (f32_to_bf16_bits(hi) << 16);
+  typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+  bf16x2_t v;
+  v[0] = (__bf16)lo;
+  v[1] = (__bf16)hi;
+  return __builtin_bit_cast(uint32_t, v);
 }
 
 // Element access for the two storage types (bf16 bits or fp32).
@@ -37,7 +44,9 @@ template <typename T> struct Elem;
 template <> struct Elem<bf16_t> {
   static constexpr int VEC = 8;  // elements per 16-byte vector
   __device__ __forceinline__ static float to_f32(bf16_t x) { return bf16_bits_to_f32(x); }
-  __device__ __forceinline__ static bf16_t from_f32(float f) { return (bf16_t)f32_to_bf16_bits(f); }
+  __device__ __forceinline__ static bf16_t from_f32(float f) {
+    return __builtin_bit_cast(bf16_t, (__bf16)f);
+  }
   // Unpack one 16-byte vector to 8 floats.
   __device__ __forceinline__ static void unpack(const u32x4& v, float* out) {
 #pragma unroll

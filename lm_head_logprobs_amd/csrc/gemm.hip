@@ -3,54 +3,35 @@
 // Both operands are K-contiguous ("NT"): A [M,K] and B [N,K] row-major.  The
 // three contractions of the head all take this form once the backward
 // operands are laid out K-contiguous:
-//   forward   S^T[V,Tc]  = W[V,H]     . h_c[Tc,H]^T        (K = H)
-//   dh        dh[Tc,H]   = G[Tc,V]    . (W^T)[H,V]^T       (K = V, split-K)
-//   dW        dW[V,H]    = G^T[V,Tc]  . (h_c^T)[H,Tc]^T    (K = Tc)
-// bf16 inputs use v_mfma_f32_32x32x16_bf16, fp32 inputs v_mfma_f32_32x32x2_f32;
-// both accumulate in fp32 and share the 32x32 accumulator layout
-//   lane l, register r  ->  row 8*(r/4) + 4*(l/32) + r%4,  column l%32.
+//   forward   S^T[V,Tc]  = W[V,H]      . h_c[Tc,H]^T       (K = H)
+//   dh        dh[Tc,H]   = G[Tc,V]     . (W^T)[H,V]^T      (K = V, split-K)
+//   dW        dW[V,H]    = G^T[V,Tc]   . (h_c^T)[H,Tc]^T   (K = Tc)
+// Accumulation is fp32; both MFMA shapes used here share the 32x32
+// accumulator layout  lane l, register r -> row 8*(r/4) + 4*(l/32) + r%4,
+// column l%32.
 //
-// Tiling: a 256-thread workgroup (4 waves as 2x2) owns a BM x BN tile; each
-// wave owns (BM/2) x (BN/2) as 32x32 MFMA blocks.  K advances BK at a time
-// through two LDS buffers: the next tile's global loads are issued before the
-// MFMAs on the current one, then written to the other buffer.  Rows of LDS are
-// padded by 16 bytes.  Workgroups are remapped so that consecutive tiles land
-// on one XCD (dispatch is round-robin over the 8 XCDs) and grouped 8 tiles
-// along M so neighbours share B panels in that XCD's L2.
+// bf16 kernel (the hot path).  A 256-thread workgroup (4 waves as 2x2) owns a
+// 256 x 256 output tile; each wave owns 128 x 128 as 4 x 4 blocks of
+// v_mfma_f32_32x32x16_bf16 with its 256 accumulators in AGPRs.  K advances 32
+// at a time through a 4-stage ring of LDS buffers (32 KB each: A then B).
+// Operand tiles are copied global -> LDS by buffer_load_dwordx4 ... lds: each
+// wave instruction fills 1 KB of LDS (16 bytes per lane, consecutive), no
+// VGPR staging.  Loads run three stages ahead; a stage is waited for with an
+// explicit vmcnt and one barrier.  Out-of-range rows or K columns are given a
+// buffer offset past the descriptor's range, which the hardware reads as zero.
+// In LDS a tile row is 64 bytes (32 bf16 = four 16-byte chunks); chunk c of
+// row r is stored at position c ^ ((r >> 1) & 3), so the 8 lanes of a
+// ds_read_b128 phase that read one chunk of 8 consecutive rows hit disjoint
+// banks.  Workgroups are remapped so consecutive tiles land on one XCD
+// (dispatch is round-robin over the 8 XCDs) and grouped 8 tiles along M so
+// neighbours share B panels in that XCD's L2.
+//
+// fp32 kernel (small problems).  Same tile mapping and epilogues, register
+// staged loads, v_mfma_f32_32x32x2_f32.
 #include "kernels.h"
 
 namespace rl {
 namespace {
-
-template <typename T> struct MM;
-template <> struct MM<bf16_t> {
-  static constexpr int KSTEP = 16;
-  typedef bf16x8 frag_t;
-  __device__ __forceinline__ static f32x16 mma(frag_t a, frag_t b, f32x16 c) {
-    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
-  }
-  // Rows r0..r0+31, K slice k0..k0+15: lane l takes 8 consecutive K values of
-  // row r0 + l%32 starting at k0 + 8*(l/32).  Both operands use the same K map.
-  __device__ __forceinline__ static frag_t load(const bf16_t* s, int ld, int r0, int k0,
-                                                int lane) {
-    return *reinterpret_cast<const frag_t*>(s + (r0 + (lane & 31)) * ld + k0 + 8 * (lane >> 5));
-  }
-};
-template <> struct MM<float> {
-  static constexpr int KSTEP = 2;
-  typedef float frag_t;
-  __device__ __forceinline__ static f32x16 mma(frag_t a, frag_t b, f32x16 c) {
-    return __builtin_amdgcn_mfma_f32_32x32x2f32(a, b, c, 0, 0, 0);
-  }
-  __device__ __forceinline__ static frag_t load(const float* s, int ld, int r0, int k0,
-                                                int lane) {
-    return s[(r0 + (lane & 31)) * ld + k0 + (lane >> 5)];
-  }
-};
-
-template <typename T> struct Tile;
-template <> struct Tile<bf16_t> { static constexpr int BM = 128, BN = 128, BK = 64; };
-template <> struct Tile<float> { static constexpr int BM = 128, BN = 128, BK = 32; };
 
 constexpr int NT = 256;
 constexpr int GROUP_M = 8;
@@ -90,202 +71,162 @@ struct EpiCtx {
   int wave_m;          // 0/1
   int lane;
   int split;
-  float* red;  // LDS scratch, at least 2 * BN * 2 floats
+  char* smem;          // the workgroup's LDS (free once the main loop is done)
+  int smem_bytes;
 };
 
-template <typename T, class Epi>
-__global__ void __launch_bounds__(NT) gemm_nt_kernel(const T* __restrict__ A, int64_t lda,
-                                                     const T* __restrict__ B, int64_t ldb,
-                                                     int64_t M, int64_t N, int64_t K,
-                                                     int64_t k_split, int tiles_m, int tiles_n,
-                                                     int splits, Epi epi) {
-  constexpr int BM = Tile<T>::BM, BN = Tile<T>::BN, BK = Tile<T>::BK;
-  constexpr int VEC = Elem<T>::VEC;
-  constexpr int LD = BK + VEC;  // padded row, in elements
-  constexpr int WM = BM / 2, WN = BN / 2;
-  constexpr int MB = WM / 32, NB = WN / 32;
-  constexpr int KV = BK / VEC;  // vectors per tile row
-  constexpr int A_IT = BM * KV / NT, B_IT = BN * KV / NT;
-  static_assert(A_IT * NT == BM * KV && B_IT * NT == BN * KV, "tile/threads mismatch");
-
-  __shared__ __attribute__((aligned(16))) T As[2][BM * LD];
-  __shared__ __attribute__((aligned(16))) T Bs[2][BN * LD];
-
-  const TileCoord tc = map_tile(tiles_m, tiles_n, splits, BM, BN);
-  if (!tc.valid) return;
-  const int tid = threadIdx.x;
-  const int wave = tid >> 6, lane = tid & 63;
-  const int wm = wave >> 1, wn = wave & 1;
-  const int64_t kb = (int64_t)tc.split * k_split;
-  const int64_t ke = min(K, kb + k_split);
-  const int nk = (int)ceil_div(max<int64_t>(ke - kb, 0), BK);
-
-  u32x4 ra[A_IT], rb[B_IT];
-  auto gload = [&](int kt) {
-    const int64_t k0 = kb + (int64_t)kt * BK;
-#pragma unroll
-    for (int i = 0; i < A_IT; ++i) {
-      const int q = tid + NT * i;
-      const int row = q / KV, kv = (q % KV) * VEC;
-      const int64_t gr = tc.m0 + row, gk = k0 + kv;
-      u32x4 v = {0u, 0u, 0u, 0u};
-      if (gr < M && gk < ke) v = *reinterpret_cast<const u32x4*>(A + gr * lda + gk);
-      ra[i] = v;
-    }
-#pragma unroll
-    for (int i = 0; i < B_IT; ++i) {
-      const int q = tid + NT * i;
-      const int row = q / KV, kv = (q % KV) * VEC;
-      const int64_t gr = tc.n0 + row, gk = k0 + kv;
-      u32x4 v = {0u, 0u, 0u, 0u};
-      if (gr < N && gk < ke) v = *reinterpret_cast<const u32x4*>(B + gr * ldb + gk);
-      rb[i] = v;
-    }
-  };
-  auto sstore = [&](int buf) {
-#pragma unroll
-    for (int i = 0; i < A_IT; ++i) {
-      const int q = tid + NT * i;
-      const int row = q / KV, kv = (q % KV) * VEC;
-      *reinterpret_cast<u32x4*>(&As[buf][row * LD + kv]) = ra[i];
-    }
-#pragma unroll
-    for (int i = 0; i < B_IT; ++i) {
-      const int q = tid + NT * i;
-      const int row = q / KV, kv = (q % KV) * VEC;
-      *reinterpret_cast<u32x4*>(&Bs[buf][row * LD + kv]) = rb[i];
-    }
-  };
-
-  f32x16 acc[MB][NB];
-#pragma unroll
-  for (int i = 0; i < MB; ++i)
-#pragma unroll
-    for (int j = 0; j < NB; ++j)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
-
-  if (nk > 0) {
-    gload(0);
-    sstore(0);
-    __syncthreads();
-  }
-  for (int kt = 0; kt < nk; ++kt) {
-    const int buf = kt & 1;
-    if (kt + 1 < nk) gload(kt + 1);
-#pragma unroll
-    for (int kk = 0; kk < BK; kk += MM<T>::KSTEP) {
-      typename MM<T>::frag_t a[MB], b[NB];
-#pragma unroll
-      for (int i = 0; i < MB; ++i) a[i] = MM<T>::load(As[buf], LD, wm * WM + 32 * i, kk, lane);
-#pragma unroll
-      for (int j = 0; j < NB; ++j) b[j] = MM<T>::load(Bs[buf], LD, wn * WN + 32 * j, kk, lane);
-#pragma unroll
-      for (int i = 0; i < MB; ++i)
-#pragma unroll
-        for (int j = 0; j < NB; ++j) acc[i][j] = MM<T>::mma(a[i], b[j], acc[i][j]);
-    }
-    if (kt + 1 < nk) sstore(buf ^ 1);
-    __syncthreads();
-  }
-
-  EpiCtx ctx;
-  ctx.m0 = tc.m0;
-  ctx.n0 = tc.n0;
-  ctx.wm_off = wm * WM;
-  ctx.wn_off = wn * WN;
-  ctx.wave_m = wm;
-  ctx.lane = lane;
-  ctx.split = tc.split;
-  ctx.red = reinterpret_cast<float*>(&As[0][0]);
-  epi.template apply<MB, NB, BN>(acc, ctx);
-}
-
-// Row/column of accumulator element (i, j, r) for this lane.
+// Row of accumulator element (i, r) of this lane inside the wave tile.
 __device__ __forceinline__ int acc_row(int i, int r, int lane) {
   return 32 * i + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
 }
 
+// ------------------------------------------------------------- epilogues ---
+
 // Forward epilogue: rows are vocabulary entries, columns tokens.  Per column
-// and block tile: m = max z, s = sum e^(z-m), t = sum e^(z-m) (z-m) over the
-// tile's valid rows; optionally stores e^(z-m) to Pt[v, t].
+// (token) and block tile of BM vocabulary rows: m = max z, s = sum e^(z-m),
+// t = sum e^(z-m)(z-m) over the valid rows, with z = inv_t * acc.  When P is
+// given, e^(z-m) is stored token-major: P[t, v] (leading dimension ldp).
+// The exponent is formed as one fma on the raw accumulator,
+// (acc * inv_t - m) * log2(e), fed to exp2; t is accumulated in that scaled
+// unit and multiplied by ln 2 once.
 template <typename T> struct FwdEpi {
   float inv_t;
   int64_t V, Tc, J;
   float *pm, *ps, *pt;
-  T* Pt;
+  T* P;
   int64_t ldp;
 
-  template <int MB, int NB, int BN>
-  __device__ __forceinline__ void apply(f32x16 (&acc)[MB][NB], const EpiCtx& c) const {
-    const int64_t jt = c.m0 / FWD_VTILE;
+  template <bool FULL, int MB, int NB, int BM, int BN>
+  __device__ __forceinline__ void columns(f32x16 (&acc)[MB][NB], const EpiCtx& c, int vrows,
+                                          float* red, uint16_t* stg) const {
+    constexpr float LOG2E = 1.4426950408889634f;
+    constexpr bool STAGE = sizeof(T) == 2;
+    constexpr int CH = BM / 8;  // 16-byte chunks per staged token row
     const int lc = c.lane & 31;
-    float* red = c.red;  // [2][BN] maxima then [2][BN] s and [2][BN] t
-    float mcol[NB];
+    const bool store = P != nullptr;
+    // Column maxima of the raw accumulators (inv_t > 0 keeps the order).
+    float mraw[NB];
 #pragma unroll
     for (int j = 0; j < NB; ++j) {
       float mx = -INFINITY;
 #pragma unroll
       for (int i = 0; i < MB; ++i)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int64_t row = c.m0 + c.wm_off + acc_row(i, r, c.lane);
-          if (row < V) mx = fmaxf(mx, acc[i][j][r] * inv_t);
-        }
+        for (int r = 0; r < 16; ++r)
+          if (FULL || acc_row(i, r, c.lane) < vrows) mx = fmaxf(mx, acc[i][j][r]);
       mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
-      mcol[j] = mx;
+      if (c.lane < 32) red[c.wave_m * BN + c.wn_off + 32 * j + lc] = mx;
     }
-    __syncthreads();  // the LDS main-loop buffers are free from here
-#pragma unroll
-    for (int j = 0; j < NB; ++j)
-      if (c.lane < 32) red[c.wave_m * BN + c.wn_off + 32 * j + lc] = mcol[j];
     __syncthreads();
 #pragma unroll
     for (int j = 0; j < NB; ++j) {
       const int col = c.wn_off + 32 * j + lc;
-      mcol[j] = fmaxf(red[col], red[BN + col]);
+      mraw[j] = fmaxf(red[col], red[BN + col]);
     }
-    float scol[NB], tcol[NB];
+    const float k2 = inv_t * LOG2E;
+    float* rs = red + 2 * BN;
+    float* rt = red + 4 * BN;
 #pragma unroll
     for (int j = 0; j < NB; ++j) {
-      const int64_t col = c.n0 + c.wn_off + 32 * j + lc;
+      const int colb = c.wn_off + 32 * j + lc;
+      const float off = -mraw[j] * k2;
       float s = 0.0f, t = 0.0f;
 #pragma unroll
       for (int i = 0; i < MB; ++i)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int64_t row = c.m0 + c.wm_off + acc_row(i, r, c.lane);
-          if (row < V) {
-            const float d = acc[i][j][r] * inv_t - mcol[j];
-            const float e = __expf(d);
-            s += e;
-            t += e * d;
-            if (Pt != nullptr && col < Tc) Pt[row * ldp + col] = Elem<T>::from_f32(e);
+        for (int rq = 0; rq < 4; ++rq) {
+          float e4[4];
+#pragma unroll
+          for (int r3 = 0; r3 < 4; ++r3) {
+            const int r = rq * 4 + r3;
+            float e = 0.0f;
+            if (FULL || acc_row(i, r, c.lane) < vrows) {
+              const float d2 = fmaf(acc[i][j][r], k2, off);  // (z - m) log2(e)
+              e = __builtin_amdgcn_exp2f(d2);
+              s += e;
+              t = fmaf(e, d2, t);
+            }
+            e4[r3] = e;
+          }
+          if (store) {
+            const int vloc = c.wm_off + acc_row(i, rq * 4, c.lane);  // multiple of 4
+            if constexpr (STAGE) {
+              const int chunk = (vloc >> 3) ^ (colb & (CH - 1));
+              typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+              bf16x4 pk;
+#pragma unroll
+              for (int r3 = 0; r3 < 4; ++r3) pk[r3] = (__bf16)e4[r3];
+              *reinterpret_cast<bf16x4*>(stg + colb * BM + chunk * 8 + (vloc & 7)) = pk;
+            } else {
+              const int64_t col = c.n0 + colb;
+              if (col < Tc) {
+#pragma unroll
+                for (int r3 = 0; r3 < 4; ++r3) {
+                  const int64_t v = c.m0 + vloc + r3;
+                  if (v < V) P[col * ldp + v] = Elem<T>::from_f32(e4[r3]);
+                }
+              }
+            }
           }
         }
       s += __shfl_xor(s, 32, 64);
       t += __shfl_xor(t, 32, 64);
-      scol[j] = s;
-      tcol[j] = t;
-    }
-    float* rs = red + 2 * BN;
-    float* rt = red + 4 * BN;
-#pragma unroll
-    for (int j = 0; j < NB; ++j)
       if (c.lane < 32) {
-        rs[c.wave_m * BN + c.wn_off + 32 * j + lc] = scol[j];
-        rt[c.wave_m * BN + c.wn_off + 32 * j + lc] = tcol[j];
+        rs[c.wave_m * BN + colb] = s;
+        rt[c.wave_m * BN + colb] = t * 0.6931471805599453f;  // back to units of z
       }
+    }
+    (void)mraw;
+  }
+
+  template <int MB, int NB, int BM, int BN>
+  __device__ __forceinline__ void apply(f32x16 (&acc)[MB][NB], const EpiCtx& c) const {
+    const int64_t jt = c.m0 / BM;
+    __syncthreads();  // the main loop's LDS is free from here
+    float* red = reinterpret_cast<float*>(c.smem);  // [2][BN] x 3
+    uint16_t* stg = reinterpret_cast<uint16_t*>(c.smem + 6 * BN * sizeof(float));
+    const int64_t vr = V - c.m0 - c.wm_off;
+    const int vrows = (int)(vr < 0 ? 0 : (vr > 2 * BM ? 2 * BM : vr));
+    if (c.m0 + BM <= V)
+      columns<true, MB, NB, BM, BN>(acc, c, vrows, red, stg);
+    else
+      columns<false, MB, NB, BM, BN>(acc, c, vrows, red, stg);
     __syncthreads();
+    const int tid = threadIdx.x;
     if (c.wave_m == 0 && c.lane < 32) {
+      const int lc = c.lane & 31;
 #pragma unroll
       for (int j = 0; j < NB; ++j) {
         const int colb = c.wn_off + 32 * j + lc;
         const int64_t col = c.n0 + colb;
         if (col < Tc) {
-          pm[col * J + jt] = mcol[j];
-          ps[col * J + jt] = rs[colb] + rs[BN + colb];
-          pt[col * J + jt] = rt[colb] + rt[BN + colb];
+          pm[col * J + jt] = fmaxf(red[colb], red[BN + colb]) * inv_t;
+          ps[col * J + jt] = red[2 * BN + colb] + red[3 * BN + colb];
+          pt[col * J + jt] = red[4 * BN + colb] + red[5 * BN + colb];
+        }
+      }
+    }
+    if constexpr (sizeof(T) == 2) {
+      if (P == nullptr) return;
+      // Coalesced copy-out: thread tid moves chunk tid % CH of token rows
+      // tid / CH, tid / CH + NT / CH, ...
+      constexpr int CH = BM / 8;
+      constexpr int ROWS_PER_PASS = NT / CH;
+      const int ch = tid % CH;
+      const int64_t vrem = V - c.m0;
+      const int64_t trem = Tc - c.n0;
+      if ((int64_t)ch * 8 >= vrem) return;
+      const bool whole = (int64_t)ch * 8 + 8 <= vrem;
+      T* dst = P + (c.n0 + tid / CH) * ldp + c.m0 + ch * 8;
+      const int64_t step = (int64_t)ROWS_PER_PASS * ldp;
+      for (int tl = tid / CH; tl < BN && tl < trem; tl += ROWS_PER_PASS, dst += step) {
+        const u32x4 val =
+            *reinterpret_cast<const u32x4*>(stg + tl * BM + ((ch ^ (tl & (CH - 1))) * 8));
+        if (whole) {
+          *reinterpret_cast<u32x4*>(dst) = val;
+        } else {
+          const uint16_t* e = reinterpret_cast<const uint16_t*>(&val);
+          for (int k = 0; k < vrem - ch * 8; ++k) reinterpret_cast<uint16_t*>(dst)[k] = e[k];
         }
       }
     }
@@ -296,7 +237,7 @@ template <typename T> struct FwdEpi {
 struct StoreEpi {
   float* C;
   int64_t ldc, split_stride, M, N;
-  template <int MB, int NB, int BN>
+  template <int MB, int NB, int BM, int BN>
   __device__ __forceinline__ void apply(f32x16 (&acc)[MB][NB], const EpiCtx& c) const {
     float* Cs = C + (int64_t)c.split * split_stride;
     const int lc = c.lane & 31;
@@ -320,7 +261,7 @@ struct DwEpi {
   float* C;
   int64_t ldc, M, N;
   int accumulate;
-  template <int MB, int NB, int BN>
+  template <int MB, int NB, int BM, int BN>
   __device__ __forceinline__ void apply(f32x16 (&acc)[MB][NB], const EpiCtx& c) const {
     const int lc = c.lane & 31;
 #pragma unroll
@@ -341,37 +282,294 @@ struct DwEpi {
   }
 };
 
-template <typename T, class Epi>
-hipError_t launch(const T* A, int64_t lda, const T* B, int64_t ldb, int64_t M, int64_t N,
-                  int64_t K, int splits, int64_t k_split, const Epi& epi, hipStream_t s) {
-  constexpr int BM = Tile<T>::BM, BN = Tile<T>::BN;
-  const int64_t tm = ceil_div(M, BM), tn = ceil_div(N, BN);
+// ------------------------------------------------------------ bf16 kernel ---
+
+constexpr int BF_BM = 256, BF_BN = 256, BF_BK = 32, BF_ST = 4;
+constexpr int BF_STAGE_A = BF_BM * BF_BK * 2;  // bytes
+constexpr int BF_STAGE = (BF_BM + BF_BN) * BF_BK * 2;
+constexpr int BF_LDS = BF_ST * BF_STAGE + 8192;  // ring + epilogue scratch (136 KB)
+static_assert(BF_LDS >= 6 * BF_BN * 4 + BF_BN * BF_BM * 2, "forward epilogue staging");
+
+// Buffer descriptor (gfx9): base, stride 0, num_records = bytes, default config.
+__device__ __forceinline__ i32x4 make_rsrc(const void* base, uint32_t bytes) {
+  const uint64_t a = reinterpret_cast<uint64_t>(base);
+  i32x4 r;
+  r[0] = __builtin_amdgcn_readfirstlane((int32_t)(a & 0xffffffffu));
+  r[1] = __builtin_amdgcn_readfirstlane((int32_t)(a >> 32));
+  r[2] = __builtin_amdgcn_readfirstlane((int32_t)bytes);
+  r[3] = 0x00020000;
+  return r;
+}
+
+// 16 bytes per lane from `rsrc` + voffset into LDS at lds_addr + 16 * lane
+// (lds_addr wave-uniform).  Issued as inline asm so the compiler adds no
+// vmcnt waits of its own; the main loop waits explicitly.  Offsets past the
+// descriptor's range read zeros.
+__device__ __forceinline__ void load_lds16(i32x4 rsrc, uint32_t lds_addr, int voffset) {
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
+               :: "s"(lds_addr), "v"(voffset), "s"(rsrc) : "memory");
+}
+
+// s_waitcnt vmcnt(n) with the other counters left alone (gfx9 encoding).
+template <int n>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(n >= 0 && n < 64, "vmcnt");
+  __builtin_amdgcn_s_waitcnt((n & 15) | ((n >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+
+constexpr int OOB = (int)0x80000000;
+
+template <class Epi>
+__global__ void __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(1, 1)))
+gemm_bf16_kernel(const bf16_t* __restrict__ A, int64_t lda, const bf16_t* __restrict__ B,
+                 int64_t ldb, int64_t M, int64_t N, int64_t K, int64_t k_split, int tiles_m,
+                 int tiles_n, int splits, Epi epi) {
+  __shared__ __attribute__((aligned(1024))) char lds[BF_LDS];
+  const TileCoord tc = map_tile(tiles_m, tiles_n, splits, BF_BM, BF_BN);
+  if (!tc.valid) return;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wm = wave >> 1, wn = wave & 1;
+  const int64_t kb = (int64_t)tc.split * k_split;
+  const int64_t ke = min(K, kb + k_split);
+  const int nk = (int)ceil_div(max<int64_t>(ke - kb, 0), BF_BK);
+  const int64_t rows_a = min<int64_t>(M - tc.m0, BF_BM), rows_b = min<int64_t>(N - tc.n0, BF_BN);
+  // Descriptors cover this tile's row panels; all offsets stay below 2^31.
+  const i32x4 rsa = make_rsrc(A + tc.m0 * lda, (uint32_t)(rows_a * lda * 2));
+  const i32x4 rsb = make_rsrc(B + tc.n0 * ldb, (uint32_t)(rows_b * ldb * 2));
+  // This thread's 4 + 4 LDS slots of a stage: slot p = (wave*4 + i)*64 + lane,
+  // tile row p/4, stored chunk p%4 = logical chunk (p%4) ^ ((row>>1)&3).
+  int offa[4], offb[4], kc[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int p = (wave * 4 + i) * 64 + lane;
+    const int row = p >> 2, ch = (p & 3) ^ ((row >> 1) & 3);
+    kc[i] = 8 * ch;
+    offa[i] = row < rows_a ? (int)((row * lda + kb + 8 * ch) * 2) : OOB;
+    offb[i] = row < rows_b ? (int)((row * ldb + kb + 8 * ch) * 2) : OOB;
+  }
+  const uint32_t lds_base = (uint32_t)reinterpret_cast<uintptr_t>(lds);
+  auto issue = [&](int kt) {
+    const int k0 = kt * BF_BK;
+    const uint32_t sa = lds_base + (uint32_t)((kt % BF_ST) * BF_STAGE);
+    const uint32_t sb = sa + BF_STAGE_A;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const bool kok = kb + k0 + kc[i] < ke;
+      load_lds16(rsa, sa + (uint32_t)((wave * 4 + i) * 1024), kok ? offa[i] + 2 * k0 : OOB);
+      load_lds16(rsb, sb + (uint32_t)((wave * 4 + i) * 1024), kok ? offb[i] + 2 * k0 : OOB);
+    }
+  };
+
+  f32x16 acc[4][4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
+
+#pragma unroll
+  for (int s = 0; s < BF_ST - 1; ++s)
+    if (s < nk) issue(s);
+  for (int kt = 0; kt < nk; ++kt) {
+    // Stage kt has landed once at most the two younger stages (8 loads each)
+    // are still outstanding for this wave; the barrier makes it visible to all.
+    if (kt + 2 < nk)
+      wait_vmcnt<16>();
+    else if (kt + 1 < nk)
+      wait_vmcnt<8>();
+    else
+      wait_vmcnt<0>();
+    __syncthreads();
+    // The buffer of stage kt-1 is free: every wave has passed this barrier.
+    if (kt + BF_ST - 1 < nk) issue(kt + BF_ST - 1);
+    const char* sa = lds + (kt % BF_ST) * BF_STAGE;
+    const char* sb = sa + BF_STAGE_A;
+#pragma unroll
+    for (int s = 0; s < 2; ++s) {
+      bf16x8 a[4], b[4];
+      const int ch = 2 * s + (lane >> 5);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int row = wm * 128 + 32 * i + (lane & 31);
+        a[i] = *reinterpret_cast<const bf16x8*>(sa + row * 64 + 16 * (ch ^ ((row >> 1) & 3)));
+      }
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int row = wn * 128 + 32 * j + (lane & 31);
+        b[j] = *reinterpret_cast<const bf16x8*>(sb + row * 64 + 16 * (ch ^ ((row >> 1) & 3)));
+      }
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[i], b[j], acc[i][j], 0, 0, 0);
+    }
+  }
+
+  EpiCtx ctx;
+  ctx.m0 = tc.m0;
+  ctx.n0 = tc.n0;
+  ctx.wm_off = wm * 128;
+  ctx.wn_off = wn * 128;
+  ctx.wave_m = wm;
+  ctx.lane = lane;
+  ctx.split = tc.split;
+  ctx.smem = lds;
+  ctx.smem_bytes = BF_LDS;
+  epi.template apply<4, 4, BF_BM, BF_BN>(acc, ctx);
+}
+
+// ------------------------------------------------------------ fp32 kernel ---
+
+constexpr int F_BM = 128, F_BN = 128, F_BK = 16;
+
+template <class Epi>
+__global__ void __launch_bounds__(NT) gemm_f32_kernel(const float* __restrict__ A, int64_t lda,
+                                                      const float* __restrict__ B, int64_t ldb,
+                                                      int64_t M, int64_t N, int64_t K,
+                                                      int64_t k_split, int tiles_m, int tiles_n,
+                                                      int splits, Epi epi) {
+  constexpr int VEC = 4, LD = F_BK + VEC;
+  constexpr int MB = 2, NB = 2, KV = F_BK / VEC;
+  constexpr int A_IT = F_BM * KV / NT, B_IT = F_BN * KV / NT;
+  __shared__ __attribute__((aligned(16))) float As[2][F_BM * LD];
+  __shared__ __attribute__((aligned(16))) float Bs[2][F_BN * LD];
+  __shared__ __attribute__((aligned(16))) char scratch[6 * F_BN * 4];
+  const TileCoord tc = map_tile(tiles_m, tiles_n, splits, F_BM, F_BN);
+  if (!tc.valid) return;
+  const int tid = threadIdx.x;
+  const int wave = tid >> 6, lane = tid & 63;
+  const int wm = wave >> 1, wn = wave & 1;
+  const int64_t kb = (int64_t)tc.split * k_split;
+  const int64_t ke = min(K, kb + k_split);
+  const int nk = (int)ceil_div(max<int64_t>(ke - kb, 0), F_BK);
+  u32x4 ra[A_IT], rb[B_IT];
+  auto gload = [&](int kt) {
+    const int64_t k0 = kb + (int64_t)kt * F_BK;
+#pragma unroll
+    for (int i = 0; i < A_IT; ++i) {
+      const int q = tid + NT * i;
+      const int row = q / KV, kv = (q % KV) * VEC;
+      const int64_t gr = tc.m0 + row, gk = k0 + kv;
+      u32x4 v = {0u, 0u, 0u, 0u};
+      if (gr < M && gk < ke) v = *reinterpret_cast<const u32x4*>(A + gr * lda + gk);
+      ra[i] = v;
+    }
+#pragma unroll
+    for (int i = 0; i < B_IT; ++i) {
+      const int q = tid + NT * i;
+      const int row = q / KV, kv = (q % KV) * VEC;
+      const int64_t gr = tc.n0 + row, gk = k0 + kv;
+      u32x4 v = {0u, 0u, 0u, 0u};
+      if (gr < N && gk < ke) v = *reinterpret_cast<const u32x4*>(B + gr * ldb + gk);
+      rb[i] = v;
+    }
+  };
+  auto sstore = [&](int buf) {
+#pragma unroll
+    for (int i = 0; i < A_IT; ++i) {
+      const int q = tid + NT * i;
+      *reinterpret_cast<u32x4*>(&As[buf][(q / KV) * LD + (q % KV) * VEC]) = ra[i];
+    }
+#pragma unroll
+    for (int i = 0; i < B_IT; ++i) {
+      const int q = tid + NT * i;
+      *reinterpret_cast<u32x4*>(&Bs[buf][(q / KV) * LD + (q % KV) * VEC]) = rb[i];
+    }
+  };
+  f32x16 acc[MB][NB];
+#pragma unroll
+  for (int i = 0; i < MB; ++i)
+#pragma unroll
+    for (int j = 0; j < NB; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
+  if (nk > 0) {
+    gload(0);
+    sstore(0);
+    __syncthreads();
+  }
+  for (int kt = 0; kt < nk; ++kt) {
+    const int buf = kt & 1;
+    if (kt + 1 < nk) gload(kt + 1);
+#pragma unroll
+    for (int kk = 0; kk < F_BK; kk += 2) {
+      float a[MB], b[NB];
+#pragma unroll
+      for (int i = 0; i < MB; ++i)
+        a[i] = As[buf][(wm * 64 + 32 * i + (lane & 31)) * LD + kk + (lane >> 5)];
+#pragma unroll
+      for (int j = 0; j < NB; ++j)
+        b[j] = Bs[buf][(wn * 64 + 32 * j + (lane & 31)) * LD + kk + (lane >> 5)];
+#pragma unroll
+      for (int i = 0; i < MB; ++i)
+#pragma unroll
+        for (int j = 0; j < NB; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x2f32(a[i], b[j], acc[i][j], 0, 0, 0);
+    }
+    if (kt + 1 < nk) sstore(buf ^ 1);
+    __syncthreads();
+  }
+  EpiCtx ctx;
+  ctx.m0 = tc.m0;
+  ctx.n0 = tc.n0;
+  ctx.wm_off = wm * 64;
+  ctx.wn_off = wn * 64;
+  ctx.wave_m = wm;
+  ctx.lane = lane;
+  ctx.split = tc.split;
+  ctx.smem = scratch;
+  ctx.smem_bytes = sizeof(scratch);
+  epi.template apply<MB, NB, F_BM, F_BN>(acc, ctx);
+}
+
+template <class Epi>
+hipError_t launch_bf16(const bf16_t* A, int64_t lda, const bf16_t* B, int64_t ldb, int64_t M,
+                       int64_t N, int64_t K, int splits, int64_t k_split, const Epi& epi,
+                       hipStream_t s) {
+  const int64_t tm = ceil_div(M, BF_BM), tn = ceil_div(N, BF_BN);
   const int64_t total = tm * tn * splits;
   if (total <= 0) return hipSuccess;
   if (total > (int64_t)1 << 30) return hipErrorInvalidValue;
-  const int64_t grid = round_up(total, 8);
-  hipLaunchKernelGGL((gemm_nt_kernel<T, Epi>), dim3((unsigned)grid), dim3(NT), 0, s, A, lda, B,
-                     ldb, M, N, K, k_split, (int)tm, (int)tn, splits, epi);
+  // Buffer offsets are 32-bit: a tile's row panel must stay below 2 GiB.
+  if ((int64_t)BF_BM * std::max(lda, ldb) * 2 >= ((int64_t)1 << 31)) return hipErrorInvalidValue;
+  hipLaunchKernelGGL((gemm_bf16_kernel<Epi>), dim3((unsigned)round_up(total, 8)), dim3(NT), 0, s,
+                     A, lda, B, ldb, M, N, K, k_split, (int)tm, (int)tn, splits, epi);
+  return hipGetLastError();
+}
+
+template <class Epi>
+hipError_t launch_f32(const float* A, int64_t lda, const float* B, int64_t ldb, int64_t M,
+                      int64_t N, int64_t K, int splits, int64_t k_split, const Epi& epi,
+                      hipStream_t s) {
+  const int64_t tm = ceil_div(M, F_BM), tn = ceil_div(N, F_BN);
+  const int64_t total = tm * tn * splits;
+  if (total <= 0) return hipSuccess;
+  if (total > (int64_t)1 << 30) return hipErrorInvalidValue;
+  hipLaunchKernelGGL((gemm_f32_kernel<Epi>), dim3((unsigned)round_up(total, 8)), dim3(NT), 0, s,
+                     A, lda, B, ldb, M, N, K, k_split, (int)tm, (int)tn, splits, epi);
   return hipGetLastError();
 }
 
 }  // namespace
 
-int gemm_k_tile(int dtype) { return dtype == RL_DTYPE_BF16 ? Tile<bf16_t>::BK : Tile<float>::BK; }
+int gemm_k_tile(int dtype) { return dtype == RL_DTYPE_BF16 ? BF_BK : F_BK; }
+int fwd_vtile(int dtype) { return dtype == RL_DTYPE_BF16 ? BF_BM : F_BM; }
 
 hipError_t gemm_fwd(int dtype, const void* W, const void* hc, int64_t V, int64_t Tc, int64_t H,
                     const FwdEpiArgs& a, hipStream_t s) {
-  static_assert(Tile<bf16_t>::BM == FWD_VTILE && Tile<float>::BM == FWD_VTILE, "vocab tile");
   if (dtype == RL_DTYPE_BF16) {
     FwdEpi<bf16_t> e{a.inv_t, a.V, a.Tc, a.J, a.part_m, a.part_s, a.part_t,
-                     static_cast<bf16_t*>(a.Pt), a.ldp};
-    return launch<bf16_t>(static_cast<const bf16_t*>(W), H, static_cast<const bf16_t*>(hc), H, V,
-                          Tc, H, 1, round_up(H, Tile<bf16_t>::BK), e, s);
+                     static_cast<bf16_t*>(a.P), a.ldp};
+    return launch_bf16(static_cast<const bf16_t*>(W), H, static_cast<const bf16_t*>(hc), H, V, Tc,
+                       H, 1, round_up(H, BF_BK), e, s);
   }
   FwdEpi<float> e{a.inv_t, a.V, a.Tc, a.J, a.part_m, a.part_s, a.part_t,
-                  static_cast<float*>(a.Pt), a.ldp};
-  return launch<float>(static_cast<const float*>(W), H, static_cast<const float*>(hc), H, V, Tc,
-                       H, 1, round_up(H, Tile<float>::BK), e, s);
+                  static_cast<float*>(a.P), a.ldp};
+  return launch_f32(static_cast<const float*>(W), H, static_cast<const float*>(hc), H, V, Tc, H,
+                    1, round_up(H, F_BK), e, s);
 }
 
 hipError_t gemm_store(int dtype, const void* A, int64_t lda, const void* B, int64_t ldb,
@@ -379,10 +577,10 @@ hipError_t gemm_store(int dtype, const void* A, int64_t lda, const void* B, int6
                       int64_t ldc, int64_t split_stride, hipStream_t s) {
   StoreEpi e{C, ldc, split_stride, M, N};
   if (dtype == RL_DTYPE_BF16)
-    return launch<bf16_t>(static_cast<const bf16_t*>(A), lda, static_cast<const bf16_t*>(B), ldb,
-                          M, N, K, splits, k_split, e, s);
-  return launch<float>(static_cast<const float*>(A), lda, static_cast<const float*>(B), ldb, M, N,
-                       K, splits, k_split, e, s);
+    return launch_bf16(static_cast<const bf16_t*>(A), lda, static_cast<const bf16_t*>(B), ldb, M,
+                       N, K, splits, k_split, e, s);
+  return launch_f32(static_cast<const float*>(A), lda, static_cast<const float*>(B), ldb, M, N, K,
+                    splits, k_split, e, s);
 }
 
 hipError_t gemm_dw(int dtype, const void* A, int64_t lda, const void* B, int64_t ldb, int64_t M,
@@ -390,10 +588,10 @@ hipError_t gemm_dw(int dtype, const void* A, int64_t lda, const void* B, int64_t
   DwEpi e{C, ldc, M, N, accumulate};
   const int bk = gemm_k_tile(dtype);
   if (dtype == RL_DTYPE_BF16)
-    return launch<bf16_t>(static_cast<const bf16_t*>(A), lda, static_cast<const bf16_t*>(B), ldb,
-                          M, N, K, 1, round_up(K, bk), e, s);
-  return launch<float>(static_cast<const float*>(A), lda, static_cast<const float*>(B), ldb, M, N,
-                       K, 1, round_up(K, bk), e, s);
+    return launch_bf16(static_cast<const bf16_t*>(A), lda, static_cast<const bf16_t*>(B), ldb, M,
+                       N, K, 1, round_up(K, bk), e, s);
+  return launch_f32(static_cast<const float*>(A), lda, static_cast<const float*>(B), ldb, M, N, K,
+                    1, round_up(K, bk), e, s);
 }
 
 }  // namespace rl

@@ -52,32 +52,35 @@ __device__ __forceinline__ float dot_row_part(const T* __restrict__ x, const T* 
   return acc;
 }
 
-// dst[c][r] = src[r][c]; zero for R <= r < Rpad.  64 x 64 tiles through LDS.
+// dst[c][r] = src[r][c] for r < R, zero for R <= r < Rpad (c < C).  64 x 64
+// tiles through LDS; 16-byte loads of source rows and 16-byte stores of
+// destination rows.  C and ld_src are multiples of the vector width.
 template <typename T>
 __global__ void __launch_bounds__(NT) transpose_kernel(const T* __restrict__ src, int64_t ld_src,
                                                        int64_t R, int64_t C, T* __restrict__ dst,
                                                        int64_t Rpad) {
-  __shared__ T tile[64][65];
+  constexpr int VEC = Elem<T>::VEC, CPR = 64 / VEC;  // chunks per 64-element row
+  __shared__ T tile[64][64 + VEC];                    // [c][r]
   const int64_t r0 = (int64_t)blockIdx.x * 64, c0 = (int64_t)blockIdx.y * 64;
-  const int tr = threadIdx.x >> 2, tc = (threadIdx.x & 3) * 16;
-  {
-    const int64_t r = r0 + tr;
+  for (int q = threadIdx.x; q < 64 * CPR; q += NT) {
+    const int rl = q / CPR, cl = (q % CPR) * VEC;
+    const int64_t r = r0 + rl, c = c0 + cl;
+    u32x4 v = {0u, 0u, 0u, 0u};
+    if (r < R && c < C) v = *reinterpret_cast<const u32x4*>(src + r * ld_src + c);
+    const T* e = reinterpret_cast<const T*>(&v);
 #pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      const int64_t c = c0 + tc + i;
-      tile[tr][tc + i] = (r < R && c < C) ? src[r * ld_src + c] : Elem<T>::from_f32(0.0f);
-    }
+    for (int k = 0; k < VEC; ++k) tile[cl + k][rl] = e[k];
   }
   __syncthreads();
-  {
-    const int64_t c = c0 + tr;
-    if (c < C) {
+  for (int q = threadIdx.x; q < 64 * CPR; q += NT) {
+    const int cl = q / CPR, rl = (q % CPR) * VEC;
+    const int64_t c = c0 + cl, r = r0 + rl;
+    if (c >= C || r >= Rpad) continue;
+    u32x4 v;
+    T* e = reinterpret_cast<T*>(&v);
 #pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const int64_t r = r0 + tc + i;
-        if (r < Rpad) dst[c * Rpad + r] = tile[tc + i][tr];
-      }
-    }
+    for (int k = 0; k < VEC; ++k) e[k] = tile[cl][rl + k];
+    *reinterpret_cast<u32x4*>(dst + c * Rpad + r) = v;
   }
 }
 
@@ -198,51 +201,62 @@ __global__ void __launch_bounds__(NT) combine_kernel(CombineArgs a) {
   }
 }
 
-// Gt (in place over Pt) and G from Pt = e^(z - m_tile).  64 (vocab) x 64
-// (token) tiles.  Columns Tc..Tcpad of Gt and Vpad padding of G are zeroed.
+// G (in place over P) and Gt from P = e^(z - m_tile) (token-major [Tc, ldp]):
+// g[t, v] = kap[t] * exp(m[t, v / vtile] - lse[t]) * P[t, v].  Tiles of 64
+// tokens x 128 vocabulary entries (one online-softmax tile column per WG).
+// Padding is written as zeros: G columns V..ldp and Gt columns Tc..Tck, which
+// the dh and dW contractions read as part of their K ranges.
 template <typename T>
-__global__ void __launch_bounds__(NT) form_g_kernel(T* __restrict__ Pt, int64_t ldp,
-                                                    T* __restrict__ G, int64_t ldg,
+__global__ void __launch_bounds__(NT) form_g_kernel(T* __restrict__ P, int64_t ldp,
+                                                    T* __restrict__ Gt, int64_t ldgt,
                                                     const float* __restrict__ part_m, int64_t J,
-                                                    const float* __restrict__ lse,
+                                                    int vtile, const float* __restrict__ lse,
                                                     const float* __restrict__ kap, int64_t V,
-                                                    int64_t Tc) {
+                                                    int64_t Tc, int write_g) {
+  constexpr int VEC = Elem<T>::VEC, CPR = 128 / VEC;  // chunks per 128-wide P row
   __shared__ float scale[64];
-  __shared__ T tile[64][65];
-  const int64_t t0 = (int64_t)blockIdx.x * 64, v0 = (int64_t)blockIdx.y * 64;
-  const int tid = threadIdx.x;
-  if (tid < 64) {
-    const int64_t t = t0 + tid;
-    scale[tid] = (t < Tc) ? kap[t] * __expf(part_m[t * J + v0 / FWD_VTILE] - lse[t]) : 0.0f;
+  __shared__ T tile[128][64 + VEC];  // [v][t]
+  const int64_t t0 = (int64_t)blockIdx.x * 64, v0 = (int64_t)blockIdx.y * 128;
+  if (threadIdx.x < 64) {
+    const int64_t t = t0 + threadIdx.x;
+    scale[threadIdx.x] =
+        (t < Tc) ? kap[t] * __expf(part_m[t * J + v0 / vtile] - lse[t]) : 0.0f;
   }
   __syncthreads();
-  const int r = tid >> 2, cc = (tid & 3) * 16;
-  {
-    const int64_t v = v0 + r;
-    if (v < V) {
-      T* row = Pt + v * ldp + t0 + cc;
+  for (int q = threadIdx.x; q < 64 * CPR; q += NT) {
+    const int tl = q / CPR, vl = (q % CPR) * VEC;
+    const int64_t t = t0 + tl, v = v0 + vl;
+    float g[VEC];
+    if (t < Tc) {
+      T* row = P + t * ldp + v;
+      const u32x4 raw = *reinterpret_cast<const u32x4*>(row);
+      float x[VEC];
+      Elem<T>::unpack(raw, x);
+      const float sc = scale[tl];
 #pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const int64_t t = t0 + cc + i;
-        const float g = (t < Tc) ? scale[cc + i] * Elem<T>::to_f32(row[i]) : 0.0f;
-        const T gv = Elem<T>::from_f32(g);
-        row[i] = gv;
-        tile[cc + i][r] = gv;
-      }
+      for (int k = 0; k < VEC; ++k) g[k] = (v + k < V) ? sc * x[k] : 0.0f;
+      const u32x4 packed = Elem<T>::pack(g);
+      if (write_g) *reinterpret_cast<u32x4*>(row) = packed;
+      Elem<T>::unpack(packed, g);  // the rounded values go to Gt as well
     } else {
 #pragma unroll
-      for (int i = 0; i < 16; ++i) tile[cc + i][r] = Elem<T>::from_f32(0.0f);
+      for (int k = 0; k < VEC; ++k) g[k] = 0.0f;
     }
-  }
-  if (G == nullptr) return;
-  __syncthreads();
-  {
-    const int64_t t = t0 + r;
-    if (t < Tc) {
-      T* grow = G + t * ldg + v0 + cc;
 #pragma unroll
-      for (int i = 0; i < 16; ++i) grow[i] = tile[r][cc + i];
-    }
+    for (int k = 0; k < VEC; ++k) tile[vl + k][tl] = Elem<T>::from_f32(g[k]);
+  }
+  if (Gt == nullptr) return;
+  __syncthreads();
+  constexpr int CPT = 64 / VEC;  // chunks per 64-token Gt row segment
+  for (int q = threadIdx.x; q < 128 * CPT; q += NT) {
+    const int vl = q / CPT, tl = (q % CPT) * VEC;
+    const int64_t v = v0 + vl;
+    if (v >= V) continue;
+    u32x4 out;
+    T* e = reinterpret_cast<T*>(&out);
+#pragma unroll
+    for (int k = 0; k < VEC; ++k) e[k] = tile[vl][tl + k];
+    *reinterpret_cast<u32x4*>(Gt + v * ldgt + t0 + tl) = out;
   }
 }
 
@@ -383,17 +397,18 @@ hipError_t combine(int dtype, const CombineArgs& a, hipStream_t s) {
   return hipGetLastError();
 }
 
-hipError_t form_g(int dtype, void* Pt, int64_t ldp, void* G, int64_t ldg, const float* part_m,
-                  int64_t J, const float* lse_c, const float* kappa_c, int64_t V, int64_t Vpad,
-                  int64_t Tc, int64_t Tcpad, hipStream_t s) {
-  (void)Vpad;
-  const dim3 grid((unsigned)ceil_div(Tcpad, 64), (unsigned)ceil_div(V, 64));
+hipError_t form_g(int dtype, void* P, int64_t ldp, void* Gt, int64_t ldgt, const float* part_m,
+                  int64_t J, int vtile, const float* lse_c, const float* kappa_c, int64_t V,
+                  int64_t Tc, int64_t Tck, int write_g, hipStream_t s) {
+  const dim3 grid((unsigned)ceil_div(Tck, 64), (unsigned)ceil_div(ldp, 128));
   if (dtype == RL_DTYPE_BF16)
-    hipLaunchKernelGGL(form_g_kernel<bf16_t>, grid, dim3(NT), 0, s, static_cast<bf16_t*>(Pt), ldp,
-                       static_cast<bf16_t*>(G), ldg, part_m, J, lse_c, kappa_c, V, Tc);
+    hipLaunchKernelGGL(form_g_kernel<bf16_t>, grid, dim3(NT), 0, s, static_cast<bf16_t*>(P), ldp,
+                       static_cast<bf16_t*>(Gt), ldgt, part_m, J, vtile, lse_c, kappa_c, V, Tc,
+                       write_g);
   else
-    hipLaunchKernelGGL(form_g_kernel<float>, grid, dim3(NT), 0, s, static_cast<float*>(Pt), ldp,
-                       static_cast<float*>(G), ldg, part_m, J, lse_c, kappa_c, V, Tc);
+    hipLaunchKernelGGL(form_g_kernel<float>, grid, dim3(NT), 0, s, static_cast<float*>(P), ldp,
+                       static_cast<float*>(Gt), ldgt, part_m, J, vtile, lse_c, kappa_c, V, Tc,
+                       write_g);
   return hipGetLastError();
 }
 

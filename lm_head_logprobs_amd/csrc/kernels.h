@@ -5,9 +5,9 @@
 
 namespace rl {
 
-// Forward GEMM tile extent along the vocabulary: the online-softmax partials
-// are kept per (token, block of FWD_VTILE vocabulary rows).
-constexpr int FWD_VTILE = 128;
+// Forward GEMM tile extent along the vocabulary for a dtype: the
+// online-softmax partials are kept per (token, block of that many rows).
+int fwd_vtile(int dtype);
 
 struct FwdEpiArgs {
   float inv_t;
@@ -15,7 +15,7 @@ struct FwdEpiArgs {
   float* part_m;         // [Tc, J] tile max of z
   float* part_s;         // [Tc, J] sum exp(z - m)
   float* part_t;         // [Tc, J] sum exp(z - m) (z - m)
-  void* Pt;              // [V, ldp] exp(z - m) per element (dtype of h/W), or null
+  void* P;               // [Tc, ldp] exp(z - m) per element (dtype of h/W), or null
   int64_t ldp;
 };
 
@@ -70,11 +70,12 @@ constexpr int STAT_LOSS = 0, STAT_MASKED = 1, STAT_SMASS = 2, STAT_HAS_SUPPORT =
               STAT_TVFAIL = 4, STAT_KL = 5, STAT_ABS_KAPPA = 6, STAT_ENTROPY = 7, STAT_N = 8;
 hipError_t combine(int dtype, const CombineArgs& a, hipStream_t s);
 
-// G^T (in place over Pt) and G from Pt = exp(z - m_tile):
-// g = kappa_s[t] * exp(m[t, v / FWD_VTILE] - lse[t]) * Pt[v, t].
-hipError_t form_g(int dtype, void* Pt, int64_t ldp, void* G, int64_t ldg, const float* part_m,
-                  int64_t J, const float* lse_c, const float* kappa_c, int64_t V, int64_t Vpad,
-                  int64_t Tc, int64_t Tcpad, hipStream_t s);
+// G (in place over P, if write_g) and Gt from P = exp(z - m_tile):
+// g[t, v] = kappa_s[t] * exp(m[t, v / vtile] - lse[t]) * P[t, v].
+// ldp must be a multiple of 128; Gt columns up to Tck (multiple of 64).
+hipError_t form_g(int dtype, void* P, int64_t ldp, void* Gt, int64_t ldgt, const float* part_m,
+                  int64_t J, int vtile, const float* lse_c, const float* kappa_c, int64_t V,
+                  int64_t Tc, int64_t Tck, int write_g, hipStream_t s);
 
 // dh[t] = sum_s part[s][t] + sum over label/entries of coef * W[v] ; grad dtype.
 hipError_t finalize_dh(int dtype, int grad_dtype, const float* part, int splits,
