@@ -104,8 +104,10 @@ struct Plan {
   int splits;
   int64_t k_split;
   size_t o_pm, o_ps, o_pt, o_lse, o_kap, o_stats, o_coef;
-  size_t o_P, o_Gt, o_Wt, o_ht, o_dhp;
+  size_t o_P, o_G, o_Gt, o_Wt, o_ht, o_dhp;
   int vtile;
+  bool tiled;             // bf16 dense backward: operands in the tiled block layout
+  int64_t Tc256, KB_v, KB_t;
   size_t o_ka, o_kb, o_ia, o_ib, o_hist, o_start, o_rows;
   size_t total;
 };
@@ -185,21 +187,37 @@ rl_status make_plan(const rl_loss_cfg* c, bool has_support, bool want_dh, bool w
   p->o_kap = L.take(p->N, 4);
   p->o_stats = L.take(p->N, 4 * STAT_N);
   p->o_coef = L.take(p->E, 4);
-  p->o_P = p->o_Gt = p->o_Wt = p->o_ht = p->o_dhp = 0;
+  p->o_P = p->o_G = p->o_Gt = p->o_Wt = p->o_ht = p->o_dhp = 0;
+  p->tiled = p->dense && p->dtype == RL_DTYPE_BF16;
+  p->Tc256 = round_up(p->Tc, TILE_ROWS);
+  p->KB_v = p->Vpad / TILE_K;
+  p->KB_t = p->Tc256 / TILE_K;
   if (p->dense) {
-    int64_t vt, tv;
-    if (!mul_ok(p->V, p->Tcpad, &vt) || !mul_ok(p->Tc, p->Vpad, &tv)) return RL_E_ARG;
-    p->o_P = L.take(tv, p->esz);  // e^(z - m) token-major, then G in place
-    if (p->want_dW) {
-      p->o_Gt = L.take(vt, p->esz);
-      p->o_ht = L.take(p->H * p->Tcpad, p->esz);
-    }
-    if (p->want_dh) {
-      int64_t hv, sth;
-      if (!mul_ok(p->H, p->Vpad, &hv) || !mul_ok((int64_t)p->splits * p->Tc, p->H, &sth))
-        return RL_E_ARG;
-      p->o_Wt = L.take(hv, p->esz);
-      p->o_dhp = L.take(sth, 4);
+    int64_t vt, tv, hv, sth;
+    const int64_t H256 = round_up(p->H, TILE_ROWS);
+    if (!mul_ok(p->Vpad, p->Tc256, &vt) || !mul_ok(p->Tc256, p->Vpad, &tv) ||
+        !mul_ok(H256, p->Vpad, &hv) || !mul_ok((int64_t)p->splits * p->Tc, p->H, &sth))
+      return RL_E_ARG;
+    p->o_P = L.take(tv, p->esz);  // e^(z - m) token-major [Tc, Vpad] (fp32: then G in place)
+    if (p->tiled) {
+      if (p->want_dh) {
+        p->o_G = L.take(tv, 2);
+        p->o_Wt = L.take(hv, 2);
+        p->o_dhp = L.take(sth, 4);
+      }
+      if (p->want_dW) {
+        p->o_Gt = L.take(vt, 2);
+        p->o_ht = L.take(H256 * p->Tc256, 2);
+      }
+    } else {
+      if (p->want_dW) {
+        p->o_Gt = L.take(p->V * p->Tcpad, p->esz);
+        p->o_ht = L.take(p->H * p->Tcpad, p->esz);
+      }
+      if (p->want_dh) {
+        p->o_Wt = L.take(p->H * p->Vpad, p->esz);
+        p->o_dhp = L.take(sth, 4);
+      }
     }
   }
   p->o_ka = p->o_kb = p->o_ia = p->o_ib = p->o_hist = p->o_start = p->o_rows = 0;
@@ -341,6 +359,7 @@ rl_status rl_loss_fwd_bwd(const void* h, const void* W, const int32_t* labels,
   float *pm = F(p.o_pm), *ps = F(p.o_ps), *pt = F(p.o_pt);
   float *lse = F(p.o_lse), *kap = F(p.o_kap), *stats = F(p.o_stats), *coef = F(p.o_coef);
   void* P = p.dense ? ws + p.o_P : nullptr;
+  void* G = (p.tiled && p.want_dh) ? ws + p.o_G : nullptr;
   void* Gt = (p.dense && p.want_dW) ? ws + p.o_Gt : nullptr;
   void* Wt = (p.dense && p.want_dh) ? ws + p.o_Wt : nullptr;
   void* ht = (p.dense && p.want_dW) ? ws + p.o_ht : nullptr;
@@ -351,7 +370,12 @@ rl_status rl_loss_fwd_bwd(const void* h, const void* W, const int32_t* labels,
                         cfg->icepop_hi};
   const float inv_D = 1.0f / cfg->loss_norm;
 
-  if (p.dense && p.want_dh) RL_TRY(timed(K_TRANSPOSE_W, s, [&] { return transpose_pad(p.dtype, W, p.H, p.V, p.H, Wt, p.Vpad, s); }));
+  if (p.dense && p.want_dh)
+    RL_TRY(timed(K_TRANSPOSE_W, s, [&] {
+      return p.tiled ? to_tiled_t(static_cast<const bf16_t*>(W), p.H, p.V, p.H,
+                                  static_cast<bf16_t*>(Wt), p.KB_v, p.KB_v, s)
+                     : transpose_pad(p.dtype, W, p.H, p.V, p.H, Wt, p.Vpad, s);
+    }));
 
   for (int64_t c0 = 0; c0 < p.N; c0 += p.Tc) {
     const int64_t tc = std::min(p.Tc, p.N - c0);
@@ -395,7 +419,28 @@ rl_status rl_loss_fwd_bwd(const void* h, const void* W, const int32_t* labels,
     ca.o_token_loss = out->token_loss;
     ca.o_support_lp = has_support ? out->support_logprobs : nullptr;
     RL_TRY(timed(K_COMBINE, s, [&] { return combine(p.dtype, ca, s); }));
-    if (p.dense) {
+    if (p.tiled) {
+      RL_TRY(timed(K_FORM_G, s, [&] {
+        return form_g_tiled(static_cast<const bf16_t*>(P), p.Vpad, static_cast<bf16_t*>(G), p.KB_v,
+                            static_cast<bf16_t*>(Gt), p.KB_t, pm, p.J, p.vtile, lse + c0,
+                            kap + c0, p.V, tc, s);
+      }));
+      if (p.want_dh)
+        RL_TRY(timed(K_GEMM_DH, s, [&] {
+          return gemm_store(p.dtype, G, p.KB_v, Wt, p.KB_v, tc, p.H, p.Vpad, p.splits, p.k_split,
+                            dhp, p.H, p.Tc * p.H, s);
+        }));
+      if (p.want_dW) {
+        RL_TRY(timed(K_TRANSPOSE_H, s, [&] {
+          return to_tiled_t(static_cast<const bf16_t*>(hc), p.H, tc, p.H,
+                            static_cast<bf16_t*>(ht), p.KB_t, ceil_div(tc, TILE_K), s);
+        }));
+        const int acc = (c0 > 0 || cfg->accumulate_dW) ? 1 : 0;
+        RL_TRY(timed(K_GEMM_DW, s, [&] {
+          return gemm_dw(p.dtype, Gt, p.KB_t, ht, p.KB_t, p.V, p.H, tc, out->dW, p.H, acc, s);
+        }));
+      }
+    } else if (p.dense) {
       RL_TRY(timed(K_FORM_G, s, [&] {
         return form_g(p.dtype, P, p.Vpad, Gt, p.Tcpad, pm, p.J, p.vtile, lse + c0, kap + c0, p.V,
                       tc, tck, p.want_dh ? 1 : 0, s);

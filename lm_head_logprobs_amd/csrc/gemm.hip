@@ -17,12 +17,15 @@
 // Operand tiles are copied global -> LDS by buffer_load_dwordx4 ... lds: each
 // wave instruction fills 1 KB of LDS (16 bytes per lane, consecutive), no
 // VGPR staging.  Loads run three stages ahead; a stage is waited for with an
-// explicit vmcnt and one barrier.  Out-of-range rows or K columns are given a
+// explicit vmcnt and one barrier, placed between the two K-steps of a stage so
+// MFMAs are in flight across it.  Out-of-range rows or K columns are given a
 // buffer offset past the descriptor's range, which the hardware reads as zero.
 // In LDS a tile row is 64 bytes (32 bf16 = four 16-byte chunks); chunk c of
 // row r is stored at position c ^ ((r >> 1) & 3), so the 8 lanes of a
 // ds_read_b128 phase that read one chunk of 8 consecutive rows hit disjoint
-// banks.  Workgroups are remapped so consecutive tiles land on one XCD
+// banks.  The backward operands arrive in a tiled layout whose 16 KB blocks
+// are exactly this LDS image, so each stage load is one contiguous copy
+// (row-major operands with 300 KB row strides touch 256 pages per stage).  Workgroups are remapped so consecutive tiles land on one XCD
 // (dispatch is round-robin over the 8 XCDs) and grouped 8 tiles along M so
 // neighbours share B panels in that XCD's L2.
 //
@@ -289,14 +292,15 @@ constexpr int BF_STAGE_A = BF_BM * BF_BK * 2;  // bytes
 constexpr int BF_STAGE = (BF_BM + BF_BN) * BF_BK * 2;
 constexpr int BF_LDS = BF_ST * BF_STAGE + 8192;  // ring + epilogue scratch (136 KB)
 static_assert(BF_LDS >= 6 * BF_BN * 4 + BF_BN * BF_BM * 2, "forward epilogue staging");
+static_assert(BF_STAGE_A == TILE_BLOCK_BYTES, "a stage of one operand is one tiled block");
 
 // Buffer descriptor (gfx9): base, stride 0, num_records = bytes, default config.
 __device__ __forceinline__ i32x4 make_rsrc(const void* base, uint32_t bytes) {
   const uint64_t a = reinterpret_cast<uint64_t>(base);
   i32x4 r;
-  r[0] = __builtin_amdgcn_readfirstlane((int32_t)(a & 0xffffffffu));
-  r[1] = __builtin_amdgcn_readfirstlane((int32_t)(a >> 32));
-  r[2] = __builtin_amdgcn_readfirstlane((int32_t)bytes);
+  r[0] = (int32_t)(a & 0xffffffffu);
+  r[1] = (int32_t)(a >> 32);
+  r[2] = (int32_t)bytes;
   r[3] = 0x00020000;
   return r;
 }
@@ -306,6 +310,9 @@ __device__ __forceinline__ i32x4 make_rsrc(const void* base, uint32_t bytes) {
 // vmcnt waits of its own; the main loop waits explicitly.  Offsets past the
 // descriptor's range read zeros.
 __device__ __forceinline__ void load_lds16(i32x4 rsrc, uint32_t lds_addr, int voffset) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i) rsrc[i] = __builtin_amdgcn_readfirstlane(rsrc[i]);
+  lds_addr = __builtin_amdgcn_readfirstlane(lds_addr);
   asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
                :: "s"(lds_addr), "v"(voffset), "s"(rsrc) : "memory");
 }
@@ -317,9 +324,31 @@ __device__ __forceinline__ void wait_vmcnt() {
   __builtin_amdgcn_s_waitcnt((n & 15) | ((n >> 4) << 14) | (7 << 4) | (15 << 8));
 }
 
+// Wait until the oldest stage not yet waited for has landed, given how many
+// younger stages (8 loads per thread each) were issued after it.
+__device__ __forceinline__ void wait_stage(int younger) {
+  if (younger >= 2)
+    wait_vmcnt<16>();
+  else if (younger == 1)
+    wait_vmcnt<8>();
+  else
+    wait_vmcnt<0>();
+}
+
 constexpr int OOB = (int)0x80000000;
 
-template <class Epi>
+// TILED = false: A [M, lda] and B [N, ldb] row-major, any K (multiple of 8).
+// TILED = true: A and B in the tiled block layout (tiled_offset in
+// kernels.h) with lda / ldb = blocks per 256-row panel; K is a multiple of 32
+// or the blocks are zero past K.
+//
+// Software pipeline per stage kt (two K-steps s0, s1 of 16): fragments of s1
+// are read, the MFMAs of s0 issue, then the wave waits for stage kt+1 and
+// passes the barrier while those MFMAs execute, refills the buffer of stage
+// kt (fully read), reads the s0 fragments of stage kt+1 and issues the MFMAs
+// of s1.  Every wave has read all of stage kt before anyone passes the
+// barrier, so the refill cannot race with fragment reads.
+template <bool TILED, class Epi>
 __global__ void __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(1, 1)))
 gemm_bf16_kernel(const bf16_t* __restrict__ A, int64_t lda, const bf16_t* __restrict__ B,
                  int64_t ldb, int64_t M, int64_t N, int64_t K, int64_t k_split, int tiles_m,
@@ -333,33 +362,67 @@ gemm_bf16_kernel(const bf16_t* __restrict__ A, int64_t lda, const bf16_t* __rest
   const int64_t kb = (int64_t)tc.split * k_split;
   const int64_t ke = min(K, kb + k_split);
   const int nk = (int)ceil_div(max<int64_t>(ke - kb, 0), BF_BK);
-  const int64_t rows_a = min<int64_t>(M - tc.m0, BF_BM), rows_b = min<int64_t>(N - tc.n0, BF_BN);
-  // Descriptors cover this tile's row panels; all offsets stay below 2^31.
-  const i32x4 rsa = make_rsrc(A + tc.m0 * lda, (uint32_t)(rows_a * lda * 2));
-  const i32x4 rsb = make_rsrc(B + tc.n0 * ldb, (uint32_t)(rows_b * ldb * 2));
-  // This thread's 4 + 4 LDS slots of a stage: slot p = (wave*4 + i)*64 + lane,
-  // tile row p/4, stored chunk p%4 = logical chunk (p%4) ^ ((row>>1)&3).
+  i32x4 rsa, rsb;
   int offa[4], offb[4], kc[4];
+  if constexpr (TILED) {
+    // Panel of this tile: blocks [m0/256 * lda + kb/32, ...), 16 KB each.
+    const int64_t ba = (tc.m0 / BF_BM) * lda + kb / BF_BK;
+    const int64_t bb = (tc.n0 / BF_BN) * ldb + kb / BF_BK;
+    rsa = make_rsrc(A + ba * (TILE_BLOCK_BYTES / 2), (uint32_t)(nk * TILE_BLOCK_BYTES));
+    rsb = make_rsrc(B + bb * (TILE_BLOCK_BYTES / 2), (uint32_t)(nk * TILE_BLOCK_BYTES));
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int p = (wave * 4 + i) * 64 + lane;
-    const int row = p >> 2, ch = (p & 3) ^ ((row >> 1) & 3);
-    kc[i] = 8 * ch;
-    offa[i] = row < rows_a ? (int)((row * lda + kb + 8 * ch) * 2) : OOB;
-    offb[i] = row < rows_b ? (int)((row * ldb + kb + 8 * ch) * 2) : OOB;
+    for (int i = 0; i < 4; ++i) {
+      offa[i] = offb[i] = ((wave * 4 + i) * 64 + lane) * 16;
+      kc[i] = 0;
+    }
+  } else {
+    const int64_t rows_a = min<int64_t>(M - tc.m0, BF_BM), rows_b = min<int64_t>(N - tc.n0, BF_BN);
+    rsa = make_rsrc(A + tc.m0 * lda, (uint32_t)(rows_a * lda * 2));
+    rsb = make_rsrc(B + tc.n0 * ldb, (uint32_t)(rows_b * ldb * 2));
+    // Slot p = (wave*4 + i)*64 + lane: tile row p/4, stored chunk p%4 holds
+    // logical chunk (p%4) ^ ((row>>1)&3).
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int p = (wave * 4 + i) * 64 + lane;
+      const int row = p >> 2, ch = (p & 3) ^ ((row >> 1) & 3);
+      kc[i] = 8 * ch;
+      offa[i] = row < rows_a ? (int)((row * lda + kb + 8 * ch) * 2) : OOB;
+      offb[i] = row < rows_b ? (int)((row * ldb + kb + 8 * ch) * 2) : OOB;
+    }
   }
   const uint32_t lds_base = (uint32_t)reinterpret_cast<uintptr_t>(lds);
   auto issue = [&](int kt) {
-    const int k0 = kt * BF_BK;
     const uint32_t sa = lds_base + (uint32_t)((kt % BF_ST) * BF_STAGE);
     const uint32_t sb = sa + BF_STAGE_A;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const bool kok = kb + k0 + kc[i] < ke;
-      load_lds16(rsa, sa + (uint32_t)((wave * 4 + i) * 1024), kok ? offa[i] + 2 * k0 : OOB);
-      load_lds16(rsb, sb + (uint32_t)((wave * 4 + i) * 1024), kok ? offb[i] + 2 * k0 : OOB);
+      int oa, ob;
+      if constexpr (TILED) {
+        oa = offa[i] + kt * TILE_BLOCK_BYTES;
+        ob = offb[i] + kt * TILE_BLOCK_BYTES;
+      } else {
+        const int k0 = kt * BF_BK;
+        const bool kok = kb + k0 + kc[i] < ke;
+        oa = kok ? offa[i] + 2 * k0 : OOB;
+        ob = kok ? offb[i] + 2 * k0 : OOB;
+      }
+      load_lds16(rsa, sa + (uint32_t)((wave * 4 + i) * 1024), oa);
+      load_lds16(rsb, sb + (uint32_t)((wave * 4 + i) * 1024), ob);
     }
   };
+  // Byte offsets of this lane's fragments inside a stage, per K-step.
+  int fa[2][4], fb[2][4];
+#pragma unroll
+  for (int s = 0; s < 2; ++s) {
+    const int ch = 2 * s + (lane >> 5);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      int row = wm * 128 + 32 * i + (lane & 31);
+      fa[s][i] = row * 64 + 16 * (ch ^ ((row >> 1) & 3));
+      row = wn * 128 + 32 * i + (lane & 31);
+      fb[s][i] = BF_STAGE_A + row * 64 + 16 * (ch ^ ((row >> 1) & 3));
+    }
+  }
 
   f32x16 acc[4][4];
 #pragma unroll
@@ -369,42 +432,49 @@ gemm_bf16_kernel(const bf16_t* __restrict__ A, int64_t lda, const bf16_t* __rest
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
 
+  if (nk > 0) {
 #pragma unroll
-  for (int s = 0; s < BF_ST - 1; ++s)
-    if (s < nk) issue(s);
-  for (int kt = 0; kt < nk; ++kt) {
-    // Stage kt has landed once at most the two younger stages (8 loads each)
-    // are still outstanding for this wave; the barrier makes it visible to all.
-    if (kt + 2 < nk)
-      wait_vmcnt<16>();
-    else if (kt + 1 < nk)
-      wait_vmcnt<8>();
-    else
-      wait_vmcnt<0>();
+    for (int s = 0; s < BF_ST - 1; ++s)
+      if (s < nk) issue(s);
+    bf16x8 a0[4], b0[4], a1[4], b1[4];
+    wait_stage(min(nk - 1, BF_ST - 2));
     __syncthreads();
-    // The buffer of stage kt-1 is free: every wave has passed this barrier.
-    if (kt + BF_ST - 1 < nk) issue(kt + BF_ST - 1);
-    const char* sa = lds + (kt % BF_ST) * BF_STAGE;
-    const char* sb = sa + BF_STAGE_A;
+    if (BF_ST - 1 < nk) issue(BF_ST - 1);
 #pragma unroll
-    for (int s = 0; s < 2; ++s) {
-      bf16x8 a[4], b[4];
-      const int ch = 2 * s + (lane >> 5);
+    for (int i = 0; i < 4; ++i) {
+      a0[i] = *reinterpret_cast<const bf16x8*>(lds + fa[0][i]);
+      b0[i] = *reinterpret_cast<const bf16x8*>(lds + fb[0][i]);
+    }
+    for (int kt = 0; kt < nk; ++kt) {
+      const char* st = lds + (kt % BF_ST) * BF_STAGE;
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const int row = wm * 128 + 32 * i + (lane & 31);
-        a[i] = *reinterpret_cast<const bf16x8*>(sa + row * 64 + 16 * (ch ^ ((row >> 1) & 3)));
-      }
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int row = wn * 128 + 32 * j + (lane & 31);
-        b[j] = *reinterpret_cast<const bf16x8*>(sb + row * 64 + 16 * (ch ^ ((row >> 1) & 3)));
+        a1[i] = *reinterpret_cast<const bf16x8*>(st + fa[1][i]);
+        b1[i] = *reinterpret_cast<const bf16x8*>(st + fb[1][i]);
       }
 #pragma unroll
       for (int i = 0; i < 4; ++i)
 #pragma unroll
         for (int j = 0; j < 4; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[i], b[j], acc[i][j], 0, 0, 0);
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a0[i], b0[j], acc[i][j], 0, 0, 0);
+      if (kt + 1 < nk) {
+        // Stage kt+1 has landed once at most the stages issued after it
+        // (kt+2, kt+3) are outstanding.
+        wait_stage(min(nk - 2 - kt, BF_ST - 2));
+        __syncthreads();
+        if (kt + BF_ST < nk) issue(kt + BF_ST);  // into the buffer of stage kt
+        const char* sn = lds + ((kt + 1) % BF_ST) * BF_STAGE;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          a0[i] = *reinterpret_cast<const bf16x8*>(sn + fa[0][i]);
+          b0[i] = *reinterpret_cast<const bf16x8*>(sn + fb[0][i]);
+        }
+      }
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a1[i], b1[j], acc[i][j], 0, 0, 0);
     }
   }
 
@@ -525,7 +595,7 @@ __global__ void __launch_bounds__(NT) gemm_f32_kernel(const float* __restrict__ 
   epi.template apply<MB, NB, F_BM, F_BN>(acc, ctx);
 }
 
-template <class Epi>
+template <bool TILED, class Epi>
 hipError_t launch_bf16(const bf16_t* A, int64_t lda, const bf16_t* B, int64_t ldb, int64_t M,
                        int64_t N, int64_t K, int splits, int64_t k_split, const Epi& epi,
                        hipStream_t s) {
@@ -533,10 +603,12 @@ hipError_t launch_bf16(const bf16_t* A, int64_t lda, const bf16_t* B, int64_t ld
   const int64_t total = tm * tn * splits;
   if (total <= 0) return hipSuccess;
   if (total > (int64_t)1 << 30) return hipErrorInvalidValue;
-  // Buffer offsets are 32-bit: a tile's row panel must stay below 2 GiB.
-  if ((int64_t)BF_BM * std::max(lda, ldb) * 2 >= ((int64_t)1 << 31)) return hipErrorInvalidValue;
-  hipLaunchKernelGGL((gemm_bf16_kernel<Epi>), dim3((unsigned)round_up(total, 8)), dim3(NT), 0, s,
-                     A, lda, B, ldb, M, N, K, k_split, (int)tm, (int)tn, splits, epi);
+  // Buffer offsets are 32-bit: a tile's operand panel must stay below 2 GiB.
+  const int64_t panel = TILED ? ceil_div(k_split, BF_BK) * TILE_BLOCK_BYTES
+                              : (int64_t)BF_BM * std::max(lda, ldb) * 2;
+  if (panel >= ((int64_t)1 << 31)) return hipErrorInvalidValue;
+  hipLaunchKernelGGL((gemm_bf16_kernel<TILED, Epi>), dim3((unsigned)round_up(total, 8)), dim3(NT),
+                     0, s, A, lda, B, ldb, M, N, K, k_split, (int)tm, (int)tn, splits, epi);
   return hipGetLastError();
 }
 
@@ -563,8 +635,8 @@ hipError_t gemm_fwd(int dtype, const void* W, const void* hc, int64_t V, int64_t
   if (dtype == RL_DTYPE_BF16) {
     FwdEpi<bf16_t> e{a.inv_t, a.V, a.Tc, a.J, a.part_m, a.part_s, a.part_t,
                      static_cast<bf16_t*>(a.P), a.ldp};
-    return launch_bf16(static_cast<const bf16_t*>(W), H, static_cast<const bf16_t*>(hc), H, V, Tc,
-                       H, 1, round_up(H, BF_BK), e, s);
+    return launch_bf16<false>(static_cast<const bf16_t*>(W), H, static_cast<const bf16_t*>(hc), H,
+                              V, Tc, H, 1, round_up(H, BF_BK), e, s);
   }
   FwdEpi<float> e{a.inv_t, a.V, a.Tc, a.J, a.part_m, a.part_s, a.part_t,
                   static_cast<float*>(a.P), a.ldp};
@@ -576,9 +648,9 @@ hipError_t gemm_store(int dtype, const void* A, int64_t lda, const void* B, int6
                       int64_t M, int64_t N, int64_t K, int splits, int64_t k_split, float* C,
                       int64_t ldc, int64_t split_stride, hipStream_t s) {
   StoreEpi e{C, ldc, split_stride, M, N};
-  if (dtype == RL_DTYPE_BF16)
-    return launch_bf16(static_cast<const bf16_t*>(A), lda, static_cast<const bf16_t*>(B), ldb, M,
-                       N, K, splits, k_split, e, s);
+  if (dtype == RL_DTYPE_BF16)  // tiled operands
+    return launch_bf16<true>(static_cast<const bf16_t*>(A), lda, static_cast<const bf16_t*>(B),
+                             ldb, M, N, K, splits, k_split, e, s);
   return launch_f32(static_cast<const float*>(A), lda, static_cast<const float*>(B), ldb, M, N, K,
                     splits, k_split, e, s);
 }
@@ -587,9 +659,9 @@ hipError_t gemm_dw(int dtype, const void* A, int64_t lda, const void* B, int64_t
                    int64_t N, int64_t K, float* C, int64_t ldc, int accumulate, hipStream_t s) {
   DwEpi e{C, ldc, M, N, accumulate};
   const int bk = gemm_k_tile(dtype);
-  if (dtype == RL_DTYPE_BF16)
-    return launch_bf16(static_cast<const bf16_t*>(A), lda, static_cast<const bf16_t*>(B), ldb, M,
-                       N, K, 1, round_up(K, bk), e, s);
+  if (dtype == RL_DTYPE_BF16)  // tiled operands
+    return launch_bf16<true>(static_cast<const bf16_t*>(A), lda, static_cast<const bf16_t*>(B),
+                             ldb, M, N, K, 1, round_up(K, bk), e, s);
   return launch_f32(static_cast<const float*>(A), lda, static_cast<const float*>(B), ldb, M, N, K,
                     1, round_up(K, bk), e, s);
 }

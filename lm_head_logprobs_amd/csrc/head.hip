@@ -260,6 +260,99 @@ __global__ void __launch_bounds__(NT) form_g_kernel(T* __restrict__ P, int64_t l
   }
 }
 
+// src [S rows, C cols] row-major -> tiled [C rows, S cols] (see kernels.h).
+// One workgroup writes one 16 KB block (256 tiled rows x 32 tiled columns):
+// it reads the 32 x 256 source patch with 16-byte loads into LDS, then writes
+// the block contiguously in its swizzled order.  Out-of-range entries are 0.
+__global__ void __launch_bounds__(NT) to_tiled_t_kernel(const bf16_t* __restrict__ src,
+                                                        int64_t ld_src, int64_t S, int64_t C,
+                                                        bf16_t* __restrict__ dst, int64_t KB) {
+  constexpr int PITCH = TILE_ROWS + 8;
+  __shared__ __attribute__((aligned(16))) bf16_t tile[TILE_K][PITCH];  // [k][row]
+  const int64_t rb = blockIdx.x, kb = blockIdx.y;
+  const int64_t c0 = rb * TILE_ROWS, s0 = kb * TILE_K;
+  for (int q = threadIdx.x; q < TILE_K * (TILE_ROWS / 8); q += NT) {
+    const int sl = q / (TILE_ROWS / 8), cl = (q % (TILE_ROWS / 8)) * 8;
+    const int64_t sr = s0 + sl, c = c0 + cl;
+    u32x4 v = {0u, 0u, 0u, 0u};
+    if (sr < S && c < C) v = *reinterpret_cast<const u32x4*>(src + sr * ld_src + c);
+    *reinterpret_cast<u32x4*>(&tile[sl][cl]) = v;
+  }
+  __syncthreads();
+  bf16_t* blk = dst + (rb * KB + kb) * (TILE_ROWS * TILE_K);
+  for (int p = threadIdx.x; p < TILE_ROWS * 4; p += NT) {
+    const int r = p >> 2, ch = (p & 3) ^ ((r >> 1) & 3);
+    u32x4 out;
+    bf16_t* e = reinterpret_cast<bf16_t*>(&out);
+#pragma unroll
+    for (int k = 0; k < 8; ++k) e[k] = tile[8 * ch + k][r];
+    *reinterpret_cast<u32x4*>(blk + p * 8) = out;
+  }
+}
+
+// bf16 G / Gt in the tiled layout from P = e^(z - m_tile) (token-major).
+// One workgroup handles 32 tokens x 256 vocabulary entries: scale
+// g = kap[t] exp(m[t, v/vtile] - lse[t]) P[t, v] into LDS, then write the 32
+// rows of 8 G blocks (2 KB contiguous each) and one whole Gt block (16 KB).
+// Tokens >= Tc and entries >= V are written as zeros.
+__global__ void __launch_bounds__(NT) form_g_tiled_kernel(
+    const bf16_t* __restrict__ P, int64_t ldp, bf16_t* __restrict__ G, int64_t KB_g,
+    bf16_t* __restrict__ Gt, int64_t KB_gt, const float* __restrict__ part_m, int64_t J,
+    int vtile, const float* __restrict__ lse, const float* __restrict__ kap, int64_t V,
+    int64_t Tc) {
+  constexpr int TT = 32, VV = 256, PITCH = VV + 8;
+  __shared__ float scale[TT];
+  __shared__ __attribute__((aligned(16))) bf16_t tile[TT][PITCH];  // [token][vocab]
+  const int64_t t0 = (int64_t)blockIdx.x * TT, v0 = (int64_t)blockIdx.y * VV;
+  if (threadIdx.x < TT) {
+    const int64_t t = t0 + threadIdx.x;
+    scale[threadIdx.x] =
+        (t < Tc) ? kap[t] * __expf(part_m[t * J + v0 / vtile] - lse[t]) : 0.0f;
+  }
+  __syncthreads();
+  for (int q = threadIdx.x; q < TT * (VV / 8); q += NT) {
+    const int tl = q / (VV / 8), vl = (q % (VV / 8)) * 8;
+    const int64_t t = t0 + tl, v = v0 + vl;
+    u32x4 out = {0u, 0u, 0u, 0u};
+    if (t < Tc) {
+      const u32x4 raw = *reinterpret_cast<const u32x4*>(P + t * ldp + v);
+      float x[8];
+      Elem<bf16_t>::unpack(raw, x);
+      const float sc = scale[tl];
+#pragma unroll
+      for (int k = 0; k < 8; ++k) x[k] = (v + k < V) ? sc * x[k] : 0.0f;
+      out = Elem<bf16_t>::pack(x);
+    }
+    *reinterpret_cast<u32x4*>(&tile[tl][vl]) = out;
+  }
+  __syncthreads();
+  if (G != nullptr) {
+    // 8 K-blocks x 32 rows x 4 chunks; consecutive q -> consecutive 16 bytes.
+    const int64_t rbase = t0 % TILE_ROWS;
+    bf16_t* panel = G + ((t0 / TILE_ROWS) * KB_g + v0 / TILE_K) * (TILE_ROWS * TILE_K);
+    for (int q = threadIdx.x; q < 8 * TT * 4; q += NT) {
+      const int kbl = q / (TT * 4), rem = q % (TT * 4);
+      const int rl = rem >> 2, pc = rem & 3;
+      const int64_t r = rbase + rl;
+      const int ch = pc ^ (int)((r >> 1) & 3);
+      const u32x4 val = *reinterpret_cast<const u32x4*>(&tile[rl][kbl * TILE_K + ch * 8]);
+      *reinterpret_cast<u32x4*>(panel + (int64_t)kbl * (TILE_ROWS * TILE_K) + r * TILE_K + pc * 8) =
+          val;
+    }
+  }
+  if (Gt != nullptr) {
+    bf16_t* blk = Gt + ((v0 / TILE_ROWS) * KB_gt + t0 / TILE_K) * (TILE_ROWS * TILE_K);
+    for (int p = threadIdx.x; p < TILE_ROWS * 4; p += NT) {
+      const int r = p >> 2, ch = (p & 3) ^ ((r >> 1) & 3);
+      u32x4 out;
+      bf16_t* e = reinterpret_cast<bf16_t*>(&out);
+#pragma unroll
+      for (int k = 0; k < 8; ++k) e[k] = tile[8 * ch + k][r];
+      *reinterpret_cast<u32x4*>(blk + p * 8) = out;
+    }
+  }
+}
+
 template <typename T, typename GT>
 __global__ void __launch_bounds__(NT) finalize_dh_kernel(
     const float* __restrict__ part, int splits, int64_t split_stride, const T* __restrict__ W,
@@ -409,6 +502,23 @@ hipError_t form_g(int dtype, void* P, int64_t ldp, void* Gt, int64_t ldgt, const
     hipLaunchKernelGGL(form_g_kernel<float>, grid, dim3(NT), 0, s, static_cast<float*>(P), ldp,
                        static_cast<float*>(Gt), ldgt, part_m, J, vtile, lse_c, kappa_c, V, Tc,
                        write_g);
+  return hipGetLastError();
+}
+
+hipError_t to_tiled_t(const bf16_t* src, int64_t ld_src, int64_t S, int64_t C, bf16_t* dst,
+                      int64_t KB, int64_t kb_write, hipStream_t s) {
+  const dim3 grid((unsigned)ceil_div(C, TILE_ROWS), (unsigned)kb_write);
+  hipLaunchKernelGGL(to_tiled_t_kernel, grid, dim3(NT), 0, s, src, ld_src, S, C, dst, KB);
+  return hipGetLastError();
+}
+
+hipError_t form_g_tiled(const bf16_t* P, int64_t ldp, bf16_t* G, int64_t KB_g, bf16_t* Gt,
+                        int64_t KB_gt, const float* part_m, int64_t J, int vtile,
+                        const float* lse_c, const float* kappa_c, int64_t V, int64_t Tc,
+                        hipStream_t s) {
+  const dim3 grid((unsigned)(round_up(Tc, TILE_ROWS) / 32), (unsigned)ceil_div(ldp, 256));
+  hipLaunchKernelGGL(form_g_tiled_kernel, grid, dim3(NT), 0, s, P, ldp, G, KB_g, Gt, KB_gt, part_m,
+                     J, vtile, lse_c, kappa_c, V, Tc);
   return hipGetLastError();
 }
 

@@ -35,6 +35,31 @@ hipError_t gemm_dw(int dtype, const void* A, int64_t lda, const void* B, int64_t
 
 int gemm_k_tile(int dtype);
 
+// Tiled block layout of a bf16 operand [R rows, K columns] (the backward
+// GEMM operands): 256 x 32 blocks of 16 KB, block (rb, kb) at index
+// rb * KB + kb (KB = blocks per 256-row panel); inside a block row r holds
+// four 16-byte chunks, logical chunk c stored at position c ^ ((r >> 1) & 3).
+// Rows >= R and columns >= K of a block are zero.
+constexpr int TILE_ROWS = 256, TILE_K = 32, TILE_BLOCK_BYTES = TILE_ROWS * TILE_K * 2;
+__host__ __device__ inline int64_t tiled_offset(int64_t r, int64_t k, int64_t KB) {
+  return ((r / TILE_ROWS) * KB + k / TILE_K) * (TILE_ROWS * TILE_K) + (r % TILE_ROWS) * TILE_K +
+         ((((k % TILE_K) >> 3) ^ (((r % TILE_ROWS) >> 1) & 3)) << 3) + (k & 7);
+}
+
+// src [S rows, C cols] row-major (ld_src) -> tiled [C rows, S cols] with KB
+// blocks per panel; the blocks kb < kb_write of every panel are written (zeros
+// past S and C).
+hipError_t to_tiled_t(const bf16_t* src, int64_t ld_src, int64_t S, int64_t C, bf16_t* dst,
+                      int64_t KB, int64_t kb_write, hipStream_t s);
+
+// bf16: from P (token-major [Tc, ldp]) write G tiled [Tc rows, K = ldp] (KB_g
+// blocks per panel) and Gt tiled [ldp rows, K = tokens] (KB_gt blocks per
+// panel), scaled as form_g; either output may be null.
+hipError_t form_g_tiled(const bf16_t* P, int64_t ldp, bf16_t* G, int64_t KB_g, bf16_t* Gt,
+                        int64_t KB_gt, const float* part_m, int64_t J, int vtile,
+                        const float* lse_c, const float* kappa_c, int64_t V, int64_t Tc,
+                        hipStream_t s);
+
 // dst[c][r] = src[r][c] for r < R, 0 for R <= r < Rpad; c < C.
 hipError_t transpose_pad(int dtype, const void* src, int64_t ld_src, int64_t R, int64_t C,
                          void* dst, int64_t Rpad, hipStream_t s);
