@@ -144,15 +144,24 @@ def _sample(n, k, seed):
     return np.sort(np.random.default_rng(seed).choice(n, size=k, replace=False))
 
 
-@pytest.mark.parametrize("name", ["c3_head16k_ipo"])
+FULL = ["c3_head16k_ipo", "c4_head16k_ipo_topp_replay", "c5a_head64k_draws_ipo_k1",
+        "c5b_head64k_draws_reinforce"]
+
+
+@pytest.mark.parametrize("name", FULL)
 def test_full_size_sampled_tokens(name):
-    """The benchmarked launch configuration at full size (N=16384, H=2048,
-    V=152064): per-token outputs and dh rows on a token sample against the
-    oracle token by token; the loss against the sum of the per-token losses;
-    dW rows summing to zero (each token's logit gradient sums to zero over
-    the vocabulary)."""
+    """The benchmarked launch configuration at full size (H=2048, V=152064;
+    16384 or 65536 tokens): per-token outputs, support log-probs and dh rows
+    on a token sample against the oracle token by token; the loss against the
+    fp64 sum of the per-token losses; the batch passes validation; dW column
+    sums vanish (each token's logit gradient sums to zero over the
+    vocabulary)."""
+    from lm_head_logprobs_amd import ops as _ops
     wl = make_head(name, device=DEV)
-    print(f"[case] {name} full size", flush=True)
+    print(f"[case] {name} full size N={wl.N} nnz={wl.nnz} info={wl.info}", flush=True)
+    st, flags = _ops.validate(wl.labels, wl.infer_logprobs, wl.adv, wl.V, wl.offsets, wl.ids,
+                              wl.u, wl.logq, wl.params["replayed"])
+    assert flags == 0, hex(flags)
     _, got = run_head(wl)
     tok = _sample(wl.N, 24, 1)
     ref = ohead.from_workload(wl, tokens=tok, want_grads=True)
@@ -160,23 +169,25 @@ def test_full_size_sampled_tokens(name):
     ok = ~near
     dh_err = rel_fro(got["dh"][tok][ok], ref["dh"][ok])
     assert dh_err <= 1e-2, dh_err
-    # loss = sum of per-token losses / D, summed here in fp64
     total = got["token_loss"].sum() / wl.params["loss_norm"]
     assert abs(got["loss"][0] - total) <= 1e-5 * abs(total) + 1e-7
-    # column sums of dW vanish: sum_v dL/dz_{t,v} = 0 for every token, so the
-    # label terms (scale sum_t |s_t w_t| |h_t| / D) cancel against the softmax part.
+    # Column sums of dW: the label, support and softmax parts of each token's
+    # logit gradient cancel; scale = sum_t (|s_t| (w_t + sum_e c_e) + beta sum_e u_e) |h_t| / D.
     col = got["dW"].sum(axis=0)
     hn = np.linalg.norm(to_np(wl.h), axis=1)
-    scale = np.sum(np.abs(got["weight"] * to_np(wl.adv)) * hn) / wl.params["loss_norm"]
+    a = np.abs(to_np(wl.adv))
+    beta = ohead.kl_beta(wl.params)
+    scale = np.sum((a * (np.abs(got["weight"]) + 5.0) + 2 * beta) * hn) / wl.params["loss_norm"]
     assert np.linalg.norm(col) <= 1e-3 * scale
 
 
-@pytest.mark.parametrize("name", ["c3_head16k_ipo"])
+@pytest.mark.parametrize("name", ["c3_head16k_ipo", "c5b_head64k_draws_reinforce"])
 def test_full_size_dW_on_token_sample(name):
     """Full-size launch with the advantage zeroed outside a token sample (no
     KL): only sampled tokens carry gradient, so dW over all 152064 rows is the
     oracle's dW from those tokens."""
-    n = 16384
+    from synth.gen import HEAD_CONFIGS
+    n = HEAD_CONFIGS[name]["N"]
     mask = torch.zeros(n, dtype=torch.bool)
     tok = _sample(n, 16, 2)
     mask[torch.as_tensor(tok)] = True
