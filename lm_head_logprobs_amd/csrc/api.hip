@@ -29,12 +29,12 @@ using namespace rl;
 enum ProfKind {
   K_GEMM_FWD, K_COMBINE, K_FORM_G, K_GEMM_DH, K_TRANSPOSE_H, K_GEMM_DW, K_FINALIZE_DH,
   K_TRANSPOSE_W, K_CSR_ROWS, K_CSC_BUILD, K_SPARSE_DW, K_REDUCE, K_ELEMENTWISE, K_VALIDATE,
-  K_COUNT
+  K_ELEM_FINAL, K_COUNT
 };
 const char* const kProfNames[K_COUNT] = {
     "gemm_fwd",   "combine",   "form_g",   "gemm_dh",   "transpose_h",
     "gemm_dw",    "finalize_dh", "transpose_w", "csr_rows", "csc_build",
-    "sparse_dw",  "reduce",    "elementwise", "validate"};
+    "sparse_dw",  "reduce",    "elementwise", "validate", "elementwise_final"};
 
 struct ProfRec {
   int kind;
@@ -522,6 +522,9 @@ rl_status rl_loss_elementwise(const float* lp, const float* lq, const float* adv
   RL_TRY(timed(K_ELEMENTWISE, s, [&] {
     return rl::elementwise(lp, lq, adv, N, *cfg, out->mask_word, out->w_primary,
                            static_cast<double*>(workspace), out->sums, s);
+  }));
+  RL_TRY(timed(K_ELEM_FINAL, s, [&] {
+    return rl::elementwise_final(static_cast<const double*>(workspace), N, out->sums, s);
   }));
   return RL_OK;
 }
