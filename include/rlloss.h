@@ -228,11 +228,17 @@ typedef struct rl_elem_out {
   double* sums;         /* [RL_ELEM_SUM_COUNT] required */
 } rl_elem_out;
 
-/* Workspace bytes for rl_loss_elementwise with N tokens. */
+/* Largest N rl_loss_elementwise accepts. */
+#define RL_ELEM_MAX_N (((int64_t)1) << 38)
+
+/* Workspace bytes for rl_loss_elementwise with N tokens (at most
+ * RL_ELEM_SUM_COUNT * 1024 doubles, 296 KiB). */
 rl_status rl_elementwise_workspace_size(int64_t N, size_t* bytes);
 
 /*
- * rl_loss_elementwise -- one pass over lp, lq, A [N] fp32 (device).
+ * rl_loss_elementwise -- one pass over lp, lq, A [N] fp32 (device), 1 <= N <=
+ * RL_ELEM_MAX_N.  lp, lq, adv, mask_word and w_primary 16-byte aligned.  The
+ * sums are deterministic: the same inputs give the same bits on every call.
  * Errors: RL_E_ARG, RL_E_CFG, RL_E_WORKSPACE, RL_E_HIP.
  */
 rl_status rl_loss_elementwise(const float* lp, const float* lq, const float* adv, int64_t N,

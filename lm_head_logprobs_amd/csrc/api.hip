@@ -488,7 +488,7 @@ rl_status rl_loss_fwd_bwd(const void* h, const void* W, const int32_t* labels,
 }
 
 rl_status rl_elementwise_workspace_size(int64_t N, size_t* bytes) {
-  if (bytes == nullptr || N < 1) return RL_E_ARG;
+  if (bytes == nullptr || N < 1 || N > RL_ELEM_MAX_N) return RL_E_ARG;
   int64_t b;
   if (!mul_ok(elem_num_blocks(N), (int64_t)RL_ELEM_SUM_COUNT * 8, &b)) return RL_E_ARG;
   *bytes = (size_t)b;
@@ -499,7 +499,7 @@ rl_status rl_loss_elementwise(const float* lp, const float* lq, const float* adv
                               const rl_elem_cfg* cfg, const rl_elem_out* out, void* workspace,
                               size_t workspace_bytes, void* stream) {
   if (lp == nullptr || lq == nullptr || adv == nullptr || cfg == nullptr || out == nullptr ||
-      out->sums == nullptr || N < 1)
+      out->sums == nullptr || N < 1 || N > RL_ELEM_MAX_N)
     return RL_E_ARG;
   if (!aligned(lp, 16) || !aligned(lq, 16) || !aligned(adv, 16) ||
       (out->mask_word && !aligned(out->mask_word, 16)) ||

@@ -13,215 +13,392 @@
 //  * decoupled PPO with token-level truncated IS ("Decoupled, 3-policy PPO
 //    Importance Sampling", "Importance Sampling / Token Level"), with the
 //    proximal policy equal to the trainer policy: w = min(r, U), l = -w A.
-// Each 256-thread block handles 2048 consecutive tokens (two 16-byte loads per
-// stream per thread, non-temporal), writes a uint16 mask word and the primary
-// IPO weight per token, and one row of fp64 partial sums (fp32 per thread over
-// 8 tokens, fp64 from the wave reduction on).  A single-block pass then sums
-// the block rows in a fixed order, so the totals are deterministic.
+//
+// The pass reads 12 bytes and writes 6 per token, so it is HBM-bound only if
+// the arithmetic stays below about 70 VALU operations per token (wave64 fp32
+// VALU issues one instruction per 4 cycles per SIMD).  To get there:
+//  * |P - Q| = |Q (r - 1)| needs two exponentials, not three;
+//  * the eps count is a template parameter (no per-eps branches);
+//  * every mask bit's count is the popcount of the compare's own lane mask,
+//    accumulated per wave on the scalar unit, which runs beside the VALU;
+//  * the loss and weight sums are plain fp32 FMAs per thread.
+// The grid holds at most kMaxBlocks blocks, all resident at once.  Each block
+// writes one fp64 row of the RL_ELEM_SUM_COUNT sums, stored sum-major, and a
+// second launch with one block per sum adds the rows in a fixed order, so the
+// totals are deterministic.
 #include "kernels.h"
 
 namespace rl {
 namespace {
 
 constexpr int NT = 256;
-constexpr int PER = 8;  // tokens per thread (multiple of 4)
+constexpr int kMaxBlocks = 1024;  // 4 resident 256-thread blocks per CU, 256 CUs
 constexpr int NS = RL_ELEM_SUM_COUNT;
 
 struct ElemP {
-  int n_eps, primary;
   float eps[RL_ELEM_MAX_EPS];
-  float M, lo, hi, cl, ch, c, U;
+  float eps_primary;
+  float M, lo, hi;
+  float clo, chi;  // 1 - clip_low, 1 + clip_high
+  float c, U;
 };
 
-__device__ __forceinline__ void token(float lp, float lq, float A, const ElemP& p, float* acc,
-                                      uint32_t* word, float* wprim) {
-  const float P = __expf(lp), Q = __expf(lq), r = __expf(lp - lq);
-  const float dPQ = fabsf(P - Q);
+template <int NE>
+struct Sums {
+  static constexpr int NF = 2 * NE + 7;  // fp32 per-thread sums
+  static constexpr int NC = NE + 5;      // wave-uniform mask-bit counts
+  // float slots
+  static constexpr int IPO = 0;          // 2i: sum w*(-A lp), 2i+1: sum w
+  static constexpr int ICE = 2 * NE;     // loss, weight
+  static constexpr int REINF = 2 * NE + 2;
+  static constexpr int PPO_J = 2 * NE + 3;   // sum J   (loss = -sum)
+  static constexpr int PPO_D = 2 * NE + 4;   // sum lp - lq (kl = -sum)
+  static constexpr int TIS_WA = 2 * NE + 5;  // sum w A (loss = -sum)
+  static constexpr int TIS_W = 2 * NE + 6;
+  // count slots
+  static constexpr int C_IPO = 0;        // masked count per eps
+  static constexpr int C_LOW = NE, C_HIGH = NE + 1, C_CLIP = NE + 2, C_DUAL = NE + 3,
+                       C_TRUNC = NE + 4;
+};
+
+// min / max as one v_med3_f32 (no NaN canonicalisation of the operands;
+// the inputs are finite)
+__device__ __forceinline__ float fmin_(float a, float b) {
+  return __builtin_amdgcn_fmed3f(a, b, -__builtin_inff());
+}
+__device__ __forceinline__ float fmax_(float a, float b) {
+  return __builtin_amdgcn_fmed3f(a, b, __builtin_inff());
+}
+
+__device__ __forceinline__ uint32_t lane_count(bool b) {
+  return (uint32_t)__builtin_popcountll(__builtin_amdgcn_ballot_w64(b));
+}
+
+// One token.  Returns its mask word; adds into the per-thread float sums f
+// and the per-wave counts c.  Every lane of the wave must call it (the counts
+// are popcounts of whole-wave lane masks).  With GUARD, lanes whose `ok` is
+// false (past the end of the input) contribute nothing.
+template <int NE, bool GUARD>
+__device__ __forceinline__ uint32_t token(float lp, float lq, float A, bool ok, const ElemP& p,
+                                          float* f, uint32_t* c, float* wprim) {
+  using S = Sums<NE>;
+  if (GUARD && !ok) lp = lq = A = 0.0f;  // zero loss terms; weights are zeroed below
+  const float d = lp - lq;
+  const float r = __expf(d);
+  const float Q = __expf(lq);
+  const float dPQ = fabsf(fmaf(Q, r, -Q));  // |P - Q| with P = Q r
+  const float Alp = -A * lp;
+  const float rm = (GUARD && !ok) ? 0.0f : fmin_(r, p.M);
   uint32_t wd = 0;
-  float wp = 0.0f;
 #pragma unroll
-  for (int i = 0; i < RL_ELEM_MAX_EPS; ++i) {
-    if (i < p.n_eps) {
-      const bool masked = dPQ > p.eps[i];
-      const float w = masked ? 0.0f : fminf(r, p.M);
-      wd |= (uint32_t)masked << (RL_ELEM_BIT_IPO0 + i);
-      acc[3 * i + 0] += masked ? 0.0f : 1.0f;
-      acc[3 * i + 1] += -A * w * lp;
-      acc[3 * i + 2] += w;
-      if (i == p.primary) wp = w;
-    }
+  for (int i = 0; i < NE; ++i) {
+    const bool masked = dPQ > p.eps[i];  // false for the zeroed lanes (eps >= 0)
+    const float w = masked ? 0.0f : rm;
+    f[S::IPO + 2 * i] = fmaf(w, Alp, f[S::IPO + 2 * i]);
+    f[S::IPO + 2 * i + 1] += w;
+    wd |= masked ? (1u << (RL_ELEM_BIT_IPO0 + i)) : 0u;
+    c[S::C_IPO + i] += lane_count(masked);
   }
+  *wprim = dPQ > p.eps_primary ? 0.0f : rm;
   {
-    const bool low = r < p.lo, high = r > p.hi, kept = !(low || high);
-    const float w = kept ? r : 0.0f;
-    wd |= ((uint32_t)low << RL_ELEM_BIT_ICEPOP_LOW) | ((uint32_t)high << RL_ELEM_BIT_ICEPOP_HIGH);
-    acc[RL_ELEM_ICEPOP_KEPT] += kept ? 1.0f : 0.0f;
-    acc[RL_ELEM_ICEPOP_LOW] += low ? 1.0f : 0.0f;
-    acc[RL_ELEM_ICEPOP_HIGH] += high ? 1.0f : 0.0f;
-    acc[RL_ELEM_ICEPOP_LOSS] += -A * w * lp;
-    acc[RL_ELEM_ICEPOP_WEIGHT] += w;
+    bool low = r < p.lo, high = r > p.hi;
+    if (GUARD) low = low && ok, high = high && ok;
+    const float w = (low || high || (GUARD && !ok)) ? 0.0f : r;
+    f[S::ICE] = fmaf(w, Alp, f[S::ICE]);
+    f[S::ICE + 1] += w;
+    wd |= (low ? (1u << RL_ELEM_BIT_ICEPOP_LOW) : 0u) |
+          (high ? (1u << RL_ELEM_BIT_ICEPOP_HIGH) : 0u);
+    c[S::C_LOW] += lane_count(low);
+    c[S::C_HIGH] += lane_count(high);
   }
-  acc[RL_ELEM_REINFORCE_LOSS] += -A * lp;
+  f[S::REINF] += Alp;
   {
+    // with A = 0 every term below is 0 and neither bit is set
     const float J1 = r * A;
-    const float J2 = fminf(fmaxf(r, 1.0f - p.cl), 1.0f + p.ch) * A;
-    const float Jmin = fminf(J1, J2);
+    const float J2 = __builtin_amdgcn_fmed3f(r, p.clo, p.chi) * A;
+    const float Jmin = fmin_(J1, J2);
     const float cA = p.c * A;
     const bool neg = A < 0.0f;
     const bool dual = neg && (cA > Jmin);
-    const float J = neg ? fmaxf(Jmin, cA) : Jmin;
+    const float J = neg ? fmax_(Jmin, cA) : Jmin;
     const bool clip = J2 < J1;
-    wd |= ((uint32_t)clip << RL_ELEM_BIT_PPO_CLIP) | ((uint32_t)dual << RL_ELEM_BIT_DUAL_CLIP);
-    acc[RL_ELEM_PPO_LOSS] += -J;
-    acc[RL_ELEM_PPO_CLIP] += clip ? 1.0f : 0.0f;
-    acc[RL_ELEM_PPO_CLIP_LOWER] += dual ? 1.0f : 0.0f;
-    acc[RL_ELEM_PPO_KL] += lq - lp;
+    f[S::PPO_J] += J;
+    f[S::PPO_D] += d;
+    wd |= (clip ? (1u << RL_ELEM_BIT_PPO_CLIP) : 0u) |
+          (dual ? (1u << RL_ELEM_BIT_DUAL_CLIP) : 0u);
+    c[S::C_CLIP] += lane_count(clip);
+    c[S::C_DUAL] += lane_count(dual);
   }
   {
-    const bool trunc = r > p.U;
-    const float w = fminf(r, p.U);
-    wd |= (uint32_t)trunc << RL_ELEM_BIT_TIS_TRUNC;
-    acc[RL_ELEM_TIS_LOSS] += -w * A;
-    acc[RL_ELEM_TIS_TRUNC] += trunc ? 1.0f : 0.0f;
-    acc[RL_ELEM_TIS_WEIGHT] += w;
+    bool trunc = r > p.U;
+    if (GUARD) trunc = trunc && ok;
+    const float w = (GUARD && !ok) ? 0.0f : fmin_(r, p.U);
+    f[S::TIS_WA] = fmaf(w, A, f[S::TIS_WA]);
+    f[S::TIS_W] += w;
+    wd |= trunc ? (1u << RL_ELEM_BIT_TIS_TRUNC) : 0u;
+    c[S::C_TRUNC] += lane_count(trunc);
   }
-  *word = wd;
+  // Pin the word and the weight in VGPRs here: otherwise the compiler sinks
+  // their selects down to the stores and keeps every lane mask of the four
+  // tokens alive in SGPRs until then.
+  float wp = *wprim;
+  __asm__ volatile("" : "+v"(wd), "+v"(wp));
   *wprim = wp;
+  return wd;
 }
 
-// Fixed-order block reduction of NS sums through LDS: every thread stores its
-// fp32 partials; lane k of each wave then adds the 64 values of sum k of its
-// wave in fp64 and lane order; finally the 4 wave results are added in wave
-// order.  Deterministic and free of cross-lane shuffles.
-__device__ __forceinline__ void block_reduce_store(const float* acc, double* out) {
-  __shared__ float vals[NS][NT + 1];
-  __shared__ double wsum[4][NS];
-  const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
+struct Chunk {
+  f32x4 lp, lq, A;
+};
+
+// The lane's 4-token vector of a whole 64-vector chunk.
+__device__ __forceinline__ Chunk load_full(const f32x4* __restrict__ lp,
+                                           const f32x4* __restrict__ lq,
+                                           const f32x4* __restrict__ adv, int ch) {
+  const int64_t v = (int64_t)ch * 64;
+  return {__builtin_nontemporal_load(lp + v), __builtin_nontemporal_load(lq + v),
+          __builtin_nontemporal_load(adv + v)};
+}
+
+// WORD / WPRIM: whether the mask words / primary weights are stored (as
+// template parameters, so the token loop has no branches around the stores).
+//
+// Work split: the input is cut into chunks of 64 4-token vectors (one 16-byte
+// vector per lane per stream).  Global wave slot s = wave * gridDim.x + block
+// takes chunks s, s + S, s + 2S, ... (S = 4 gridDim.x, all slots resident),
+// so the chunks left over after whole rounds go to wave 0 of distinct blocks,
+// which sit on distinct CUs.  Each wave loads its next chunk before it works
+// on the current one.
+template <int NE, bool WORD, bool WPRIM>
+__global__ void __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(4, 8)))
+elem_main_kernel(const float* __restrict__ lp, const float* __restrict__ lq,
+                 const float* __restrict__ adv, int64_t N, ElemP pk, uint16_t* __restrict__ word,
+                 float* __restrict__ wprim, double* __restrict__ partials) {
+  using S = Sums<NE>;
+  float f[S::NF];
+  uint32_t c[S::NC];
 #pragma unroll
-  for (int k = 0; k < NS; ++k) vals[k][threadIdx.x] = acc[k];
+  for (int k = 0; k < S::NF; ++k) f[k] = 0.0f;
+#pragma unroll
+  for (int k = 0; k < S::NC; ++k) c[k] = 0;
+  // The thresholds live in VGPRs (the asm hides that they are uniform): the
+  // SGPRs are needed for the lane masks and the wave counts.
+  ElemP p;
+#pragma unroll
+  for (int i = 0; i < NE; ++i) {
+    p.eps[i] = pk.eps[i];
+    __asm__ volatile("" : "+v"(p.eps[i]));
+  }
+  p.eps_primary = pk.eps_primary, p.M = pk.M, p.lo = pk.lo, p.hi = pk.hi;
+  p.clo = pk.clo, p.chi = pk.chi, p.c = pk.c, p.U = pk.U;
+  __asm__ volatile("" : "+v"(p.eps_primary), "+v"(p.M), "+v"(p.lo), "+v"(p.hi));
+  __asm__ volatile("" : "+v"(p.clo), "+v"(p.chi), "+v"(p.c), "+v"(p.U));
+  // Chunk indices are 32-bit (the host limits N to 2^38 tokens).
+  const int nfull = (int)(N / 256);  // chunks of 256 tokens entirely in range
+  // The wave index is made provably uniform so that every branch below is a
+  // scalar branch and the counts stay whole-wave values.
+  const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+  const int stride = 4 * (int)gridDim.x;
+  const int slot = wv * (int)gridDim.x + (int)blockIdx.x;
+  const f32x4* lp4 = reinterpret_cast<const f32x4*>(lp) + lane;
+  const f32x4* lq4 = reinterpret_cast<const f32x4*>(lq) + lane;
+  const f32x4* adv4 = reinterpret_cast<const f32x4*>(adv) + lane;
+  int nown = 0;  // whole chunks this wave covers
+  Chunk cur;
+  if (slot < nfull) cur = load_full(lp4, lq4, adv4, slot);
+  for (int ch = slot; ch < nfull; ch += stride) {
+    Chunk nxt;
+    if (ch + stride < nfull) nxt = load_full(lp4, lq4, adv4, ch + stride);
+    ++nown;
+    uint32_t wd[4];
+    float wv4[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      wd[j] = token<NE, false>(cur.lp[j], cur.lq[j], cur.A[j], true, p, f, c, &wv4[j]);
+      // one token's lane masks live at a time (they are SGPR pairs)
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    const int64_t v = (int64_t)ch * 64 + lane;
+    if constexpr (WORD) {
+      const u32x2 pk = {wd[0] | (wd[1] << 16), wd[2] | (wd[3] << 16)};
+      __builtin_nontemporal_store(pk, reinterpret_cast<u32x2*>(word) + v);
+    }
+    if constexpr (WPRIM) {
+      f32x4 o = {wv4[0], wv4[1], wv4[2], wv4[3]};
+      __builtin_nontemporal_store(o, reinterpret_cast<f32x4*>(wprim) + v);
+    }
+    cur = nxt;
+  }
+  int64_t ntok = (int64_t)nown * 256;  // tokens this wave covers (uniform)
+  // The chunk that holds the end of the input (N % 256 tokens), read token by
+  // token, belongs to the slot that the round-robin gives it.
+  if (N % 256 != 0 && nfull % stride == slot) {
+    ntok += N % 256;
+    const int64_t i0 = ((int64_t)nfull * 64 + lane) * 4;
+    float x[4], y[4], z[4], wv4[4];
+    uint32_t wd[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const bool in = i0 + j < N;
+      x[j] = in ? lp[i0 + j] : 0.0f;
+      y[j] = in ? lq[i0 + j] : 0.0f;
+      z[j] = in ? adv[i0 + j] : 0.0f;
+    }
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      wd[j] = token<NE, true>(x[j], y[j], z[j], i0 + j < N, p, f, c, &wv4[j]);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    for (int j = 0; j < 4; ++j) {
+      if (i0 + j < N) {
+        if constexpr (WORD) word[i0 + j] = (uint16_t)wd[j];
+        if constexpr (WPRIM) wprim[i0 + j] = wv4[j];
+      }
+    }
+  }
+
+  // Block reduction in a fixed order.  Float sums: every thread stores its
+  // values in LDS; lane k of each wave adds the 64 values of sum k of its
+  // wave in fp64 (four interleaved chains, then combined); the 4 wave
+  // results are added in wave order.  Counts: wave totals, added exactly.
+  __shared__ float vals[S::NF][NT + 4];
+  __shared__ double wsum[4][S::NF];
+  __shared__ uint32_t wcnt[4][S::NC];
+  __shared__ int64_t wtok[4];
+  const int w = wv;
+#pragma unroll
+  for (int k = 0; k < S::NF; ++k) vals[k][threadIdx.x] = f[k];
+  if (lane == 0) {
+#pragma unroll
+    for (int k = 0; k < S::NC; ++k) wcnt[w][k] = c[k];
+    wtok[w] = ntok;
+  }
   __syncthreads();
-  if (lane < NS) {
-    double sacc = 0.0;
+  if (lane < S::NF) {
     const float* row = &vals[lane][w * 64];
-#pragma unroll 8
-    for (int i = 0; i < 64; ++i) sacc += (double)row[i];
-    wsum[w][lane] = sacc;
+    double s0 = 0.0, s1 = 0.0, s2 = 0.0, s3 = 0.0;
+#pragma unroll 4
+    for (int i = 0; i < 64; i += 4) {
+      const f32x4 x = *reinterpret_cast<const f32x4*>(row + i);
+      s0 += (double)x[0];
+      s1 += (double)x[1];
+      s2 += (double)x[2];
+      s3 += (double)x[3];
+    }
+    wsum[w][lane] = (s0 + s1) + (s2 + s3);
   }
   __syncthreads();
   if (threadIdx.x < NS) {
     const int k = threadIdx.x;
-    out[k] = ((wsum[0][k] + wsum[1][k]) + wsum[2][k]) + wsum[3][k];
+    const int64_t btok = wtok[0] + wtok[1] + wtok[2] + wtok[3];
+    auto fs = [&](int slot) {
+      return ((wsum[0][slot] + wsum[1][slot]) + wsum[2][slot]) + wsum[3][slot];
+    };
+    auto cs = [&](int slot) {
+      return (double)(wcnt[0][slot] + wcnt[1][slot] + wcnt[2][slot] + wcnt[3][slot]);
+    };
+    double v = 0.0;
+    if (k < 3 * RL_ELEM_MAX_EPS) {
+      const int i = k / 3, m = k % 3;
+      if (i < NE) {
+        v = m == 0 ? (double)btok - cs(S::C_IPO + i) : m == 1 ? fs(S::IPO + 2 * i)
+                                                              : fs(S::IPO + 2 * i + 1);
+      }
+    } else {
+      switch (k) {
+        case RL_ELEM_ICEPOP_KEPT: v = (double)btok - cs(S::C_LOW) - cs(S::C_HIGH); break;
+        case RL_ELEM_ICEPOP_LOW: v = cs(S::C_LOW); break;
+        case RL_ELEM_ICEPOP_HIGH: v = cs(S::C_HIGH); break;
+        case RL_ELEM_ICEPOP_LOSS: v = fs(S::ICE); break;
+        case RL_ELEM_ICEPOP_WEIGHT: v = fs(S::ICE + 1); break;
+        case RL_ELEM_REINFORCE_LOSS: v = fs(S::REINF); break;
+        case RL_ELEM_PPO_LOSS: v = -fs(S::PPO_J); break;
+        case RL_ELEM_PPO_CLIP: v = cs(S::C_CLIP); break;
+        case RL_ELEM_PPO_CLIP_LOWER: v = cs(S::C_DUAL); break;
+        case RL_ELEM_PPO_KL: v = -fs(S::PPO_D); break;
+        case RL_ELEM_TIS_LOSS: v = -fs(S::TIS_WA); break;
+        case RL_ELEM_TIS_TRUNC: v = cs(S::C_TRUNC); break;
+        case RL_ELEM_TIS_WEIGHT: v = fs(S::TIS_W); break;
+        default: break;
+      }
+    }
+    partials[(int64_t)k * gridDim.x + blockIdx.x] = v;
   }
 }
 
-__global__ void __launch_bounds__(NT) elem_main_kernel(const float* __restrict__ lp,
-                                                       const float* __restrict__ lq,
-                                                       const float* __restrict__ adv, int64_t N,
-                                                       ElemP p, uint16_t* __restrict__ word,
-                                                       float* __restrict__ wprim,
-                                                       double* __restrict__ partials) {
-  float acc[NS];
-#pragma unroll
-  for (int k = 0; k < NS; ++k) acc[k] = 0.0f;
-  // PER consecutive tokens per thread, as PER/4 16-byte vectors per stream;
-  // the vectors of one thread are NT*4 tokens apart so a wave's loads are
-  // contiguous.
-  const int64_t base = (int64_t)blockIdx.x * NT * PER + (int64_t)threadIdx.x * 4;
-  if (base + (int64_t)NT * 4 * (PER / 4 - 1) + 4 <= N) {
-    f32x4 a[PER / 4], b[PER / 4], c[PER / 4];
-#pragma unroll
-    for (int v = 0; v < PER / 4; ++v) {
-      const int64_t i0 = base + (int64_t)v * NT * 4;
-      a[v] = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(lp + i0));
-      b[v] = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(lq + i0));
-      c[v] = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(adv + i0));
-    }
-#pragma unroll
-    for (int v = 0; v < PER / 4; ++v) {
-      const int64_t i0 = base + (int64_t)v * NT * 4;
-      uint32_t wd[4];
-      float wv[4];
-#pragma unroll
-      for (int k = 0; k < 4; ++k) token(a[v][k], b[v][k], c[v][k], p, acc, &wd[k], &wv[k]);
-      if (word) {
-        uint2 pk;
-        pk.x = wd[0] | (wd[1] << 16);
-        pk.y = wd[2] | (wd[3] << 16);
-        __builtin_nontemporal_store(pk.x, reinterpret_cast<uint32_t*>(word + i0));
-        __builtin_nontemporal_store(pk.y, reinterpret_cast<uint32_t*>(word + i0) + 1);
-      }
-      if (wprim) {
-        f32x4 o = {wv[0], wv[1], wv[2], wv[3]};
-        __builtin_nontemporal_store(o, reinterpret_cast<f32x4*>(wprim + i0));
-      }
-    }
-  } else {
-    for (int v = 0; v < PER / 4; ++v)
-      for (int k = 0; k < 4; ++k) {
-        const int64_t i = base + (int64_t)v * NT * 4 + k;
-        if (i >= N) continue;
-        uint32_t wd;
-        float wv;
-        token(lp[i], lq[i], adv[i], p, acc, &wd, &wv);
-        if (word) word[i] = (uint16_t)wd;
-        if (wprim) wprim[i] = wv;
-      }
-  }
-  block_reduce_store(acc, partials + (int64_t)blockIdx.x * NS);
-}
-
-// Sum of the per-block rows: thread t adds rows t, t + NT, ... in that
-// order (all NS sums, fp64), then a fixed-order tree over the threads in LDS.
+// One block per sum: thread t adds rows t, t + NT, ... in that order, then a
+// fixed-order tree over the threads in LDS.
 __global__ void __launch_bounds__(NT) elem_final_kernel(const double* __restrict__ partials,
                                                         int64_t nb, double* __restrict__ sums) {
-  __shared__ double part[NS][NT];
-  double acc[NS];
-#pragma unroll
-  for (int k = 0; k < NS; ++k) acc[k] = 0.0;
-  for (int64_t b = threadIdx.x; b < nb; b += NT) {
-    const double* row = partials + b * NS;
-#pragma unroll
-    for (int k = 0; k < NS; ++k) acc[k] += row[k];
-  }
-#pragma unroll
-  for (int k = 0; k < NS; ++k) part[k][threadIdx.x] = acc[k];
+  __shared__ double part[NT];
+  const double* row = partials + (int64_t)blockIdx.x * nb;
+  double acc = 0.0;
+  for (int64_t b = threadIdx.x; b < nb; b += NT) acc += row[b];
+  part[threadIdx.x] = acc;
   __syncthreads();
   for (int stride = NT / 2; stride > 0; stride >>= 1) {
-    for (int q = threadIdx.x; q < NS * stride; q += NT) {
-      const int k = q / stride, i = q % stride;
-      part[k][i] += part[k][i + stride];
-    }
+    if (threadIdx.x < stride) part[threadIdx.x] += part[threadIdx.x + stride];
     __syncthreads();
   }
-  if (threadIdx.x < NS) sums[threadIdx.x] = part[threadIdx.x][0];
+  if (threadIdx.x == 0) sums[blockIdx.x] = part[0];
+}
+
+template <int NE>
+void launch_main(int64_t nb, const float* lp, const float* lq, const float* adv, int64_t N,
+                 const ElemP& p, uint16_t* word, float* wprim, double* partials, hipStream_t s) {
+  const dim3 g((unsigned)nb), b(NT);
+  if (word && wprim)
+    hipLaunchKernelGGL((elem_main_kernel<NE, true, true>), g, b, 0, s, lp, lq, adv, N, p, word,
+                       wprim, partials);
+  else if (word)
+    hipLaunchKernelGGL((elem_main_kernel<NE, true, false>), g, b, 0, s, lp, lq, adv, N, p, word,
+                       wprim, partials);
+  else if (wprim)
+    hipLaunchKernelGGL((elem_main_kernel<NE, false, true>), g, b, 0, s, lp, lq, adv, N, p, word,
+                       wprim, partials);
+  else
+    hipLaunchKernelGGL((elem_main_kernel<NE, false, false>), g, b, 0, s, lp, lq, adv, N, p, word,
+                       wprim, partials);
 }
 
 }  // namespace
 
-int64_t elem_num_blocks(int64_t N) { return std::max<int64_t>(ceil_div(N, (int64_t)NT * PER), 1); }
+int64_t elem_num_blocks(int64_t N) {
+  const int64_t nch = (std::max<int64_t>(N, 1) + 255) / 256;  // 64-vector chunks
+  return std::min<int64_t>(ceil_div(nch, (int64_t)4), kMaxBlocks);
+}
 
 hipError_t elementwise(const float* lp, const float* lq, const float* adv, int64_t N,
                        const rl_elem_cfg& c, uint16_t* word, float* w_primary, double* partials,
-                       double* sums, hipStream_t s) {
+                       double* /*sums*/, hipStream_t s) {
   ElemP p;
-  p.n_eps = c.n_eps;
-  p.primary = c.primary_eps_index;
-  for (int i = 0; i < RL_ELEM_MAX_EPS; ++i) p.eps[i] = c.eps[i];
+  for (int i = 0; i < RL_ELEM_MAX_EPS; ++i) p.eps[i] = i < c.n_eps ? c.eps[i] : 0.0f;
+  p.eps_primary = c.eps[c.primary_eps_index];
   p.M = c.max_ratio;
   p.lo = c.icepop_lo;
   p.hi = c.icepop_hi;
-  p.cl = c.clip_low;
-  p.ch = c.clip_high;
+  p.clo = 1.0f - c.clip_low;
+  p.chi = 1.0f + c.clip_high;
   p.c = c.clip_c;
   p.U = c.tis_upper;
   const int64_t nb = elem_num_blocks(N);
-  hipLaunchKernelGGL(elem_main_kernel, dim3((unsigned)nb), dim3(NT), 0, s, lp, lq, adv, N, p,
-                     word, w_primary, partials);
+  switch (c.n_eps) {
+    case 1: launch_main<1>(nb, lp, lq, adv, N, p, word, w_primary, partials, s); break;
+    case 2: launch_main<2>(nb, lp, lq, adv, N, p, word, w_primary, partials, s); break;
+    case 3: launch_main<3>(nb, lp, lq, adv, N, p, word, w_primary, partials, s); break;
+    case 4: launch_main<4>(nb, lp, lq, adv, N, p, word, w_primary, partials, s); break;
+    case 5: launch_main<5>(nb, lp, lq, adv, N, p, word, w_primary, partials, s); break;
+    case 6: launch_main<6>(nb, lp, lq, adv, N, p, word, w_primary, partials, s); break;
+    case 7: launch_main<7>(nb, lp, lq, adv, N, p, word, w_primary, partials, s); break;
+    case 8: launch_main<8>(nb, lp, lq, adv, N, p, word, w_primary, partials, s); break;
+    default: return hipErrorInvalidValue;
+  }
   return hipGetLastError();
 }
 
 hipError_t elementwise_final(const double* partials, int64_t N, double* sums, hipStream_t s) {
-  hipLaunchKernelGGL(elem_final_kernel, dim3(1), dim3(NT), 0, s, partials, elem_num_blocks(N),
+  hipLaunchKernelGGL(elem_final_kernel, dim3(NS), dim3(NT), 0, s, partials, elem_num_blocks(N),
                      sums);
   return hipGetLastError();
 }

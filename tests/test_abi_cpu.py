@@ -195,7 +195,10 @@ def test_elementwise_and_validate_host_errors():
     n = ctypes.c_size_t(0)
     assert L.lib().rl_elementwise_workspace_size(0, ctypes.byref(n)) == L.RL_E_ARG
     assert L.lib().rl_elementwise_workspace_size(2_160_000, ctypes.byref(n)) == L.RL_OK
-    assert n.value == 1055 * 37 * 8  # ceil(2160000 / 2048) blocks of 37 fp64 sums
+    assert n.value == 1024 * 37 * 8  # min(ceil(ceil(N / 256) / 4), 1024) blocks of 37 fp64 sums
+    assert L.lib().rl_elementwise_workspace_size(1000, ctypes.byref(n)) == L.RL_OK
+    assert n.value == 1 * 37 * 8
+    assert L.lib().rl_elementwise_workspace_size((1 << 38) + 1, ctypes.byref(n)) == L.RL_E_ARG
     from synth.gen import REPLAY_PARAMS
     good = ops.elem_cfg(REPLAY_PARAMS)
     N = 1000

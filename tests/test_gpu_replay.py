@@ -21,7 +21,9 @@ def _run(r):
     return rp, {k: v.cpu().numpy() for k, v in rp.o.items()}
 
 
-@pytest.mark.parametrize("N", [2_160_000, 1, 1023, 4097])
+# 2.16M: 2-3 chunks per wave, partial chunk on slot 245; 2**21: whole chunks only, two
+# rounds; 2**20 + 1: one-token partial chunk on slot 0 of the second round
+@pytest.mark.parametrize("N", [2_160_000, 1, 1023, 4097, 2_097_152, 1_048_577])
 def test_replay_parity(N):
     r = make_replay(N=N, device="cuda:0")
     print(f"[case] replay N={N}", flush=True)
