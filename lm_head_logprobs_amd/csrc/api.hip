@@ -198,10 +198,9 @@ rl_status make_plan(const rl_loss_cfg* c, bool has_support, bool want_dh, bool w
     if (!mul_ok(p->Vpad, p->Tc256, &vt) || !mul_ok(p->Tc256, p->Vpad, &tv) ||
         !mul_ok(H256, p->Vpad, &hv) || !mul_ok((int64_t)p->splits * p->Tc, p->H, &sth))
       return RL_E_ARG;
-    p->o_P = L.take(tv, p->esz);  // e^(z - m) token-major [Tc, Vpad] (fp32: then G in place)
     if (p->tiled) {
+      p->o_G = L.take(tv, 2);  // e^(z - m), then G, in the tiled layout
       if (p->want_dh) {
-        p->o_G = L.take(tv, 2);
         p->o_Wt = L.take(hv, 2);
         p->o_dhp = L.take(sth, 4);
       }
@@ -210,6 +209,7 @@ rl_status make_plan(const rl_loss_cfg* c, bool has_support, bool want_dh, bool w
         p->o_ht = L.take(H256 * p->Tc256, 2);
       }
     } else {
+      p->o_P = L.take(tv, p->esz);  // e^(z - m) token-major [Tc, Vpad], then G in place
       if (p->want_dW) {
         p->o_Gt = L.take(p->V * p->Tcpad, p->esz);
         p->o_ht = L.take(p->H * p->Tcpad, p->esz);
@@ -358,8 +358,8 @@ rl_status rl_loss_fwd_bwd(const void* h, const void* W, const int32_t* labels,
   auto I = [&](size_t o) { return reinterpret_cast<int32_t*>(ws + o); };
   float *pm = F(p.o_pm), *ps = F(p.o_ps), *pt = F(p.o_pt);
   float *lse = F(p.o_lse), *kap = F(p.o_kap), *stats = F(p.o_stats), *coef = F(p.o_coef);
-  void* P = p.dense ? ws + p.o_P : nullptr;
-  void* G = (p.tiled && p.want_dh) ? ws + p.o_G : nullptr;
+  void* G = p.tiled ? ws + p.o_G : nullptr;
+  void* P = p.tiled ? G : p.dense ? ws + p.o_P : nullptr;
   void* Gt = (p.dense && p.want_dW) ? ws + p.o_Gt : nullptr;
   void* Wt = (p.dense && p.want_dh) ? ws + p.o_Wt : nullptr;
   void* ht = (p.dense && p.want_dW) ? ws + p.o_ht : nullptr;
@@ -381,7 +381,7 @@ rl_status rl_loss_fwd_bwd(const void* h, const void* W, const int32_t* labels,
     const int64_t tc = std::min(p.Tc, p.N - c0);
     const int64_t tck = round_up(tc, 64);
     const void* hc = hb + c0 * p.H * p.esz;
-    FwdEpiArgs fa{cfg->inv_temperature, p.V, tc, p.J, pm, ps, pt, P, p.Vpad};
+    FwdEpiArgs fa{cfg->inv_temperature, p.V, tc, p.J, pm, ps, pt, P, p.tiled ? p.KB_v : p.Vpad};
     RL_TRY(timed(K_GEMM_FWD, s, [&] { return gemm_fwd(p.dtype, W, hc, p.V, tc, p.H, fa, s); }));
     CombineArgs ca{};
     ca.h = h;
@@ -421,9 +421,9 @@ rl_status rl_loss_fwd_bwd(const void* h, const void* W, const int32_t* labels,
     RL_TRY(timed(K_COMBINE, s, [&] { return combine(p.dtype, ca, s); }));
     if (p.tiled) {
       RL_TRY(timed(K_FORM_G, s, [&] {
-        return form_g_tiled(static_cast<const bf16_t*>(P), p.Vpad, static_cast<bf16_t*>(G), p.KB_v,
-                            static_cast<bf16_t*>(Gt), p.KB_t, pm, p.J, p.vtile, lse + c0,
-                            kap + c0, p.V, tc, s);
+        return form_g_blocks(static_cast<bf16_t*>(G), p.KB_v, p.want_dh ? 1 : 0,
+                             static_cast<bf16_t*>(Gt), p.KB_t, pm, p.J, p.vtile, lse + c0,
+                             kap + c0, p.V, tc, s);
       }));
       if (p.want_dh)
         RL_TRY(timed(K_GEMM_DH, s, [&] {

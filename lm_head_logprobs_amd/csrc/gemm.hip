@@ -6,14 +6,16 @@
 //   forward   S^T[V,Tc]  = W[V,H]      . h_c[Tc,H]^T       (K = H)
 //   dh        dh[Tc,H]   = G[Tc,V]     . (W^T)[H,V]^T      (K = V, split-K)
 //   dW        dW[V,H]    = G^T[V,Tc]   . (h_c^T)[H,Tc]^T   (K = Tc)
-// Accumulation is fp32; both MFMA shapes used here share the 32x32
-// accumulator layout  lane l, register r -> row 8*(r/4) + 4*(l/32) + r%4,
-// column l%32.
+// Accumulation is fp32.  The epilogues are written against an accumulator
+// layout (Acc16 / Acc32 below) that maps lane and register to row and column.
 //
 // bf16 kernel (the hot path).  A 256-thread workgroup (4 waves as 2x2) owns a
-// 256 x 256 output tile; each wave owns 128 x 128 as 4 x 4 blocks of
-// v_mfma_f32_32x32x16_bf16 with its 256 accumulators in AGPRs.  K advances 32
-// at a time through a 4-stage ring of LDS buffers (32 KB each: A then B).
+// 256 x 256 output tile; each wave owns 128 x 128 as 8 x 8 blocks of
+// v_mfma_f32_16x16x32_bf16 with its 256 accumulators in AGPRs.  With random
+// operands this shape sustains a higher MFMA rate than 32x32x16 (measured
+// about 84% against 72% of the dense peak in a loop without memory traffic).
+// K advances 32 at a time through a 4-stage ring of LDS buffers (32 KB each:
+// A then B).
 // Operand tiles are copied global -> LDS by buffer_load_dwordx4 ... lds: each
 // wave instruction fills 1 KB of LDS (16 bytes per lane, consecutive), no
 // VGPR staging.  Loads run three stages ahead; a stage is waited for with an
@@ -25,12 +27,16 @@
 // ds_read_b128 phase that read one chunk of 8 consecutive rows hit disjoint
 // banks.  The backward operands arrive in a tiled layout whose 16 KB blocks
 // are exactly this LDS image, so each stage load is one contiguous copy
-// (row-major operands with 300 KB row strides touch 256 pages per stage).  Workgroups are remapped so consecutive tiles land on one XCD
-// (dispatch is round-robin over the 8 XCDs) and grouped 8 tiles along M so
-// neighbours share B panels in that XCD's L2.
+// (row-major operands with 300 KB row strides touch 256 pages per stage).
+// Workgroups are remapped so consecutive tiles land on one XCD (dispatch is
+// round-robin over the 8 XCDs).  The forward GEMM groups 8 tiles along M;
+// the backward GEMMs walk blocks of 4 x 8 tiles with N fastest, so the 32
+// tiles an XCD runs at once cover at most 8 N-tiles and each slice of the
+// large operand (G or G^T) is fetched into that XCD's L2 once for all of
+// them.
 //
 // fp32 kernel (small problems).  Same tile mapping and epilogues, register
-// staged loads, v_mfma_f32_32x32x2_f32.
+// staged loads, v_mfma_f32_32x32x2_f32 (layout Acc32).
 #include "kernels.h"
 
 namespace rl {
@@ -38,6 +44,7 @@ namespace {
 
 constexpr int NT = 256;
 constexpr int GROUP_M = 8;
+constexpr int OOB = (int)0x80000000;  // a buffer offset past any descriptor's range
 
 struct TileCoord {
   int64_t m0, n0;
@@ -67,6 +74,33 @@ __device__ __forceinline__ TileCoord map_tile(int tiles_m, int tiles_n, int spli
   return tc;
 }
 
+// Blocks of 4 x 8 tiles (M x N), N fastest inside a block, blocks walked
+// along N and then M; same XCD remap as map_tile.
+__device__ __forceinline__ TileCoord map_tile_blocks(int tiles_m, int tiles_n, int splits,
+                                                     int BM, int BN) {
+  constexpr int BMT = 4, BNT = 8;
+  TileCoord tc;
+  const int nwg = gridDim.x;  // a multiple of 8
+  const int bid = blockIdx.x;
+  const int logical = (bid & 7) * (nwg >> 3) + (bid >> 3);
+  const int per_split = tiles_m * tiles_n;
+  tc.valid = logical < per_split * splits;
+  if (!tc.valid) return tc;
+  tc.split = logical / per_split;
+  const int rem = logical - tc.split * per_split;
+  const int band = rem / (BMT * tiles_n);  // BMT rows of tiles
+  const int first_m = band * BMT;
+  const int hm = min(BMT, tiles_m - first_m);
+  const int within = rem - band * BMT * tiles_n;
+  const int blk = within / (hm * BNT);
+  const int first_n = blk * BNT;
+  const int wn = min(BNT, tiles_n - first_n);
+  const int inb = within - blk * hm * BNT;
+  tc.m0 = (int64_t)(first_m + inb / wn) * BM;
+  tc.n0 = (int64_t)(first_n + inb % wn) * BN;
+  return tc;
+}
+
 // Epilogue context handed to the epilogue functors.
 struct EpiCtx {
   int64_t m0, n0;
@@ -78,35 +112,70 @@ struct EpiCtx {
   int smem_bytes;
 };
 
-// Row of accumulator element (i, r) of this lane inside the wave tile.
-__device__ __forceinline__ int acc_row(int i, int r, int lane) {
-  return 32 * i + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
-}
+// Accumulator layouts.  Register r of block (i, j) in lane l holds the wave
+// tile's element (row(i, r, l), col(j, l)); the lanes holding one column are
+// combined with col_max / col_sum (a fixed butterfly, so the result does not
+// depend on timing), after which col_owner lanes hold the column's value.
+// Registers 4q .. 4q+3 always hold four consecutive rows.
+struct Acc32 {  // v_mfma_f32_32x32x* : 32 x 32 blocks, 16 registers per lane
+  using V = f32x16;
+  static constexpr int R = 16;
+  static __device__ __forceinline__ int row(int i, int r, int lane) {
+    return 32 * i + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
+  }
+  static __device__ __forceinline__ int col(int j, int lane) { return 32 * j + (lane & 31); }
+  static __device__ __forceinline__ float col_max(float x) {
+    return fmaxf(x, __shfl_xor(x, 32, 64));
+  }
+  static __device__ __forceinline__ float col_sum(float x) { return x + __shfl_xor(x, 32, 64); }
+  static __device__ __forceinline__ bool col_owner(int lane) { return lane < 32; }
+};
+struct Acc16 {  // v_mfma_f32_16x16x32_bf16 : 16 x 16 blocks, 4 registers per lane
+  using V = f32x4;
+  static constexpr int R = 4;
+  static __device__ __forceinline__ int row(int i, int r, int lane) {
+    return 16 * i + 4 * (lane >> 4) + r;
+  }
+  static __device__ __forceinline__ int col(int j, int lane) { return 16 * j + (lane & 15); }
+  static __device__ __forceinline__ float col_max(float x) {
+    x = fmaxf(x, __shfl_xor(x, 16, 64));
+    return fmaxf(x, __shfl_xor(x, 32, 64));
+  }
+  static __device__ __forceinline__ float col_sum(float x) {
+    x += __shfl_xor(x, 16, 64);
+    return x + __shfl_xor(x, 32, 64);
+  }
+  static __device__ __forceinline__ bool col_owner(int lane) { return lane < 16; }
+};
 
 // ------------------------------------------------------------- epilogues ---
 
 // Forward epilogue: rows are vocabulary entries, columns tokens.  Per column
 // (token) and block tile of BM vocabulary rows: m = max z, s = sum e^(z-m),
 // t = sum e^(z-m)(z-m) over the valid rows, with z = inv_t * acc.  When P is
-// given, e^(z-m) is stored token-major: P[t, v] (leading dimension ldp).
-// The exponent is formed as one fma on the raw accumulator,
-// (acc * inv_t - m) * log2(e), fed to exp2; t is accumulated in that scaled
-// unit and multiplied by ln 2 once.
+// given, e^(z-m) is stored per element: bf16 into the tiled block layout of G
+// (tiled_offset with ldp blocks per 256-token panel; every position of the
+// tile is written, the dense-gradient pass zeroes those past V and Tc), fp32
+// token-major P[t, v] (leading dimension ldp).  The exponent is formed as one
+// fma on the raw accumulator, (acc * inv_t - m) * log2(e), fed to exp2; t is
+// accumulated in that scaled unit and multiplied by ln 2 once.
 template <typename T> struct FwdEpi {
+  static constexpr bool TILED_P = sizeof(T) == 2;
   float inv_t;
   int64_t V, Tc, J;
   float *pm, *ps, *pt;
   T* P;
   int64_t ldp;
 
-  template <bool FULL, int MB, int NB, int BM, int BN>
-  __device__ __forceinline__ void columns(f32x16 (&acc)[MB][NB], const EpiCtx& c, int vrows,
-                                          float* red, uint16_t* stg) const {
+  // No data-dependent branches while the accumulators are live: validity is
+  // a select, the P store is a template parameter, and every lane writes the
+  // reduced column values (all lanes of a column hold the same value after
+  // the butterfly), so the main loop keeps each accumulator in place.
+  template <class L, bool FULL, bool STORE, int MB, int NB, int BM, int BN>
+  __device__ __forceinline__ void columns(typename L::V (&acc)[MB][NB], const EpiCtx& c,
+                                          int vrows, float* red) const {
     constexpr float LOG2E = 1.4426950408889634f;
-    constexpr bool STAGE = sizeof(T) == 2;
-    constexpr int CH = BM / 8;  // 16-byte chunks per staged token row
-    const int lc = c.lane & 31;
-    const bool store = P != nullptr;
+    static_assert(!TILED_P || (BN == TILE_ROWS && BM % TILE_K == 0), "tile = token panel");
     // Column maxima of the raw accumulators (inv_t > 0 keeps the order).
     float mraw[NB];
 #pragma unroll
@@ -115,15 +184,17 @@ template <typename T> struct FwdEpi {
 #pragma unroll
       for (int i = 0; i < MB; ++i)
 #pragma unroll
-        for (int r = 0; r < 16; ++r)
-          if (FULL || acc_row(i, r, c.lane) < vrows) mx = fmaxf(mx, acc[i][j][r]);
-      mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
-      if (c.lane < 32) red[c.wave_m * BN + c.wn_off + 32 * j + lc] = mx;
+        for (int r = 0; r < L::R; ++r) {
+          const bool ok = FULL || L::row(i, r, c.lane) < vrows;
+          mx = fmaxf(mx, ok ? acc[i][j][r] : -INFINITY);
+        }
+      mx = L::col_max(mx);
+      red[c.wave_m * BN + c.wn_off + L::col(j, c.lane)] = mx;
     }
     __syncthreads();
 #pragma unroll
     for (int j = 0; j < NB; ++j) {
-      const int col = c.wn_off + 32 * j + lc;
+      const int col = c.wn_off + L::col(j, c.lane);
       mraw[j] = fmaxf(red[col], red[BN + col]);
     }
     const float k2 = inv_t * LOG2E;
@@ -131,35 +202,38 @@ template <typename T> struct FwdEpi {
     float* rt = red + 4 * BN;
 #pragma unroll
     for (int j = 0; j < NB; ++j) {
-      const int colb = c.wn_off + 32 * j + lc;
+      const int colb = c.wn_off + L::col(j, c.lane);
       const float off = -mraw[j] * k2;
       float s = 0.0f, t = 0.0f;
 #pragma unroll
       for (int i = 0; i < MB; ++i)
 #pragma unroll
-        for (int rq = 0; rq < 4; ++rq) {
+        for (int rq = 0; rq < L::R / 4; ++rq) {
           float e4[4];
 #pragma unroll
           for (int r3 = 0; r3 < 4; ++r3) {
             const int r = rq * 4 + r3;
-            float e = 0.0f;
-            if (FULL || acc_row(i, r, c.lane) < vrows) {
-              const float d2 = fmaf(acc[i][j][r], k2, off);  // (z - m) log2(e)
-              e = __builtin_amdgcn_exp2f(d2);
-              s += e;
-              t = fmaf(e, d2, t);
-            }
+            const bool ok = FULL || L::row(i, r, c.lane) < vrows;
+            const float d2 = fmaf(acc[i][j][r], k2, off);  // (z - m) log2(e)
+            const float e = ok ? __builtin_amdgcn_exp2f(d2) : 0.0f;
+            s += e;
+            t = fmaf(e, d2, t);
             e4[r3] = e;
           }
-          if (store) {
-            const int vloc = c.wm_off + acc_row(i, rq * 4, c.lane);  // multiple of 4
-            if constexpr (STAGE) {
-              const int chunk = (vloc >> 3) ^ (colb & (CH - 1));
+          if constexpr (STORE) {
+            const int vloc = c.wm_off + L::row(i, rq * 4, c.lane);  // multiple of 4
+            if constexpr (TILED_P) {
+              // 4 consecutive vocabulary entries of token colb: 8 bytes of one
+              // 16-byte chunk of G's tiled layout (BN = 256 tokens = a panel)
               typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
               bf16x4 pk;
 #pragma unroll
               for (int r3 = 0; r3 < 4; ++r3) pk[r3] = (__bf16)e4[r3];
-              *reinterpret_cast<bf16x4*>(stg + colb * BM + chunk * 8 + (vloc & 7)) = pk;
+              const int64_t off =
+                  ((c.n0 / TILE_ROWS) * ldp + (c.m0 + vloc) / TILE_K) * (TILE_ROWS * TILE_K) +
+                  colb * TILE_K + ((((vloc % TILE_K) >> 3) ^ ((colb >> 1) & 3)) << 3) +
+                  (vloc & 7);
+              *reinterpret_cast<bf16x4*>(P + off) = pk;
             } else {
               const int64_t col = c.n0 + colb;
               if (col < Tc) {
@@ -172,35 +246,38 @@ template <typename T> struct FwdEpi {
             }
           }
         }
-      s += __shfl_xor(s, 32, 64);
-      t += __shfl_xor(t, 32, 64);
-      if (c.lane < 32) {
-        rs[c.wave_m * BN + colb] = s;
-        rt[c.wave_m * BN + colb] = t * 0.6931471805599453f;  // back to units of z
-      }
+      s = L::col_sum(s);
+      t = L::col_sum(t);
+      rs[c.wave_m * BN + colb] = s;
+      rt[c.wave_m * BN + colb] = t * 0.6931471805599453f;  // back to units of z
     }
     (void)mraw;
   }
 
-  template <int MB, int NB, int BM, int BN>
-  __device__ __forceinline__ void apply(f32x16 (&acc)[MB][NB], const EpiCtx& c) const {
+  template <class L, int MB, int NB, int BM, int BN>
+  __device__ __forceinline__ void apply(typename L::V (&acc)[MB][NB], const EpiCtx& c) const {
     const int64_t jt = c.m0 / BM;
     __syncthreads();  // the main loop's LDS is free from here
     float* red = reinterpret_cast<float*>(c.smem);  // [2][BN] x 3
-    uint16_t* stg = reinterpret_cast<uint16_t*>(c.smem + 6 * BN * sizeof(float));
     const int64_t vr = V - c.m0 - c.wm_off;
     const int vrows = (int)(vr < 0 ? 0 : (vr > 2 * BM ? 2 * BM : vr));
-    if (c.m0 + BM <= V)
-      columns<true, MB, NB, BM, BN>(acc, c, vrows, red, stg);
-    else
-      columns<false, MB, NB, BM, BN>(acc, c, vrows, red, stg);
+    const bool full = c.m0 + BM <= V;
+    if (P != nullptr) {
+      if (full)
+        columns<L, true, true, MB, NB, BM, BN>(acc, c, vrows, red);
+      else
+        columns<L, false, true, MB, NB, BM, BN>(acc, c, vrows, red);
+    } else {
+      if (full)
+        columns<L, true, false, MB, NB, BM, BN>(acc, c, vrows, red);
+      else
+        columns<L, false, false, MB, NB, BM, BN>(acc, c, vrows, red);
+    }
     __syncthreads();
-    const int tid = threadIdx.x;
-    if (c.wave_m == 0 && c.lane < 32) {
-      const int lc = c.lane & 31;
+    if (c.wave_m == 0 && L::col_owner(c.lane)) {
 #pragma unroll
       for (int j = 0; j < NB; ++j) {
-        const int colb = c.wn_off + 32 * j + lc;
+        const int colb = c.wn_off + L::col(j, c.lane);
         const int64_t col = c.n0 + colb;
         if (col < Tc) {
           pm[col * J + jt] = fmaxf(red[colb], red[BN + colb]) * inv_t;
@@ -209,79 +286,63 @@ template <typename T> struct FwdEpi {
         }
       }
     }
-    if constexpr (sizeof(T) == 2) {
-      if (P == nullptr) return;
-      // Coalesced copy-out: thread tid moves chunk tid % CH of token rows
-      // tid / CH, tid / CH + NT / CH, ...
-      constexpr int CH = BM / 8;
-      constexpr int ROWS_PER_PASS = NT / CH;
-      const int ch = tid % CH;
-      const int64_t vrem = V - c.m0;
-      const int64_t trem = Tc - c.n0;
-      if ((int64_t)ch * 8 >= vrem) return;
-      const bool whole = (int64_t)ch * 8 + 8 <= vrem;
-      T* dst = P + (c.n0 + tid / CH) * ldp + c.m0 + ch * 8;
-      const int64_t step = (int64_t)ROWS_PER_PASS * ldp;
-      for (int tl = tid / CH; tl < BN && tl < trem; tl += ROWS_PER_PASS, dst += step) {
-        const u32x4 val =
-            *reinterpret_cast<const u32x4*>(stg + tl * BM + ((ch ^ (tl & (CH - 1))) * 8));
-        if (whole) {
-          *reinterpret_cast<u32x4*>(dst) = val;
-        } else {
-          const uint16_t* e = reinterpret_cast<const uint16_t*>(&val);
-          for (int k = 0; k < vrem - ch * 8; ++k) reinterpret_cast<uint16_t*>(dst)[k] = e[k];
-        }
-      }
-    }
   }
 };
+
+// Branch-free fp32 store of the wave tile (=, or += when ACC) through a
+// buffer descriptor spanning the workgroup tile: elements outside [M, N]
+// get an offset past the descriptor's range, whose stores the hardware drops
+// and whose loads read 0.  Keeping the epilogue free of branches lets the
+// compiler keep every accumulator in one register block through the main
+// loop.  Offsets are 32-bit: the launchers require ldc < 2^21.
+template <class L, bool ACC, int MB, int NB, int BM, int BN>
+__device__ __forceinline__ void store_tile(typename L::V (&acc)[MB][NB], const EpiCtx& c,
+                                           float* C, int64_t ldc, int64_t M, int64_t N) {
+  const int64_t rows = min<int64_t>(M - c.m0, BM), cols = min<int64_t>(N - c.n0, BN);
+  // The tile origin is uniform; readfirstlane makes that visible to the
+  // compiler so the descriptor lives in SGPRs (no per-store waterfall).
+  const uint64_t a = reinterpret_cast<uint64_t>(C + c.m0 * ldc + c.n0);
+  const uint64_t au = ((uint64_t)__builtin_amdgcn_readfirstlane((uint32_t)(a >> 32)) << 32) |
+                      (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)a);
+  const int bytes = __builtin_amdgcn_readfirstlane((int)(((rows - 1) * ldc + cols) * 4));
+  const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+      reinterpret_cast<void*>(au), (short)0, bytes, 0x00020000);
+  const int ld = (int)ldc;
+#pragma unroll
+  for (int i = 0; i < MB; ++i)
+#pragma unroll
+    for (int j = 0; j < NB; ++j) {
+      const int cl = c.wn_off + L::col(j, c.lane);
+#pragma unroll
+      for (int r = 0; r < L::R; ++r) {
+        const int rl = c.wm_off + L::row(i, r, c.lane);
+        const int off = (rl < rows && cl < cols) ? (rl * ld + cl) * 4 : OOB;
+        float v = acc[i][j][r];
+        if constexpr (ACC)
+          v += __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rs, off, 0, 0));
+        __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, v), rs, off, 0, 0);
+      }
+    }
+}
 
 // C[split][row][col] = acc  (fp32).
 struct StoreEpi {
   float* C;
   int64_t ldc, split_stride, M, N;
-  template <int MB, int NB, int BM, int BN>
-  __device__ __forceinline__ void apply(f32x16 (&acc)[MB][NB], const EpiCtx& c) const {
-    float* Cs = C + (int64_t)c.split * split_stride;
-    const int lc = c.lane & 31;
-#pragma unroll
-    for (int i = 0; i < MB; ++i)
-#pragma unroll
-      for (int j = 0; j < NB; ++j) {
-        const int64_t col = c.n0 + c.wn_off + 32 * j + lc;
-        if (col >= N) continue;
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int64_t row = c.m0 + c.wm_off + acc_row(i, r, c.lane);
-          if (row < M) Cs[row * ldc + col] = acc[i][j][r];
-        }
-      }
+  template <class L, int MB, int NB, int BM, int BN>
+  __device__ __forceinline__ void apply(typename L::V (&acc)[MB][NB], const EpiCtx& c) const {
+    store_tile<L, false, MB, NB, BM, BN>(acc, c, C + (int64_t)c.split * split_stride, ldc, M, N);
   }
 };
 
-// dW[row][col] (=|+=) acc.
+// dW[row][col] = acc, or += acc when ACC.
+template <bool ACC>
 struct DwEpi {
   float* C;
   int64_t ldc, M, N;
-  int accumulate;
-  template <int MB, int NB, int BM, int BN>
-  __device__ __forceinline__ void apply(f32x16 (&acc)[MB][NB], const EpiCtx& c) const {
-    const int lc = c.lane & 31;
-#pragma unroll
-    for (int i = 0; i < MB; ++i)
-#pragma unroll
-      for (int j = 0; j < NB; ++j) {
-        const int64_t col = c.n0 + c.wn_off + 32 * j + lc;
-        if (col >= N) continue;
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int64_t row = c.m0 + c.wm_off + acc_row(i, r, c.lane);
-          if (row < M) {
-            float* p = C + row * ldc + col;
-            *p = accumulate ? (*p + acc[i][j][r]) : acc[i][j][r];
-          }
-        }
-      }
+  template <class L, int MB, int NB, int BM, int BN>
+  __device__ __forceinline__ void apply(typename L::V (&acc)[MB][NB], const EpiCtx& c) const {
+    store_tile<L, ACC, MB, NB, BM, BN>(acc, c, C, ldc, M, N);
   }
 };
 
@@ -290,8 +351,8 @@ struct DwEpi {
 constexpr int BF_BM = 256, BF_BN = 256, BF_BK = 32, BF_ST = 4;
 constexpr int BF_STAGE_A = BF_BM * BF_BK * 2;  // bytes
 constexpr int BF_STAGE = (BF_BM + BF_BN) * BF_BK * 2;
-constexpr int BF_LDS = BF_ST * BF_STAGE + 8192;  // ring + epilogue scratch (136 KB)
-static_assert(BF_LDS >= 6 * BF_BN * 4 + BF_BN * BF_BM * 2, "forward epilogue staging");
+constexpr int BF_LDS = BF_ST * BF_STAGE;  // the ring; the epilogues reuse it (128 KB)
+static_assert(BF_LDS >= 6 * BF_BN * 4, "forward epilogue reductions");
 static_assert(BF_STAGE_A == TILE_BLOCK_BYTES, "a stage of one operand is one tiled block");
 
 // Buffer descriptor (gfx9): base, stride 0, num_records = bytes, default config.
@@ -335,26 +396,25 @@ __device__ __forceinline__ void wait_stage(int younger) {
     wait_vmcnt<0>();
 }
 
-constexpr int OOB = (int)0x80000000;
-
 // TILED = false: A [M, lda] and B [N, ldb] row-major, any K (multiple of 8).
 // TILED = true: A and B in the tiled block layout (tiled_offset in
 // kernels.h) with lda / ldb = blocks per 256-row panel; K is a multiple of 32
 // or the blocks are zero past K.
 //
-// Software pipeline per stage kt (two K-steps s0, s1 of 16): fragments of s1
-// are read, the MFMAs of s0 issue, then the wave waits for stage kt+1 and
-// passes the barrier while those MFMAs execute, refills the buffer of stage
-// kt (fully read), reads the s0 fragments of stage kt+1 and issues the MFMAs
-// of s1.  Every wave has read all of stage kt before anyone passes the
-// barrier, so the refill cannot race with fragment reads.
+// Software pipeline per stage kt (one K-step of 32): the MFMAs of row blocks
+// 0..3 issue from fragments read during the previous stage, then the wave
+// waits for stage kt+1 and passes the barrier while those MFMAs execute,
+// refills the buffer of stage kt (whose fragments every wave read before the
+// barrier), reads stage kt+1's fragments and issues the MFMAs of row blocks
+// 4..7.  The refill therefore cannot race with fragment reads.
 template <bool TILED, class Epi>
 __global__ void __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(1, 1)))
 gemm_bf16_kernel(const bf16_t* __restrict__ A, int64_t lda, const bf16_t* __restrict__ B,
                  int64_t ldb, int64_t M, int64_t N, int64_t K, int64_t k_split, int tiles_m,
                  int tiles_n, int splits, Epi epi) {
   __shared__ __attribute__((aligned(1024))) char lds[BF_LDS];
-  const TileCoord tc = map_tile(tiles_m, tiles_n, splits, BF_BM, BF_BN);
+  const TileCoord tc = TILED ? map_tile_blocks(tiles_m, tiles_n, splits, BF_BM, BF_BN)
+                              : map_tile(tiles_m, tiles_n, splits, BF_BM, BF_BN);
   if (!tc.valid) return;
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -410,53 +470,46 @@ gemm_bf16_kernel(const bf16_t* __restrict__ A, int64_t lda, const bf16_t* __rest
       load_lds16(rsb, sb + (uint32_t)((wave * 4 + i) * 1024), ob);
     }
   };
-  // Byte offsets of this lane's fragments inside a stage, per K-step.
-  int fa[2][4], fb[2][4];
-#pragma unroll
-  for (int s = 0; s < 2; ++s) {
-    const int ch = 2 * s + (lane >> 5);
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      int row = wm * 128 + 32 * i + (lane & 31);
-      fa[s][i] = row * 64 + 16 * (ch ^ ((row >> 1) & 3));
-      row = wn * 128 + 32 * i + (lane & 31);
-      fb[s][i] = BF_STAGE_A + row * 64 + 16 * (ch ^ ((row >> 1) & 3));
-    }
+  // Fragment byte offsets inside a stage: in 16-row block i the lane reads
+  // row 16 i + lane % 16, 16-byte chunk lane / 16 (k = 8 (lane / 16) .. +7).
+  // Sixteen rows down keep (row >> 1) & 3, so block i sits at +1 KB * i.
+  int fa0, fb0;
+  {
+    const int ch = lane >> 4;
+    int row = wm * 128 + (lane & 15);
+    fa0 = row * 64 + 16 * (ch ^ ((row >> 1) & 3));
+    row = wn * 128 + (lane & 15);
+    fb0 = BF_STAGE_A + row * 64 + 16 * (ch ^ ((row >> 1) & 3));
   }
 
-  f32x16 acc[4][4];
+  f32x4 acc[8][8];
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
+  for (int i = 0; i < 8; ++i)
 #pragma unroll
-    for (int j = 0; j < 4; ++j)
+    for (int j = 0; j < 8; ++j)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
+      for (int r = 0; r < 4; ++r) acc[i][j][r] = 0.0f;
 
   if (nk > 0) {
 #pragma unroll
     for (int s = 0; s < BF_ST - 1; ++s)
       if (s < nk) issue(s);
-    bf16x8 a0[4], b0[4], a1[4], b1[4];
     wait_stage(min(nk - 1, BF_ST - 2));
     __syncthreads();
     if (BF_ST - 1 < nk) issue(BF_ST - 1);
+    bf16x8 ca[8], cb[8];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      a0[i] = *reinterpret_cast<const bf16x8*>(lds + fa[0][i]);
-      b0[i] = *reinterpret_cast<const bf16x8*>(lds + fb[0][i]);
+    for (int i = 0; i < 8; ++i) {
+      ca[i] = *reinterpret_cast<const bf16x8*>(lds + fa0 + 1024 * i);
+      cb[i] = *reinterpret_cast<const bf16x8*>(lds + fb0 + 1024 * i);
     }
     for (int kt = 0; kt < nk; ++kt) {
-      const char* st = lds + (kt % BF_ST) * BF_STAGE;
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        a1[i] = *reinterpret_cast<const bf16x8*>(st + fa[1][i]);
-        b1[i] = *reinterpret_cast<const bf16x8*>(st + fb[1][i]);
-      }
+      bf16x8 na[8], nb[8];
 #pragma unroll
       for (int i = 0; i < 4; ++i)
 #pragma unroll
-        for (int j = 0; j < 4; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a0[i], b0[j], acc[i][j], 0, 0, 0);
+        for (int j = 0; j < 8; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ca[i], cb[j], acc[i][j], 0, 0, 0);
       if (kt + 1 < nk) {
         // Stage kt+1 has landed once at most the stages issued after it
         // (kt+2, kt+3) are outstanding.
@@ -465,19 +518,29 @@ gemm_bf16_kernel(const bf16_t* __restrict__ A, int64_t lda, const bf16_t* __rest
         if (kt + BF_ST < nk) issue(kt + BF_ST);  // into the buffer of stage kt
         const char* sn = lds + ((kt + 1) % BF_ST) * BF_STAGE;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          a0[i] = *reinterpret_cast<const bf16x8*>(sn + fa[0][i]);
-          b0[i] = *reinterpret_cast<const bf16x8*>(sn + fb[0][i]);
+        for (int i = 0; i < 8; ++i) {
+          na[i] = *reinterpret_cast<const bf16x8*>(sn + fa0 + 1024 * i);
+          nb[i] = *reinterpret_cast<const bf16x8*>(sn + fb0 + 1024 * i);
         }
       }
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
+      for (int i = 4; i < 8; ++i)
 #pragma unroll
-        for (int j = 0; j < 4; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a1[i], b1[j], acc[i][j], 0, 0, 0);
+        for (int j = 0; j < 8; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ca[i], cb[j], acc[i][j], 0, 0, 0);
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        ca[i] = na[i];
+        cb[i] = nb[i];
+      }
     }
   }
-
+  // Hand the accumulators to the epilogue as AGPR blocks: this keeps the
+  // register allocator from rotating them through the main loop.
+#pragma unroll
+  for (int i = 0; i < 8; ++i)
+#pragma unroll
+    for (int j = 0; j < 8; ++j) __asm__ volatile("" : "+a"(acc[i][j]));
   EpiCtx ctx;
   ctx.m0 = tc.m0;
   ctx.n0 = tc.n0;
@@ -488,7 +551,7 @@ gemm_bf16_kernel(const bf16_t* __restrict__ A, int64_t lda, const bf16_t* __rest
   ctx.split = tc.split;
   ctx.smem = lds;
   ctx.smem_bytes = BF_LDS;
-  epi.template apply<4, 4, BF_BM, BF_BN>(acc, ctx);
+  epi.template apply<Acc16, 8, 8, BF_BM, BF_BN>(acc, ctx);
 }
 
 // ------------------------------------------------------------ fp32 kernel ---
@@ -592,7 +655,7 @@ __global__ void __launch_bounds__(NT) gemm_f32_kernel(const float* __restrict__ 
   ctx.split = tc.split;
   ctx.smem = scratch;
   ctx.smem_bytes = sizeof(scratch);
-  epi.template apply<MB, NB, F_BM, F_BN>(acc, ctx);
+  epi.template apply<Acc32, MB, NB, F_BM, F_BN>(acc, ctx);
 }
 
 template <bool TILED, class Epi>
@@ -647,6 +710,7 @@ hipError_t gemm_fwd(int dtype, const void* W, const void* hc, int64_t V, int64_t
 hipError_t gemm_store(int dtype, const void* A, int64_t lda, const void* B, int64_t ldb,
                       int64_t M, int64_t N, int64_t K, int splits, int64_t k_split, float* C,
                       int64_t ldc, int64_t split_stride, hipStream_t s) {
+  if (ldc >= ((int64_t)1 << 21)) return hipErrorInvalidValue;
   StoreEpi e{C, ldc, split_stride, M, N};
   if (dtype == RL_DTYPE_BF16)  // tiled operands
     return launch_bf16<true>(static_cast<const bf16_t*>(A), lda, static_cast<const bf16_t*>(B),
@@ -657,13 +721,16 @@ hipError_t gemm_store(int dtype, const void* A, int64_t lda, const void* B, int6
 
 hipError_t gemm_dw(int dtype, const void* A, int64_t lda, const void* B, int64_t ldb, int64_t M,
                    int64_t N, int64_t K, float* C, int64_t ldc, int accumulate, hipStream_t s) {
-  DwEpi e{C, ldc, M, N, accumulate};
+  if (ldc >= ((int64_t)1 << 21)) return hipErrorInvalidValue;
   const int bk = gemm_k_tile(dtype);
-  if (dtype == RL_DTYPE_BF16)  // tiled operands
-    return launch_bf16<true>(static_cast<const bf16_t*>(A), lda, static_cast<const bf16_t*>(B),
-                             ldb, M, N, K, 1, round_up(K, bk), e, s);
-  return launch_f32(static_cast<const float*>(A), lda, static_cast<const float*>(B), ldb, M, N, K,
-                    1, round_up(K, bk), e, s);
+  auto run = [&](auto e) {
+    if (dtype == RL_DTYPE_BF16)  // tiled operands
+      return launch_bf16<true>(static_cast<const bf16_t*>(A), lda, static_cast<const bf16_t*>(B),
+                               ldb, M, N, K, 1, round_up(K, bk), e, s);
+    return launch_f32(static_cast<const float*>(A), lda, static_cast<const float*>(B), ldb, M, N,
+                      K, 1, round_up(K, bk), e, s);
+  };
+  return accumulate ? run(DwEpi<true>{C, ldc, M, N}) : run(DwEpi<false>{C, ldc, M, N});
 }
 
 }  // namespace rl

@@ -290,66 +290,53 @@ __global__ void __launch_bounds__(NT) to_tiled_t_kernel(const bf16_t* __restrict
   }
 }
 
-// bf16 G / Gt in the tiled layout from P = e^(z - m_tile) (token-major).
-// One workgroup handles 32 tokens x 256 vocabulary entries: scale
-// g = kap[t] exp(m[t, v/vtile] - lse[t]) P[t, v] into LDS, then write the 32
-// rows of 8 G blocks (2 KB contiguous each) and one whole Gt block (16 KB).
-// Tokens >= Tc and entries >= V are written as zeros.
-__global__ void __launch_bounds__(NT) form_g_tiled_kernel(
-    const bf16_t* __restrict__ P, int64_t ldp, bf16_t* __restrict__ G, int64_t KB_g,
-    bf16_t* __restrict__ Gt, int64_t KB_gt, const float* __restrict__ part_m, int64_t J,
-    int vtile, const float* __restrict__ lse, const float* __restrict__ kap, int64_t V,
-    int64_t Tc) {
-  constexpr int TT = 32, VV = 256, PITCH = VV + 8;
-  __shared__ float scale[TT];
-  __shared__ __attribute__((aligned(16))) bf16_t tile[TT][PITCH];  // [token][vocab]
-  const int64_t t0 = (int64_t)blockIdx.x * TT, v0 = (int64_t)blockIdx.y * VV;
-  if (threadIdx.x < TT) {
-    const int64_t t = t0 + threadIdx.x;
-    scale[threadIdx.x] =
-        (t < Tc) ? kap[t] * __expf(part_m[t * J + v0 / vtile] - lse[t]) : 0.0f;
-  }
-  __syncthreads();
-  for (int q = threadIdx.x; q < TT * (VV / 8); q += NT) {
-    const int tl = q / (VV / 8), vl = (q % (VV / 8)) * 8;
-    const int64_t t = t0 + tl, v = v0 + vl;
-    u32x4 out = {0u, 0u, 0u, 0u};
-    if (t < Tc) {
-      const u32x4 raw = *reinterpret_cast<const u32x4*>(P + t * ldp + v);
-      float x[8];
-      Elem<bf16_t>::unpack(raw, x);
-      const float sc = scale[tl];
+// Dense-gradient pass over the tiled layout (bf16).  The forward GEMM left
+// e^(z - m_j) in G's tiled blocks; each workgroup takes one 16 KB block
+// (256 tokens x 32 vocabulary entries, one vocabulary tile j), scales every
+// element by kappa_t e^(m_tj - LSE_t) (zero past Tc and V), writes it back in
+// place when G is wanted, and writes its transpose as eight 2 KB pieces of
+// the Gt blocks (rows = vocabulary, K = tokens) through an LDS transpose.
+__global__ void __launch_bounds__(NT) form_g_blocks_kernel(
+    bf16_t* __restrict__ G, int64_t KB_g, int write_g, bf16_t* __restrict__ Gt, int64_t KB_gt,
+    const float* __restrict__ part_m, int64_t J, int vtile, const float* __restrict__ lse,
+    const float* __restrict__ kap, int64_t V, int64_t Tc) {
+  constexpr int PITCH = TILE_ROWS + 8;                                   // 528 bytes
+  __shared__ __attribute__((aligned(16))) bf16_t tt[TILE_K][PITCH];  // [vocab][token]
+  const int64_t tp = blockIdx.x, kb = blockIdx.y;
+  bf16_t* blk = G + (tp * KB_g + kb) * (TILE_ROWS * TILE_K);
+  const int64_t jt = kb * TILE_K / vtile;
 #pragma unroll
-      for (int k = 0; k < 8; ++k) x[k] = (v + k < V) ? sc * x[k] : 0.0f;
-      out = Elem<bf16_t>::pack(x);
-    }
-    *reinterpret_cast<u32x4*>(&tile[tl][vl]) = out;
-  }
-  __syncthreads();
-  if (G != nullptr) {
-    // 8 K-blocks x 32 rows x 4 chunks; consecutive q -> consecutive 16 bytes.
-    const int64_t rbase = t0 % TILE_ROWS;
-    bf16_t* panel = G + ((t0 / TILE_ROWS) * KB_g + v0 / TILE_K) * (TILE_ROWS * TILE_K);
-    for (int q = threadIdx.x; q < 8 * TT * 4; q += NT) {
-      const int kbl = q / (TT * 4), rem = q % (TT * 4);
-      const int rl = rem >> 2, pc = rem & 3;
-      const int64_t r = rbase + rl;
-      const int ch = pc ^ (int)((r >> 1) & 3);
-      const u32x4 val = *reinterpret_cast<const u32x4*>(&tile[rl][kbl * TILE_K + ch * 8]);
-      *reinterpret_cast<u32x4*>(panel + (int64_t)kbl * (TILE_ROWS * TILE_K) + r * TILE_K + pc * 8) =
-          val;
-    }
-  }
-  if (Gt != nullptr) {
-    bf16_t* blk = Gt + ((v0 / TILE_ROWS) * KB_gt + t0 / TILE_K) * (TILE_ROWS * TILE_K);
-    for (int p = threadIdx.x; p < TILE_ROWS * 4; p += NT) {
-      const int r = p >> 2, ch = (p & 3) ^ ((r >> 1) & 3);
-      u32x4 out;
-      bf16_t* e = reinterpret_cast<bf16_t*>(&out);
+  for (int q = 0; q < 4; ++q) {
+    const int p = threadIdx.x + NT * q;  // 16-byte chunk of the block
+    const int r = p >> 2, lc = (p & 3) ^ ((r >> 1) & 3);
+    const int64_t t = tp * TILE_ROWS + r, v = kb * TILE_K + lc * 8;
+    const float sc = t < Tc ? kap[t] * __expf(part_m[t * J + jt] - lse[t]) : 0.0f;
+    float x[8];
+    Elem<bf16_t>::unpack(*reinterpret_cast<const u32x4*>(blk + p * 8), x);
 #pragma unroll
-      for (int k = 0; k < 8; ++k) e[k] = tile[8 * ch + k][r];
-      *reinterpret_cast<u32x4*>(blk + p * 8) = out;
+    for (int k = 0; k < 8; ++k) x[k] = (v + k < V) ? sc * x[k] : 0.0f;
+    const u32x4 out = Elem<bf16_t>::pack(x);
+    if (write_g) *reinterpret_cast<u32x4*>(blk + p * 8) = out;
+    if (Gt != nullptr) {
+      const bf16_t* e = reinterpret_cast<const bf16_t*>(&out);
+#pragma unroll
+      for (int k = 0; k < 8; ++k) tt[lc * 8 + k][r] = e[k];
     }
+  }
+  if (Gt == nullptr) return;
+  __syncthreads();
+  // Piece g covers tokens 32 g .. 32 g + 31 of this panel: rows
+  // (kb * 32) % 256 + rr of Gt block (vocab panel kb / 8, token block 8 tp + g).
+  const int64_t vb = kb * TILE_K / TILE_ROWS, rbase = (kb * TILE_K) % TILE_ROWS;
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const int p = threadIdx.x + NT * q;
+    const int g = p >> 7, rr = (p >> 2) & 31, pc = p & 3;
+    const int64_t row = rbase + rr;
+    const int lc = pc ^ (int)((row >> 1) & 3);
+    const u32x4 val = *reinterpret_cast<const u32x4*>(&tt[rr][g * 32 + lc * 8]);
+    bf16_t* dst = Gt + ((vb * KB_gt + tp * 8 + g) * (TILE_ROWS * TILE_K)) + row * TILE_K + pc * 8;
+    *reinterpret_cast<u32x4*>(dst) = val;
   }
 }
 
@@ -512,13 +499,13 @@ hipError_t to_tiled_t(const bf16_t* src, int64_t ld_src, int64_t S, int64_t C, b
   return hipGetLastError();
 }
 
-hipError_t form_g_tiled(const bf16_t* P, int64_t ldp, bf16_t* G, int64_t KB_g, bf16_t* Gt,
-                        int64_t KB_gt, const float* part_m, int64_t J, int vtile,
-                        const float* lse_c, const float* kappa_c, int64_t V, int64_t Tc,
-                        hipStream_t s) {
-  const dim3 grid((unsigned)(round_up(Tc, TILE_ROWS) / 32), (unsigned)ceil_div(ldp, 256));
-  hipLaunchKernelGGL(form_g_tiled_kernel, grid, dim3(NT), 0, s, P, ldp, G, KB_g, Gt, KB_gt, part_m,
-                     J, vtile, lse_c, kappa_c, V, Tc);
+hipError_t form_g_blocks(bf16_t* G, int64_t KB_g, int write_g, bf16_t* Gt, int64_t KB_gt,
+                         const float* part_m, int64_t J, int vtile, const float* lse_c,
+                         const float* kappa_c, int64_t V, int64_t Tc, hipStream_t s) {
+  if (Tc <= 0) return hipSuccess;
+  const dim3 grid((unsigned)ceil_div(Tc, TILE_ROWS), (unsigned)KB_g);
+  hipLaunchKernelGGL(form_g_blocks_kernel, grid, dim3(NT), 0, s, G, KB_g, write_g, Gt, KB_gt,
+                     part_m, J, vtile, lse_c, kappa_c, V, Tc);
   return hipGetLastError();
 }
 

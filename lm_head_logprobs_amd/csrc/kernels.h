@@ -15,7 +15,8 @@ struct FwdEpiArgs {
   float* part_m;         // [Tc, J] tile max of z
   float* part_s;         // [Tc, J] sum exp(z - m)
   float* part_t;         // [Tc, J] sum exp(z - m) (z - m)
-  void* P;               // [Tc, ldp] exp(z - m) per element (dtype of h/W), or null
+  void* P;               // exp(z - m) per element, or null: bf16 into G's tiled layout
+                         // (ldp = blocks per 256-token panel), fp32 token-major [Tc, ldp]
   int64_t ldp;
 };
 
@@ -52,13 +53,14 @@ __host__ __device__ inline int64_t tiled_offset(int64_t r, int64_t k, int64_t KB
 hipError_t to_tiled_t(const bf16_t* src, int64_t ld_src, int64_t S, int64_t C, bf16_t* dst,
                       int64_t KB, int64_t kb_write, hipStream_t s);
 
-// bf16: from P (token-major [Tc, ldp]) write G tiled [Tc rows, K = ldp] (KB_g
-// blocks per panel) and Gt tiled [ldp rows, K = tokens] (KB_gt blocks per
-// panel), scaled as form_g; either output may be null.
-hipError_t form_g_tiled(const bf16_t* P, int64_t ldp, bf16_t* G, int64_t KB_g, bf16_t* Gt,
-                        int64_t KB_gt, const float* part_m, int64_t J, int vtile,
-                        const float* lse_c, const float* kappa_c, int64_t V, int64_t Tc,
-                        hipStream_t s);
+// bf16 dense gradient in the tiled layout: G holds e^(z - m) as left by the
+// forward GEMM (KB_g blocks per 256-token panel, panels covering Tc); every
+// element becomes kappa_t e^(m_tj - LSE_t) e^(z - m_tj) (zero past Tc and V),
+// written back in place when write_g, and transposed into Gt (rows =
+// vocabulary, KB_gt blocks of 32 tokens per panel) when Gt is not null.
+hipError_t form_g_blocks(bf16_t* G, int64_t KB_g, int write_g, bf16_t* Gt, int64_t KB_gt,
+                         const float* part_m, int64_t J, int vtile, const float* lse_c,
+                         const float* kappa_c, int64_t V, int64_t Tc, hipStream_t s);
 
 // dst[c][r] = src[r][c] for r < R, 0 for R <= r < Rpad; c < C.
 hipError_t transpose_pad(int dtype, const void* src, int64_t ld_src, int64_t R, int64_t C,
