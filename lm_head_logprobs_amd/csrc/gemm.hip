@@ -9,9 +9,11 @@
 // Accumulation is fp32.  The epilogues are written against an accumulator
 // layout (Acc16 / Acc32 below) that maps lane and register to row and column.
 //
-// bf16 kernel (the hot path).  A 256-thread workgroup (4 waves as 2x2) owns a
-// 256 x 256 output tile; each wave owns 128 x 128 as 8 x 8 blocks of
-// v_mfma_f32_16x16x32_bf16 with its 256 accumulators in AGPRs.  With random
+// bf16 kernel (the hot path).  A 512-thread workgroup (8 waves as 2x4, two
+// per SIMD) owns a 256 x 256 output tile; each wave owns 128 x 64 as 8 x 4
+// blocks of v_mfma_f32_16x16x32_bf16 with its 128 accumulators in AGPRs.
+// With two waves per SIMD one wave's MFMAs keep the matrix pipe busy while
+// the other issues its loads or waits at the barrier.  With random
 // operands this shape sustains a higher MFMA rate than 32x32x16 (measured
 // about 84% against 72% of the dense peak in a loop without memory traffic).
 // K advances 32 at a time through a 4-stage ring of LDS buffers (32 KB each:
@@ -386,12 +388,13 @@ __device__ __forceinline__ void wait_vmcnt() {
 }
 
 // Wait until the oldest stage not yet waited for has landed, given how many
-// younger stages (8 loads per thread each) were issued after it.
+// younger stages (LPS loads per thread each) were issued after it.
+template <int LPS>
 __device__ __forceinline__ void wait_stage(int younger) {
   if (younger >= 2)
-    wait_vmcnt<16>();
+    wait_vmcnt<2 * LPS>();
   else if (younger == 1)
-    wait_vmcnt<8>();
+    wait_vmcnt<LPS>();
   else
     wait_vmcnt<0>();
 }
@@ -401,6 +404,9 @@ __device__ __forceinline__ void wait_stage(int younger) {
 // kernels.h) with lda / ldb = blocks per 256-row panel; K is a multiple of 32
 // or the blocks are zero past K.
 //
+constexpr int BF_NT = 512;  // 8 waves
+constexpr int BF_LPS = 4;   // direct-to-LDS loads per thread per stage (2 A + 2 B)
+
 // Software pipeline per stage kt (one K-step of 32): the MFMAs of row blocks
 // 0..3 issue from fragments read during the previous stage, then the wave
 // waits for stage kt+1 and passes the barrier while those MFMAs execute,
@@ -408,7 +414,7 @@ __device__ __forceinline__ void wait_stage(int younger) {
 // barrier), reads stage kt+1's fragments and issues the MFMAs of row blocks
 // 4..7.  The refill therefore cannot race with fragment reads.
 template <bool TILED, class Epi>
-__global__ void __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(1, 1)))
+__global__ void __launch_bounds__(BF_NT) __attribute__((amdgpu_waves_per_eu(2, 2)))
 gemm_bf16_kernel(const bf16_t* __restrict__ A, int64_t lda, const bf16_t* __restrict__ B,
                  int64_t ldb, int64_t M, int64_t N, int64_t K, int64_t k_split, int tiles_m,
                  int tiles_n, int splits, Epi epi) {
@@ -417,13 +423,13 @@ gemm_bf16_kernel(const bf16_t* __restrict__ A, int64_t lda, const bf16_t* __rest
                               : map_tile(tiles_m, tiles_n, splits, BF_BM, BF_BN);
   if (!tc.valid) return;
   const int tid = threadIdx.x, lane = tid & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int wm = wave >> 1, wn = wave & 1;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // 0..7
+  const int wm = wave >> 2, wn = wave & 3;                      // 128 x 64 sub-tile
   const int64_t kb = (int64_t)tc.split * k_split;
   const int64_t ke = min(K, kb + k_split);
   const int nk = (int)ceil_div(max<int64_t>(ke - kb, 0), BF_BK);
   i32x4 rsa, rsb;
-  int offa[4], offb[4], kc[4];
+  int offa[2], offb[2], kc[2];
   if constexpr (TILED) {
     // Panel of this tile: blocks [m0/256 * lda + kb/32, ...), 16 KB each.
     const int64_t ba = (tc.m0 / BF_BM) * lda + kb / BF_BK;
@@ -431,19 +437,19 @@ gemm_bf16_kernel(const bf16_t* __restrict__ A, int64_t lda, const bf16_t* __rest
     rsa = make_rsrc(A + ba * (TILE_BLOCK_BYTES / 2), (uint32_t)(nk * TILE_BLOCK_BYTES));
     rsb = make_rsrc(B + bb * (TILE_BLOCK_BYTES / 2), (uint32_t)(nk * TILE_BLOCK_BYTES));
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      offa[i] = offb[i] = ((wave * 4 + i) * 64 + lane) * 16;
+    for (int i = 0; i < 2; ++i) {
+      offa[i] = offb[i] = ((wave * 2 + i) * 64 + lane) * 16;
       kc[i] = 0;
     }
   } else {
     const int64_t rows_a = min<int64_t>(M - tc.m0, BF_BM), rows_b = min<int64_t>(N - tc.n0, BF_BN);
     rsa = make_rsrc(A + tc.m0 * lda, (uint32_t)(rows_a * lda * 2));
     rsb = make_rsrc(B + tc.n0 * ldb, (uint32_t)(rows_b * ldb * 2));
-    // Slot p = (wave*4 + i)*64 + lane: tile row p/4, stored chunk p%4 holds
+    // Slot p = (wave*2 + i)*64 + lane: tile row p/4, stored chunk p%4 holds
     // logical chunk (p%4) ^ ((row>>1)&3).
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int p = (wave * 4 + i) * 64 + lane;
+    for (int i = 0; i < 2; ++i) {
+      const int p = (wave * 2 + i) * 64 + lane;
       const int row = p >> 2, ch = (p & 3) ^ ((row >> 1) & 3);
       kc[i] = 8 * ch;
       offa[i] = row < rows_a ? (int)((row * lda + kb + 8 * ch) * 2) : OOB;
@@ -455,7 +461,7 @@ gemm_bf16_kernel(const bf16_t* __restrict__ A, int64_t lda, const bf16_t* __rest
     const uint32_t sa = lds_base + (uint32_t)((kt % BF_ST) * BF_STAGE);
     const uint32_t sb = sa + BF_STAGE_A;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
+    for (int i = 0; i < 2; ++i) {
       int oa, ob;
       if constexpr (TILED) {
         oa = offa[i] + kt * TILE_BLOCK_BYTES;
@@ -466,8 +472,8 @@ gemm_bf16_kernel(const bf16_t* __restrict__ A, int64_t lda, const bf16_t* __rest
         oa = kok ? offa[i] + 2 * k0 : OOB;
         ob = kok ? offb[i] + 2 * k0 : OOB;
       }
-      load_lds16(rsa, sa + (uint32_t)((wave * 4 + i) * 1024), oa);
-      load_lds16(rsb, sb + (uint32_t)((wave * 4 + i) * 1024), ob);
+      load_lds16(rsa, sa + (uint32_t)((wave * 2 + i) * 1024), oa);
+      load_lds16(rsb, sb + (uint32_t)((wave * 2 + i) * 1024), ob);
     }
   };
   // Fragment byte offsets inside a stage: in 16-row block i the lane reads
@@ -478,15 +484,15 @@ gemm_bf16_kernel(const bf16_t* __restrict__ A, int64_t lda, const bf16_t* __rest
     const int ch = lane >> 4;
     int row = wm * 128 + (lane & 15);
     fa0 = row * 64 + 16 * (ch ^ ((row >> 1) & 3));
-    row = wn * 128 + (lane & 15);
+    row = wn * 64 + (lane & 15);
     fb0 = BF_STAGE_A + row * 64 + 16 * (ch ^ ((row >> 1) & 3));
   }
 
-  f32x4 acc[8][8];
+  f32x4 acc[8][4];
 #pragma unroll
   for (int i = 0; i < 8; ++i)
 #pragma unroll
-    for (int j = 0; j < 8; ++j)
+    for (int j = 0; j < 4; ++j)
 #pragma unroll
       for (int r = 0; r < 4; ++r) acc[i][j][r] = 0.0f;
 
@@ -494,45 +500,42 @@ gemm_bf16_kernel(const bf16_t* __restrict__ A, int64_t lda, const bf16_t* __rest
 #pragma unroll
     for (int s = 0; s < BF_ST - 1; ++s)
       if (s < nk) issue(s);
-    wait_stage(min(nk - 1, BF_ST - 2));
+    wait_stage<BF_LPS>(min(nk - 1, BF_ST - 2));
     __syncthreads();
     if (BF_ST - 1 < nk) issue(BF_ST - 1);
-    bf16x8 ca[8], cb[8];
+    bf16x8 ca[8], cb[4];
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      ca[i] = *reinterpret_cast<const bf16x8*>(lds + fa0 + 1024 * i);
-      cb[i] = *reinterpret_cast<const bf16x8*>(lds + fb0 + 1024 * i);
-    }
+    for (int i = 0; i < 8; ++i) ca[i] = *reinterpret_cast<const bf16x8*>(lds + fa0 + 1024 * i);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) cb[j] = *reinterpret_cast<const bf16x8*>(lds + fb0 + 1024 * j);
     for (int kt = 0; kt < nk; ++kt) {
-      bf16x8 na[8], nb[8];
+      bf16x8 na[8], nb[4];
 #pragma unroll
       for (int i = 0; i < 4; ++i)
 #pragma unroll
-        for (int j = 0; j < 8; ++j)
+        for (int j = 0; j < 4; ++j)
           acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ca[i], cb[j], acc[i][j], 0, 0, 0);
       if (kt + 1 < nk) {
         // Stage kt+1 has landed once at most the stages issued after it
         // (kt+2, kt+3) are outstanding.
-        wait_stage(min(nk - 2 - kt, BF_ST - 2));
+        wait_stage<BF_LPS>(min(nk - 2 - kt, BF_ST - 2));
         __syncthreads();
         if (kt + BF_ST < nk) issue(kt + BF_ST);  // into the buffer of stage kt
         const char* sn = lds + ((kt + 1) % BF_ST) * BF_STAGE;
 #pragma unroll
-        for (int i = 0; i < 8; ++i) {
-          na[i] = *reinterpret_cast<const bf16x8*>(sn + fa0 + 1024 * i);
-          nb[i] = *reinterpret_cast<const bf16x8*>(sn + fb0 + 1024 * i);
-        }
+        for (int i = 0; i < 8; ++i) na[i] = *reinterpret_cast<const bf16x8*>(sn + fa0 + 1024 * i);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) nb[j] = *reinterpret_cast<const bf16x8*>(sn + fb0 + 1024 * j);
       }
 #pragma unroll
       for (int i = 4; i < 8; ++i)
 #pragma unroll
-        for (int j = 0; j < 8; ++j)
+        for (int j = 0; j < 4; ++j)
           acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ca[i], cb[j], acc[i][j], 0, 0, 0);
 #pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        ca[i] = na[i];
-        cb[i] = nb[i];
-      }
+      for (int i = 0; i < 8; ++i) ca[i] = na[i];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) cb[j] = nb[j];
     }
   }
   // Hand the accumulators to the epilogue as AGPR blocks: this keeps the
@@ -540,18 +543,18 @@ gemm_bf16_kernel(const bf16_t* __restrict__ A, int64_t lda, const bf16_t* __rest
 #pragma unroll
   for (int i = 0; i < 8; ++i)
 #pragma unroll
-    for (int j = 0; j < 8; ++j) __asm__ volatile("" : "+a"(acc[i][j]));
+    for (int j = 0; j < 4; ++j) __asm__ volatile("" : "+a"(acc[i][j]));
   EpiCtx ctx;
   ctx.m0 = tc.m0;
   ctx.n0 = tc.n0;
   ctx.wm_off = wm * 128;
-  ctx.wn_off = wn * 128;
+  ctx.wn_off = wn * 64;
   ctx.wave_m = wm;
   ctx.lane = lane;
   ctx.split = tc.split;
   ctx.smem = lds;
   ctx.smem_bytes = BF_LDS;
-  epi.template apply<Acc16, 8, 8, BF_BM, BF_BN>(acc, ctx);
+  epi.template apply<Acc16, 8, 4, BF_BM, BF_BN>(acc, ctx);
 }
 
 // ------------------------------------------------------------ fp32 kernel ---
@@ -670,8 +673,9 @@ hipError_t launch_bf16(const bf16_t* A, int64_t lda, const bf16_t* B, int64_t ld
   const int64_t panel = TILED ? ceil_div(k_split, BF_BK) * TILE_BLOCK_BYTES
                               : (int64_t)BF_BM * std::max(lda, ldb) * 2;
   if (panel >= ((int64_t)1 << 31)) return hipErrorInvalidValue;
-  hipLaunchKernelGGL((gemm_bf16_kernel<TILED, Epi>), dim3((unsigned)round_up(total, 8)), dim3(NT),
-                     0, s, A, lda, B, ldb, M, N, K, k_split, (int)tm, (int)tn, splits, epi);
+  hipLaunchKernelGGL((gemm_bf16_kernel<TILED, Epi>), dim3((unsigned)round_up(total, 8)),
+                     dim3(BF_NT), 0, s, A, lda, B, ldb, M, N, K, k_split, (int)tm, (int)tn, splits,
+                     epi);
   return hipGetLastError();
 }
 
