@@ -39,6 +39,8 @@
 //
 // fp32 kernel (small problems).  Same tile mapping and epilogues, register
 // staged loads, v_mfma_f32_32x32x2_f32 (layout Acc32).
+#include <type_traits>
+
 #include "kernels.h"
 
 namespace rl {
@@ -161,13 +163,18 @@ struct Acc16 {  // v_mfma_f32_16x16x32_bf16 : 16 x 16 blocks, 4 registers per la
 // token-major P[t, v] (leading dimension ldp).  The exponent is formed as one
 // fma on the raw accumulator, (acc * inv_t - m) * log2(e), fed to exp2; t is
 // accumulated in that scaled unit and multiplied by ln 2 once.
-template <typename T> struct FwdEpi {
+// FULL: every tile of the launch lies inside V (the edge row of tiles, if
+// any, gets a launch of its own); STORE: P is written.  Both are fixed per
+// kernel so that no branch around the epilogue's variants keeps the
+// accumulators alive in scratch.  m_base is the launch's first vocabulary row.
+template <typename T, bool FULL_, bool STORE_> struct FwdEpi {
   static constexpr bool TILED_P = sizeof(T) == 2;
   float inv_t;
   int64_t V, Tc, J;
   float *pm, *ps, *pt;
   T* P;
   int64_t ldp;
+  int64_t m_base;
 
   // No data-dependent branches while the accumulators are live: validity is
   // a select, the P store is a template parameter, and every lane writes the
@@ -202,6 +209,24 @@ template <typename T> struct FwdEpi {
     const float k2 = inv_t * LOG2E;
     float* rs = red + 2 * BN;
     float* rt = red + 4 * BN;
+    // Tiled P addresses (layout Acc16): element rows 16 i + 4 g (g = lane/16,
+    // 4 consecutive rows per lane), column 16 j + lane % 16.  Sixteen columns
+    // to the right is +512 elements, 32 rows down +8192; what remains depends
+    // only on the lane and the parity of i, so two per-lane pointers cover all
+    // stores (the identity holds because wn_off and 16 j are multiples of 16
+    // and wm_off of 32).
+    T* pl[2] = {nullptr, nullptr};
+    if constexpr (TILED_P && STORE) {
+      static_assert(std::is_same<L, Acc16>::value, "tiled P store assumes the 16x16 layout");
+      const int g = c.lane >> 4, l = c.lane & 15;
+      T* pw = P +
+              ((c.n0 / TILE_ROWS) * ldp + (m_base + c.m0 + c.wm_off) / TILE_K) *
+                  (TILE_ROWS * TILE_K) +
+              c.wn_off * TILE_K;
+#pragma unroll
+      for (int par = 0; par < 2; ++par)
+        pl[par] = pw + l * TILE_K + ((((2 * par + (g >> 1)) ^ ((l >> 1) & 3)) << 3) + 4 * (g & 1));
+    }
 #pragma unroll
     for (int j = 0; j < NB; ++j) {
       const int colb = c.wn_off + L::col(j, c.lane);
@@ -231,17 +256,14 @@ template <typename T> struct FwdEpi {
               bf16x4 pk;
 #pragma unroll
               for (int r3 = 0; r3 < 4; ++r3) pk[r3] = (__bf16)e4[r3];
-              const int64_t off =
-                  ((c.n0 / TILE_ROWS) * ldp + (c.m0 + vloc) / TILE_K) * (TILE_ROWS * TILE_K) +
-                  colb * TILE_K + ((((vloc % TILE_K) >> 3) ^ ((colb >> 1) & 3)) << 3) +
-                  (vloc & 7);
-              *reinterpret_cast<bf16x4*>(P + off) = pk;
+              *reinterpret_cast<bf16x4*>(pl[i & 1] + (i >> 1) * (TILE_ROWS * TILE_K) +
+                                         16 * j * TILE_K) = pk;
             } else {
               const int64_t col = c.n0 + colb;
               if (col < Tc) {
 #pragma unroll
                 for (int r3 = 0; r3 < 4; ++r3) {
-                  const int64_t v = c.m0 + vloc + r3;
+                  const int64_t v = m_base + c.m0 + vloc + r3;
                   if (v < V) P[col * ldp + v] = Elem<T>::from_f32(e4[r3]);
                 }
               }
@@ -258,23 +280,12 @@ template <typename T> struct FwdEpi {
 
   template <class L, int MB, int NB, int BM, int BN>
   __device__ __forceinline__ void apply(typename L::V (&acc)[MB][NB], const EpiCtx& c) const {
-    const int64_t jt = c.m0 / BM;
-    __syncthreads();  // the main loop's LDS is free from here
+    const int64_t jt = (m_base + c.m0) / BM;
+    __syncthreads();  // the previous users of the scratch area are done
     float* red = reinterpret_cast<float*>(c.smem);  // [2][BN] x 3
-    const int64_t vr = V - c.m0 - c.wm_off;
+    const int64_t vr = V - m_base - c.m0 - c.wm_off;
     const int vrows = (int)(vr < 0 ? 0 : (vr > 2 * BM ? 2 * BM : vr));
-    const bool full = c.m0 + BM <= V;
-    if (P != nullptr) {
-      if (full)
-        columns<L, true, true, MB, NB, BM, BN>(acc, c, vrows, red);
-      else
-        columns<L, false, true, MB, NB, BM, BN>(acc, c, vrows, red);
-    } else {
-      if (full)
-        columns<L, true, false, MB, NB, BM, BN>(acc, c, vrows, red);
-      else
-        columns<L, false, false, MB, NB, BM, BN>(acc, c, vrows, red);
-    }
+    columns<L, FULL_, STORE_, MB, NB, BM, BN>(acc, c, vrows, red);
     __syncthreads();
     if (c.wave_m == 0 && L::col_owner(c.lane)) {
 #pragma unroll
@@ -699,16 +710,38 @@ int fwd_vtile(int dtype) { return dtype == RL_DTYPE_BF16 ? BF_BM : F_BM; }
 
 hipError_t gemm_fwd(int dtype, const void* W, const void* hc, int64_t V, int64_t Tc, int64_t H,
                     const FwdEpiArgs& a, hipStream_t s) {
-  if (dtype == RL_DTYPE_BF16) {
-    FwdEpi<bf16_t> e{a.inv_t, a.V, a.Tc, a.J, a.part_m, a.part_s, a.part_t,
-                     static_cast<bf16_t*>(a.P), a.ldp};
-    return launch_bf16<false>(static_cast<const bf16_t*>(W), H, static_cast<const bf16_t*>(hc), H,
-                              V, Tc, H, 1, round_up(H, BF_BK), e, s);
-  }
-  FwdEpi<float> e{a.inv_t, a.V, a.Tc, a.J, a.part_m, a.part_s, a.part_t,
-                  static_cast<float*>(a.P), a.ldp};
-  return launch_f32(static_cast<const float*>(W), H, static_cast<const float*>(hc), H, V, Tc, H,
-                    1, round_up(H, F_BK), e, s);
+  // Full tiles, then the edge row of tiles (if V is not a multiple of the
+  // tile height) in a launch of its own.
+  auto run = [&](auto tag_t, auto store) -> hipError_t {
+    using T = decltype(tag_t);
+    constexpr bool STORE = decltype(store)::value;
+    const int BM = sizeof(T) == 2 ? BF_BM : F_BM;
+    const int64_t Vfull = V / BM * BM;
+    const T* Wt = static_cast<const T*>(W);
+    auto launch = [&](auto epi, const T* A, int64_t M) -> hipError_t {
+      if constexpr (sizeof(T) == 2)
+        return launch_bf16<false>(A, H, static_cast<const bf16_t*>(hc), H, M, Tc, H, 1,
+                                  round_up(H, BF_BK), epi, s);
+      else
+        return launch_f32(A, H, static_cast<const float*>(hc), H, M, Tc, H, 1, round_up(H, F_BK),
+                          epi, s);
+    };
+    if (Vfull > 0) {
+      FwdEpi<T, true, STORE> e{a.inv_t, a.V, a.Tc, a.J, a.part_m, a.part_s, a.part_t,
+                               static_cast<T*>(a.P), a.ldp, 0};
+      const hipError_t err = launch(e, Wt, Vfull);
+      if (err != hipSuccess) return err;
+    }
+    if (V > Vfull) {
+      FwdEpi<T, false, STORE> e{a.inv_t, a.V, a.Tc, a.J, a.part_m, a.part_s, a.part_t,
+                                static_cast<T*>(a.P), a.ldp, Vfull};
+      return launch(e, Wt + Vfull * H, V - Vfull);
+    }
+    return hipSuccess;
+  };
+  if (dtype == RL_DTYPE_BF16)
+    return a.P ? run(bf16_t{}, std::true_type{}) : run(bf16_t{}, std::false_type{});
+  return a.P ? run(float{}, std::true_type{}) : run(float{}, std::false_type{});
 }
 
 hipError_t gemm_store(int dtype, const void* A, int64_t lda, const void* B, int64_t ldb,
