@@ -524,7 +524,8 @@ rl_status rl_loss_elementwise(const float* lp, const float* lq, const float* adv
                            static_cast<double*>(workspace), out->sums, s);
   }));
   RL_TRY(timed(K_ELEM_FINAL, s, [&] {
-    return rl::elementwise_final(static_cast<const double*>(workspace), N, out->sums, s);
+    return rl::elementwise_final(static_cast<const double*>(workspace), N, cfg->n_eps,
+                                 out->sums, s);
   }));
   return RL_OK;
 }

@@ -23,9 +23,10 @@
 //    accumulated per wave on the scalar unit, which runs beside the VALU;
 //  * the loss and weight sums are plain fp32 FMAs per thread.
 // The grid holds at most kMaxBlocks blocks, all resident at once.  Each block
-// writes one fp64 row of the RL_ELEM_SUM_COUNT sums, stored sum-major, and a
-// second launch with one block per sum adds the rows in a fixed order, so the
-// totals are deterministic.
+// writes its raw totals (float sums, counts, tokens) in fp64, stored
+// total-major, and a second launch with one block per output sum combines
+// the raw totals that output needs over the blocks in a fixed order, so the
+// results are deterministic.
 #include "kernels.h"
 
 namespace rl {
@@ -68,6 +69,52 @@ __device__ __forceinline__ float fmin_(float a, float b) {
 }
 __device__ __forceinline__ float fmax_(float a, float b) {
   return __builtin_amdgcn_fmed3f(a, b, __builtin_inff());
+}
+
+template <int CTRL, int ROW_MASK>
+__device__ __forceinline__ float dpp_add(float x) {
+  // lanes outside ROW_MASK, and lanes whose source falls outside their row,
+  // receive 0
+  return x + __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, ROW_MASK,
+                                                        0xf, true));
+}
+
+// Wave totals of NF per-lane float sums, in a fixed order, stored as fp64 to
+// dst[0 .. NF).  A transposing butterfly (gfx950 lane swaps):
+//  * permlane32_swap of sums x, y gives (x lanes 0-31 | y lanes 0-31) and
+//    (x lanes 32-63 | y lanes 32-63); their sum holds 32 partials of x in
+//    lanes 0-31 and 32 of y in lanes 32-63 (one add for two sums);
+//  * permlane16_swap of two such values swaps 16-lane rows the same way, so
+//    their sum holds four sums with 16 partials each, one per row: row r
+//    holds sum 4j + (0, 2, 1, 3)[r];
+//  * an inclusive scan inside each row (row shifts by 1, 2, 4, 8) leaves the
+//    row total in the row's lane 15.
+template <int NF>
+__device__ __forceinline__ void wave_totals(const float* f, double* dst, int lane) {
+  constexpr int NG = (NF + 1) / 2, NH = (NG + 1) / 2;
+  float g[2 * NH];
+#pragma unroll
+  for (int i = 0; i < NG; ++i) {
+    const float x = f[2 * i], y = 2 * i + 1 < NF ? f[2 * i + 1] : 0.0f;
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(y),
+                                                    false, false);
+    g[i] = __uint_as_float(r[0]) + __uint_as_float(r[1]);
+  }
+  if constexpr (NG < 2 * NH) g[NG] = 0.0f;
+  const int r = lane >> 4;
+  const int off = ((r & 1) << 1) | (r >> 1);
+#pragma unroll
+  for (int j = 0; j < NH; ++j) {
+    const auto s = __builtin_amdgcn_permlane16_swap(__float_as_uint(g[2 * j]),
+                                                    __float_as_uint(g[2 * j + 1]), false, false);
+    float h = __uint_as_float(s[0]) + __uint_as_float(s[1]);
+    h = dpp_add<0x111, 0xf>(h);  // row_shr:1
+    h = dpp_add<0x112, 0xf>(h);  // row_shr:2
+    h = dpp_add<0x114, 0xf>(h);  // row_shr:4
+    h = dpp_add<0x118, 0xf>(h);  // row_shr:8
+    const int id = 4 * j + off;
+    if ((lane & 15) == 15 && id < NF) dst[id] = (double)h;
+  }
 }
 
 __device__ __forceinline__ uint32_t lane_count(bool b) {
@@ -258,90 +305,106 @@ elem_main_kernel(const float* __restrict__ lp, const float* __restrict__ lq,
     }
   }
 
-  // Block reduction in a fixed order.  Float sums: every thread stores its
-  // values in LDS; lane k of each wave adds the 64 values of sum k of its
-  // wave in fp64 (four interleaved chains, then combined); the 4 wave
-  // results are added in wave order.  Counts: wave totals, added exactly.
-  __shared__ float vals[S::NF][NT + 4];
-  __shared__ double wsum[4][S::NF];
-  __shared__ uint32_t wcnt[4][S::NC];
-  __shared__ int64_t wtok[4];
+  // Block reduction in a fixed order, into the block's row of raw totals:
+  // the NF float sums, then the NC counts, then the token count.  Float sums:
+  // a fixed fp32 butterfly over the wave's lanes, then the 4 wave totals
+  // added in wave order in fp64.  Counts: wave totals (already scalar), added exactly.
+  constexpr int NR = S::NF + S::NC + 1;
+  static_assert(NR == 3 * NE + 13 && NR <= NS, "raw totals must fit the workspace rows");
+  __shared__ double wtot[4][NR];
   const int w = wv;
-#pragma unroll
-  for (int k = 0; k < S::NF; ++k) vals[k][threadIdx.x] = f[k];
+  wave_totals<S::NF>(f, wtot[w], lane);
   if (lane == 0) {
 #pragma unroll
-    for (int k = 0; k < S::NC; ++k) wcnt[w][k] = c[k];
-    wtok[w] = ntok;
+    for (int k = 0; k < S::NC; ++k) wtot[w][S::NF + k] = (double)c[k];
+    wtot[w][NR - 1] = (double)ntok;
   }
   __syncthreads();
-  if (lane < S::NF) {
-    const float* row = &vals[lane][w * 64];
-    double s0 = 0.0, s1 = 0.0, s2 = 0.0, s3 = 0.0;
-#pragma unroll 4
-    for (int i = 0; i < 64; i += 4) {
-      const f32x4 x = *reinterpret_cast<const f32x4*>(row + i);
-      s0 += (double)x[0];
-      s1 += (double)x[1];
-      s2 += (double)x[2];
-      s3 += (double)x[3];
-    }
-    wsum[w][lane] = (s0 + s1) + (s2 + s3);
-  }
-  __syncthreads();
-  if (threadIdx.x < NS) {
+  if (threadIdx.x < NR) {
     const int k = threadIdx.x;
-    const int64_t btok = wtok[0] + wtok[1] + wtok[2] + wtok[3];
-    auto fs = [&](int slot) {
-      return ((wsum[0][slot] + wsum[1][slot]) + wsum[2][slot]) + wsum[3][slot];
-    };
-    auto cs = [&](int slot) {
-      return (double)(wcnt[0][slot] + wcnt[1][slot] + wcnt[2][slot] + wcnt[3][slot]);
-    };
-    double v = 0.0;
-    if (k < 3 * RL_ELEM_MAX_EPS) {
-      const int i = k / 3, m = k % 3;
-      if (i < NE) {
-        v = m == 0 ? (double)btok - cs(S::C_IPO + i) : m == 1 ? fs(S::IPO + 2 * i)
-                                                              : fs(S::IPO + 2 * i + 1);
-      }
-    } else {
-      switch (k) {
-        case RL_ELEM_ICEPOP_KEPT: v = (double)btok - cs(S::C_LOW) - cs(S::C_HIGH); break;
-        case RL_ELEM_ICEPOP_LOW: v = cs(S::C_LOW); break;
-        case RL_ELEM_ICEPOP_HIGH: v = cs(S::C_HIGH); break;
-        case RL_ELEM_ICEPOP_LOSS: v = fs(S::ICE); break;
-        case RL_ELEM_ICEPOP_WEIGHT: v = fs(S::ICE + 1); break;
-        case RL_ELEM_REINFORCE_LOSS: v = fs(S::REINF); break;
-        case RL_ELEM_PPO_LOSS: v = -fs(S::PPO_J); break;
-        case RL_ELEM_PPO_CLIP: v = cs(S::C_CLIP); break;
-        case RL_ELEM_PPO_CLIP_LOWER: v = cs(S::C_DUAL); break;
-        case RL_ELEM_PPO_KL: v = -fs(S::PPO_D); break;
-        case RL_ELEM_TIS_LOSS: v = -fs(S::TIS_WA); break;
-        case RL_ELEM_TIS_TRUNC: v = cs(S::C_TRUNC); break;
-        case RL_ELEM_TIS_WEIGHT: v = fs(S::TIS_W); break;
-        default: break;
-      }
-    }
-    partials[(int64_t)k * gridDim.x + blockIdx.x] = v;
+    partials[(int64_t)k * gridDim.x + blockIdx.x] =
+        ((wtot[0][k] + wtot[1][k]) + wtot[2][k]) + wtot[3][k];
   }
 }
 
-// One block per sum: thread t adds rows t, t + NT, ... in that order, then a
-// fixed-order tree over the threads in LDS.
+// Which raw totals make up output sum k: v = t * tokens + ca * raw[a] + cb *
+// raw[b], the coefficients 0 or +-1 (a, b index the raw rows; an output
+// with no term reads the token row with coefficient 0).
+struct OutMap {
+  int a, b;
+  double ct, ca, cb;
+};
+
+__device__ OutMap out_map(int k, int NE) {
+  const int NF = 2 * NE + 7, NC = NE + 5, TOK = NF + NC;
+  const int ICE = 2 * NE, REINF = 2 * NE + 2, PPO_J = 2 * NE + 3, PPO_D = 2 * NE + 4,
+            TIS_WA = 2 * NE + 5, TIS_W = 2 * NE + 6;
+  const int C_LOW = NF + NE, C_HIGH = NF + NE + 1, C_CLIP = NF + NE + 2, C_DUAL = NF + NE + 3,
+            C_TRUNC = NF + NE + 4;
+  if (k < 3 * RL_ELEM_MAX_EPS) {
+    const int i = k / 3, m = k % 3;
+    if (i >= NE) return {TOK, 0, 0.0, 0.0, 0.0};
+    if (m == 0) return {NF + i, 0, 1.0, -1.0, 0.0};  // tokens - masked
+    return {2 * i + (m - 1), 0, 0.0, 1.0, 0.0};
+  }
+  switch (k) {
+    case RL_ELEM_ICEPOP_KEPT: return {C_LOW, C_HIGH, 1.0, -1.0, -1.0};
+    case RL_ELEM_ICEPOP_LOW: return {C_LOW, 0, 0.0, 1.0, 0.0};
+    case RL_ELEM_ICEPOP_HIGH: return {C_HIGH, 0, 0.0, 1.0, 0.0};
+    case RL_ELEM_ICEPOP_LOSS: return {ICE, 0, 0.0, 1.0, 0.0};
+    case RL_ELEM_ICEPOP_WEIGHT: return {ICE + 1, 0, 0.0, 1.0, 0.0};
+    case RL_ELEM_REINFORCE_LOSS: return {REINF, 0, 0.0, 1.0, 0.0};
+    case RL_ELEM_PPO_LOSS: return {PPO_J, 0, 0.0, -1.0, 0.0};
+    case RL_ELEM_PPO_CLIP: return {C_CLIP, 0, 0.0, 1.0, 0.0};
+    case RL_ELEM_PPO_CLIP_LOWER: return {C_DUAL, 0, 0.0, 1.0, 0.0};
+    case RL_ELEM_PPO_KL: return {PPO_D, 0, 0.0, -1.0, 0.0};
+    case RL_ELEM_TIS_LOSS: return {TIS_WA, 0, 0.0, -1.0, 0.0};
+    case RL_ELEM_TIS_TRUNC: return {C_TRUNC, 0, 0.0, 1.0, 0.0};
+    case RL_ELEM_TIS_WEIGHT: return {TIS_W, 0, 0.0, 1.0, 0.0};
+    default: return {TOK, 0, 0.0, 0.0, 0.0};
+  }
+}
+
+// One block per output sum.  Thread t adds, for each raw row the output
+// uses, that row's values of blocks t, t + NT, ... in that order (all loads
+// of a round issued together); wave 0 then adds the four waves' values per
+// lane and a fixed xor-shuffle tree over its lanes.  Rows with a zero coefficient are not read, so a non-finite float sum
+// never reaches a count.  An output combines at most one float sum (with
+// coefficient +-1) with exact integer counts, so summing each row on its own
+// gives the same value as summing the per-block combinations.
 __global__ void __launch_bounds__(NT) elem_final_kernel(const double* __restrict__ partials,
-                                                        int64_t nb, double* __restrict__ sums) {
+                                                        int64_t nb, int NE,
+                                                        double* __restrict__ sums) {
   __shared__ double part[NT];
-  const double* row = partials + (int64_t)blockIdx.x * nb;
+  const OutMap m = out_map((int)blockIdx.x, NE);
+  const int TOK = 3 * NE + 12;
+  const double* row[3] = {partials + (int64_t)m.a * nb, partials + (int64_t)TOK * nb,
+                          partials + (int64_t)m.b * nb};
+  const double co[3] = {m.ca, m.ct, m.cb};
   double acc = 0.0;
-  for (int64_t b = threadIdx.x; b < nb; b += NT) acc += row[b];
+  for (int64_t base = threadIdx.x; base < nb; base += 4 * NT) {
+    double x[3][4];
+#pragma unroll
+    for (int r = 0; r < 3; ++r)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int64_t b = base + (int64_t)j * NT;
+        x[r][j] = (co[r] != 0.0 && b < nb) ? row[r][b] : 0.0;
+      }
+#pragma unroll
+    for (int r = 0; r < 3; ++r)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) acc += co[r] * x[r][j];
+  }
   part[threadIdx.x] = acc;
   __syncthreads();
-  for (int stride = NT / 2; stride > 0; stride >>= 1) {
-    if (threadIdx.x < stride) part[threadIdx.x] += part[threadIdx.x + stride];
-    __syncthreads();
+  if (threadIdx.x < 64) {
+    const int l = threadIdx.x;
+    double v = ((part[l] + part[l + 64]) + part[l + 128]) + part[l + 192];
+#pragma unroll
+    for (int d = 32; d > 0; d >>= 1) v += __shfl_xor(v, d);
+    if (l == 0) sums[blockIdx.x] = v;
   }
-  if (threadIdx.x == 0) sums[blockIdx.x] = part[0];
 }
 
 template <int NE>
@@ -397,8 +460,9 @@ hipError_t elementwise(const float* lp, const float* lq, const float* adv, int64
   return hipGetLastError();
 }
 
-hipError_t elementwise_final(const double* partials, int64_t N, double* sums, hipStream_t s) {
-  hipLaunchKernelGGL(elem_final_kernel, dim3(NS), dim3(NT), 0, s, partials, elem_num_blocks(N),
+hipError_t elementwise_final(const double* partials, int64_t N, int n_eps, double* sums,
+                            hipStream_t s) {
+  hipLaunchKernelGGL(elem_final_kernel, dim3(NS), dim3(NT), 0, s, partials, elem_num_blocks(N), n_eps,
                      sums);
   return hipGetLastError();
 }

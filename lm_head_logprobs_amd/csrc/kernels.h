@@ -140,7 +140,9 @@ int64_t elem_num_blocks(int64_t N);
 hipError_t elementwise(const float* lp, const float* lq, const float* adv, int64_t N,
                        const rl_elem_cfg& c, uint16_t* word, float* w_primary, double* partials,
                        double* sums, hipStream_t s);
-hipError_t elementwise_final(const double* partials, int64_t N, double* sums, hipStream_t s);
+// partials: the main pass's per-block raw totals; n_eps selects their layout.
+hipError_t elementwise_final(const double* partials, int64_t N, int n_eps, double* sums,
+                             hipStream_t s);
 
 // Validation.
 hipError_t validate(int64_t N, int64_t V, int64_t nnz, const int32_t* labels,
