@@ -42,6 +42,7 @@ struct ElemP {
   float M, lo, hi;
   float clo, chi;  // 1 - clip_low, 1 + clip_high
   float c, U;
+  float ninf, pinf;  // -inf, +inf, held in VGPRs (see fmin_)
 };
 
 template <int NE>
@@ -62,13 +63,15 @@ struct Sums {
                        C_TRUNC = NE + 4;
 };
 
-// min / max as one v_med3_f32 (no NaN canonicalisation of the operands;
-// the inputs are finite)
-__device__ __forceinline__ float fmin_(float a, float b) {
-  return __builtin_amdgcn_fmed3f(a, b, -__builtin_inff());
+// min / max as one v_med3_f32 against an infinity the compiler cannot see
+// (with a literal infinity it turns the median into v_min / v_max, which in
+// IEEE mode need their operands quieted first: two extra operations).  The
+// inputs are finite.
+__device__ __forceinline__ float fmin_(float a, float b, const ElemP& p) {
+  return __builtin_amdgcn_fmed3f(a, b, p.ninf);
 }
-__device__ __forceinline__ float fmax_(float a, float b) {
-  return __builtin_amdgcn_fmed3f(a, b, __builtin_inff());
+__device__ __forceinline__ float fmax_(float a, float b, const ElemP& p) {
+  return __builtin_amdgcn_fmed3f(a, b, p.pinf);
 }
 
 template <int CTRL, int ROW_MASK>
@@ -135,7 +138,7 @@ __device__ __forceinline__ uint32_t token(float lp, float lq, float A, bool ok, 
   const float Q = __expf(lq);
   const float dPQ = fabsf(fmaf(Q, r, -Q));  // |P - Q| with P = Q r
   const float Alp = -A * lp;
-  const float rm = (GUARD && !ok) ? 0.0f : fmin_(r, p.M);
+  const float rm = (GUARD && !ok) ? 0.0f : fmin_(r, p.M, p);
   uint32_t wd = 0;
 #pragma unroll
   for (int i = 0; i < NE; ++i) {
@@ -163,11 +166,11 @@ __device__ __forceinline__ uint32_t token(float lp, float lq, float A, bool ok, 
     // with A = 0 every term below is 0 and neither bit is set
     const float J1 = r * A;
     const float J2 = __builtin_amdgcn_fmed3f(r, p.clo, p.chi) * A;
-    const float Jmin = fmin_(J1, J2);
+    const float Jmin = fmin_(J1, J2, p);
     const float cA = p.c * A;
     const bool neg = A < 0.0f;
     const bool dual = neg && (cA > Jmin);
-    const float J = neg ? fmax_(Jmin, cA) : Jmin;
+    const float J = neg ? fmax_(Jmin, cA, p) : Jmin;
     const bool clip = J2 < J1;
     f[S::PPO_J] += J;
     f[S::PPO_D] += d;
@@ -179,7 +182,7 @@ __device__ __forceinline__ uint32_t token(float lp, float lq, float A, bool ok, 
   {
     bool trunc = r > p.U;
     if (GUARD) trunc = trunc && ok;
-    const float w = (GUARD && !ok) ? 0.0f : fmin_(r, p.U);
+    const float w = (GUARD && !ok) ? 0.0f : fmin_(r, p.U, p);
     f[S::TIS_WA] = fmaf(w, A, f[S::TIS_WA]);
     f[S::TIS_W] += w;
     wd |= trunc ? (1u << RL_ELEM_BIT_TIS_TRUNC) : 0u;
@@ -240,6 +243,8 @@ elem_main_kernel(const float* __restrict__ lp, const float* __restrict__ lq,
   p.clo = pk.clo, p.chi = pk.chi, p.c = pk.c, p.U = pk.U;
   __asm__ volatile("" : "+v"(p.eps_primary), "+v"(p.M), "+v"(p.lo), "+v"(p.hi));
   __asm__ volatile("" : "+v"(p.clo), "+v"(p.chi), "+v"(p.c), "+v"(p.U));
+  p.ninf = -__builtin_inff(), p.pinf = __builtin_inff();
+  __asm__ volatile("" : "+v"(p.ninf), "+v"(p.pinf));
   // Chunk indices are 32-bit (the host limits N to 2^38 tokens).
   const int nfull = (int)(N / 256);  // chunks of 256 tokens entirely in range
   // The wave index is made provably uniform so that every branch below is a
