@@ -210,6 +210,45 @@ def copy_floor(torch, copies, N, steps):
             "GB/s": 16.0 * N / (ms * 1e-3) / 1e9}
 
 
+def event_overhead(torch, steps):
+    """An event pair around nothing, timed like the per-launch events: the
+    fixed part of a short kernel's event-measured duration."""
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    tot = 0.0
+    for _ in range(steps):
+        e0.record()
+        e1.record()
+        e1.synchronize()
+        tot += e0.elapsed_time(e1)
+    return tot / steps
+
+
+def replay_16x(torch, L, ops, r, steps):
+    """The same pass over 16 N tokens (the replay input repeated 16 times), two
+    rotated copies of 1.24 GB: launch and tail costs amortise at this size."""
+    big = [ops.Replay(r.lp.repeat(16), r.lq.repeat(16), r.adv.repeat(16), r.params)
+           for _ in range(2)]
+    for i in range(4):
+        big[i % 2]()
+    torch.cuda.synchronize()
+    L.rl_profile_begin()
+    n = max(steps // 2, 4)
+    for i in range(n):
+        big[i % 2]()
+    torch.cuda.synchronize()
+    prof = L.rl_profile_end()
+    cnt, tot = prof["elementwise"]
+    avg = tot / cnt
+    byt = 18.0 * big[0].N
+    gbs = byt / (avg * 1e-3) / 1e9
+    out = {"tokens": big[0].N, "launches": cnt, "avg_ms": avg,
+           "algorithmic_bytes_per_launch": byt, "GB/s": gbs, "frac": gbs / PEAK_HBM_GBS}
+    del big
+    torch.cuda.empty_cache()
+    return out
+
+
 def bench_replay(args, torch):
     from lm_head_logprobs_amd import _lib as L
     from lm_head_logprobs_amd import ops
@@ -251,6 +290,8 @@ def bench_replay(args, torch):
         "kernels": {"elementwise": {"launches": n, "avg_ms": avg},
                     "elementwise_final": {"launches": nf, "avg_ms": totf / max(nf, 1)}},
         "torch_elementwise_floor": copy_floor(torch, copies, r.N, args.steps),
+        "replay_16x": replay_16x(torch, L, ops, r, args.steps),
+        "event_pair_overhead_ms": event_overhead(torch, args.steps),
         "cpu_baseline": None,
     }, None
 
