@@ -10,8 +10,10 @@ the tensors it returns.
 
 from .gen import (  # noqa: F401
     HEAD_CONFIGS,
+    MIS_PARAMS,
     HeadWorkload,
     ReplayWorkload,
     make_head,
     make_replay,
+    replay_sequences,
 )

@@ -334,3 +334,46 @@ def make_replay(N: int = 2_160_000, device="cpu", seed: int = 1002) -> ReplayWor
     return ReplayWorkload(N=N, lp=lp.float(), lq=lq.float(), adv=adv,
                           params=dict(REPLAY_PARAMS),
                           info=dict(seed=seed, clamped_to_zero=clamped))
+
+
+# Sequence-aware rollout correction on the replay (Rollout Correction Methods
+# page, "Config keys"): geometric-level TIS in clip mode, sequence-level
+# rejection with the TIS bounds, the veto at the low end of the page's typical
+# range, batch normalisation on.
+MIS_PARAMS = dict(
+    tis_level="geometric",
+    tis_mode="clip",
+    tis_lower=0.5,
+    tis_upper=2.0,
+    use_rs=True,
+    rs_level="sequence",
+    rs_lower=None,
+    rs_upper=None,
+    veto=1e-4,
+    batch_normalize=True,
+)
+
+
+def replay_sequences(N: int, seed: int = 1002, median: float = 1024.0, sigma_log: float = 1.0,
+                     max_len: int = 32768) -> torch.Tensor:
+    """Offsets [S + 1] (int64, CPU) cutting N replay tokens into responses.
+
+    The pages give no response lengths for the replayed agentic run; lengths
+    are lognormal (median 1024 tokens, sigma of the log 1.0), rounded, clipped
+    to [1, max_len], and the last response is cut to end at N.
+    """
+    g = _gen("cpu", seed, "scale")
+    lens = []
+    total = 0
+    while total < N:
+        z = torch.randn(4096, generator=g, dtype=torch.float64)
+        L = torch.clamp(torch.round(median * torch.exp(sigma_log * z)), 1, max_len).long()
+        for x in L.tolist():
+            if total >= N:
+                break
+            x = min(x, N - total)
+            lens.append(x)
+            total += x
+    off = torch.zeros(len(lens) + 1, dtype=torch.int64)
+    off[1:] = torch.cumsum(torch.tensor(lens, dtype=torch.int64), 0)
+    return off

@@ -61,3 +61,16 @@ def test_replay_generator_recipe():
     assert 0.55 < near.mean() < 0.72
     assert r.info["clamped_to_zero"] > 0
     assert torch.equal(make_replay(N=1000).lp, make_replay(N=1000).lp)
+
+
+def test_replay_sequences_recipe():
+    from synth import replay_sequences
+    off = replay_sequences(2_160_000)
+    n = torch.diff(off)
+    assert int(off[0]) == 0 and int(off[-1]) == 2_160_000
+    assert int(n.min()) >= 1 and int(n.max()) <= 32768
+    # lognormal with median 1024 and sigma_log 1: the sample median is near 1024
+    assert 900 < float(n[:-1].double().median()) < 1160
+    assert torch.equal(off, replay_sequences(2_160_000))
+    small = replay_sequences(10)
+    assert int(small[-1]) == 10 and torch.all(torch.diff(small) >= 1)
