@@ -246,6 +246,125 @@ rl_status rl_loss_elementwise(const float* lp, const float* lq, const float* adv
                               void* workspace, size_t workspace_bytes, void* stream);
 
 /* ---------------------------------------------------------------------------
+ * Sequence-aware rollout correction over a replay (Rollout Correction Methods
+ * page: "Config keys", "Importance Sampling", "Rejection Sampling", "Veto
+ * Mechanism"; metrics from "Mismatch Monitoring Metrics" and "IS/RS
+ * Correction Metrics").  The replay has no separate proximal policy
+ * (pi_old := pi_train), so per token d = lp - lq, the token ratio is
+ * rho = e^d and the decoupled PPO inner ratio is 1.  With sequences s given
+ * by offsets and n_s tokens each:
+ *   IS weight:  token  log w = d_t;  sequence  log w = sum_s d;
+ *               geometric  log w = (1/n_s) sum_s d
+ *   TIS mode:   truncate  w' = min(w, U);  clip  w' = min(max(w, L), U);
+ *               mask  w' = w if L <= w <= U else 0 (the token stays in the
+ *               loss average)
+ *   RS:         statistic  token rho_t;  sequence (1/n_s) sum_s rho;
+ *               geometric  e^{(1/n_s) sum_s d}; outside [rs_lower, rs_upper]
+ *               the token (or the whole sequence) is rejected: weight 0, out
+ *               of the loss average
+ *   veto:       veto > 0: a sequence holding a token with rho < veto is
+ *               rejected whole (with or without RS)
+ *   batch norm: factor = kept / sum over kept tokens of w' (1 when off or
+ *               when that sum is 0)
+ *   loss:       l_t = -factor w'_t A_t over kept tokens; loss = sum / kept
+ * Bounds are inclusive; decisions compare log weights with log bounds.
+ * ------------------------------------------------------------------------ */
+typedef enum rl_is_level {
+  RL_LEVEL_TOKEN = 0,
+  RL_LEVEL_SEQUENCE = 1,
+  RL_LEVEL_GEOMETRIC = 2
+} rl_is_level;
+
+typedef enum rl_tis_mode { RL_TIS_TRUNCATE = 0, RL_TIS_CLIP = 1, RL_TIS_MASK = 2 } rl_tis_mode;
+
+typedef struct rl_mis_cfg {
+  int32_t tis_level;       /* rl_is_level                                      */
+  int32_t tis_mode;        /* rl_tis_mode                                      */
+  float tis_lower;         /* L > 0 (truncate ignores it)                      */
+  float tis_upper;         /* U >= L                                           */
+  int32_t use_rs;          /* 0 or 1                                           */
+  int32_t rs_level;        /* rl_is_level                                      */
+  float rs_lower;          /* > 0; NaN: tis_lower                              */
+  float rs_upper;          /* >= rs_lower; NaN: tis_upper                      */
+  float veto;              /* 0: off; > 0: the veto threshold C                */
+  int32_t batch_normalize; /* 0 or 1                                           */
+} rl_mis_cfg;
+
+/* Per-token flag bits (uint8 per token). */
+#define RL_MIS_F_TIS_LOW 0x01     /* w below L (clip, mask)                        */
+#define RL_MIS_F_TIS_HIGH 0x02    /* w above U (truncate, clip, mask)              */
+#define RL_MIS_F_RS_LOW 0x04      /* rejection statistic below rs_lower            */
+#define RL_MIS_F_RS_HIGH 0x08     /* rejection statistic above rs_upper            */
+#define RL_MIS_F_VETO 0x10        /* the token's sequence is vetoed                */
+#define RL_MIS_F_CATASTROPHIC 0x20 /* the token's own rho is below the veto        */
+#define RL_MIS_F_REJECTED 0x40    /* out of the loss (RS or veto)                  */
+
+/* Indices into rl_mis_out.metrics (fp64).  Token means over the N tokens
+ * unless stated; "per sequence" values are the mean over sequences of the
+ * per-sequence quantity, with log ppl_s = -(1/n_s) sum_s log pi. */
+enum {
+  RL_MIS_TRAINING_LOG_PPL = 0,   /* per sequence: log ppl of lp                    */
+  RL_MIS_TRAINING_PPL,           /* per sequence: e^(log ppl of lp)                */
+  RL_MIS_ROLLOUT_LOG_PPL,        /* per sequence                                   */
+  RL_MIS_ROLLOUT_PPL,            /* per sequence                                   */
+  RL_MIS_KL,                     /* mean of lq - lp                                */
+  RL_MIS_K3_KL,                  /* mean of e^d - d - 1                            */
+  RL_MIS_LOG_PPL_DIFF,           /* per sequence: training - rollout log ppl       */
+  RL_MIS_LOG_PPL_ABS_DIFF,       /* per sequence: |training - rollout log ppl|     */
+  RL_MIS_PPL_RATIO,              /* per sequence: e^(training - rollout log ppl)   */
+  RL_MIS_CHI2_TOKEN,             /* mean of rho^2, minus 1                         */
+  RL_MIS_CHI2_SEQ,               /* mean over sequences of e^(2 sum_s d), minus 1  */
+  RL_MIS_LOGPROB_ABS_DIFF,       /* mean of |d|                                    */
+  RL_MIS_TIS_WEIGHT_BEFORE_BOUND, /* mean of w                                     */
+  RL_MIS_TIS_WEIGHT_AFTER_BOUND, /* mean of w'                                     */
+  RL_MIS_TIS_FRACTION_LOW,       /* fraction with w < L (clip, mask)               */
+  RL_MIS_TIS_FRACTION_HIGH,      /* fraction with w > U (truncate, clip, mask)     */
+  RL_MIS_RS_FRACTION_LOW,        /* fraction rejected below rs_lower               */
+  RL_MIS_RS_FRACTION_HIGH,       /* fraction rejected above rs_upper               */
+  RL_MIS_CATASTROPHIC_TOKEN_FRACTION,
+  RL_MIS_CATASTROPHIC_SEQ_FRACTION, /* over sequences                              */
+  RL_MIS_IS_RATIO_MEAN_AFTER_TIS_RS, /* mean of the weight output (rejected: 0)    */
+  RL_MIS_BATCH_NORM_FACTOR,
+  RL_MIS_IS_RATIO_MEAN_FINAL,    /* over kept tokens, factor included              */
+  RL_MIS_IS_RATIO_MIN_FINAL,     /* over kept tokens (0 if none)                   */
+  RL_MIS_IS_RATIO_MAX_FINAL,     /* over kept tokens (0 if none)                   */
+  RL_MIS_LOSS,                   /* loss_sum / kept (0 if none)                    */
+  RL_MIS_LOSS_SUM,
+  RL_MIS_KEPT_TOKENS,
+  RL_MIS_REJECTED_TOKENS,
+  RL_MIS_METRIC_COUNT = 29
+};
+
+typedef struct rl_mis_out {
+  float* weight;    /* [N] nullable: w' of kept tokens, 0 for rejected ones,
+                       before batch normalisation (the final weight is
+                       metrics[RL_MIS_BATCH_NORM_FACTOR] * weight)           */
+  uint8_t* flags;   /* [N] nullable: RL_MIS_F_* bits                         */
+  double* metrics;  /* [RL_MIS_METRIC_COUNT] required                        */
+} rl_mis_out;
+
+/* Largest N rl_mis_replay accepts. */
+#define RL_MIS_MAX_N ((((int64_t)1) << 31) - 256)
+
+/* Workspace bytes for rl_mis_replay with N tokens in S sequences. */
+rl_status rl_mis_workspace_size(int64_t N, int64_t S, size_t* bytes);
+
+/*
+ * rl_mis_replay -- the correction pass over lp, lq, adv [N] fp32 (device,
+ * 16-byte aligned; weight 16-byte and flags 4-byte aligned when given),
+ * 1 <= N <= RL_MIS_MAX_N, cut into S >= 1 sequences by int64 offsets
+ * [S + 1] given both on the host (checked: offsets[0] = 0, strictly
+ * increasing, offsets[S] = N) and on the device (the same values; not
+ * re-checked).  Deterministic.  Errors: RL_E_ARG, RL_E_CFG (unknown level
+ * or mode, bounds not 0 < L <= U, veto < 0 or not finite), RL_E_CSR (bad
+ * offsets), RL_E_WORKSPACE, RL_E_HIP.
+ */
+rl_status rl_mis_replay(const float* lp, const float* lq, const float* adv, int64_t N,
+                        const int64_t* seq_offsets_host, const int64_t* seq_offsets_dev,
+                        int64_t S, const rl_mis_cfg* cfg, const rl_mis_out* out,
+                        void* workspace, size_t workspace_bytes, void* stream);
+
+/* ---------------------------------------------------------------------------
  * Sampler-evidence validation of a CSR support (prime-rl PR 4233, "What
  * changes": checked on the GPU on the CSR entries once per step, before the
  * optimizer).  Flag bits written to *flags_dev (bitwise OR over all items):

@@ -25,12 +25,26 @@ METRIC_NAMES = ("masked_fraction", "support_mass", "mask_tv", "kl", "kl_beta", "
 RL_METRIC_COUNT = len(METRIC_NAMES)
 RL_ELEM_MAX_EPS = 8
 RL_ELEM_SUM_COUNT = 37
+RL_LEVEL_TOKEN, RL_LEVEL_SEQUENCE, RL_LEVEL_GEOMETRIC = range(3)
+RL_TIS_TRUNCATE, RL_TIS_CLIP, RL_TIS_MASK = range(3)
+MIS_METRIC_NAMES = (
+    "training_log_ppl", "training_ppl", "rollout_log_ppl", "rollout_ppl", "kl", "k3_kl",
+    "log_ppl_diff", "log_ppl_abs_diff", "ppl_ratio", "chi2_token", "chi2_seq",
+    "logprob_abs_diff", "tis_weight_before_bound", "tis_weight_after_bound",
+    "tis_fraction_low", "tis_fraction_high", "rs_fraction_low", "rs_fraction_high",
+    "catastrophic_token_fraction", "catastrophic_seq_fraction", "is_ratio_mean_after_tis_rs",
+    "batch_norm_factor", "is_ratio_mean_final", "is_ratio_min_final", "is_ratio_max_final",
+    "loss", "loss_sum", "kept_tokens", "rejected_tokens")
+RL_MIS_METRIC_COUNT = len(MIS_METRIC_NAMES)
+RL_MIS_MAX_N = (1 << 31) - 256
 
 EXPORTED = (
     "rl_loss_workspace_size",
     "rl_loss_fwd_bwd",
     "rl_elementwise_workspace_size",
     "rl_loss_elementwise",
+    "rl_mis_workspace_size",
+    "rl_mis_replay",
     "rl_validate_support",
     "rl_validate_support_sync",
     "rl_profile_begin",
@@ -76,6 +90,21 @@ class RlElemOut(ctypes.Structure):
                 ("sums", ctypes.c_void_p)]
 
 
+class RlMisCfg(ctypes.Structure):
+    _fields_ = [
+        ("tis_level", ctypes.c_int32), ("tis_mode", ctypes.c_int32),
+        ("tis_lower", ctypes.c_float), ("tis_upper", ctypes.c_float),
+        ("use_rs", ctypes.c_int32), ("rs_level", ctypes.c_int32),
+        ("rs_lower", ctypes.c_float), ("rs_upper", ctypes.c_float),
+        ("veto", ctypes.c_float), ("batch_normalize", ctypes.c_int32),
+    ]
+
+
+class RlMisOut(ctypes.Structure):
+    _fields_ = [("weight", ctypes.c_void_p), ("flags", ctypes.c_void_p),
+                ("metrics", ctypes.c_void_p)]
+
+
 class RlProfileEntry(ctypes.Structure):
     _fields_ = [("name", ctypes.c_char * 32), ("launches", ctypes.c_int64),
                 ("total_ms", ctypes.c_double)]
@@ -112,6 +141,11 @@ def lib() -> ctypes.CDLL:
         L.rl_loss_elementwise.argtypes = [vp, vp, vp, i64, ctypes.POINTER(RlElemCfg),
                                           ctypes.POINTER(RlElemOut), vp, sz, vp]
         L.rl_loss_elementwise.restype = ctypes.c_int
+        L.rl_mis_workspace_size.argtypes = [i64, i64, ctypes.POINTER(sz)]
+        L.rl_mis_workspace_size.restype = ctypes.c_int
+        L.rl_mis_replay.argtypes = [vp, vp, vp, i64, vp, vp, i64, ctypes.POINTER(RlMisCfg),
+                                    ctypes.POINTER(RlMisOut), vp, sz, vp]
+        L.rl_mis_replay.restype = ctypes.c_int
         L.rl_validate_support.argtypes = [i64, i64, i64, vp, vp, vp, vp, vp, vp, vp, vp, i32, vp,
                                           vp]
         L.rl_validate_support.restype = ctypes.c_int
@@ -193,6 +227,24 @@ def rl_loss_elementwise(lp, lq, adv, N, cfg: RlElemCfg, out: RlElemOut, workspac
                                    _stream(stream))
     if check and st != RL_OK:
         raise RlError(st, "rl_loss_elementwise")
+    return st
+
+
+def rl_mis_workspace_size(N: int, S: int) -> int:
+    n = ctypes.c_size_t(0)
+    st = lib().rl_mis_workspace_size(int(N), int(S), ctypes.byref(n))
+    if st != RL_OK:
+        raise RlError(st, "rl_mis_workspace_size")
+    return n.value
+
+
+def rl_mis_replay(lp, lq, adv, N, seq_offsets_host, seq_offsets_dev, S, cfg: RlMisCfg,
+                  out: RlMisOut, workspace, workspace_bytes, stream=None, check=True) -> int:
+    st = lib().rl_mis_replay(_ptr(lp), _ptr(lq), _ptr(adv), int(N), _ptr(seq_offsets_host),
+                             _ptr(seq_offsets_dev), int(S), ctypes.byref(cfg), ctypes.byref(out),
+                             _ptr(workspace), int(workspace_bytes), _stream(stream))
+    if check and st != RL_OK:
+        raise RlError(st, "rl_mis_replay")
     return st
 
 

@@ -9,7 +9,8 @@ import subprocess
 HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 BUILD = os.path.join(HERE, "_build")
-SOURCES = ("api.hip", "gemm.hip", "head.hip", "sparse.hip", "elementwise.hip", "validate.hip")
+SOURCES = ("api.hip", "gemm.hip", "head.hip", "sparse.hip", "elementwise.hip", "mis.hip",
+           "validate.hip")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = [
     "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC",

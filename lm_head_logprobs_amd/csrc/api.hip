@@ -29,12 +29,13 @@ using namespace rl;
 enum ProfKind {
   K_GEMM_FWD, K_COMBINE, K_FORM_G, K_GEMM_DH, K_TRANSPOSE_H, K_GEMM_DW, K_FINALIZE_DH,
   K_TRANSPOSE_W, K_CSR_ROWS, K_CSC_BUILD, K_SPARSE_DW, K_REDUCE, K_ELEMENTWISE, K_VALIDATE,
-  K_ELEM_FINAL, K_COUNT
+  K_ELEM_FINAL, K_MIS_CHUNK, K_MIS_SEQ, K_MIS_TOKEN, K_MIS_RAW, K_MIS_METRICS, K_COUNT
 };
 const char* const kProfNames[K_COUNT] = {
     "gemm_fwd",   "combine",   "form_g",   "gemm_dh",   "transpose_h",
     "gemm_dw",    "finalize_dh", "transpose_w", "csr_rows", "csc_build",
-    "sparse_dw",  "reduce",    "elementwise", "validate", "elementwise_final"};
+    "sparse_dw",  "reduce",    "elementwise", "validate", "elementwise_final",
+    "mis_chunk",  "mis_seq",   "mis_token", "mis_raw",  "mis_metrics"};
 
 struct ProfRec {
   int kind;
@@ -527,6 +528,58 @@ rl_status rl_loss_elementwise(const float* lp, const float* lq, const float* adv
     return rl::elementwise_final(static_cast<const double*>(workspace), N, cfg->n_eps,
                                  out->sums, s);
   }));
+  return RL_OK;
+}
+
+rl_status rl_mis_workspace_size(int64_t N, int64_t S, size_t* bytes) {
+  if (bytes == nullptr || N < 1 || N > RL_MIS_MAX_N || S < 1 || S > N) return RL_E_ARG;
+  *bytes = (size_t)rl::mis_layout(N, S).bytes;
+  return RL_OK;
+}
+
+namespace {
+bool level_ok(int32_t v) { return v >= RL_LEVEL_TOKEN && v <= RL_LEVEL_GEOMETRIC; }
+bool bound_ok(float lo, float hi) {
+  return std::isfinite(lo) && std::isfinite(hi) && lo > 0.0f && hi >= lo;
+}
+}  // namespace
+
+rl_status rl_mis_replay(const float* lp, const float* lq, const float* adv, int64_t N,
+                        const int64_t* seq_offsets_host, const int64_t* seq_offsets_dev,
+                        int64_t S, const rl_mis_cfg* cfg, const rl_mis_out* out,
+                        void* workspace, size_t workspace_bytes, void* stream) {
+  if (lp == nullptr || lq == nullptr || adv == nullptr || seq_offsets_host == nullptr ||
+      seq_offsets_dev == nullptr || cfg == nullptr || out == nullptr || out->metrics == nullptr ||
+      N < 1 || N > RL_MIS_MAX_N || S < 1 || S > N)
+    return RL_E_ARG;
+  if (!aligned(lp, 16) || !aligned(lq, 16) || !aligned(adv, 16) ||
+      !aligned(seq_offsets_dev, 8) || (out->weight && !aligned(out->weight, 16)) ||
+      (out->flags && !aligned(out->flags, 4)))
+    return RL_E_ARG;
+  const rl_mis_cfg& c = *cfg;
+  if (!level_ok(c.tis_level) || !level_ok(c.rs_level) || c.tis_mode < RL_TIS_TRUNCATE ||
+      c.tis_mode > RL_TIS_MASK || (c.use_rs != 0 && c.use_rs != 1) ||
+      (c.batch_normalize != 0 && c.batch_normalize != 1))
+    return RL_E_CFG;
+  if (!bound_ok(c.tis_lower, c.tis_upper) || !std::isfinite(c.veto) || c.veto < 0.0f)
+    return RL_E_CFG;
+  const float rlo = std::isnan(c.rs_lower) ? c.tis_lower : c.rs_lower;
+  const float rhi = std::isnan(c.rs_upper) ? c.tis_upper : c.rs_upper;
+  if (!bound_ok(rlo, rhi)) return RL_E_CFG;
+  if (seq_offsets_host[0] != 0 || seq_offsets_host[S] != N) return RL_E_CSR;
+  for (int64_t i = 0; i < S; ++i)
+    if (seq_offsets_host[i + 1] <= seq_offsets_host[i]) return RL_E_CSR;
+  const rl::MisLayout L = rl::mis_layout(N, S);
+  if (workspace == nullptr || workspace_bytes < (size_t)L.bytes || !aligned(workspace, 16))
+    return RL_E_WORKSPACE;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const int kinds[5] = {K_MIS_CHUNK, K_MIS_SEQ, K_MIS_TOKEN, K_MIS_RAW, K_MIS_METRICS};
+  for (int st = 0; st < 5; ++st) {
+    RL_TRY(timed(kinds[st], s, [&] {
+      return rl::mis_stage(st, lp, lq, adv, N, seq_offsets_dev, S, c, out->weight, out->flags,
+                           out->metrics, workspace, s);
+    }));
+  }
   return RL_OK;
 }
 

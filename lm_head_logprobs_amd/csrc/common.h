@@ -122,5 +122,51 @@ __device__ __forceinline__ float wave_max(float v) {
   return v;
 }
 
+template <int CTRL, int ROW_MASK>
+__device__ __forceinline__ float dpp_add(float x) {
+  // lanes outside ROW_MASK, and lanes whose source falls outside their row,
+  // receive 0
+  return x + __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, ROW_MASK,
+                                                        0xf, true));
+}
+
+// Wave totals of NF per-lane float sums, in a fixed order, stored as fp64 to
+// dst[0 .. NF).  A transposing butterfly (gfx950 lane swaps):
+//  * permlane32_swap of sums x, y gives (x lanes 0-31 | y lanes 0-31) and
+//    (x lanes 32-63 | y lanes 32-63); their sum holds 32 partials of x in
+//    lanes 0-31 and 32 of y in lanes 32-63 (one add for two sums);
+//  * permlane16_swap of two such values swaps 16-lane rows the same way, so
+//    their sum holds four sums with 16 partials each, one per row: row r
+//    holds sum 4j + (0, 2, 1, 3)[r];
+//  * an inclusive scan inside each row (row shifts by 1, 2, 4, 8) leaves the
+//    row total in the row's lane 15.
+template <int NF>
+__device__ __forceinline__ void wave_totals(const float* f, double* dst, int lane) {
+  constexpr int NG = (NF + 1) / 2, NH = (NG + 1) / 2;
+  float g[2 * NH];
+#pragma unroll
+  for (int i = 0; i < NG; ++i) {
+    const float x = f[2 * i], y = 2 * i + 1 < NF ? f[2 * i + 1] : 0.0f;
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(y),
+                                                    false, false);
+    g[i] = __uint_as_float(r[0]) + __uint_as_float(r[1]);
+  }
+  if constexpr (NG < 2 * NH) g[NG] = 0.0f;
+  const int r = lane >> 4;
+  const int off = ((r & 1) << 1) | (r >> 1);
+#pragma unroll
+  for (int j = 0; j < NH; ++j) {
+    const auto s = __builtin_amdgcn_permlane16_swap(__float_as_uint(g[2 * j]),
+                                                    __float_as_uint(g[2 * j + 1]), false, false);
+    float h = __uint_as_float(s[0]) + __uint_as_float(s[1]);
+    h = dpp_add<0x111, 0xf>(h);  // row_shr:1
+    h = dpp_add<0x112, 0xf>(h);  // row_shr:2
+    h = dpp_add<0x114, 0xf>(h);  // row_shr:4
+    h = dpp_add<0x118, 0xf>(h);  // row_shr:8
+    const int id = 4 * j + off;
+    if ((lane & 15) == 15 && id < NF) dst[id] = (double)h;
+  }
+}
+
 __host__ __device__ static inline int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 __host__ __device__ static inline int64_t round_up(int64_t a, int64_t b) { return ceil_div(a, b) * b; }

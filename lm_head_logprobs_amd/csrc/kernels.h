@@ -144,6 +144,18 @@ hipError_t elementwise(const float* lp, const float* lq, const float* adv, int64
 hipError_t elementwise_final(const double* partials, int64_t N, int n_eps, double* sums,
                              hipStream_t s);
 
+// Sequence-aware rollout correction over a replay (five launches in order:
+// stage 0 chunk totals, 1 sequences, 2 tokens, 3 raw totals, 4 metrics).
+// Workspace offsets in bytes from the workspace base; N tokens, S sequences.
+struct MisLayout {
+  int64_t nch, nb1, nb2, nb3;
+  int64_t ct, firstseq, bitmap, seq_w, seq_flags, part1, part2, part3, raw, bytes;
+};
+MisLayout mis_layout(int64_t N, int64_t S);
+hipError_t mis_stage(int stage, const float* lp, const float* lq, const float* adv, int64_t N,
+                     const int64_t* off_dev, int64_t S, const rl_mis_cfg& c, float* weight,
+                     uint8_t* flags, double* metrics, void* ws, hipStream_t s);
+
 // Validation.
 hipError_t validate(int64_t N, int64_t V, int64_t nnz, const int32_t* labels,
                     const float* infer_lp, const float* adv, const int64_t* off,

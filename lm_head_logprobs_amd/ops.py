@@ -141,6 +141,61 @@ class Replay:
                                      self.ws_bytes, stream=stream, check=check)
 
 
+_LEVELS = {"token": L.RL_LEVEL_TOKEN, "sequence": L.RL_LEVEL_SEQUENCE,
+           "geometric": L.RL_LEVEL_GEOMETRIC}
+_MODES = {"truncate": L.RL_TIS_TRUNCATE, "clip": L.RL_TIS_CLIP, "mask": L.RL_TIS_MASK}
+
+
+def mis_cfg(params: dict) -> L.RlMisCfg:
+    c = L.RlMisCfg()
+    c.tis_level = _LEVELS[params["tis_level"]]
+    c.tis_mode = _MODES[params["tis_mode"]]
+    c.tis_lower = float(params["tis_lower"])
+    c.tis_upper = float(params["tis_upper"])
+    c.use_rs = int(bool(params["use_rs"]))
+    c.rs_level = _LEVELS[params["rs_level"]]
+    nan = float("nan")
+    c.rs_lower = nan if params.get("rs_lower") is None else float(params["rs_lower"])
+    c.rs_upper = nan if params.get("rs_upper") is None else float(params["rs_upper"])
+    c.veto = float(params["veto"])
+    c.batch_normalize = int(bool(params["batch_normalize"]))
+    return c
+
+
+class MisReplay:
+    """Preallocated outputs, device offsets and workspace for rl_mis_replay.
+
+    offsets: int64 [S + 1] on the host (CPU tensor); a device copy is made once.
+    """
+
+    def __init__(self, lp, lq, adv, offsets, params):
+        dev = lp.device
+        self.N = lp.numel()
+        self.args = (lp, lq, adv)
+        self.offsets_host = offsets.to(torch.int64).contiguous().cpu()
+        self.S = self.offsets_host.numel() - 1
+        self.offsets_dev = self.offsets_host.to(dev)
+        self.cfg = mis_cfg(params)
+        self.o = dict(weight=torch.empty(self.N, device=dev, dtype=torch.float32),
+                      flags=torch.empty(self.N, device=dev, dtype=torch.uint8),
+                      metrics=torch.empty(L.RL_MIS_METRIC_COUNT, device=dev, dtype=torch.float64))
+        self.out = L.RlMisOut()
+        for k, v in self.o.items():
+            setattr(self.out, k, v.data_ptr())
+        self.ws_bytes = L.rl_mis_workspace_size(self.N, self.S)
+        self.workspace = torch.empty(self.ws_bytes, device=dev, dtype=torch.uint8)
+
+    def __call__(self, stream=None, check=True):
+        lp, lq, adv = self.args
+        return L.rl_mis_replay(lp, lq, adv, self.N, self.offsets_host, self.offsets_dev, self.S,
+                               self.cfg, self.out, self.workspace, self.ws_bytes, stream=stream,
+                               check=check)
+
+    def metrics(self) -> dict:
+        m = self.o["metrics"].cpu().numpy()
+        return {k: float(m[i]) for i, k in enumerate(L.MIS_METRIC_NAMES)}
+
+
 def validate(labels, infer_logprobs, adv, V, offsets_host=None, ids=None, u=None, logq=None,
              replayed=False, sync=True):
     dev = labels.device

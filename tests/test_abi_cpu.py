@@ -27,7 +27,7 @@ def _declared():
 
 def test_every_declared_symbol_is_exported():
     names = _declared()
-    assert len(names) == 10
+    assert len(names) == 12
     out = subprocess.run(["nm", "-D", "--defined-only", L.LIB_PATH], capture_output=True,
                          text=True, check=True).stdout
     exported = {ln.split()[-1] for ln in out.splitlines() if " T " in ln}
@@ -57,6 +57,16 @@ def test_struct_layout_matches_header():
     assert ctypes.sizeof(L.RlLossOut) == 10 * 8
     assert ctypes.sizeof(L.RlElemCfg) == 2 * 4 + 8 * 4 + 7 * 4
     assert ctypes.sizeof(L.RlElemOut) == 3 * 8
+    assert ctypes.sizeof(L.RlMisCfg) == 10 * 4
+    assert ctypes.sizeof(L.RlMisOut) == 3 * 8
+
+
+def test_mis_metric_order_matches_header():
+    src = open(HEADER).read()
+    block = src[src.index("RL_MIS_TRAINING_LOG_PPL = 0"):src.index("RL_MIS_METRIC_COUNT = ")]
+    names = re.findall(r"RL_MIS_([A-Z0-9_]+)", block)
+    assert [n.lower() for n in names] == list(L.MIS_METRIC_NAMES)
+    assert f"RL_MIS_METRIC_COUNT = {len(names)}" in src
 
 
 class HostBufs:
@@ -236,6 +246,51 @@ def test_elementwise_and_validate_host_errors():
     st = L.lib().rl_validate_support(0, 50, 0, lab, ilq, A, None, None, None, None, None, 0, flags,
                                      None)
     assert st == L.RL_E_ARG
+
+
+def test_mis_host_errors_return_before_launch():
+    hb = HostBufs()
+    n = ctypes.c_size_t(0)
+    ws_size = L.lib().rl_mis_workspace_size
+    assert ws_size(0, 1, ctypes.byref(n)) == L.RL_E_ARG
+    assert ws_size(10, 0, ctypes.byref(n)) == L.RL_E_ARG
+    assert ws_size(10, 11, ctypes.byref(n)) == L.RL_E_ARG
+    assert ws_size(L.RL_MIS_MAX_N + 1, 1, ctypes.byref(n)) == L.RL_E_ARG
+    assert ws_size(2_160_000, 1282, ctypes.byref(n)) == L.RL_OK
+    # chunk records, first sequences, bitmap, per-sequence data and partials: a few 0.1 B/token
+    assert 2_160_000 * 0.2 < n.value < 2_160_000 * 0.5
+    from synth.gen import MIS_PARAMS
+    N, S = 1000, 3
+    off = np.array([0, 10, 600, 1000], np.int64)
+    lp, lq, adv = hb.buf(4 * N), hb.buf(4 * N), hb.buf(4 * N)
+    offd = hb.buf(8 * (S + 1))
+    assert ws_size(N, S, ctypes.byref(n)) == L.RL_OK
+    ws = hb.buf(n.value)
+    out = L.RlMisOut()
+    out.metrics = hb.buf(8 * L.RL_MIS_METRIC_COUNT)
+
+    def call(cfg=None, offh=off, ws_bytes=None, o=out, s_=S, flags=None):
+        cfg = cfg if cfg is not None else ops.mis_cfg(MIS_PARAMS)
+        if flags is not None:
+            o = L.RlMisOut()
+            o.metrics, o.flags = out.metrics, flags
+        return L.lib().rl_mis_replay(lp, lq, adv, N, offh.ctypes.data, offd, s_, ctypes.byref(cfg),
+                                     ctypes.byref(o), ws, n.value if ws_bytes is None else ws_bytes,
+                                     None)
+
+    for field, val in (("tis_level", 3), ("rs_level", -1), ("tis_mode", 3), ("use_rs", 2),
+                       ("batch_normalize", 5), ("tis_lower", 0.0), ("tis_upper", 0.1),
+                       ("tis_upper", float("inf")), ("veto", -1.0), ("veto", float("inf")),
+                       ("rs_lower", 0.0), ("rs_upper", 0.01)):
+        c = ops.mis_cfg(MIS_PARAMS)
+        setattr(c, field, val)
+        assert call(c) == L.RL_E_CFG, (field, val)
+    for bad in ([1, 10, 600, 1000], [0, 10, 10, 1000], [0, 600, 10, 1000], [0, 10, 600, 999]):
+        assert call(offh=np.array(bad, np.int64)) == L.RL_E_CSR, bad
+    assert call(ws_bytes=n.value - 1) == L.RL_E_WORKSPACE
+    assert call(flags=hb.buf(N) + 2) == L.RL_E_ARG  # flags must be 4-byte aligned
+    assert call(o=L.RlMisOut()) == L.RL_E_ARG       # metrics required
+    assert call(s_=0) == L.RL_E_ARG
 
 
 def test_missing_library_fails_loudly(monkeypatch, tmp_path):
