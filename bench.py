@@ -37,6 +37,7 @@ GEMMS = ("gemm_fwd", "gemm_dh", "gemm_dw")
 KERNEL_SOURCES = {
     "gemm": ("gemm.hip", "common.h", "kernels.h"),
     "elementwise": ("elementwise.hip", "common.h", "kernels.h"),
+    "mis_token": ("mis.hip", "common.h", "kernels.h"),
 }
 
 
@@ -108,6 +109,33 @@ def cpu_baseline(wl, target_s: float, seed: int = 0):
                    f"fp64 forward + dense backward (dh rows, dW from those tokens), "
                    f"{dt:.1f} s on {cores} host cores"),
     }
+
+
+def cpu_baseline_replay(kind, host, target_s):
+    """The replay oracles (numpy fp64, vectorised) over the whole 2,160,000-token
+    input, repeated until about target_s seconds have passed."""
+    from threadpoolctl import threadpool_limits
+
+    from oracle import mis as om
+    from oracle import replay as orp
+
+    # numpy's elementwise kernels run on one thread (no BLAS call here)
+    with threadpool_limits(limits=1):
+        n_pass, t0 = 0, time.perf_counter()
+        while True:
+            if kind == "replay":
+                orp.replay_reference(host["lp"], host["lq"], host["adv"], host["params"])
+            else:
+                om.mis_reference(host["lp"], host["lq"], host["adv"], host["offsets"],
+                                 host["params"])
+            n_pass += 1
+            dt = time.perf_counter() - t0
+            if dt >= target_s or n_pass >= 200:
+                break
+    N = len(host["lp"])
+    return {"value": n_pass * N / dt, "unit": "tokens/s", "cores": 1, "kind": "oracle",
+            "sample": (f"the whole input ({N} tokens) {n_pass} times, fp64 numpy on one "
+                       f"thread, {dt:.1f} s")}
 
 
 def bench_head(args, torch):
@@ -210,6 +238,14 @@ def copy_floor(torch, copies, N, steps):
             "GB/s": 16.0 * N / (ms * 1e-3) / 1e9}
 
 
+def wl_replay_host():
+    """The replay input on the host, for the oracle CPU baseline."""
+    from synth import make_replay
+
+    r = make_replay()
+    return {"lp": r.lp.numpy(), "lq": r.lq.numpy(), "adv": r.adv.numpy(), "params": r.params}
+
+
 def event_overhead(torch, steps):
     """An event pair around nothing, timed like the per-launch events: the
     fixed part of a short kernel's event-measured duration."""
@@ -296,6 +332,63 @@ def bench_replay(args, torch):
     }, None
 
 
+def bench_mis(args, torch):
+    """Sequence-aware rollout correction over the replay: one call of
+    rl_mis_replay (five launches) per step."""
+    from lm_head_logprobs_amd import _lib as L
+    from lm_head_logprobs_amd import ops
+    from synth import MIS_PARAMS, make_replay, replay_sequences
+
+    r = make_replay(device="cuda:0")
+    off = replay_sequences(r.N)
+    params = dict(MIS_PARAMS)
+    # 16 independent copies (> 620 MB) so that every pass reads HBM
+    copies = [ops.MisReplay(r.lp.clone(), r.lq.clone(), r.adv.clone(), off, params)
+              for _ in range(16)]
+    for i in range(args.warmup):
+        copies[i % 16]()
+    torch.cuda.synchronize()
+    L.rl_profile_begin()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for i in range(args.steps):
+        copies[i % 16]()
+    e1.record()
+    torch.cuda.synchronize()
+    prof = L.rl_profile_end()
+    ms = e0.elapsed_time(e1) / args.steps
+    kern = {k: {"launches": n, "avg_ms": t / n} for k, (n, t) in prof.items()}
+    tok = kern["mis_token"]["avg_ms"]
+    byt = 17.0 * r.N  # reads lp, lq, A; writes the fp32 weight and the uint8 flags
+    achieved = byt / (tok * 1e-3) / 1e9
+    pass_ms = sum(v["avg_ms"] for v in kern.values())
+    pass_bytes = 25.0 * r.N  # + the first pass over lp, lq (8 B/token)
+    out = {
+        "metric": "tokens/s sequence-aware rollout correction (IS/RS/veto + metrics, fp32)",
+        "value": r.N / (ms * 1e-3), "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": ms, "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "fp32", "data": "synthetic",
+        "config": {"workload": "c2_mis", "tokens": r.N, "sequences": int(off.numel() - 1),
+                   "tis": f'{params["tis_level"]}/{params["tis_mode"]}',
+                   "rs": params["rs_level"] if params["use_rs"] else "off",
+                   "veto": params["veto"], "batch_normalize": params["batch_normalize"]},
+        "roofline": {"bound": "hbm", "achieved": achieved, "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                     "frac": achieved / PEAK_HBM_GBS,
+                     "traffic": read_traffic("mis_token", "c2_mis"),
+                     "kernel": "mis_token (the per-token pass)", "avg_launch_ms": tok,
+                     "algorithmic_bytes_per_launch": byt},
+        "whole_pass": {"kernels_ms": pass_ms, "algorithmic_bytes": pass_bytes,
+                       "GB/s": pass_bytes / (pass_ms * 1e-3) / 1e9},
+        "kernels": kern,
+        "event_pair_overhead_ms": event_overhead(torch, args.steps),
+        "cpu_baseline": None,
+    }
+    host = {"lp": r.lp.cpu().numpy(), "lq": r.lq.cpu().numpy(), "adv": r.adv.cpu().numpy(),
+            "offsets": off.numpy(), "params": params}
+    return out, host
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -303,7 +396,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="c3_head16k_ipo",
                     help="c3_head16k_ipo (default), c4_head16k_ipo_topp_replay, "
-                         "c5a_head64k_draws_ipo_k1, c5b_head64k_draws_reinforce, c2_replay")
+                         "c5a_head64k_draws_ipo_k1, c5b_head64k_draws_reinforce, c2_replay, "
+                         "c2_mis")
     ap.add_argument("--token-chunk", type=int, default=0)
     ap.add_argument("--cpu-seconds", type=float, default=15.0,
                     help="target length of the oracle CPU baseline sample")
@@ -322,8 +416,14 @@ def main():
     if not torch.cuda.is_available():
         print("bench.py: no GPU visible", file=sys.stderr)
         sys.exit(1)
+    host = None
     if args.workload == "c2_replay":
         out, wl = bench_replay(args, torch)
+        r = wl_replay_host()
+        host = ("replay", r)
+    elif args.workload == "c2_mis":
+        out, h = bench_mis(args, torch)
+        wl, host = None, ("mis", h)
     else:
         out, wl = bench_head(args, torch)
     if args.copy_calibration:
@@ -334,6 +434,8 @@ def main():
     if wl is not None:
         out["cpu_baseline"] = (None if args.no_cpu_baseline
                                else cpu_baseline(wl, args.cpu_seconds))
+    elif host is not None and not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline_replay(host[0], host[1], args.cpu_seconds)
     print(json.dumps(out), flush=True)
 
 

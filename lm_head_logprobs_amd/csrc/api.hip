@@ -29,13 +29,13 @@ using namespace rl;
 enum ProfKind {
   K_GEMM_FWD, K_COMBINE, K_FORM_G, K_GEMM_DH, K_TRANSPOSE_H, K_GEMM_DW, K_FINALIZE_DH,
   K_TRANSPOSE_W, K_CSR_ROWS, K_CSC_BUILD, K_SPARSE_DW, K_REDUCE, K_ELEMENTWISE, K_VALIDATE,
-  K_ELEM_FINAL, K_MIS_CHUNK, K_MIS_SEQ, K_MIS_TOKEN, K_MIS_RAW, K_MIS_METRICS, K_COUNT
+  K_ELEM_FINAL, K_MIS_CHUNK, K_MIS_SEQ, K_MIS_TOKEN, K_MIS_FINAL, K_COUNT
 };
 const char* const kProfNames[K_COUNT] = {
     "gemm_fwd",   "combine",   "form_g",   "gemm_dh",   "transpose_h",
     "gemm_dw",    "finalize_dh", "transpose_w", "csr_rows", "csc_build",
     "sparse_dw",  "reduce",    "elementwise", "validate", "elementwise_final",
-    "mis_chunk",  "mis_seq",   "mis_token", "mis_raw",  "mis_metrics"};
+    "mis_chunk",  "mis_seq",   "mis_token", "mis_final"};
 
 struct ProfRec {
   int kind;
@@ -573,8 +573,8 @@ rl_status rl_mis_replay(const float* lp, const float* lq, const float* adv, int6
   if (workspace == nullptr || workspace_bytes < (size_t)L.bytes || !aligned(workspace, 16))
     return RL_E_WORKSPACE;
   hipStream_t s = static_cast<hipStream_t>(stream);
-  const int kinds[5] = {K_MIS_CHUNK, K_MIS_SEQ, K_MIS_TOKEN, K_MIS_RAW, K_MIS_METRICS};
-  for (int st = 0; st < 5; ++st) {
+  const int kinds[4] = {K_MIS_CHUNK, K_MIS_SEQ, K_MIS_TOKEN, K_MIS_FINAL};
+  for (int st = 0; st < 4; ++st) {
     RL_TRY(timed(kinds[st], s, [&] {
       return rl::mis_stage(st, lp, lq, adv, N, seq_offsets_dev, S, c, out->weight, out->flags,
                            out->metrics, workspace, s);

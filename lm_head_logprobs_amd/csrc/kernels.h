@@ -144,12 +144,12 @@ hipError_t elementwise(const float* lp, const float* lq, const float* adv, int64
 hipError_t elementwise_final(const double* partials, int64_t N, int n_eps, double* sums,
                              hipStream_t s);
 
-// Sequence-aware rollout correction over a replay (five launches in order:
-// stage 0 chunk totals, 1 sequences, 2 tokens, 3 raw totals, 4 metrics).
+// Sequence-aware rollout correction over a replay (four launches in order:
+// stage 0 chunk totals, 1 sequences, 2 tokens, 3 raw totals and metrics).
 // Workspace offsets in bytes from the workspace base; N tokens, S sequences.
 struct MisLayout {
   int64_t nch, nb1, nb2, nb3;
-  int64_t ct, firstseq, bitmap, seq_w, seq_flags, part1, part2, part3, raw, bytes;
+  int64_t ct, firstseq, bitmap, seq_w, seq_flags, part1, part2, part3, bytes;
 };
 MisLayout mis_layout(int64_t N, int64_t S);
 hipError_t mis_stage(int stage, const float* lp, const float* lq, const float* adv, int64_t N,

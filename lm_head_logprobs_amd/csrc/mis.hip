@@ -16,7 +16,7 @@
 //  3. chunks again: each token finds its sequence from the chunk's first
 //     sequence and a popcount of the start bits before it, then its bounded
 //     weight, flags, and the sums for batch normalisation and the loss;
-//  4. one block per raw total, then one thread forms the metrics.
+//  4. one block: the raw totals in a fixed order, then the metrics.
 // Token log ratios are formed in fp64 (exact for fp32 inputs), so token-level
 // decisions are the exact comparisons of the definition.
 #include "kernels.h"
@@ -410,58 +410,54 @@ mis_token_kernel(const float* __restrict__ lp, const float* __restrict__ lq,
   }
 }
 
-// ---- stage 4: raw totals, then the metrics -----------------------------------
-// Block r reduces raw row r over the blocks of its stage: threads take rows
-// t, t + NT, ... in order, then a fixed xor tree in wave 0.  Rows R3_MIN and
-// R3_MAX reduce with min and max.
-__global__ void __launch_bounds__(NT)
-mis_raw_kernel(const double* __restrict__ part1, int64_t nb1, const double* __restrict__ part2,
-               int64_t nb2, const double* __restrict__ part3, int64_t nb3,
-               double* __restrict__ raw) {
-  __shared__ double sh[NT];
-  const int r = blockIdx.x;
-  const double* row;
-  int64_t nb;
-  int op = 0;  // 0 sum, 1 min, 2 max
-  if (r < R1_COUNT) {
-    row = part1 + (int64_t)r * nb1, nb = nb1;
-  } else if (r < R1_COUNT + R2_COUNT) {
-    row = part2 + (int64_t)(r - R1_COUNT) * nb2, nb = nb2;
-  } else {
-    const int k = r - R1_COUNT - R2_COUNT;
-    row = part3 + (int64_t)k * nb3, nb = nb3;
-    op = k == R3_MIN ? 1 : k == R3_MAX ? 2 : 0;
-  }
-  const double id = op == 1 ? __builtin_inf() : op == 2 ? -__builtin_inf() : 0.0;
-  double acc = id;
-  for (int64_t b = threadIdx.x; b < nb; b += NT) {
-    const double x = row[b];
-    acc = op == 1 ? fmin(acc, x) : op == 2 ? fmax(acc, x) : acc + x;
-  }
-  sh[threadIdx.x] = acc;
-  __syncthreads();
-  if (threadIdx.x < 64) {
-    const int l = threadIdx.x;
-    double v;
-    if (op == 0) {
-      v = ((sh[l] + sh[l + 64]) + sh[l + 128]) + sh[l + 192];
-#pragma unroll
-      for (int d = 32; d > 0; d >>= 1) v += __shfl_xor(v, d, 64);
-    } else if (op == 1) {
-      v = fmin(fmin(sh[l], sh[l + 64]), fmin(sh[l + 128], sh[l + 192]));
-      v = wave_min_d(v);
-    } else {
-      v = fmax(fmax(sh[l], sh[l + 64]), fmax(sh[l + 128], sh[l + 192]));
-#pragma unroll
-      for (int d = 32; d > 0; d >>= 1) v = fmax(v, __shfl_xor(v, d, 64));
-    }
-    if (l == 0) raw[r] = v;
-  }
-}
+// ---- stage 4: raw totals and the metrics, one block ------------------------------
+// Wave w reduces raw rows w, w + 16, ...: lane l adds entries l, l + 64, ...
+// of the row in order, then a fixed xor tree (min and max for R3_MIN and
+// R3_MAX).  Thread 0 then forms the metrics.
+constexpr int FT = 1024;  // threads of the final block
 
-__global__ void mis_metrics_kernel(const double* __restrict__ raw, int64_t N, int64_t S,
-                                   int tis_level, int batch_norm, double* __restrict__ m) {
-  if (threadIdx.x != 0 || blockIdx.x != 0) return;
+__global__ void __launch_bounds__(FT)
+mis_final_kernel(const double* __restrict__ part1, int64_t nb1, const double* __restrict__ part2,
+                 int64_t nb2, const double* __restrict__ part3, int64_t nb3, int64_t N, int64_t S,
+                 int tis_level, int batch_norm, double* __restrict__ m) {
+  __shared__ double raw[R_TOTAL];
+  const int wv = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  for (int r = wv; r < R_TOTAL; r += FT / 64) {
+    const double* row;
+    int64_t nb;
+    int op = 0;  // 0 sum, 1 min, 2 max
+    if (r < R1_COUNT) {
+      row = part1 + (int64_t)r * nb1, nb = nb1;
+    } else if (r < R1_COUNT + R2_COUNT) {
+      row = part2 + (int64_t)(r - R1_COUNT) * nb2, nb = nb2;
+    } else {
+      const int k = r - R1_COUNT - R2_COUNT;
+      row = part3 + (int64_t)k * nb3, nb = nb3;
+      op = k == R3_MIN ? 1 : k == R3_MAX ? 2 : 0;
+    }
+    const double id = op == 1 ? __builtin_inf() : op == 2 ? -__builtin_inf() : 0.0;
+    double v = id;
+    // rows hold at most kMaxBlocks = 1024 entries: 16 per lane, all loads of a
+    // round issued before the first add
+    for (int64_t base = lane; base < nb; base += 64 * 16) {
+      double x[16];
+#pragma unroll
+      for (int j = 0; j < 16; ++j) {
+        const int64_t b = base + 64 * j;
+        x[j] = b < nb ? row[b] : id;
+      }
+#pragma unroll
+      for (int j = 0; j < 16; ++j) v = op == 1 ? fmin(v, x[j]) : op == 2 ? fmax(v, x[j]) : v + x[j];
+    }
+#pragma unroll
+    for (int d = 32; d > 0; d >>= 1) {
+      const double o = __shfl_xor(v, d, 64);
+      v = op == 1 ? fmin(v, o) : op == 2 ? fmax(v, o) : v + o;
+    }
+    if (lane == 0) raw[r] = v;
+  }
+  __syncthreads();
+  if (threadIdx.x != 0) return;
   const double* r1 = raw;
   const double* r2 = raw + R1_COUNT;
   const double* r3 = raw + R1_COUNT + R2_COUNT;
@@ -527,7 +523,6 @@ MisLayout mis_layout(int64_t N, int64_t S) {
   L.part1 = take(R1_COUNT * L.nb1 * 8);
   L.part2 = take(R2_COUNT * L.nb2 * 8);
   L.part3 = take(R3_COUNT * L.nb3 * 8);
-  L.raw = take(R_TOTAL * 8);
   L.bytes = o;
   return L;
 }
@@ -545,7 +540,6 @@ hipError_t mis_stage(int stage, const float* lp, const float* lq, const float* a
   double* part1 = reinterpret_cast<double*>(base + L.part1);
   double* part2 = reinterpret_cast<double*>(base + L.part2);
   double* part3 = reinterpret_cast<double*>(base + L.part3);
-  double* raw = reinterpret_cast<double*>(base + L.raw);
   MisP p;
   p.tis_level = c.tis_level, p.tis_mode = c.tis_mode, p.use_rs = c.use_rs;
   p.rs_level = c.rs_level, p.veto_on = c.veto > 0.0f;
@@ -568,13 +562,9 @@ hipError_t mis_stage(int stage, const float* lp, const float* lq, const float* a
       hipLaunchKernelGGL(mis_token_kernel, dim3((unsigned)L.nb3), dim3(NT), 0, s, lp, lq, adv, N,
                          nch, (int)S, p, seq_w, seq_flags, firstseq, bitmap, weight, flags, part3);
       break;
-    case 3:
-      hipLaunchKernelGGL(mis_raw_kernel, dim3(R_TOTAL), dim3(NT), 0, s, part1, L.nb1, part2,
-                         L.nb2, part3, L.nb3, raw);
-      break;
     default:
-      hipLaunchKernelGGL(mis_metrics_kernel, dim3(1), dim3(64), 0, s, raw, N, S, c.tis_level,
-                         c.batch_normalize, metrics);
+      hipLaunchKernelGGL(mis_final_kernel, dim3(1), dim3(FT), 0, s, part1, L.nb1, part2, L.nb2,
+                         part3, L.nb3, N, S, c.tis_level, c.batch_normalize, metrics);
       break;
   }
   return hipGetLastError();
