@@ -12,7 +12,12 @@ top-p support with u = q, or K sampler draws with u = 1/K, "sum_v u_v f(v)"
 bullets of the PR description), and the KL over the same support is
 sum_e u_e (log q(v_e) - log p(v_e)) ("What changes", KL bullet; one formula for
 the exact and the k1 estimator, exact meaning u = q on a replayed support).
-beta_t = kl_coeff (staleness "none").  The loss is L = sum_t loss_t / D.
+beta_t = kl_coeff with kl_staleness "none"; with "inv_sqrt" the same bullet
+scales the KL by the token's policy age (engine weight-version lag), read here
+as beta_t = kl_coeff / sqrt(1 + age_t).  An entropy bonus with coefficient
+gamma subtracts gamma * H_t from loss_t (the Tencent article on KL/clip/entropy,
+section 3: the policy loss minus entropy_coeff times the aggregated entropy).
+The loss is L = sum_t loss_t / D.
 
 Readings taken where the pages are silent (each listed in the design notes):
 * w(a) and every w_e are held constant in the gradient (score-function form;
@@ -24,10 +29,14 @@ Readings taken where the pages are silent (each listed in the design notes):
   entries and add up.
 * A missing per-entry sampler log-prob defaults to log u_e (valid on a
   replayed support, where u = q).
+* Without an age input every token has age 0.  Metrics "kl/beta" and
+  "kl/age0" of the PR's metrics bullet are the mean beta_t and the mean KL
+  over tokens of age 0.
 
-Gradient (w, c held constant), with kappa_t = s_t (w_t - sum_e c_e) + beta sum_e u_e:
-  dL/dz_t = ( kappa_t p_t - s_t w_t e_a + sum_e (s_t c_e - beta u_e) e_{v_e} ) / D
-because d log p(v) / dz = e_v - p.  Then dh = (dL/dz) W / tau and
+Gradient (w, c held constant), with kappa_t = s_t (w_t - sum_e c_e) + beta_t sum_e u_e:
+  dL/dz_t = ( kappa_t p_t + gamma p_t (log p_t + H_t) - s_t w_t e_a
+              + sum_e (s_t c_e - beta_t u_e) e_{v_e} ) / D
+because d log p(v) / dz = e_v - p and dH/dz = -p (log p + H).  Then dh = (dL/dz) W / tau and
 dW = (dL/dz)^T h / tau.  The oracle always forms the dense gradient.
 """
 
@@ -43,6 +52,7 @@ METRIC_NAMES = (
     "kl_beta",
     "max_abs_kappa",
     "entropy_mean",
+    "kl_age0",
 )
 
 
@@ -57,14 +67,24 @@ def kl_beta(params):
     return float(params.get("kl_coeff", 0.0))
 
 
+def beta_per_token(params, age):
+    """beta_t: kl_coeff, divided by sqrt(1 + age_t) under kl_staleness inv_sqrt."""
+    beta = kl_beta(params)
+    age = np.asarray(age, np.float64)
+    if params.get("kl_staleness", "none") == "inv_sqrt":
+        return beta / np.sqrt(1.0 + age)
+    return np.full(age.shape, beta)
+
+
 def head_reference(h, W, labels, infer_logprobs, adv, params, offsets=None, ids=None,
-                   u=None, logq=None, tokens=None, want_grads=True, chunk=None):
+                   u=None, logq=None, tokens=None, want_grads=True, chunk=None, age=None):
     """Dense fp64 forward + backward.
 
     h [N,H], W [V,H] (any float dtype; read exactly), labels [N] ints,
     infer_logprobs [N], adv [N], CSR offsets [N+1] / ids / u / logq (or None).
     params: loss_type, ipo_eps, max_ratio, icepop_lo, icepop_hi, adv_tau,
-    kl_coeff, kl_estimator, inv_temperature, loss_norm (D).
+    kl_coeff, kl_estimator, kl_staleness, entropy_coeff, inv_temperature,
+    loss_norm (D).  age: per-token policy age [N] (None: all 0).
 
     ``tokens`` restricts the evaluation to a subset of token indices (the
     per-token outputs and dh rows of those tokens, and dW from those tokens
@@ -80,7 +100,9 @@ def head_reference(h, W, labels, infer_logprobs, adv, params, offsets=None, ids=
     inv_t = float(params.get("inv_temperature", 1.0))
     D = float(params["loss_norm"])
     s_all = float(params.get("adv_tau", 1.0)) * np.asarray(adv, np.float64)
-    beta = kl_beta(params)
+    beta_all = beta_per_token(params, np.zeros(N) if age is None else age)
+    gamma = float(params.get("entropy_coeff", 0.0))
+    age_all = np.zeros(N, np.int64) if age is None else np.asarray(age, np.int64)
     has_support = offsets is not None and ids is not None
     if has_support:
         offsets = np.asarray(offsets, np.int64)
@@ -92,6 +114,7 @@ def head_reference(h, W, labels, infer_logprobs, adv, params, offsets=None, ids=
         logprobs=np.zeros(n_tok), entropy=np.zeros(n_tok), lse=np.zeros(n_tok),
         weight=np.zeros(n_tok), keep=np.zeros(n_tok, bool), token_loss=np.zeros(n_tok),
         kappa=np.zeros(n_tok), kl=np.zeros(n_tok), support_mass=np.zeros(n_tok),
+        beta=np.zeros(n_tok),
         support_count=np.zeros(n_tok, np.int64),
     )
     sup_lp = {}  # entry index -> log p(v_e)
@@ -116,6 +139,7 @@ def head_reference(h, W, labels, infer_logprobs, adv, params, offsets=None, ids=
         lq = np.asarray(infer_logprobs, np.float64)[rows]
         w, keep = _w.weight(lp, lq, params)
         s = s_all[rows]
+        beta = beta_all[rows]
         sum_c = np.zeros(len(rows))
         cent = np.zeros(len(rows))
         sum_u = np.zeros(len(rows))
@@ -145,12 +169,14 @@ def head_reference(h, W, labels, infer_logprobs, adv, params, offsets=None, ids=
                 for k in range(e0, e1):
                     sup_lp[k] = lpe[k - e0]
                 if want_grads:
-                    np.add.at(G[i], v, s[i] * ce - beta * ue)
-        klterm = kl if beta != 0.0 else np.zeros_like(kl)
-        loss = -s * (w * lp - cent) + beta * klterm
+                    np.add.at(G[i], v, s[i] * ce - beta[i] * ue)
+        klterm = kl if kl_beta(params) != 0.0 else np.zeros_like(kl)
+        loss = -s * (w * lp - cent) + beta * klterm - gamma * ent
         kappa = s * (w - sum_c) + beta * sum_u
         if want_grads:
             G += kappa[:, None] * p
+            if gamma != 0.0:
+                G += gamma * p * (logp + ent[:, None])
             G[np.arange(len(rows)), a] -= s * w
             G /= D
             dh[sel] = inv_t * (G @ W)
@@ -165,6 +191,7 @@ def head_reference(h, W, labels, infer_logprobs, adv, params, offsets=None, ids=
         out["kl"][sel] = klterm
         out["support_mass"][sel] = smass
         out["support_count"][sel] = cnt
+        out["beta"][sel] = beta
     out["loss"] = out["token_loss"].sum() / D
     if want_grads:
         out["dh"] = dh
@@ -182,9 +209,11 @@ def head_reference(h, W, labels, infer_logprobs, adv, params, offsets=None, ids=
         support_mass=float(out["support_mass"][has].mean()) if has.any() else 0.0,
         mask_tv=float(np.mean(np.abs(P - Q) > params.get("ipo_eps", 0.3))) if n_tok else 0.0,
         kl=float(out["kl"].mean()) if n_tok else 0.0,
-        kl_beta=beta,
+        kl_beta=float(out["beta"].mean()) if n_tok else 0.0,
         max_abs_kappa=float(np.abs(out["kappa"]).max()) if n_tok else 0.0,
         entropy_mean=float(out["entropy"].mean()) if n_tok else 0.0,
+        kl_age0=(float(out["kl"][age_all[tok] == 0].mean())
+                 if np.any(age_all[tok] == 0) else 0.0),
     )
     return out
 

@@ -193,13 +193,20 @@ def test_exact_kl_equals_dense_kl_on_full_support():
 
 # ---------------------------------------------------- head: gradient pins ----
 
-def _frozen_loss(h, W, labels, adv, prm, offsets, ids, u, logq, w_lab, c_e, lq_e):
-    """The loss with every importance weight frozen, written with scipy's log_softmax."""
+def _frozen_loss(h, W, labels, adv, prm, offsets, ids, u, logq, w_lab, c_e, lq_e, age=None):
+    """The loss with every importance weight frozen, written with scipy's log_softmax
+    and entropy (scipy.special.entr); beta_t = kl_coeff / sqrt(1 + age_t) when
+    kl_staleness is inv_sqrt."""
     inv_t = prm["inv_temperature"]
-    lps = sps.log_softmax(inv_t * (h @ W.T), axis=1)
-    beta = ohead.kl_beta(prm)
+    zz = inv_t * (h @ W.T)
+    lps = sps.log_softmax(zz, axis=1)
+    ent = sps.entr(sps.softmax(zz, axis=1)).sum(axis=1)
+    gamma = prm.get("entropy_coeff", 0.0)
     total = 0.0
     for t in range(len(labels)):
+        beta = ohead.kl_beta(prm)
+        if prm.get("kl_staleness", "none") == "inv_sqrt":
+            beta /= math.sqrt(1.0 + age[t])
         s = prm["adv_tau"] * adv[t]
         term = w_lab[t] * lps[t, labels[t]]
         kl = 0.0
@@ -207,22 +214,25 @@ def _frozen_loss(h, W, labels, adv, prm, offsets, ids, u, logq, w_lab, c_e, lq_e
             for e in range(offsets[t], offsets[t + 1]):
                 term -= c_e[e] * lps[t, ids[e]]
                 kl += u[e] * (lq_e[e] - lps[t, ids[e]])
-        total += -s * term + beta * kl
+        total += -s * term + beta * kl - gamma * ent[t]
     return total / prm["loss_norm"]
 
 
-@pytest.mark.parametrize("lt,est,support", [
-    ("ipo", "k1", "ragged"), ("icepop", "exact", "draws"), ("reinforce", "none", "draws"),
-    ("ipo", "none", None),
+@pytest.mark.parametrize("lt,est,support,extra", [
+    ("ipo", "k1", "ragged", {}), ("icepop", "exact", "draws", {}),
+    ("reinforce", "none", "draws", {}), ("ipo", "none", None, {}),
+    ("ipo", "k1", "ragged", {"kl_staleness": "inv_sqrt", "entropy_coeff": 0.4}),
+    ("reinforce", "none", None, {"entropy_coeff": -0.7}),
 ])
-def test_gradients_match_frozen_weight_finite_differences(lt, est, support):
+def test_gradients_match_frozen_weight_finite_differences(lt, est, support, extra):
     # Central differences of the loss with w_t and c_e frozen at the base point
     # (the sg[.] reading) against the oracle's dh and dW.
     h, W, labels, lq, adv, offsets, ids, u, logq = _tiny_problem(5, N=5, H=4, V=13,
                                                                   support=support, K=5)
     prm = _params(loss_type=lt, kl_coeff=0.3, kl_estimator=est, adv_tau=1.3, loss_norm=2.5,
-                  inv_temperature=0.9, icepop_lo=0.2, icepop_hi=5.0, ipo_eps=0.6)
-    out = ohead.head_reference(h, W, labels, lq, adv, prm, offsets, ids, u, logq)
+                  inv_temperature=0.9, icepop_lo=0.2, icepop_hi=5.0, ipo_eps=0.6, **extra)
+    age = np.array([0, 3, 1, 8, 0])
+    out = ohead.head_reference(h, W, labels, lq, adv, prm, offsets, ids, u, logq, age=age)
     w_lab = out["weight"]
     c_e = lq_e = None
     if offsets is not None:
@@ -231,7 +241,7 @@ def test_gradients_match_frozen_weight_finite_differences(lt, est, support):
         c_e = u * we
         lq_e = logq
     f = lambda hh, WW: _frozen_loss(hh, WW, labels, adv, prm, offsets, ids, u, logq,
-                                    w_lab, c_e, lq_e)
+                                    w_lab, c_e, lq_e, age)
     assert f(h, W) == pytest.approx(out["loss"], rel=1e-12, abs=1e-14)
     step = 1e-5
     g_h = np.zeros_like(h)
@@ -248,6 +258,44 @@ def test_gradients_match_frozen_weight_finite_differences(lt, est, support):
         g_W[idx] = (f(h, Wp) - f(h, Wm)) / (2 * step)
     assert np.linalg.norm(out["dh"] - g_h) <= 1e-7 * np.linalg.norm(g_h) + 1e-12
     assert np.linalg.norm(out["dW"] - g_W) <= 1e-7 * np.linalg.norm(g_W) + 1e-12
+
+
+def test_inv_sqrt_staleness_closed_form_and_metrics():
+    # beta_t = kl_coeff / sqrt(1 + age): ages 0, 3, 8 give kl_coeff, kl_coeff / 2,
+    # kl_coeff / 3; kl/beta is their mean and kl/age0 the mean KL of age-0 tokens.
+    h, W, labels, lq, adv, offsets, ids, u, logq = _tiny_problem(8, N=4, H=4, V=9,
+                                                                  support="draws", K=3)
+    base = _params(kl_coeff=0.6, kl_estimator="k1")
+    age = np.array([0, 3, 0, 8])
+    r0 = ohead.head_reference(h, W, labels, lq, adv, base, offsets, ids, u, logq, age=age)
+    r1 = ohead.head_reference(h, W, labels, lq, adv, dict(base, kl_staleness="inv_sqrt"),
+                              offsets, ids, u, logq, age=age)
+    kl = r0["kl"]
+    assert np.allclose(r1["token_loss"] - r0["token_loss"],
+                       kl * 0.6 * (np.array([1, 1 / 2, 1, 1 / 3]) - 1), rtol=0, atol=1e-14)
+    assert r1["metrics"]["kl_beta"] == pytest.approx(0.6 * (1 + 1 / 2 + 1 + 1 / 3) / 4, rel=1e-14)
+    assert r1["metrics"]["kl_age0"] == pytest.approx((kl[0] + kl[2]) / 2, rel=1e-14)
+    assert r0["metrics"]["kl_beta"] == pytest.approx(0.6, rel=1e-15)
+    # no age input: every token is fresh
+    r2 = ohead.head_reference(h, W, labels, lq, adv, dict(base, kl_staleness="inv_sqrt"),
+                              offsets, ids, u, logq)
+    assert np.array_equal(r2["token_loss"], r0["token_loss"])
+
+
+def test_entropy_bonus_at_uniform_logits():
+    # W = 0: p is uniform, H = log V and log p + H = 0, so the bonus adds
+    # -gamma log V to every token loss and nothing to the gradient.
+    N, H, V = 4, 3, 13
+    h, _, labels, lq, adv, offsets, ids, u, logq = _tiny_problem(2, N, H, V, support="ragged")
+    W = np.zeros((V, H))
+    prm = _params(loss_type="reinforce", loss_norm=2.0)
+    r0 = ohead.head_reference(h, W, labels, lq, adv, prm, offsets, ids, u, logq)
+    r1 = ohead.head_reference(h, W, labels, lq, adv, dict(prm, entropy_coeff=0.35), offsets, ids,
+                              u, logq)
+    assert np.allclose(r1["token_loss"] - r0["token_loss"], -0.35 * math.log(V), atol=1e-14)
+    assert r1["loss"] - r0["loss"] == pytest.approx(-0.35 * math.log(V) * N / 2.0, rel=1e-12)
+    assert np.allclose(r1["dh"], r0["dh"], atol=1e-15) and np.allclose(r1["dW"], r0["dW"],
+                                                                       atol=1e-15)
 
 
 def test_full_support_with_u_equal_p_cancels_centering():
