@@ -6,7 +6,7 @@
  *   log p_t = log_softmax(z_t)                   (full vocabulary)
  *   loss_t  = -adv_tau * A_t * ( w(a_t) * log p_t(a_t)
  *                                - sum_e sg[u_e * w_e] * log p_t(v_e) )
- *             + beta * KL(q || p)
+ *             + beta_t * KL(q || p) - entropy_coeff * H_t
  *   L       = sum_t loss_t / D
  * with w the importance weight of the loss type ("What changes": ipo
  * 1(|p-q| <= eps) * min(p/q, max_importance_ratio); icepop
@@ -15,7 +15,11 @@
  * "TokenSupport" bullet), and KL(q || p) = sum_e u_e (log q(v_e) - log p(v_e))
  * over the same support (KL bullet; exact estimator on a replayed support
  * with u = q, k1 on sampler draws with u = 1/K).  Importance weights are
- * held constant in the gradient.
+ * held constant in the gradient.  beta_t = kl_coeff, divided by
+ * sqrt(1 + age_t) under the inv_sqrt KL staleness with a per-token policy
+ * age (KL bullet).  H_t is the entropy of the training softmax; the entropy
+ * bonus follows the Tencent article on KL/clip/entropy, section 3 (policy
+ * loss minus entropy_coeff times the entropy).
  *
  * Conventions for every entry point:
  *  - Array arguments are device pointers unless the name ends in _host.
@@ -67,11 +71,17 @@ typedef enum rl_kl_estimator {
   RL_KL_K1 = 2      /* sampler draws, u = 1/K: the k1 estimate            */
 } rl_kl_estimator;
 
+typedef enum rl_kl_staleness {
+  RL_STALENESS_NONE = 0,     /* beta_t = kl_coeff                               */
+  RL_STALENESS_INV_SQRT = 1  /* beta_t = kl_coeff / sqrt(1 + policy_age[t])     */
+} rl_kl_staleness;
+
 typedef enum rl_backward {
-  RL_BWD_AUTO = 0,    /* SPARSE for reinforce without KL on a support, else DENSE */
+  RL_BWD_AUTO = 0,    /* SPARSE for reinforce without KL or entropy bonus on a
+                         support, else DENSE                                      */
   RL_BWD_DENSE = 1,   /* full softmax backward through the LM head                */
   RL_BWD_SPARSE = 2,  /* gradient only on label + support entries (requires
-                         reinforce, no KL, a support)                              */
+                         reinforce, no KL, no entropy bonus, a support)            */
   RL_BWD_NONE = 3     /* forward only: no dh, no dW                                */
 } rl_backward;
 
@@ -81,10 +91,11 @@ enum {
   RL_METRIC_SUPPORT_MASS = 1,    /* mean over tokens with a support of sum_e u_e p/q      */
   RL_METRIC_MASK_TV = 2,         /* fraction of tokens with |p - q| > ipo_eps (label)     */
   RL_METRIC_KL = 3,              /* mean KL_t (0 without KL)                              */
-  RL_METRIC_KL_BETA = 4,         /* beta                                                  */
+  RL_METRIC_KL_BETA = 4,         /* mean beta_t (0 without KL)                            */
   RL_METRIC_MAX_ABS_KAPPA = 5,   /* max_t |kappa_t|, the net softmax coefficient          */
   RL_METRIC_ENTROPY_MEAN = 6,    /* mean entropy of the training softmax                  */
-  RL_METRIC_COUNT = 7
+  RL_METRIC_KL_AGE0 = 7,         /* mean KL_t over tokens of policy age 0 (0 if none)     */
+  RL_METRIC_COUNT = 8
 };
 
 typedef struct rl_loss_cfg {
@@ -100,7 +111,7 @@ typedef struct rl_loss_cfg {
   int32_t backward;     /* rl_backward                                          */
   int32_t replayed;     /* 1: the support is a replayed truncated set, u = q    */
   int32_t accumulate_dW;/* 1: dW += gradient, 0: dW = gradient                  */
-  int32_t reserved0;    /* must be 0                                            */
+  int32_t kl_staleness; /* rl_kl_staleness                                      */
   float ipo_eps;        /* IPO threshold on |p - q|, >= 0                       */
   float max_ratio;      /* IPO cap on p/q, > 0                                  */
   float icepop_lo;      /* IcePop band, 0 <= lo <= hi                           */
@@ -109,6 +120,8 @@ typedef struct rl_loss_cfg {
   float kl_coeff;       /* beta, >= 0                                           */
   float inv_temperature;/* 1/tau, > 0                                           */
   float loss_norm;      /* D, > 0 (the caller passes e.g. the token count)      */
+  float entropy_coeff;  /* entropy bonus gamma, finite (0 = off)                */
+  int32_t reserved1;    /* must be 0                                            */
 } rl_loss_cfg;
 
 typedef struct rl_loss_out {
@@ -141,6 +154,10 @@ rl_status rl_loss_workspace_size(const rl_loss_cfg* cfg, int32_t has_support,
  *  labels            [N] int32       sampled token ids, in [0, V)
  *  infer_logprobs    [N] fp32        sampler log q(label), finite, <= 0
  *  adv               [N] fp32        advantages A_t
+ *  policy_age        [N] int32       nullable: per-token policy age (engine
+ *                                    weight-version lag) for the inv_sqrt KL
+ *                                    staleness; NULL = every token has age 0;
+ *                                    negative ages are read as 0
  *  csr_offsets_host  [N+1] int64     host; NULL = no support (then nnz = 0)
  *  csr_offsets_dev   [N+1] int64     device copy of the same offsets
  *  csr_ids           [nnz] int32     support ids in [0, V); repeats allowed
@@ -149,8 +166,10 @@ rl_status rl_loss_workspace_size(const rl_loss_cfg* cfg, int32_t has_support,
  *  workspace         device, >= rl_loss_workspace_size() bytes, any contents
  *
  * Backward: dh = (dL/dz) W / tau, dW = (dL/dz)^T h / tau with
- *   dL/dz_t = (kappa_t p_t - s_t w_t e_a + sum_e (s_t u_e w_e - beta u_e) e_{v_e}) / D,
- *   kappa_t = s_t (w_t - sum_e u_e w_e) + beta sum_e u_e,  s_t = adv_tau A_t.
+ *   dL/dz_t = (kappa_t p_t + gamma p_t (log p_t + H_t) - s_t w_t e_a
+ *              + sum_e (s_t u_e w_e - beta_t u_e) e_{v_e}) / D,
+ *   kappa_t = s_t (w_t - sum_e u_e w_e) + beta_t sum_e u_e,  s_t = adv_tau A_t,
+ *   gamma = entropy_coeff.
  * The sparse backward drops the kappa_t p_t term (exact when kappa_t = 0,
  * e.g. reinforce without KL with sum_e u_e = 1 per row; the
  * RL_METRIC_MAX_ABS_KAPPA metric reports the dropped coefficient).
@@ -158,7 +177,8 @@ rl_status rl_loss_workspace_size(const rl_loss_cfg* cfg, int32_t has_support,
  */
 rl_status rl_loss_fwd_bwd(const void* h, const void* W, const int32_t* labels,
                           const float* infer_logprobs, const float* adv,
-                          const int64_t* csr_offsets_host, const int64_t* csr_offsets_dev,
+                          const int32_t* policy_age, const int64_t* csr_offsets_host,
+                          const int64_t* csr_offsets_dev,
                           const int32_t* csr_ids, const float* csr_u, const float* csr_logq,
                           const rl_loss_cfg* cfg, const rl_loss_out* out,
                           void* workspace, size_t workspace_bytes, void* stream);

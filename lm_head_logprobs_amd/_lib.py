@@ -19,9 +19,10 @@ RL_OK, RL_E_ARG, RL_E_CFG, RL_E_CSR, RL_E_WORKSPACE, RL_E_HIP, RL_E_INVALID_INPU
 RL_DTYPE_FP32, RL_DTYPE_BF16 = 0, 1
 RL_LOSS_IPO, RL_LOSS_ICEPOP, RL_LOSS_REINFORCE = 0, 1, 2
 RL_KL_NONE, RL_KL_EXACT, RL_KL_K1 = 0, 1, 2
+RL_STALENESS_NONE, RL_STALENESS_INV_SQRT = 0, 1
 RL_BWD_AUTO, RL_BWD_DENSE, RL_BWD_SPARSE, RL_BWD_NONE = 0, 1, 2, 3
 METRIC_NAMES = ("masked_fraction", "support_mass", "mask_tv", "kl", "kl_beta", "max_abs_kappa",
-                "entropy_mean")
+                "entropy_mean", "kl_age0")
 RL_METRIC_COUNT = len(METRIC_NAMES)
 RL_ELEM_MAX_EPS = 8
 RL_ELEM_SUM_COUNT = 37
@@ -61,11 +62,12 @@ class RlLossCfg(ctypes.Structure):
         ("dtype", ctypes.c_int32), ("grad_dtype", ctypes.c_int32),
         ("loss_type", ctypes.c_int32), ("kl_estimator", ctypes.c_int32),
         ("backward", ctypes.c_int32), ("replayed", ctypes.c_int32),
-        ("accumulate_dW", ctypes.c_int32), ("reserved0", ctypes.c_int32),
+        ("accumulate_dW", ctypes.c_int32), ("kl_staleness", ctypes.c_int32),
         ("ipo_eps", ctypes.c_float), ("max_ratio", ctypes.c_float),
         ("icepop_lo", ctypes.c_float), ("icepop_hi", ctypes.c_float),
         ("adv_tau", ctypes.c_float), ("kl_coeff", ctypes.c_float),
         ("inv_temperature", ctypes.c_float), ("loss_norm", ctypes.c_float),
+        ("entropy_coeff", ctypes.c_float), ("reserved1", ctypes.c_int32),
     ]
 
 
@@ -132,7 +134,7 @@ def lib() -> ctypes.CDLL:
         L.rl_loss_workspace_size.argtypes = [ctypes.POINTER(RlLossCfg), i32, i32, i32,
                                              ctypes.POINTER(sz)]
         L.rl_loss_workspace_size.restype = ctypes.c_int
-        L.rl_loss_fwd_bwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp,
+        L.rl_loss_fwd_bwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp,
                                       ctypes.POINTER(RlLossCfg), ctypes.POINTER(RlLossOut), vp,
                                       sz, vp]
         L.rl_loss_fwd_bwd.restype = ctypes.c_int
@@ -200,11 +202,11 @@ def rl_loss_workspace_size(cfg: RlLossCfg, has_support: bool, want_dh: bool, wan
     return n.value
 
 
-def rl_loss_fwd_bwd(h, W, labels, infer_logprobs, adv, csr_offsets_host, csr_offsets_dev, csr_ids,
-                    csr_u, csr_logq, cfg: RlLossCfg, out: RlLossOut, workspace, workspace_bytes,
-                    stream=None, check=True) -> int:
+def rl_loss_fwd_bwd(h, W, labels, infer_logprobs, adv, policy_age, csr_offsets_host,
+                    csr_offsets_dev, csr_ids, csr_u, csr_logq, cfg: RlLossCfg, out: RlLossOut,
+                    workspace, workspace_bytes, stream=None, check=True) -> int:
     st = lib().rl_loss_fwd_bwd(_ptr(h), _ptr(W), _ptr(labels), _ptr(infer_logprobs), _ptr(adv),
-                               _ptr(csr_offsets_host), _ptr(csr_offsets_dev), _ptr(csr_ids),
+                               _ptr(policy_age), _ptr(csr_offsets_host), _ptr(csr_offsets_dev), _ptr(csr_ids),
                                _ptr(csr_u), _ptr(csr_logq), ctypes.byref(cfg), ctypes.byref(out),
                                _ptr(workspace), int(workspace_bytes), _stream(stream))
     if check and st != RL_OK:

@@ -9,7 +9,8 @@
 //   2. combine: per token LSE and entropy from the partials, label and
 //      support logits by fp32 dot products, weights, KL, loss, kappa and the
 //      per-entry gradient coefficients
-//   3. dense backward only: form G (= kappa/D p) from P in both layouts,
+//   3. dense backward only: form G (= (kappa p + gamma p (log p + H)) / D)
+//      from P in both layouts,
 //      dh partials = G (W^T)^T split over V, dW (+)= G^T (h_c^T)^T
 //   4. dh = partials + label/support rows of W scaled by their coefficients
 // After the chunks: the label/support terms of dW via vocabulary buckets, then
@@ -120,7 +121,7 @@ rl_status check_cfg(const rl_loss_cfg* c, bool has_support) {
   if (c->V > (int64_t)INT32_MAX - 2 || c->N > (int64_t)INT32_MAX) return RL_E_ARG;
   if (c->N + c->nnz > (int64_t)INT32_MAX) return RL_E_ARG;
   if (!has_support && c->nnz != 0) return RL_E_ARG;
-  if (c->token_chunk < 0 || c->reserved0 != 0) return RL_E_ARG;
+  if (c->token_chunk < 0 || c->reserved1 != 0) return RL_E_ARG;
   if ((c->dtype != RL_DTYPE_FP32 && c->dtype != RL_DTYPE_BF16) ||
       (c->grad_dtype != RL_DTYPE_FP32 && c->grad_dtype != RL_DTYPE_BF16))
     return RL_E_ARG;
@@ -132,6 +133,9 @@ rl_status check_cfg(const rl_loss_cfg* c, bool has_support) {
   if (!(c->loss_norm > 0.0f) || !finite(c->loss_norm)) return RL_E_CFG;
   if (c->kl_estimator < RL_KL_NONE || c->kl_estimator > RL_KL_K1) return RL_E_CFG;
   if (!(c->kl_coeff >= 0.0f) || !finite(c->kl_coeff)) return RL_E_CFG;
+  if (c->kl_staleness != RL_STALENESS_NONE && c->kl_staleness != RL_STALENESS_INV_SQRT)
+    return RL_E_CFG;
+  if (!finite(c->entropy_coeff)) return RL_E_CFG;
   const bool kl_active = c->kl_estimator != RL_KL_NONE && c->kl_coeff > 0.0f;
   if (kl_active && !has_support) return RL_E_CFG;
   if (c->kl_estimator == RL_KL_EXACT && !c->replayed) return RL_E_CFG;
@@ -139,7 +143,9 @@ rl_status check_cfg(const rl_loss_cfg* c, bool has_support) {
   if (c->replayed && !has_support) return RL_E_CFG;
   if (c->accumulate_dW != 0 && c->accumulate_dW != 1) return RL_E_CFG;
   if (c->backward < RL_BWD_AUTO || c->backward > RL_BWD_NONE) return RL_E_CFG;
-  const bool sparse_ok = c->loss_type == RL_LOSS_REINFORCE && !kl_active && has_support;
+  // the entropy bonus puts a dense term on every logit
+  const bool sparse_ok = c->loss_type == RL_LOSS_REINFORCE && !kl_active && has_support &&
+                         c->entropy_coeff == 0.0f;
   if (c->backward == RL_BWD_SPARSE && !sparse_ok) return RL_E_CFG;
   return RL_OK;
 }
@@ -161,8 +167,10 @@ rl_status make_plan(const rl_loss_cfg* c, bool has_support, bool want_dh, bool w
   p->beta = p->kl_active ? c->kl_coeff : 0.0f;
   int mode = c->backward;
   if (mode == RL_BWD_AUTO)
-    mode = (c->loss_type == RL_LOSS_REINFORCE && !p->kl_active && has_support) ? RL_BWD_SPARSE
-                                                                               : RL_BWD_DENSE;
+    mode = (c->loss_type == RL_LOSS_REINFORCE && !p->kl_active && has_support &&
+            c->entropy_coeff == 0.0f)
+               ? RL_BWD_SPARSE
+               : RL_BWD_DENSE;
   p->mode = mode;
   p->want_dh = want_dh && mode != RL_BWD_NONE;
   p->want_dW = want_dW && mode != RL_BWD_NONE;
@@ -325,7 +333,7 @@ rl_status rl_loss_workspace_size(const rl_loss_cfg* cfg, int32_t has_support, in
 
 rl_status rl_loss_fwd_bwd(const void* h, const void* W, const int32_t* labels,
                           const float* infer_logprobs, const float* adv,
-                          const int64_t* csr_offsets_host, const int64_t* csr_offsets_dev,
+                          const int32_t* policy_age, const int64_t* csr_offsets_host, const int64_t* csr_offsets_dev,
                           const int32_t* csr_ids, const float* csr_u, const float* csr_logq,
                           const rl_loss_cfg* cfg, const rl_loss_out* out, void* workspace,
                           size_t workspace_bytes, void* stream) {
@@ -370,6 +378,7 @@ rl_status rl_loss_fwd_bwd(const void* h, const void* W, const int32_t* labels,
   const WeightParams wp{cfg->loss_type, cfg->ipo_eps, cfg->max_ratio, cfg->icepop_lo,
                         cfg->icepop_hi};
   const float inv_D = 1.0f / cfg->loss_norm;
+  const float gs = cfg->entropy_coeff * cfg->inv_temperature * inv_D;  // entropy term of G
 
   if (p.dense && p.want_dh)
     RL_TRY(timed(K_TRANSPOSE_W, s, [&] {
@@ -407,6 +416,9 @@ rl_status rl_loss_fwd_bwd(const void* h, const void* W, const int32_t* labels,
     ca.wp = wp;
     ca.adv_tau = cfg->adv_tau;
     ca.beta = p.beta;
+    ca.age = policy_age;
+    ca.staleness = cfg->kl_staleness;
+    ca.gamma = cfg->entropy_coeff;
     ca.inv_t = cfg->inv_temperature;
     ca.inv_D = inv_D;
     ca.lse = lse;
@@ -424,7 +436,7 @@ rl_status rl_loss_fwd_bwd(const void* h, const void* W, const int32_t* labels,
       RL_TRY(timed(K_FORM_G, s, [&] {
         return form_g_blocks(static_cast<bf16_t*>(G), p.KB_v, p.want_dh ? 1 : 0,
                              static_cast<bf16_t*>(Gt), p.KB_t, pm, p.J, p.vtile, lse + c0,
-                             kap + c0, p.V, tc, s);
+                             kap + c0, gs, p.V, tc, s);
       }));
       if (p.want_dh)
         RL_TRY(timed(K_GEMM_DH, s, [&] {
@@ -443,8 +455,8 @@ rl_status rl_loss_fwd_bwd(const void* h, const void* W, const int32_t* labels,
       }
     } else if (p.dense) {
       RL_TRY(timed(K_FORM_G, s, [&] {
-        return form_g(p.dtype, P, p.Vpad, Gt, p.Tcpad, pm, p.J, p.vtile, lse + c0, kap + c0, p.V,
-                      tc, tck, p.want_dh ? 1 : 0, s);
+        return form_g(p.dtype, P, p.Vpad, Gt, p.Tcpad, pm, p.J, p.vtile, lse + c0, kap + c0, gs,
+                      p.V, tc, tck, p.want_dh ? 1 : 0, s);
       }));
       if (p.want_dh)
         RL_TRY(timed(K_GEMM_DH, s, [&] {

@@ -126,6 +126,10 @@ __global__ void __launch_bounds__(NT) combine_kernel(CombineArgs a) {
   bool keep;
   const float w = rl_weight(lp, lq, a.wp, &keep);
   const float s = a.adv_tau * a.adv[t];
+  // beta_t: the KL coefficient, scaled by 1/sqrt(1 + age) under inv_sqrt staleness
+  const int32_t age = a.age != nullptr ? max(a.age[t], 0) : 0;
+  const float beta =
+      a.staleness == RL_STALENESS_INV_SQRT ? a.beta * rsqrtf(1.0f + (float)age) : a.beta;
 
   // Support entries: one wave per entry, entries strided over the 4 waves;
   // each wave keeps its own running sums, combined in wave order.
@@ -155,7 +159,7 @@ __global__ void __launch_bounds__(NT) combine_kernel(CombineArgs a) {
       kl += ue * (lqe - lpe);
       sm += ue * __expf(lpe - lqe);
       if (lane == 0) {
-        a.coef[a.N + e] = (s * ce - a.beta * ue) * a.inv_t * a.inv_D;
+        a.coef[a.N + e] = (s * ce - beta * ue) * a.inv_t * a.inv_D;
         if (a.o_support_lp != nullptr) a.o_support_lp[e] = lpe;
       }
     }
@@ -179,10 +183,12 @@ __global__ void __launch_bounds__(NT) combine_kernel(CombineArgs a) {
     kl = acc[3];
     sm = acc[4];
     const float klt = a.beta != 0.0f ? kl : 0.0f;
-    const float loss = -s * (w * lp - cent) + a.beta * klt;
-    const float kappa = s * (w - sc) + a.beta * su;
+    const float loss = -s * (w * lp - cent) + beta * klt - a.gamma * ent;
+    const float kappa = s * (w - sc) + beta * su;
     a.lse[t] = lse;
-    a.kappa_s[t] = kappa * a.inv_t * a.inv_D;
+    // the dense coefficient with the entropy bonus folded in:
+    // p (kappa + gamma (log p + H)) = p (kappa + gamma (H - lse) + gamma z)
+    a.kappa_s[t] = (kappa + a.gamma * (ent - lse)) * a.inv_t * a.inv_D;
     a.coef[t] = -s * w * a.inv_t * a.inv_D;
     float* st = a.stats + t * STAT_N;
     st[STAT_LOSS] = loss;
@@ -193,6 +199,9 @@ __global__ void __launch_bounds__(NT) combine_kernel(CombineArgs a) {
     st[STAT_KL] = klt;
     st[STAT_ABS_KAPPA] = fabsf(kappa);
     st[STAT_ENTROPY] = ent;
+    st[STAT_BETA] = beta;
+    st[STAT_KL_AGE0] = age == 0 ? klt : 0.0f;
+    st[STAT_AGE0] = age == 0 ? 1.0f : 0.0f;
     if (a.o_logprobs) a.o_logprobs[t] = lp;
     if (a.o_entropy) a.o_entropy[t] = ent;
     if (a.o_weight) a.o_weight[t] = w;
@@ -202,7 +211,8 @@ __global__ void __launch_bounds__(NT) combine_kernel(CombineArgs a) {
 }
 
 // G (in place over P) and Gt from P = e^(z - m_tile) (token-major [Tc, ldp]):
-// g[t, v] = kap[t] * exp(m[t, v / vtile] - lse[t]) * P[t, v].  Tiles of 64
+// g[t, v] = exp(m - lse[t]) * P[t, v] * (kap[t] + gs (m + log P[t, v])) with
+// m = m[t, v / vtile] (gs = 0 without the entropy bonus).  Tiles of 64
 // tokens x 128 vocabulary entries (one online-softmax tile column per WG).
 // Padding is written as zeros: G columns V..ldp and Gt columns Tc..Tck, which
 // the dh and dW contractions read as part of their K ranges.
@@ -211,16 +221,19 @@ __global__ void __launch_bounds__(NT) form_g_kernel(T* __restrict__ P, int64_t l
                                                     T* __restrict__ Gt, int64_t ldgt,
                                                     const float* __restrict__ part_m, int64_t J,
                                                     int vtile, const float* __restrict__ lse,
-                                                    const float* __restrict__ kap, int64_t V,
-                                                    int64_t Tc, int write_g) {
+                                                    const float* __restrict__ kap, float gs,
+                                                    int64_t V, int64_t Tc, int write_g) {
   constexpr int VEC = Elem<T>::VEC, CPR = 128 / VEC;  // chunks per 128-wide P row
-  __shared__ float scale[64];
+  __shared__ float scale[64], scale_b[64], mtile[64];
   __shared__ T tile[128][64 + VEC];  // [v][t]
   const int64_t t0 = (int64_t)blockIdx.x * 64, v0 = (int64_t)blockIdx.y * 128;
   if (threadIdx.x < 64) {
     const int64_t t = t0 + threadIdx.x;
-    scale[threadIdx.x] =
-        (t < Tc) ? kap[t] * __expf(part_m[t * J + v0 / vtile] - lse[t]) : 0.0f;
+    const float m = t < Tc ? part_m[t * J + v0 / vtile] : 0.0f;
+    const float e = t < Tc ? __expf(m - lse[t]) : 0.0f;
+    scale[threadIdx.x] = t < Tc ? kap[t] * e : 0.0f;
+    scale_b[threadIdx.x] = gs * e;
+    mtile[threadIdx.x] = m;
   }
   __syncthreads();
   for (int q = threadIdx.x; q < 64 * CPR; q += NT) {
@@ -233,8 +246,16 @@ __global__ void __launch_bounds__(NT) form_g_kernel(T* __restrict__ P, int64_t l
       float x[VEC];
       Elem<T>::unpack(raw, x);
       const float sc = scale[tl];
+      if (gs != 0.0f) {
+        // entropy bonus: x (sc + sb (m + log x)), 0 where x underflowed
+        const float sb = scale_b[tl], m = mtile[tl];
 #pragma unroll
-      for (int k = 0; k < VEC; ++k) g[k] = (v + k < V) ? sc * x[k] : 0.0f;
+        for (int k = 0; k < VEC; ++k)
+          g[k] = (v + k < V && x[k] > 0.0f) ? x[k] * (sc + sb * (m + __logf(x[k]))) : 0.0f;
+      } else {
+#pragma unroll
+        for (int k = 0; k < VEC; ++k) g[k] = (v + k < V) ? sc * x[k] : 0.0f;
+      }
       const u32x4 packed = Elem<T>::pack(g);
       if (write_g) *reinterpret_cast<u32x4*>(row) = packed;
       Elem<T>::unpack(packed, g);  // the rounded values go to Gt as well
@@ -293,13 +314,15 @@ __global__ void __launch_bounds__(NT) to_tiled_t_kernel(const bf16_t* __restrict
 // Dense-gradient pass over the tiled layout (bf16).  The forward GEMM left
 // e^(z - m_j) in G's tiled blocks; each workgroup takes one 16 KB block
 // (256 tokens x 32 vocabulary entries, one vocabulary tile j), scales every
-// element by kappa_t e^(m_tj - LSE_t) (zero past Tc and V), writes it back in
+// element by kappa_t e^(m_tj - LSE_t) (with the entropy bonus, by
+// e^(m_tj - LSE_t) (kappa_t + gs (m_tj + log x)), kappa_t holding the rest of
+// that term) (zero past Tc and V), writes it back in
 // place when G is wanted, and writes its transpose as eight 2 KB pieces of
 // the Gt blocks (rows = vocabulary, K = tokens) through an LDS transpose.
 __global__ void __launch_bounds__(NT) form_g_blocks_kernel(
     bf16_t* __restrict__ G, int64_t KB_g, int write_g, bf16_t* __restrict__ Gt, int64_t KB_gt,
     const float* __restrict__ part_m, int64_t J, int vtile, const float* __restrict__ lse,
-    const float* __restrict__ kap, int64_t V, int64_t Tc) {
+    const float* __restrict__ kap, float gs, int64_t V, int64_t Tc) {
   constexpr int PITCH = TILE_ROWS + 8;                                   // 528 bytes
   __shared__ __attribute__((aligned(16))) bf16_t tt[TILE_K][PITCH];  // [vocab][token]
   const int64_t tp = blockIdx.x, kb = blockIdx.y;
@@ -310,11 +333,21 @@ __global__ void __launch_bounds__(NT) form_g_blocks_kernel(
     const int p = threadIdx.x + NT * q;  // 16-byte chunk of the block
     const int r = p >> 2, lc = (p & 3) ^ ((r >> 1) & 3);
     const int64_t t = tp * TILE_ROWS + r, v = kb * TILE_K + lc * 8;
-    const float sc = t < Tc ? kap[t] * __expf(part_m[t * J + jt] - lse[t]) : 0.0f;
+    const float m = t < Tc ? part_m[t * J + jt] : 0.0f;
+    const float e = t < Tc ? __expf(m - lse[t]) : 0.0f;
+    const float sc = t < Tc ? kap[t] * e : 0.0f;
     float x[8];
     Elem<bf16_t>::unpack(*reinterpret_cast<const u32x4*>(blk + p * 8), x);
+    if (gs != 0.0f) {
+      // entropy bonus: x (sc + sb (m + log x)), 0 where x underflowed
+      const float sb = gs * e;
 #pragma unroll
-    for (int k = 0; k < 8; ++k) x[k] = (v + k < V) ? sc * x[k] : 0.0f;
+      for (int k = 0; k < 8; ++k)
+        x[k] = (v + k < V && x[k] > 0.0f) ? x[k] * (sc + sb * (m + __logf(x[k]))) : 0.0f;
+    } else {
+#pragma unroll
+      for (int k = 0; k < 8; ++k) x[k] = (v + k < V) ? sc * x[k] : 0.0f;
+    }
     const u32x4 out = Elem<bf16_t>::pack(x);
     if (write_g) *reinterpret_cast<u32x4*>(blk + p * 8) = out;
     if (Gt != nullptr) {
@@ -428,9 +461,11 @@ __global__ void __launch_bounds__(1024) reduce_final_kernel(const float* __restr
           r[STAT_HAS_SUPPORT] > 0 ? (float)(r[STAT_SMASS] / r[STAT_HAS_SUPPORT]) : 0.0f;
       metrics[RL_METRIC_MASK_TV] = (float)(r[STAT_TVFAIL] / n);
       metrics[RL_METRIC_KL] = (float)(r[STAT_KL] / n);
-      metrics[RL_METRIC_KL_BETA] = beta;
+      metrics[RL_METRIC_KL_BETA] = (float)(r[STAT_BETA] / n);
       metrics[RL_METRIC_MAX_ABS_KAPPA] = (float)r[STAT_ABS_KAPPA];
       metrics[RL_METRIC_ENTROPY_MEAN] = (float)(r[STAT_ENTROPY] / n);
+      metrics[RL_METRIC_KL_AGE0] =
+          r[STAT_AGE0] > 0 ? (float)(r[STAT_KL_AGE0] / r[STAT_AGE0]) : 0.0f;
     }
   }
 }
@@ -478,17 +513,17 @@ hipError_t combine(int dtype, const CombineArgs& a, hipStream_t s) {
 }
 
 hipError_t form_g(int dtype, void* P, int64_t ldp, void* Gt, int64_t ldgt, const float* part_m,
-                  int64_t J, int vtile, const float* lse_c, const float* kappa_c, int64_t V,
-                  int64_t Tc, int64_t Tck, int write_g, hipStream_t s) {
+                  int64_t J, int vtile, const float* lse_c, const float* kappa_c, float gs,
+                  int64_t V, int64_t Tc, int64_t Tck, int write_g, hipStream_t s) {
   const dim3 grid((unsigned)ceil_div(Tck, 64), (unsigned)ceil_div(ldp, 128));
   if (dtype == RL_DTYPE_BF16)
     hipLaunchKernelGGL(form_g_kernel<bf16_t>, grid, dim3(NT), 0, s, static_cast<bf16_t*>(P), ldp,
-                       static_cast<bf16_t*>(Gt), ldgt, part_m, J, vtile, lse_c, kappa_c, V, Tc,
-                       write_g);
+                       static_cast<bf16_t*>(Gt), ldgt, part_m, J, vtile, lse_c, kappa_c, gs, V,
+                       Tc, write_g);
   else
     hipLaunchKernelGGL(form_g_kernel<float>, grid, dim3(NT), 0, s, static_cast<float*>(P), ldp,
-                       static_cast<float*>(Gt), ldgt, part_m, J, vtile, lse_c, kappa_c, V, Tc,
-                       write_g);
+                       static_cast<float*>(Gt), ldgt, part_m, J, vtile, lse_c, kappa_c, gs, V,
+                       Tc, write_g);
   return hipGetLastError();
 }
 
@@ -501,11 +536,11 @@ hipError_t to_tiled_t(const bf16_t* src, int64_t ld_src, int64_t S, int64_t C, b
 
 hipError_t form_g_blocks(bf16_t* G, int64_t KB_g, int write_g, bf16_t* Gt, int64_t KB_gt,
                          const float* part_m, int64_t J, int vtile, const float* lse_c,
-                         const float* kappa_c, int64_t V, int64_t Tc, hipStream_t s) {
+                         const float* kappa_c, float gs, int64_t V, int64_t Tc, hipStream_t s) {
   if (Tc <= 0) return hipSuccess;
   const dim3 grid((unsigned)ceil_div(Tc, TILE_ROWS), (unsigned)KB_g);
   hipLaunchKernelGGL(form_g_blocks_kernel, grid, dim3(NT), 0, s, G, KB_g, write_g, Gt, KB_gt,
-                     part_m, J, vtile, lse_c, kappa_c, V, Tc);
+                     part_m, J, vtile, lse_c, kappa_c, gs, V, Tc);
   return hipGetLastError();
 }
 

@@ -60,7 +60,7 @@ hipError_t to_tiled_t(const bf16_t* src, int64_t ld_src, int64_t S, int64_t C, b
 // vocabulary, KB_gt blocks of 32 tokens per panel) when Gt is not null.
 hipError_t form_g_blocks(bf16_t* G, int64_t KB_g, int write_g, bf16_t* Gt, int64_t KB_gt,
                          const float* part_m, int64_t J, int vtile, const float* lse_c,
-                         const float* kappa_c, int64_t V, int64_t Tc, hipStream_t s);
+                         const float* kappa_c, float gs, int64_t V, int64_t Tc, hipStream_t s);
 
 // dst[c][r] = src[r][c] for r < R, 0 for R <= r < Rpad; c < C.
 hipError_t transpose_pad(int dtype, const void* src, int64_t ld_src, int64_t R, int64_t C,
@@ -81,9 +81,12 @@ struct CombineArgs {
   int64_t t0, Tc, N, H, V, J, nnz;
   WeightParams wp;
   float adv_tau, beta, inv_t, inv_D;
+  const int32_t* age;  // [N] policy age or null (all 0)
+  int staleness;       // rl_kl_staleness: beta_t = beta / sqrt(1 + age_t) when inv_sqrt
+  float gamma;         // entropy bonus coefficient
   // outputs (global token index)
   float* lse;         // [N]
-  float* kappa_s;     // [N] kappa_t * inv_t / D
+  float* kappa_s;     // [N] (kappa_t + gamma (H_t - lse_t)) * inv_t / D
   float* stats;       // [N, 8] per-token reduction inputs
   float* coef;        // [N + nnz] gradient coefficient of label / entry (times inv_t / D)
   float* o_logprobs;  // nullable
@@ -94,15 +97,17 @@ struct CombineArgs {
   float* o_support_lp;  // [nnz] nullable
 };
 constexpr int STAT_LOSS = 0, STAT_MASKED = 1, STAT_SMASS = 2, STAT_HAS_SUPPORT = 3,
-              STAT_TVFAIL = 4, STAT_KL = 5, STAT_ABS_KAPPA = 6, STAT_ENTROPY = 7, STAT_N = 8;
+              STAT_TVFAIL = 4, STAT_KL = 5, STAT_ABS_KAPPA = 6, STAT_ENTROPY = 7, STAT_BETA = 8,
+              STAT_KL_AGE0 = 9, STAT_AGE0 = 10, STAT_N = 11;
 hipError_t combine(int dtype, const CombineArgs& a, hipStream_t s);
 
 // G (in place over P, if write_g) and Gt from P = exp(z - m_tile):
-// g[t, v] = kappa_s[t] * exp(m[t, v / vtile] - lse[t]) * P[t, v].
+// g[t, v] = exp(m - lse[t]) * P[t, v] * (kappa_s[t] + gs * (m + log P[t, v])),
+// m = m[t, v / vtile], gs = gamma inv_t / D (the entropy-bonus term; 0 = off).
 // ldp must be a multiple of 128; Gt columns up to Tck (multiple of 64).
 hipError_t form_g(int dtype, void* P, int64_t ldp, void* Gt, int64_t ldgt, const float* part_m,
-                  int64_t J, int vtile, const float* lse_c, const float* kappa_c, int64_t V,
-                  int64_t Tc, int64_t Tck, int write_g, hipStream_t s);
+                  int64_t J, int vtile, const float* lse_c, const float* kappa_c, float gs,
+                  int64_t V, int64_t Tc, int64_t Tck, int write_g, hipStream_t s);
 
 // dh[t] = sum_s part[s][t] + sum over label/entries of coef * W[v] ; grad dtype.
 hipError_t finalize_dh(int dtype, int grad_dtype, const float* part, int splits,

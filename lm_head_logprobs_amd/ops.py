@@ -25,6 +25,9 @@ def _dtype_code(t: torch.dtype) -> int:
     raise TypeError(f"unsupported dtype {t}")
 
 
+_STALE = {"none": L.RL_STALENESS_NONE, "inv_sqrt": L.RL_STALENESS_INV_SQRT}
+
+
 def make_cfg(N, H, V, nnz, dtype: torch.dtype, params: dict, backward=None, token_chunk=0,
              grad_dtype: torch.dtype | None = None, accumulate_dW=False) -> L.RlLossCfg:
     c = L.RlLossCfg()
@@ -37,7 +40,9 @@ def make_cfg(N, H, V, nnz, dtype: torch.dtype, params: dict, backward=None, toke
     c.backward = _BWD[backward if backward is not None else params.get("backward", "auto")]
     c.replayed = int(bool(params.get("replayed", False)))
     c.accumulate_dW = int(bool(accumulate_dW))
-    c.reserved0 = 0
+    c.kl_staleness = _STALE[params.get("kl_staleness", "none")]
+    c.entropy_coeff = float(params.get("entropy_coeff", 0.0))
+    c.reserved1 = 0
     c.ipo_eps = float(params.get("ipo_eps", 0.3))
     c.max_ratio = float(params.get("max_ratio", 5.0))
     c.icepop_lo = float(params.get("icepop_lo", 0.5))
@@ -54,7 +59,7 @@ class FusedHead:
 
     def __init__(self, h, W, labels, infer_logprobs, adv, params, offsets_host=None, ids=None,
                  u=None, logq=None, want_dh=True, want_dW=True, backward=None, token_chunk=0,
-                 grad_dtype=None, accumulate_dW=False, want_token_outputs=True):
+                 grad_dtype=None, accumulate_dW=False, want_token_outputs=True, age=None):
         dev = h.device
         N, H = h.shape
         V = W.shape[0]
@@ -64,6 +69,7 @@ class FusedHead:
         self.offsets_host = offsets_host.contiguous() if self.has_support else None
         self.offsets_dev = offsets_host.to(dev) if self.has_support else None
         self.ids, self.u, self.logq = ids, u, logq
+        self.age = age  # int32 [N] device policy age, or None
         self.cfg = make_cfg(N, H, V, nnz, h.dtype, params, backward, token_chunk, grad_dtype,
                             accumulate_dW)
         gd = grad_dtype if grad_dtype is not None else h.dtype
@@ -88,7 +94,8 @@ class FusedHead:
 
     def __call__(self, stream=None, check=True):
         h, W, labels, lq, adv = self.args
-        return L.rl_loss_fwd_bwd(h, W, labels, lq, adv, self.offsets_host, self.offsets_dev,
+        return L.rl_loss_fwd_bwd(h, W, labels, lq, adv, self.age, self.offsets_host,
+                                 self.offsets_dev,
                                  self.ids, self.u, self.logq, self.cfg, self.out, self.workspace,
                                  self.ws_bytes, stream=stream, check=check)
 

@@ -15,5 +15,6 @@ from .gen import (  # noqa: F401
     ReplayWorkload,
     make_head,
     make_replay,
+    policy_ages,
     replay_sequences,
 )

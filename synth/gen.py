@@ -377,3 +377,16 @@ def replay_sequences(N: int, seed: int = 1002, median: float = 1024.0, sigma_log
     off = torch.zeros(len(lens) + 1, dtype=torch.int64)
     off[1:] = torch.cumsum(torch.tensor(lens, dtype=torch.int64), 0)
     return off
+
+
+def policy_ages(N: int, device="cpu", seed: int = 1003, max_age: int = 8) -> torch.Tensor:
+    """Per-token policy age (inference weight-version lag) as int32 [N].
+
+    The pages name the per-token age stream without its distribution: ages
+    follow a geometric lag (P(age = k) = 2^-(k+1)), capped at max_age, so about
+    half the tokens are fresh.
+    """
+    g = _gen("cpu", seed, "extra", chunk=1)
+    u = torch.rand(N, generator=g, dtype=torch.float64)
+    age = torch.clamp(torch.floor(-torch.log2(1.0 - u)), 0, max_age).to(torch.int32)
+    return age.to(device)

@@ -32,7 +32,7 @@ def to_np(t):
 
 def run_head(wl, **kw):
     fh = ops.FusedHead(wl.h, wl.W, wl.labels, wl.infer_logprobs, wl.adv, wl.params,
-                       wl.offsets, wl.ids, wl.u, wl.logq, **kw)
+                       wl.offsets, wl.ids, wl.u, wl.logq, age=getattr(wl, "age", None), **kw)
     fh()
     torch.cuda.synchronize()
     return fh, {k: to_np(v) for k, v in fh.o.items()}
@@ -143,9 +143,12 @@ def compare_all(wl, got, ref, report=None):
         err = np.linalg.norm(got["dW"] - ref["dW"])
         assert err <= TOL_GRAD * np.linalg.norm(ref["dW"]) + f_dW, r
     m = dict(zip(ohead.METRIC_NAMES, got["metrics"]))
-    for k in ("kl", "support_mass", "entropy_mean"):
+    for k in ("kl", "support_mass", "entropy_mean", "kl_age0"):
         assert abs(m[k] - ref["metrics"][k]) <= 1e-3 * abs(ref["metrics"][k]) + 1e-5, (k, m, r)
-    assert m["kl_beta"] == np.float32(ref["metrics"]["kl_beta"])
+    if wl.params.get("kl_staleness", "none") == "none":
+        assert m["kl_beta"] == np.float32(ref["metrics"]["kl_beta"])
+    else:  # a mean of fp32 reciprocal square roots
+        assert abs(m["kl_beta"] - ref["metrics"]["kl_beta"]) <= 1e-5 * ref["metrics"]["kl_beta"]
     n_near = int(near.sum())
     for k in ("masked_fraction", "mask_tv"):
         assert abs(m[k] - ref["metrics"][k]) <= (n_near + 0.5) / wl.N, (k, m, r)

@@ -53,7 +53,7 @@ def test_profile_calls_without_launches():
 
 def test_struct_layout_matches_header():
     # The header's structs are plain C: sizes follow from field order.
-    assert ctypes.sizeof(L.RlLossCfg) == 5 * 8 + 8 * 4 + 8 * 4
+    assert ctypes.sizeof(L.RlLossCfg) == 5 * 8 + 8 * 4 + 8 * 4 + 2 * 4
     assert ctypes.sizeof(L.RlLossOut) == 10 * 8
     assert ctypes.sizeof(L.RlElemCfg) == 2 * 4 + 8 * 4 + 7 * 4
     assert ctypes.sizeof(L.RlElemOut) == 3 * 8
@@ -97,7 +97,7 @@ def _ws(cfg, sup=False):
 @pytest.mark.parametrize("mut,code", [
     (dict(N=0), L.RL_E_ARG), (dict(H=4), L.RL_E_ARG), (dict(H=20), L.RL_E_ARG),
     (dict(V=0), L.RL_E_ARG), (dict(V=2**31), L.RL_E_ARG), (dict(token_chunk=-1), L.RL_E_ARG),
-    (dict(dtype=7), L.RL_E_ARG), (dict(grad_dtype=-1), L.RL_E_ARG), (dict(reserved0=1), L.RL_E_ARG),
+    (dict(dtype=7), L.RL_E_ARG), (dict(grad_dtype=-1), L.RL_E_ARG), (dict(reserved1=1), L.RL_E_ARG),
     (dict(loss_type=3), L.RL_E_CFG), (dict(ipo_eps=-0.1), L.RL_E_CFG),
     (dict(max_ratio=0.0), L.RL_E_CFG), (dict(icepop_lo=3.0), L.RL_E_CFG),
     (dict(loss_norm=0.0), L.RL_E_CFG), (dict(loss_norm=float("nan")), L.RL_E_CFG),
@@ -106,6 +106,7 @@ def _ws(cfg, sup=False):
     (dict(kl_coeff=-1.0), L.RL_E_CFG), (dict(backward=9), L.RL_E_CFG),
     (dict(backward=L.RL_BWD_SPARSE), L.RL_E_CFG),  # sparse needs reinforce + support
     (dict(replayed=1), L.RL_E_CFG),  # replay needs a support
+    (dict(kl_staleness=2), L.RL_E_CFG), (dict(entropy_coeff=float("nan")), L.RL_E_CFG),
 ])
 def test_workspace_size_rejects(mut, code):
     cfg = ops.make_cfg(8, 16, 50, 0, __import__("torch").bfloat16, _params())
@@ -136,6 +137,14 @@ def test_support_configuration_rules():
                        params=_params(loss_type="reinforce", backward="dense"))
     assert L.lib().rl_loss_workspace_size(ctypes.byref(cfg), 1, 1, 1, ctypes.byref(n)) == L.RL_OK
     assert n.value > sparse_bytes  # the dense backward needs the [V, Tc] operand
+    # the entropy bonus makes the gradient dense: a forced sparse backward is refused and
+    # AUTO plans the dense one
+    cfg = ops.make_cfg(**base, dtype=torch.bfloat16,
+                       params=_params(loss_type="reinforce", backward="sparse", entropy_coeff=0.1))
+    assert L.lib().rl_loss_workspace_size(ctypes.byref(cfg), 1, 1, 1, ctypes.byref(n)) == L.RL_E_CFG
+    cfg.backward = L.RL_BWD_AUTO
+    assert L.lib().rl_loss_workspace_size(ctypes.byref(cfg), 1, 1, 1, ctypes.byref(n)) == L.RL_OK
+    assert n.value > sparse_bytes
 
 
 def test_workspace_size_scales_and_does_not_overflow():
@@ -177,7 +186,7 @@ def _call(hb, cfg, offsets=None, ids=True, ws_bytes=None, h=None, W=None, out=No
     if ws_bytes is None:
         ws_bytes = L.rl_loss_workspace_size(cfg, offsets is not None, True, True)
     wsp = hb.buf(ws_bytes) if ws is None else ws
-    return L.lib().rl_loss_fwd_bwd(h, W, lab, lq, adv, offp, off_dev, idp, up, None,
+    return L.lib().rl_loss_fwd_bwd(h, W, lab, lq, adv, None, offp, off_dev, idp, up, None,
                                    ctypes.byref(cfg), ctypes.byref(out), wsp, ws_bytes, None)
 
 
@@ -190,7 +199,7 @@ def test_fwd_bwd_host_errors_return_before_launch():
     need = L.rl_loss_workspace_size(cfg, False, True, True)
     assert _call(hb, cfg, ws_bytes=need - 1) == L.RL_E_WORKSPACE
     assert _call(hb, cfg, ws=hb.buf(need) + 8, ws_bytes=need) == L.RL_E_WORKSPACE  # misaligned
-    assert L.lib().rl_loss_fwd_bwd(None, None, None, None, None, None, None, None, None, None,
+    assert L.lib().rl_loss_fwd_bwd(None, None, None, None, None, None, None, None, None, None, None,
                                    ctypes.byref(cfg), None, None, 0, None) == L.RL_E_ARG
     # CSR checks on the host offsets
     cfg = ops.make_cfg(4, 16, 50, 6, torch.bfloat16, _params())

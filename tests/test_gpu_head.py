@@ -6,7 +6,7 @@ import torch
 
 from gpu_util import compare_all, compare_forward, rel_fro, run_head, to_np
 from oracle import head as ohead
-from synth import make_head
+from synth import make_head, policy_ages
 
 pytestmark = [pytest.mark.gpu,
               pytest.mark.skipif(not torch.cuda.is_available(), reason="needs a GPU")]
@@ -80,6 +80,44 @@ def test_dense_and_sparse_backward_agree_when_kappa_vanishes():
     # the dense path adds a zero G; only the rounding of dh partial sums differs
     assert rel_fro(sp["dh"], de["dh"]) <= 1e-6
     assert rel_fro(sp["dW"], de["dW"]) <= 1e-6
+
+
+def _ref(wl, **kw):
+    age = getattr(wl, "age", None)
+    return ohead.from_workload(wl, age=None if age is None else to_np(age), **kw)
+
+
+@pytest.mark.parametrize("name", ["c5a_head64k_draws_ipo_k1", "c4_head16k_ipo_topp_replay"])
+def test_kl_staleness_and_entropy_bonus(name):
+    # inv_sqrt KL staleness from per-token ages and an entropy bonus, bf16 tiled path
+    wl = _case(name)
+    wl.age = policy_ages(wl.N, device=DEV)
+    wl.params.update(kl_staleness="inv_sqrt", entropy_coeff=0.05)
+    _, got = run_head(wl)
+    ref = _ref(wl)
+    assert 0 < np.count_nonzero(to_np(wl.age)) < wl.N
+    r = compare_all(wl, got, ref)
+    print(r)
+
+
+def test_entropy_bonus_fp32_and_negative():
+    wl = make_head("c1_tiny_fp32_ipo", device=DEV)
+    print("[case] c1 fp32 with an entropy penalty", flush=True)
+    wl.params.update(entropy_coeff=-0.2)
+    _, got = run_head(wl)
+    r = compare_all(wl, got, _ref(wl))
+    print(r)
+
+
+def test_entropy_bonus_makes_reinforce_dense():
+    # reinforce without KL on a support would take the sparse backward; the
+    # entropy term puts mass on every logit, so AUTO plans the dense one
+    wl = _case("c5b_head64k_draws_reinforce")
+    wl.params.update(entropy_coeff=0.03, backward="auto")
+    _, got = run_head(wl)
+    assert np.abs(got["dW"]).sum() > 0
+    r = compare_all(wl, got, _ref(wl))
+    print(r)
 
 
 def test_token_chunking_invariance():
