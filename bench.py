@@ -82,8 +82,9 @@ def cpu_baseline(wl, target_s: float, seed: int = 0):
     W64 = d["W"].astype(np.float64)
     rng = np.random.default_rng(seed)
     args = (d["labels"], d["infer_logprobs"], d["adv"], wl.params)
+    age = getattr(wl, "age", None)
     kw = dict(offsets=d["offsets"], ids=d["ids"], u=d["u"], logq=d["logq"], want_grads=True,
-              chunk=64)
+              chunk=64, age=None if age is None else age.cpu().numpy())
     with threadpool_limits(limits=cores):
         threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
         n0 = 16
@@ -141,12 +142,21 @@ def cpu_baseline_replay(kind, host, target_s):
 def bench_head(args, torch):
     from lm_head_logprobs_amd import _lib as L
     from lm_head_logprobs_amd import ops
-    from synth import make_head
+    from synth import make_head, policy_ages
 
     dev = torch.device("cuda:0")
     wl = make_head(args.workload, device=dev)
+    age = None
+    if args.kl_staleness != "none":
+        wl.params["kl_staleness"] = args.kl_staleness
+        age = policy_ages(wl.N, device=dev)
+    if args.entropy_coeff != 0.0:
+        wl.params["entropy_coeff"] = args.entropy_coeff
+        if wl.params.get("backward") == "sparse":
+            wl.params["backward"] = "dense"  # the entropy term is dense
+    wl.age = age
     fh = ops.FusedHead(wl.h, wl.W, wl.labels, wl.infer_logprobs, wl.adv, wl.params, wl.offsets,
-                       wl.ids, wl.u, wl.logq, token_chunk=args.token_chunk)
+                       wl.ids, wl.u, wl.logq, token_chunk=args.token_chunk, age=age)
     flags = torch.zeros(1, device=dev, dtype=torch.int32)
 
     def step():
@@ -207,6 +217,8 @@ def bench_head(args, torch):
         "config": {"workload": args.workload, "tokens": N, "H": H, "V": V,
                    "loss": wl.params["loss_type"], "support_nnz": wl.nnz,
                    "kl": wl.params["kl_estimator"], "backward": wl.params["backward"],
+                   "kl_staleness": wl.params.get("kl_staleness", "none"),
+                   "entropy_coeff": wl.params.get("entropy_coeff", 0.0),
                    "token_chunk": fh.cfg.token_chunk or min(N, 16384)},
         "mfma_frac_6nhv": flops_6nhv / (ms * 1e-3) / 1e12 / peak,
         "roofline": roof,
@@ -399,6 +411,11 @@ def main():
                          "c5a_head64k_draws_ipo_k1, c5b_head64k_draws_reinforce, c2_replay, "
                          "c2_mis")
     ap.add_argument("--token-chunk", type=int, default=0)
+    ap.add_argument("--kl-staleness", default="none", choices=("none", "inv_sqrt"),
+                    help="head workloads: scale the KL by 1/sqrt(1 + policy age), with "
+                         "synthetic per-token ages")
+    ap.add_argument("--entropy-coeff", type=float, default=0.0,
+                    help="head workloads: entropy bonus coefficient")
     ap.add_argument("--cpu-seconds", type=float, default=15.0,
                     help="target length of the oracle CPU baseline sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")

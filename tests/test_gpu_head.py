@@ -183,7 +183,7 @@ def _sample(n, k, seed):
 
 
 FULL = ["c3_head16k_ipo", "c4_head16k_ipo_topp_replay", "c5a_head64k_draws_ipo_k1",
-        "c5b_head64k_draws_reinforce"]
+        "c5b_head64k_draws_reinforce", "c4_head16k_ipo_topp_replay+stale_entropy"]
 
 
 @pytest.mark.parametrize("name", FULL)
@@ -195,14 +195,18 @@ def test_full_size_sampled_tokens(name):
     sums vanish (each token's logit gradient sums to zero over the
     vocabulary)."""
     from lm_head_logprobs_amd import ops as _ops
-    wl = make_head(name, device=DEV)
+    base, _, variant = name.partition("+")
+    wl = make_head(base, device=DEV)
+    if variant == "stale_entropy":  # inv_sqrt KL staleness and an entropy bonus
+        wl.age = policy_ages(wl.N, device=DEV)
+        wl.params.update(kl_staleness="inv_sqrt", entropy_coeff=0.02)
     print(f"[case] {name} full size N={wl.N} nnz={wl.nnz} info={wl.info}", flush=True)
     st, flags = _ops.validate(wl.labels, wl.infer_logprobs, wl.adv, wl.V, wl.offsets, wl.ids,
                               wl.u, wl.logq, wl.params["replayed"])
     assert flags == 0, hex(flags)
     _, got = run_head(wl)
     tok = _sample(wl.N, 24, 1)
-    ref = ohead.from_workload(wl, tokens=tok, want_grads=True)
+    ref = _ref(wl, tokens=tok, want_grads=True)
     near, _ = compare_forward(wl, got, ref, tokens=tok)
     ok = ~near
     dh_err = rel_fro(got["dh"][tok][ok], ref["dh"][ok])
@@ -215,7 +219,9 @@ def test_full_size_sampled_tokens(name):
     hn = np.linalg.norm(to_np(wl.h), axis=1)
     a = np.abs(to_np(wl.adv))
     beta = ohead.kl_beta(wl.params)
-    scale = np.sum((a * (np.abs(got["weight"]) + 5.0) + 2 * beta) * hn) / wl.params["loss_norm"]
+    gamma = abs(wl.params.get("entropy_coeff", 0.0))
+    scale = np.sum((a * (np.abs(got["weight"]) + 5.0) + 2 * beta + 2 * gamma * np.log(wl.V)) *
+                   hn) / wl.params["loss_norm"]
     assert np.linalg.norm(col) <= 1e-3 * scale
 
 
