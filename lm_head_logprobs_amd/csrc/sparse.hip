@@ -51,30 +51,87 @@ __global__ void __launch_bounds__(RS_NT) rs_hist_kernel(const int32_t* __restric
   hist[(int64_t)threadIdx.x * nb + blockIdx.x] = cnt[threadIdx.x];
 }
 
-// Exclusive scan of n ints in place, one workgroup of 1024 threads.
-__global__ void __launch_bounds__(1024) scan_kernel(int32_t* __restrict__ a, int64_t n) {
-  __shared__ int32_t part[1024];
-  const int64_t per = ceil_div(n, 1024);
-  const int64_t b = threadIdx.x * per, e = min(n, b + per);
-  int32_t s = 0;
-  for (int64_t i = b; i < e; ++i) s += a[i];
-  part[threadIdx.x] = s;
+// Exclusive scan of n ints in place, in three launches: tiles of SC_TILE ints
+// (SC_ITEMS contiguous per thread) are summed in parallel, the tile sums are
+// scanned by one workgroup, then every tile is scanned again from its offset.
+constexpr int SC_NT = 256, SC_ITEMS = 16, SC_TILE = SC_NT * SC_ITEMS;
+
+// Inclusive prefix of v over the workgroup's threads (in thread order); the
+// total goes to *total.
+__device__ __forceinline__ int32_t block_inclusive_scan(int32_t v, int32_t* sh, int32_t* total) {
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const int32_t x = __shfl_up(v, o, 64);
+    if (lane >= o) v += x;
+  }
+  if (lane == 63) sh[w] = v;
   __syncthreads();
-  if (threadIdx.x == 0) {
-    int32_t run = 0;
-    for (int i = 0; i < 1024; ++i) {
-      const int32_t v = part[i];
-      part[i] = run;
-      run += v;
-    }
+  int32_t before = 0, all = 0;
+  for (int i = 0; i < (int)(blockDim.x >> 6); ++i) {
+    before += i < w ? sh[i] : 0;
+    all += sh[i];
   }
   __syncthreads();
-  int32_t run = part[threadIdx.x];
-  for (int64_t i = b; i < e; ++i) {
-    const int32_t v = a[i];
-    a[i] = run;
-    run += v;
+  *total = all;
+  return v + before;
+}
+
+__global__ void __launch_bounds__(SC_NT) scan_tile_sums_kernel(const int32_t* __restrict__ a,
+                                                               int64_t n,
+                                                               int32_t* __restrict__ tsum) {
+  __shared__ int32_t sh[SC_NT / 64];
+  const int64_t b = (int64_t)blockIdx.x * SC_TILE + (int64_t)threadIdx.x * SC_ITEMS;
+  int32_t v = 0;
+#pragma unroll
+  for (int j = 0; j < SC_ITEMS; ++j) v += b + j < n ? a[b + j] : 0;
+  int32_t total;
+  block_inclusive_scan(v, sh, &total);
+  if (threadIdx.x == 0) tsum[blockIdx.x] = total;
+}
+
+// One workgroup: exclusive scan of the nt tile sums, 1024 at a time.
+__global__ void __launch_bounds__(1024) scan_tsum_kernel(int32_t* __restrict__ tsum, int64_t nt) {
+  __shared__ int32_t sh[16];
+  int32_t carry = 0;
+  for (int64_t base = 0; base < nt; base += 1024) {
+    const int64_t i = base + threadIdx.x;
+    const int32_t v = i < nt ? tsum[i] : 0;
+    int32_t total;
+    const int32_t inc = block_inclusive_scan(v, sh, &total);
+    if (i < nt) tsum[i] = carry + inc - v;
+    carry += total;
   }
+}
+
+__global__ void __launch_bounds__(SC_NT) scan_apply_kernel(int32_t* __restrict__ a, int64_t n,
+                                                           const int32_t* __restrict__ tsum) {
+  __shared__ int32_t sh[SC_NT / 64];
+  const int64_t b = (int64_t)blockIdx.x * SC_TILE + (int64_t)threadIdx.x * SC_ITEMS;
+  int32_t x[SC_ITEMS];
+  int32_t v = 0;
+#pragma unroll
+  for (int j = 0; j < SC_ITEMS; ++j) {
+    x[j] = b + j < n ? a[b + j] : 0;
+    v += x[j];
+  }
+  int32_t total;
+  int32_t run = block_inclusive_scan(v, sh, &total) - v + tsum[blockIdx.x];
+#pragma unroll
+  for (int j = 0; j < SC_ITEMS; ++j) {
+    if (b + j < n) a[b + j] = run;
+    run += x[j];
+  }
+}
+
+int64_t scan_tiles(int64_t n) { return std::max<int64_t>(ceil_div(n, SC_TILE), 1); }
+
+hipError_t exclusive_scan(int32_t* a, int64_t n, int32_t* tsum, hipStream_t s) {
+  const int64_t nt = scan_tiles(n);
+  hipLaunchKernelGGL(scan_tile_sums_kernel, dim3((unsigned)nt), dim3(SC_NT), 0, s, a, n, tsum);
+  hipLaunchKernelGGL(scan_tsum_kernel, dim3(1), dim3(1024), 0, s, tsum, nt);
+  hipLaunchKernelGGL(scan_apply_kernel, dim3((unsigned)nt), dim3(SC_NT), 0, s, a, n, tsum);
+  return hipGetLastError();
 }
 
 __global__ void __launch_bounds__(RS_NT) rs_scatter_kernel(
@@ -173,7 +230,11 @@ __global__ void __launch_bounds__(256) sparse_dw_kernel(
 
 }  // namespace
 
-int64_t csc_hist_len(int64_t E) { return 256 * std::max<int64_t>(ceil_div(E, RS_BLOCK), 1); }
+// The digit histogram (256 per sort block) followed by the scan's tile sums.
+int64_t csc_hist_len(int64_t E) {
+  const int64_t n = 256 * std::max<int64_t>(ceil_div(E, RS_BLOCK), 1);
+  return n + scan_tiles(n);
+}
 
 hipError_t csc_build(const int32_t* labels, const int32_t* ids, int64_t N, int64_t nnz,
                      int64_t V, const CscWork& w, const int32_t** perm_out, hipStream_t s) {
@@ -191,7 +252,8 @@ hipError_t csc_build(const int32_t* labels, const int32_t* ids, int64_t N, int64
     const int shift = 8 * pass;
     hipLaunchKernelGGL(rs_hist_kernel, dim3((unsigned)nb), dim3(RS_NT), 0, s, ki, E, shift,
                        w.hist, nb);
-    hipLaunchKernelGGL(scan_kernel, dim3(1), dim3(1024), 0, s, w.hist, 256 * nb);
+    err = exclusive_scan(w.hist, 256 * nb, w.hist + 256 * nb, s);
+    if (err != hipSuccess) return err;
     hipLaunchKernelGGL(rs_scatter_kernel, dim3((unsigned)nb), dim3(RS_NT), 0, s, ki, ii, E, shift,
                        w.hist, nb, ko, io);
     err = hipGetLastError();
