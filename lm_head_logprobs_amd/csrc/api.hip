@@ -10,11 +10,13 @@
 //      support logits by fp32 dot products, weights, KL, loss, kappa and the
 //      per-entry gradient coefficients
 //   3. dense backward only: form G (= (kappa p + gamma p (log p + H)) / D)
-//      from P in both layouts,
-//      dh partials = G (W^T)^T split over V, dW (+)= G^T (h_c^T)^T
-//   4. dh = partials + label/support rows of W scaled by their coefficients
-// After the chunks: the label/support terms of dW via vocabulary buckets, then
-// the fixed-order loss and metric reduction.
+//      from P in both layouts, add the label and support coefficients into
+//      it (from the vocabulary-sorted entry list, built once before the
+//      chunks), dh partials = G (W^T)^T split over V, dW (+)= G^T (h_c^T)^T
+//   4. dh = the partials (dense) or the label/support rows of W scaled by
+//      their coefficients (sparse backward)
+// After the chunks: for the sparse backward, dW from the vocabulary buckets;
+// then the fixed-order loss and metric reduction.
 #include <cmath>
 #include <cstring>
 #include <mutex>
@@ -30,12 +32,12 @@ using namespace rl;
 enum ProfKind {
   K_GEMM_FWD, K_COMBINE, K_FORM_G, K_GEMM_DH, K_TRANSPOSE_H, K_GEMM_DW, K_FINALIZE_DH,
   K_TRANSPOSE_W, K_CSR_ROWS, K_CSC_BUILD, K_SPARSE_DW, K_REDUCE, K_ELEMENTWISE, K_VALIDATE,
-  K_ELEM_FINAL, K_MIS_CHUNK, K_MIS_SEQ, K_MIS_TOKEN, K_MIS_FINAL, K_COUNT
+  K_ELEM_FINAL, K_FOLD, K_MIS_CHUNK, K_MIS_SEQ, K_MIS_TOKEN, K_MIS_FINAL, K_COUNT
 };
 const char* const kProfNames[K_COUNT] = {
     "gemm_fwd",   "combine",   "form_g",   "gemm_dh",   "transpose_h",
     "gemm_dw",    "finalize_dh", "transpose_w", "csr_rows", "csc_build",
-    "sparse_dw",  "reduce",    "elementwise", "validate", "elementwise_final",
+    "sparse_dw",  "reduce",    "elementwise", "validate", "elementwise_final", "fold_sparse",
     "mis_chunk",  "mis_seq",   "mis_token", "mis_final"};
 
 struct ProfRec {
@@ -101,7 +103,7 @@ struct Plan {
   int dtype, gdtype;
   int64_t esz;
   int mode;  // resolved rl_backward
-  bool has_support, want_dh, want_dW, dense, kl_active;
+  bool has_support, want_dh, want_dW, dense, kl_active, need_csc;
   float beta;
   int splits;
   int64_t k_split;
@@ -230,7 +232,10 @@ rl_status make_plan(const rl_loss_cfg* c, bool has_support, bool want_dh, bool w
     }
   }
   p->o_ka = p->o_kb = p->o_ia = p->o_ib = p->o_hist = p->o_start = p->o_rows = 0;
-  if (p->want_dW) {
+  // The vocabulary-sorted entry list: the dense backward folds the support
+  // coefficients into G from it; the sparse backward sums the dW rows from it.
+  p->need_csc = (p->dense && has_support) || (!p->dense && p->want_dW);
+  if (p->need_csc) {
     p->o_ka = L.take(p->E, 4);
     p->o_kb = L.take(p->E, 4);
     p->o_ia = L.take(p->E, 4);
@@ -238,7 +243,7 @@ rl_status make_plan(const rl_loss_cfg* c, bool has_support, bool want_dh, bool w
     p->o_hist = L.take(csc_hist_len(p->E), 4);
     p->o_start = L.take(p->V + 2, 4);
   }
-  if ((p->want_dW) && has_support) p->o_rows = L.take(p->nnz, 4);
+  if (p->need_csc && has_support) p->o_rows = L.take(p->nnz, 4);
   if (!L.ok) return RL_E_ARG;
   p->total = L.off;
   return RL_OK;
@@ -380,6 +385,21 @@ rl_status rl_loss_fwd_bwd(const void* h, const void* W, const int32_t* labels,
   const float inv_D = 1.0f / cfg->loss_norm;
   const float gs = cfg->entropy_coeff * cfg->inv_temperature * inv_D;  // entropy term of G
 
+  // entries sorted by vocabulary id (and each support entry's token)
+  const int32_t* perm = nullptr;
+  const int32_t* skeys = nullptr;
+  int32_t* rows = (p.need_csc && has_support) ? I(p.o_rows) : nullptr;
+  CscWork cw{};
+  if (p.need_csc) {
+    cw = CscWork{I(p.o_ka), I(p.o_kb), I(p.o_ia), I(p.o_ib), I(p.o_hist), I(p.o_start),
+                 csc_hist_len(p.E)};
+    if (has_support)
+      RL_TRY(timed(K_CSR_ROWS, s, [&] { return csr_rows(csr_offsets_dev, p.N, p.nnz, rows, s); }));
+    RL_TRY(timed(K_CSC_BUILD, s, [&] {
+      return csc_build(labels, csr_ids, p.N, p.nnz, p.V, cw, &perm, &skeys, s);
+    }));
+  }
+
   if (p.dense && p.want_dh)
     RL_TRY(timed(K_TRANSPOSE_W, s, [&] {
       return p.tiled ? to_tiled_t(static_cast<const bf16_t*>(W), p.H, p.V, p.H,
@@ -438,6 +458,10 @@ rl_status rl_loss_fwd_bwd(const void* h, const void* W, const int32_t* labels,
                              static_cast<bf16_t*>(Gt), p.KB_t, pm, p.J, p.vtile, lse + c0,
                              kap + c0, gs, p.V, tc, s);
       }));
+      RL_TRY(timed(K_FOLD, s, [&] {
+        return fold_sparse(p.dtype, G, p.want_dh ? 1 : 0, Gt, 1, p.KB_v, p.KB_t, labels, skeys,
+                           perm, rows, coef, p.N, p.nnz, c0, tc, p.V, s);
+      }));
       if (p.want_dh)
         RL_TRY(timed(K_GEMM_DH, s, [&] {
           return gemm_store(p.dtype, G, p.KB_v, Wt, p.KB_v, tc, p.H, p.Vpad, p.splits, p.k_split,
@@ -458,6 +482,10 @@ rl_status rl_loss_fwd_bwd(const void* h, const void* W, const int32_t* labels,
         return form_g(p.dtype, P, p.Vpad, Gt, p.Tcpad, pm, p.J, p.vtile, lse + c0, kap + c0, gs,
                       p.V, tc, tck, p.want_dh ? 1 : 0, s);
       }));
+      RL_TRY(timed(K_FOLD, s, [&] {
+        return fold_sparse(p.dtype, P, p.want_dh ? 1 : 0, Gt, 0, p.Vpad, p.Tcpad, labels, skeys,
+                           perm, rows, coef, p.N, p.nnz, c0, tc, p.V, s);
+      }));
       if (p.want_dh)
         RL_TRY(timed(K_GEMM_DH, s, [&] {
           return gemm_store(p.dtype, P, p.Vpad, Wt, p.Vpad, tc, p.H, p.Vpad, p.splits, p.k_split,
@@ -476,19 +504,12 @@ rl_status rl_loss_fwd_bwd(const void* h, const void* W, const int32_t* labels,
       RL_TRY(timed(K_FINALIZE_DH, s, [&] {
         return finalize_dh(p.dtype, p.gdtype, dhp, p.dense ? p.splits : 0, p.Tc * p.H, W, labels,
                            has_support ? csr_offsets_dev : nullptr, csr_ids, coef, c0, tc, p.N,
-                           p.nnz, p.V, p.H, out->dh, s);
+                           p.nnz, p.V, p.H, p.dense ? 0 : 1, out->dh, s);
       }));
   }
-  if (p.want_dW) {
-    CscWork cw{I(p.o_ka), I(p.o_kb), I(p.o_ia), I(p.o_ib), I(p.o_hist), I(p.o_start),
-               csc_hist_len(p.E)};
-    int32_t* rows = has_support ? I(p.o_rows) : nullptr;
-    if (has_support)
-      RL_TRY(timed(K_CSR_ROWS, s, [&] { return csr_rows(csr_offsets_dev, p.N, p.nnz, rows, s); }));
-    const int32_t* perm = nullptr;
-    RL_TRY(timed(K_CSC_BUILD, s,
-                 [&] { return csc_build(labels, csr_ids, p.N, p.nnz, p.V, cw, &perm, s); }));
-    const int overwrite = (!p.dense && !cfg->accumulate_dW) ? 1 : 0;
+  if (!p.dense && p.want_dW) {
+    // sparse backward: dW is the label and support terms alone
+    const int overwrite = cfg->accumulate_dW ? 0 : 1;
     RL_TRY(timed(K_SPARSE_DW, s, [&] {
       return sparse_dw(p.dtype, h, p.H, p.N, p.V, cw.start, perm, rows, coef, out->dW, overwrite,
                        s);

@@ -141,12 +141,27 @@ __global__ void __launch_bounds__(NT) combine_kernel(CombineArgs a) {
     // send a read out of bounds.
     e0 = min(max(a.off[t], (int64_t)0), a.nnz);
     e1 = min(max(a.off[t + 1], e0), a.nnz);
-    for (int64_t e = e0 + wave; e < e1; e += 4) {
-      const int32_t v = a.ids[e];
-      const bool v_ok = v >= 0 && v < a.V;
-      float ze = a.inv_t * wave_sum(v_ok ? dot_row_part<T>(h, W + (int64_t)v * a.H, a.H, lane, 64)
-                                         : 0.0f);
-      if (!v_ok) ze = NAN;
+    // Wave w takes entries w, w + 4, ... in order; four of them per step so
+    // that their row loads are in flight together (the order of every sum is
+    // unchanged).
+    for (int64_t eb = e0 + wave; eb < e1; eb += 16) {
+      float zq[4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int64_t ej = eb + 4 * j;
+        const int32_t v = ej < e1 ? a.ids[ej] : -1;
+        const bool v_ok = v >= 0 && v < a.V;
+        const int64_t vs = v_ok ? v : 0;  // a valid row; its product is discarded
+        zq[j] = dot_row_part<T>(h, W + vs * a.H, a.H, lane, 64);
+        zq[j] = v_ok ? zq[j] : NAN;
+      }
+#pragma unroll
+      for (int j = 0; j < 4; ++j) zq[j] = wave_sum(zq[j]);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+      const int64_t e = eb + 4 * j;
+      if (e >= e1) break;
+      const float ze = a.inv_t * zq[j];
       const float lpe = ze - lse;
       const float ue = a.u[e];
       const float lqe = a.logq != nullptr ? a.logq[e] : logf(ue);
@@ -161,6 +176,7 @@ __global__ void __launch_bounds__(NT) combine_kernel(CombineArgs a) {
       if (lane == 0) {
         a.coef[a.N + e] = (s * ce - beta * ue) * a.inv_t * a.inv_D;
         if (a.o_support_lp != nullptr) a.o_support_lp[e] = lpe;
+      }
       }
     }
   }
@@ -373,19 +389,92 @@ __global__ void __launch_bounds__(NT) form_g_blocks_kernel(
   }
 }
 
+// ---- label and support coefficients folded into the dense operand --------------
+// Element offsets of (token tl of the chunk, vocabulary id v) in G and of
+// (v, tl) in Gt: the tiled block layouts (16-byte chunks XOR-swizzled by row)
+// or, untiled, row-major [Tc, ldg] and [V, ldgt].
+struct GIndex {
+  int tiled;
+  int64_t ldg, ldgt;  // tiled: blocks per G row panel (KB_g) and per Gt row panel (KB_gt)
+  __device__ __forceinline__ int64_t g(int64_t tl, int64_t v) const {
+    return tiled ? tiled_offset(tl, v, ldg) : tl * ldg + v;
+  }
+  __device__ __forceinline__ int64_t gt(int64_t v, int64_t tl) const {
+    return tiled ? tiled_offset(v, tl, ldgt) : v * ldgt + tl;
+  }
+};
+
+// Adds c to the operand element (tl, v) in G (when it holds G) and in Gt (when
+// present); both hold the same rounded value.  G holds the scaled operand only
+// when it was written; otherwise the previous value is read from Gt.
+template <typename T>
+__device__ __forceinline__ void fold_add(T* G, int write_g, T* Gt, const GIndex& ix, int64_t tl,
+                                         int64_t v, float c) {
+  const int64_t ig = ix.g(tl, v), igt = ix.gt(v, tl);
+  const float old = Gt != nullptr ? Elem<T>::to_f32(Gt[igt]) : Elem<T>::to_f32(G[ig]);
+  const T nv = Elem<T>::from_f32(old + c);
+  if (write_g) G[ig] = nv;
+  if (Gt != nullptr) Gt[igt] = nv;
+}
+
+// One thread per token of the chunk: its label coefficient (one entry per
+// token, so no two threads touch one element).
+template <typename T>
+__global__ void __launch_bounds__(NT) fold_labels_kernel(T* G, int write_g, T* Gt, GIndex ix,
+                                                         const int32_t* __restrict__ labels,
+                                                         const float* __restrict__ coef,
+                                                         int64_t t0, int64_t Tc, int64_t V) {
+  const int64_t tl = (int64_t)blockIdx.x * NT + threadIdx.x;
+  if (tl >= Tc) return;
+  const int32_t v = labels[t0 + tl];
+  if (v < 0 || v >= V) return;
+  fold_add(G, write_g, Gt, ix, tl, (int64_t)v, coef[t0 + tl]);
+}
+
+// One thread per position of the vocabulary-sorted entry list.  A token's
+// repeated ids are adjacent there (stable sort, entries in token order), so
+// the first position of each (id, token) run sums the run's coefficients in
+// entry order and updates the element once; the others do nothing.  Label
+// entries (index < N) are folded separately, before.
+template <typename T>
+__global__ void __launch_bounds__(NT) fold_support_kernel(
+    T* G, int write_g, T* Gt, GIndex ix, const int32_t* __restrict__ skeys,
+    const int32_t* __restrict__ perm, const int32_t* __restrict__ row_of,
+    const float* __restrict__ coef, int64_t E, int64_t N, int64_t t0, int64_t Tc, int64_t V) {
+  const int64_t p = (int64_t)blockIdx.x * NT + threadIdx.x;
+  if (p >= E) return;
+  const int32_t i = perm[p];
+  const int32_t v = skeys[p];
+  if (i < N || v < 0 || v >= V) return;
+  const int64_t t = row_of[i - N];
+  if (t < t0 || t >= t0 + Tc) return;
+  if (p > 0) {
+    const int32_t ip = perm[p - 1];
+    if (ip >= N && skeys[p - 1] == v && row_of[ip - N] == t) return;  // not the run's first
+  }
+  float c = coef[i];
+  for (int64_t q = p + 1; q < E; ++q) {
+    const int32_t iq = perm[q];
+    if (iq < N || skeys[q] != v || row_of[iq - N] != t) break;
+    c += coef[iq];
+  }
+  fold_add(G, write_g, Gt, ix, t - t0, (int64_t)v, c);
+}
+
 template <typename T, typename GT>
 __global__ void __launch_bounds__(NT) finalize_dh_kernel(
     const float* __restrict__ part, int splits, int64_t split_stride, const T* __restrict__ W,
     const int32_t* __restrict__ labels, const int64_t* __restrict__ off,
     const int32_t* __restrict__ ids, const float* __restrict__ coef, int64_t t0, int64_t N,
-    int64_t nnz, int64_t V, int64_t H, GT* __restrict__ dh) {
+    int64_t nnz, int64_t V, int64_t H, int with_sparse, GT* __restrict__ dh) {
   constexpr int VEC = 8;  // columns per thread per step
   const int64_t tl = blockIdx.x;
   const int64_t t = t0 + tl;
-  const int64_t e0 = off ? min(max(off[t], (int64_t)0), nnz) : 0;
-  const int64_t e1 = off ? min(max(off[t + 1], e0), nnz) : 0;
+  // without with_sparse the label and support terms are already in the partials
+  const int64_t e0 = (with_sparse && off) ? min(max(off[t], (int64_t)0), nnz) : 0;
+  const int64_t e1 = (with_sparse && off) ? min(max(off[t + 1], e0), nnz) : 0;
   const int32_t lab = labels[t];
-  const bool lab_ok = lab >= 0 && lab < V;
+  const bool lab_ok = with_sparse && lab >= 0 && lab < V;
   const float cl = coef[t];
   for (int64_t c = (int64_t)threadIdx.x * VEC; c < H; c += (int64_t)NT * VEC) {
     float acc[VEC];
@@ -401,13 +490,33 @@ __global__ void __launch_bounds__(NT) finalize_dh_kernel(
 #pragma unroll
       for (int i = 0; i < VEC; ++i) acc[i] = fmaf(cl, Elem<T>::to_f32(wr[i]), acc[i]);
     }
-    for (int64_t e = e0; e < e1; ++e) {
-      const float ce = coef[N + e];
-      const int32_t v = ids[e];
-      if (v < 0 || v >= V) continue;
-      const T* wr = W + (int64_t)v * H + c;
+    // entries in groups of 8 with their row loads issued together; an id
+    // outside [0, V) reads row 0 with coefficient 0
+    for (int64_t eb = e0; eb < e1; eb += 8) {
+      float ce[8];
+      const T* wr[8];
 #pragma unroll
-      for (int i = 0; i < VEC; ++i) acc[i] = fmaf(ce, Elem<T>::to_f32(wr[i]), acc[i]);
+      for (int j = 0; j < 8; ++j) {
+        const int64_t e = eb + j;
+        const int32_t v = e < e1 ? ids[e] : -1;
+        const bool ok = v >= 0 && v < V;
+        ce[j] = ok ? coef[N + e] : 0.0f;
+        wr[j] = W + (ok ? (int64_t)v : 0) * H + c;
+      }
+      constexpr int EV = Elem<T>::VEC, NV = VEC / EV;  // 16-byte loads per row piece
+      u32x4 raw[8][NV];
+#pragma unroll
+      for (int j = 0; j < 8; ++j)
+#pragma unroll
+        for (int q = 0; q < NV; ++q) raw[j][q] = *reinterpret_cast<const u32x4*>(wr[j] + q * EV);
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        float x[VEC];
+#pragma unroll
+        for (int q = 0; q < NV; ++q) Elem<T>::unpack(raw[j][q], x + q * EV);
+#pragma unroll
+        for (int i = 0; i < VEC; ++i) acc[i] = fmaf(ce[j], x[i], acc[i]);
+      }
     }
     GT* o = dh + t * H + c;
 #pragma unroll
@@ -547,20 +656,42 @@ hipError_t form_g_blocks(bf16_t* G, int64_t KB_g, int write_g, bf16_t* Gt, int64
 hipError_t finalize_dh(int dtype, int grad_dtype, const float* part, int splits,
                        int64_t split_stride, const void* W, const int32_t* labels,
                        const int64_t* off, const int32_t* ids, const float* coef, int64_t t0,
-                       int64_t Tc, int64_t N, int64_t nnz, int64_t V, int64_t H, void* dh,
-                       hipStream_t s) {
+                       int64_t Tc, int64_t N, int64_t nnz, int64_t V, int64_t H,
+                       int with_sparse, void* dh, hipStream_t s) {
   if (Tc <= 0) return hipSuccess;
   const dim3 grid((unsigned)Tc);
 #define RL_FIN(T, GT)                                                                           \
   hipLaunchKernelGGL((finalize_dh_kernel<T, GT>), grid, dim3(NT), 0, s, part, splits,          \
                      split_stride, static_cast<const T*>(W), labels, off, ids, coef, t0, N, nnz, \
-                     V, H, static_cast<GT*>(dh))
+                     V, H, with_sparse, static_cast<GT*>(dh))
   if (dtype == RL_DTYPE_BF16) {
     if (grad_dtype == RL_DTYPE_BF16) RL_FIN(bf16_t, bf16_t); else RL_FIN(bf16_t, float);
   } else {
     if (grad_dtype == RL_DTYPE_BF16) RL_FIN(float, bf16_t); else RL_FIN(float, float);
   }
 #undef RL_FIN
+  return hipGetLastError();
+}
+
+hipError_t fold_sparse(int dtype, void* G, int write_g, void* Gt, int tiled, int64_t ldg,
+                       int64_t ldgt, const int32_t* labels, const int32_t* skeys,
+                       const int32_t* perm, const int32_t* row_of, const float* coef, int64_t N,
+                       int64_t nnz, int64_t t0, int64_t Tc, int64_t V, hipStream_t s) {
+  if (Tc <= 0) return hipSuccess;
+  const GIndex ix{tiled, ldg, ldgt};
+  const int64_t E = N + nnz;
+#define RL_FOLD(T)                                                                               \
+  do {                                                                                           \
+    hipLaunchKernelGGL(fold_labels_kernel<T>, dim3((unsigned)ceil_div(Tc, NT)), dim3(NT), 0, s,  \
+                       static_cast<T*>(G), write_g, static_cast<T*>(Gt), ix, labels, coef, t0,  \
+                       Tc, V);                                                                   \
+    if (nnz > 0)                                                                                 \
+      hipLaunchKernelGGL(fold_support_kernel<T>, dim3((unsigned)ceil_div(E, NT)), dim3(NT), 0,   \
+                         s, static_cast<T*>(G), write_g, static_cast<T*>(Gt), ix, skeys, perm,  \
+                         row_of, coef, E, N, t0, Tc, V);                                         \
+  } while (0)
+  if (dtype == RL_DTYPE_BF16) RL_FOLD(bf16_t); else RL_FOLD(float);
+#undef RL_FOLD
   return hipGetLastError();
 }
 

@@ -113,8 +113,18 @@ hipError_t form_g(int dtype, void* P, int64_t ldp, void* Gt, int64_t ldgt, const
 hipError_t finalize_dh(int dtype, int grad_dtype, const float* part, int splits,
                        int64_t split_stride, const void* W, const int32_t* labels,
                        const int64_t* off, const int32_t* ids, const float* coef, int64_t t0,
-                       int64_t Tc, int64_t N, int64_t nnz, int64_t V, int64_t H, void* dh,
-                       hipStream_t s);
+                       int64_t Tc, int64_t N, int64_t nnz, int64_t V, int64_t H,
+                       int with_sparse, void* dh, hipStream_t s);
+
+// The label and support coefficients of the chunk's tokens added into the
+// dense operand (G, when write_g, and Gt, when non-null; tiled layouts with
+// ldg = KB_g, ldgt = KB_gt, else row-major strides): labels one per token,
+// then support entries from the vocabulary-sorted list (skeys / perm of
+// csc_build), a token's repeated ids summed in entry order.
+hipError_t fold_sparse(int dtype, void* G, int write_g, void* Gt, int tiled, int64_t ldg,
+                       int64_t ldgt, const int32_t* labels, const int32_t* skeys,
+                       const int32_t* perm, const int32_t* row_of, const float* coef, int64_t N,
+                       int64_t nnz, int64_t t0, int64_t Tc, int64_t V, hipStream_t s);
 
 hipError_t reduce_final(const float* stats, int64_t N, float inv_D, float beta, float* loss,
                         float* metrics, hipStream_t s);
@@ -131,7 +141,8 @@ struct CscWork {
 };
 int64_t csc_hist_len(int64_t E);
 hipError_t csc_build(const int32_t* labels, const int32_t* ids, int64_t N, int64_t nnz,
-                     int64_t V, const CscWork& w, const int32_t** perm_out, hipStream_t s);
+                     int64_t V, const CscWork& w, const int32_t** perm_out,
+                     const int32_t** keys_out, hipStream_t s);
 
 // dW[v] (=|+=) sum over entries in bucket v of coef * h[tok].
 hipError_t sparse_dw(int dtype, const void* h, int64_t H, int64_t N, int64_t V,

@@ -212,14 +212,36 @@ __global__ void __launch_bounds__(256) sparse_dw_kernel(
       float acc[VEC];
 #pragma unroll
       for (int i = 0; i < VEC; ++i) acc[i] = 0.0f;
-      for (int32_t p = s; p < e; ++p) {
-        const int32_t i = perm[p];
-        const float cf = coef[i];
-        const int64_t tok = i < N ? i : row_of[i - N];
-        if (tok < 0 || tok >= N) continue;  // entry outside every row (corrupted offsets)
-        const T* hr = h + tok * H + c;
+      // the bucket's entries in order, in groups of 8 whose loads are issued
+      // together; an entry outside every row (corrupted offsets) reads row 0
+      // with coefficient 0
+      constexpr int EV = Elem<T>::VEC, NV = VEC / EV;  // 16-byte loads per row piece
+      for (int32_t pb = s; pb < e; pb += 8) {
+        float cf[8];
+        const T* hr[8];
 #pragma unroll
-        for (int k = 0; k < VEC; ++k) acc[k] = fmaf(cf, Elem<T>::to_f32(hr[k]), acc[k]);
+        for (int j = 0; j < 8; ++j) {
+          const int32_t p = pb + j;
+          const int32_t i = p < e ? perm[p] : 0;
+          const int64_t tok = p < e ? (i < N ? (int64_t)i : (int64_t)row_of[i - N]) : -1;
+          const bool ok = tok >= 0 && tok < N;
+          cf[j] = ok ? coef[i] : 0.0f;
+          hr[j] = h + (ok ? tok : 0) * H + c;
+        }
+        u32x4 raw[8][NV];
+#pragma unroll
+        for (int j = 0; j < 8; ++j)
+#pragma unroll
+          for (int q = 0; q < NV; ++q)
+            raw[j][q] = *reinterpret_cast<const u32x4*>(hr[j] + q * EV);
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          float x[VEC];
+#pragma unroll
+          for (int q = 0; q < NV; ++q) Elem<T>::unpack(raw[j][q], x + q * EV);
+#pragma unroll
+          for (int k = 0; k < VEC; ++k) acc[k] = fmaf(cf[j], x[k], acc[k]);
+        }
       }
       float* o = dW + v * H + c;
 #pragma unroll
@@ -237,7 +259,8 @@ int64_t csc_hist_len(int64_t E) {
 }
 
 hipError_t csc_build(const int32_t* labels, const int32_t* ids, int64_t N, int64_t nnz,
-                     int64_t V, const CscWork& w, const int32_t** perm_out, hipStream_t s) {
+                     int64_t V, const CscWork& w, const int32_t** perm_out,
+                     const int32_t** keys_out, hipStream_t s) {
   const int64_t E = N + nnz;
   const int64_t nb = std::max<int64_t>(ceil_div(E, RS_BLOCK), 1);
   int bits = 1;
@@ -268,6 +291,7 @@ hipError_t csc_build(const int32_t* labels, const int32_t* ids, int64_t N, int64
   hipLaunchKernelGGL(csc_bounds_kernel, dim3((unsigned)ceil_div(E + 1, 256)), dim3(256), 0, s,
                      ki, E, V, w.start);
   *perm_out = ii;
+  if (keys_out != nullptr) *keys_out = ki;
   return hipGetLastError();
 }
 

@@ -114,17 +114,33 @@ def compare_forward(wl, got, ref, tokens=None, report=None):
 
 def grad_floors(wl, ref):
     """Absolute error floors of dh and dW from rounding the dense operand
-    G = kappa_t p_t / D to bf16 (relative 2^-9 per element, doubled for
-    margin): |dG_t W| <= 2^-9 |kappa_t| / D max_v |W_v| and
-    |dG^T h|_F <= sum_t 2^-9 |kappa_t| / D |h_t|.  They matter only when the
-    exact gradient is (near) zero, e.g. a one-word vocabulary."""
-    if wl.dtype != "bf16":
-        return 0.0, 0.0
+    G = dL/dz to the compute dtype.  G holds the softmax part kappa_t p_t and
+    the label and support coefficients (-s_t w_t at the label, s_t c_e -
+    beta_t u_e at each entry), all divided by D, so a token's row of G sums in
+    absolute value to at most (|kappa_t| + |s_t w_t| + sum_e |s_t c_e -
+    beta_t u_e|) / D.  It is rounded up to three times (the softmax part, plus
+    the label, plus a run of support entries), 2^-9 relative each in bf16
+    (2^-24 in fp32); doubled for margin: |dG_t W| <= eps k_t max_v |W_v| and
+    |dG^T h|_F <= sum_t eps k_t |h_t|.  They matter only when the exact
+    gradient is (near) zero, e.g. a one-word vocabulary."""
+    eps = 2.0**-7 if wl.dtype == "bf16" else 2.0**-22
     d = wl.to_host_numpy()
-    k = np.abs(ref["kappa"]) / wl.params["loss_norm"] * wl.params.get("inv_temperature", 1.0)
-    wmax = np.max(np.linalg.norm(d["W"], axis=1))
-    hn = np.linalg.norm(d["h"], axis=1)
-    return 2.0**-8 * np.sqrt(np.sum(k**2)) * wmax, 2.0**-8 * np.sum(k * hn)
+    prm = wl.params
+    D = prm["loss_norm"]
+    s = np.abs(d["adv"].astype(np.float64)) * abs(prm.get("adv_tau", 1.0))
+    su = np.zeros(wl.N)
+    if d["offsets"] is not None:
+        u = d["u"].astype(np.float64)
+        su = np.add.reduceat(np.concatenate([u, [0.0]]), d["offsets"][:-1]) * (
+            np.diff(d["offsets"]) > 0)
+    wmax = max(prm.get("max_ratio", 5.0), prm.get("icepop_hi", 2.0), 1.0)
+    beta = ohead.beta_per_token(prm, np.zeros(wl.N) if getattr(wl, "age", None) is None
+                                else to_np(wl.age))
+    k = (np.abs(ref["kappa"]) + s * np.abs(ref["weight"]) + s * wmax * su + beta * su)
+    k = k / D * prm.get("inv_temperature", 1.0)
+    Wn = np.max(np.linalg.norm(d["W"].astype(np.float64), axis=1))
+    hn = np.linalg.norm(d["h"].astype(np.float64), axis=1)
+    return eps * np.sqrt(np.sum(k**2)) * Wn, eps * np.sum(k * hn)
 
 
 def compare_all(wl, got, ref, report=None):

@@ -77,9 +77,11 @@ def test_dense_and_sparse_backward_agree_when_kappa_vanishes():
     assert sp["metrics"][5] == 0.0  # max |kappa|
     assert np.array_equal(sp["logprobs"], de["logprobs"])
     assert np.array_equal(sp["loss"], de["loss"])
-    # the dense path adds a zero G; only the rounding of dh partial sums differs
-    assert rel_fro(sp["dh"], de["dh"]) <= 1e-6
-    assert rel_fro(sp["dW"], de["dW"]) <= 1e-6
+    # the dense softmax part is zero; the dense path carries the label and
+    # support coefficients inside the bf16 operand G (relative rounding 2^-9
+    # per element) while the sparse path keeps them in fp32
+    assert rel_fro(sp["dh"], de["dh"]) <= 2.0**-8
+    assert rel_fro(sp["dW"], de["dW"]) <= 2.0**-8
 
 
 def _ref(wl, **kw):
