@@ -209,29 +209,34 @@ template <typename T, bool FULL_, bool STORE_> struct FwdEpi {
     const float k2 = inv_t * LOG2E;
     float* rs = red + 2 * BN;
     float* rt = red + 4 * BN;
-    // Tiled P addresses (layout Acc16): element rows 16 i + 4 g (g = lane/16,
-    // 4 consecutive rows per lane), column 16 j + lane % 16.  Sixteen columns
-    // to the right is +512 elements, 32 rows down +8192; what remains depends
-    // only on the lane and the parity of i, so two per-lane pointers cover all
-    // stores (the identity holds because wn_off and 16 j are multiples of 16
-    // and wm_off of 32).
-    T* pl[2] = {nullptr, nullptr};
+    // Tiled P stores (layout Acc16).  A lane holds 4 consecutive vocabulary
+    // rows (16 i + 4 g, g = lane / 16) of token column 16 j + lane % 16.
+    // Blocks i and i + 1 (i even) span one 32-row group, i.e. one 64-byte
+    // row of G's tiled block for each token; a 16-lane row swap
+    // (permlane16_swap on the packed values of the two blocks) leaves lane
+    // row g holding one whole 16-byte chunk of that row, chunk
+    // ((g & 1) << 1) | (g >> 1), so one 16-byte store per lane writes the
+    // 16 tokens' rows as 1 KB of contiguous memory.  Sixteen columns to the
+    // right is +512 elements, the next 32-row group +8192; the rest depends
+    // only on the lane (wn_off and 16 j are multiples of 16, so the chunk
+    // swizzle of a row depends on lane % 16 alone).
+    T* pl = nullptr;
     if constexpr (TILED_P && STORE) {
       static_assert(std::is_same<L, Acc16>::value, "tiled P store assumes the 16x16 layout");
+      static_assert(MB % 2 == 0, "row blocks pair up into 32-row groups");
       const int g = c.lane >> 4, l = c.lane & 15;
-      T* pw = P +
-              ((c.n0 / TILE_ROWS) * ldp + (m_base + c.m0 + c.wm_off) / TILE_K) *
-                  (TILE_ROWS * TILE_K) +
-              c.wn_off * TILE_K;
-#pragma unroll
-      for (int par = 0; par < 2; ++par)
-        pl[par] = pw + l * TILE_K + ((((2 * par + (g >> 1)) ^ ((l >> 1) & 3)) << 3) + 4 * (g & 1));
+      const int chunk = ((g & 1) << 1) | (g >> 1);
+      pl = P +
+           ((c.n0 / TILE_ROWS) * ldp + (m_base + c.m0 + c.wm_off) / TILE_K) *
+               (TILE_ROWS * TILE_K) +
+           (c.wn_off + l) * TILE_K + ((chunk ^ ((l >> 1) & 3)) << 3);
     }
 #pragma unroll
     for (int j = 0; j < NB; ++j) {
       const int colb = c.wn_off + L::col(j, c.lane);
       const float off = -mraw[j] * k2;
       float s = 0.0f, t = 0.0f;
+      uint32_t keep __attribute__((ext_vector_type(2))) = {0u, 0u};  // packed block i - 1
 #pragma unroll
       for (int i = 0; i < MB; ++i)
 #pragma unroll
@@ -250,14 +255,23 @@ template <typename T, bool FULL_, bool STORE_> struct FwdEpi {
           if constexpr (STORE) {
             const int vloc = c.wm_off + L::row(i, rq * 4, c.lane);  // multiple of 4
             if constexpr (TILED_P) {
-              // 4 consecutive vocabulary entries of token colb: 8 bytes of one
-              // 16-byte chunk of G's tiled layout (BN = 256 tokens = a panel)
               typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+              typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
               bf16x4 pk;
 #pragma unroll
               for (int r3 = 0; r3 < 4; ++r3) pk[r3] = (__bf16)e4[r3];
-              *reinterpret_cast<bf16x4*>(pl[i & 1] + (i >> 1) * (TILE_ROWS * TILE_K) +
-                                         16 * j * TILE_K) = pk;
+              const u32x2 w = __builtin_bit_cast(u32x2, pk);
+              if ((i & 1) == 0) {
+                keep = w;
+              } else {
+                const auto lo2 = __builtin_amdgcn_permlane16_swap(keep[0], w[0], false, false);
+                const auto hi2 = __builtin_amdgcn_permlane16_swap(keep[1], w[1], false, false);
+                const u32x4 v = {lo2[0], hi2[0], lo2[1], hi2[1]};
+                // streaming store: P is read back only after the whole GEMM
+                __builtin_nontemporal_store(
+                    v, reinterpret_cast<u32x4*>(pl + (i >> 1) * (TILE_ROWS * TILE_K) +
+                                                16 * j * TILE_K));
+              }
             } else {
               const int64_t col = c.n0 + colb;
               if (col < Tc) {
@@ -568,6 +582,207 @@ gemm_bf16_kernel(const bf16_t* __restrict__ A, int64_t lda, const bf16_t* __rest
   epi.template apply<Acc16, 8, 4, BF_BM, BF_BN>(acc, ctx);
 }
 
+// Persistent variant for row-major operands with a short K loop (the
+// forward, K = H): one workgroup per CU walks its tiles in order and the
+// stage ring runs on across tile boundaries, so the first stages of the next
+// tile are in flight while the epilogue of the current one runs (the
+// epilogue gets LDS of its own).  Tiles of XCD x are the logical tiles
+// [x * ceil(T / 8), ...) of map_tile's order, taken round-robin by its
+// workgroups, so the tiles an XCD runs at once are consecutive as before.
+// Requires K to be a multiple of BF_BK with at least BF_ST stages.  The
+// epilogue's stores count in vmcnt like the loads, in issue order; a wait
+// that ignores them (counts only younger stages) also waits for the stores
+// issued after the awaited stage, which is correct and measured to cost
+// nothing here.
+template <class Epi>
+__global__ void __launch_bounds__(BF_NT) __attribute__((amdgpu_waves_per_eu(2, 2)))
+gemm_bf16_persist(const bf16_t* __restrict__ A, int64_t lda, const bf16_t* __restrict__ B,
+                  int64_t ldb, int64_t M, int64_t N, int64_t K, int tiles_m, int tiles_n,
+                  Epi epi) {
+  __shared__ __attribute__((aligned(1024))) char lds[BF_LDS];
+  __shared__ __attribute__((aligned(16))) char scratch[6 * BF_BN * 4];
+  const int total = tiles_m * tiles_n;
+  const int per_xcd = gridDim.x >> 3;  // the grid is a multiple of 8
+  const int chunk = (int)ceil_div(total, 8);
+  const int lo = (blockIdx.x & 7) * chunk, hi = min(total, lo + chunk);
+  int t = lo + (blockIdx.x >> 3);
+  if (t >= hi) return;
+  const int tid = threadIdx.x;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // 0..7
+  const int wm = wave >> 2, wn = wave & 3;
+  const int nk = (int)ceil_div(K, BF_BK);
+  // Per-lane offsets, tile independent: the operand copy slots (rows past a
+  // tile's extent fall outside its descriptor and read zero; K is a multiple
+  // of BF_BK here) and the fragment reads.  They are formed from an opaque
+  // copy of the lane index before the first tile and again after every
+  // epilogue, so they are not live (and not spilled) across the epilogue.
+  struct LaneOffs {
+    int oa[2], ob[2], fa, fb;
+  };
+  auto lane_offs = [&]() {
+    int l;
+    __asm__ volatile("v_and_b32 %0, 63, %1" : "=v"(l) : "v"(tid));
+    LaneOffs o;
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const int p = (wave * 2 + i) * 64 + l;
+      const int row = p >> 2, ch = (p & 3) ^ ((row >> 1) & 3);
+      o.oa[i] = (int)((row * lda + 8 * ch) * 2);
+      o.ob[i] = (int)((row * ldb + 8 * ch) * 2);
+    }
+    const int ch = l >> 4;
+    int row = wm * 128 + (l & 15);
+    o.fa = row * 64 + 16 * (ch ^ ((row >> 1) & 3));
+    row = wn * 64 + (l & 15);
+    o.fb = BF_STAGE_A + row * 64 + 16 * (ch ^ ((row >> 1) & 3));
+    return o;
+  };
+  LaneOffs lof = lane_offs();
+  auto coords = [&](int lt, int64_t& m0, int64_t& n0) {
+    const int group = lt / (GROUP_M * tiles_n);
+    const int first_m = group * GROUP_M;
+    const int gsize = min(GROUP_M, tiles_m - first_m);
+    const int within = lt - group * GROUP_M * tiles_n;
+    m0 = (int64_t)(first_m + within % gsize) * BF_BM;
+    n0 = (int64_t)(within / gsize) * BF_BN;
+  };
+  // Descriptors are uniform; readfirstlane keeps them in SGPRs across the
+  // tile loop.
+  auto panel = [&](const bf16_t* X, int64_t r0, int64_t R, int64_t ld) {
+    const int64_t rows = R - r0 < BF_BM ? R - r0 : BF_BM;
+    i32x4 r = make_rsrc(X + r0 * ld, (uint32_t)(rows * ld * 2));
+#pragma unroll
+    for (int i = 0; i < 4; ++i) r[i] = __builtin_amdgcn_readfirstlane(r[i]);
+    return r;
+  };
+  int64_t m0, n0;
+  coords(t, m0, n0);
+  i32x4 rsa = panel(A, m0, M, lda), rsb = panel(B, n0, N, ldb), nrsa = rsa, nrsb = rsb;
+  int tnext = t + per_xcd;
+  bool has_next = tnext < hi;
+  int64_t nm0 = 0, nn0 = 0;
+  if (has_next) {
+    coords(tnext, nm0, nn0);
+    nrsa = panel(A, nm0, M, lda);
+    nrsb = panel(B, nn0, N, ldb);
+  }
+  const uint32_t lds_base = (uint32_t)reinterpret_cast<uintptr_t>(lds);
+  // The byte offset of stage kt passes through an opaque SGPR copy, so the
+  // per-lane offsets are formed at each issue instead of being kept as
+  // induction variables (registers are short in the K loop).
+  auto issue = [&](i32x4 ra, i32x4 rb, int kt, int slot) {
+    const uint32_t sa = lds_base + (uint32_t)(slot * BF_STAGE);
+    const uint32_t sb = sa + BF_STAGE_A;
+    int kbytes;
+    __asm__ volatile("s_lshl_b32 %0, %1, 6" : "=s"(kbytes) : "s"(kt));  // kt * BF_BK * 2
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      load_lds16(ra, sa + (uint32_t)((wave * 2 + i) * 1024), lof.oa[i] + kbytes);
+      load_lds16(rb, sb + (uint32_t)((wave * 2 + i) * 1024), lof.ob[i] + kbytes);
+    }
+  };
+  bf16x8 ca[8], cb[4];
+  auto read_frags = [&](int slot, bf16x8 (&fa)[8], bf16x8 (&fb)[4]) {
+    const char* sn = lds + slot * BF_STAGE;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) fa[i] = *reinterpret_cast<const bf16x8*>(sn + lof.fa + 1024 * i);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) fb[j] = *reinterpret_cast<const bf16x8*>(sn + lof.fb + 1024 * j);
+  };
+  // First tile: stages 0..2, then stage 0 awaited, stage 3 issued.
+  int gb = 0;  // ring position of the current tile's stage 0
+#pragma unroll
+  for (int s = 0; s < BF_ST - 1; ++s) issue(rsa, rsb, s, s);
+  wait_vmcnt<2 * BF_LPS>();
+  __syncthreads();
+  issue(rsa, rsb, BF_ST - 1, BF_ST - 1);
+  read_frags(0, ca, cb);
+  for (;;) {
+    f32x4 acc[8][4];
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) acc[i][j][r] = 0.0f;
+    // Stages 0 .. nk-2 (each also refills and reads the next stage); the last
+    // stage is peeled off below, so no fragment register is undefined on
+    // the way out of the loop.
+    for (int kt = 0; kt + 1 < nk; ++kt) {
+      bf16x8 na[8], nb[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ca[i], cb[j], acc[i][j], 0, 0, 0);
+      // Stage kt+1 has landed once at most the stages issued after it are
+      // outstanding (two, except at the end of the last tile).
+      wait_stage<BF_LPS>(has_next ? 2 : min(nk - 2 - kt, 2));
+      __syncthreads();
+      // Refill the buffer of stage kt with stage kt + 4 of this tile or,
+      // past its end, with the first stages of the next tile.
+      const int slot = (gb + kt) & (BF_ST - 1);
+      if (kt + BF_ST < nk) issue(rsa, rsb, kt + BF_ST, slot);
+      else if (has_next) issue(nrsa, nrsb, kt + BF_ST - nk, slot);
+      read_frags((gb + kt + 1) & (BF_ST - 1), na, nb);
+#pragma unroll
+      for (int i = 4; i < 8; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ca[i], cb[j], acc[i][j], 0, 0, 0);
+#pragma unroll
+      for (int i = 0; i < 8; ++i) ca[i] = na[i];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) cb[j] = nb[j];
+    }
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ca[i], cb[j], acc[i][j], 0, 0, 0);
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) __asm__ volatile("" : "+a"(acc[i][j]));
+    // The lane index enters the epilogue through an opaque copy, so that
+    // nothing the epilogue derives from it is hoisted out of the tile loop
+    // (where it would hold registers through the K loop).
+    int elane;
+    __asm__ volatile("v_and_b32 %0, 63, %1" : "=v"(elane) : "v"(tid));
+    EpiCtx ctx;
+    ctx.m0 = m0;
+    ctx.n0 = n0;
+    ctx.wm_off = wm * 128;
+    ctx.wn_off = wn * 64;
+    ctx.wave_m = wm;
+    ctx.lane = elane;
+    ctx.split = 0;
+    ctx.smem = scratch;
+    ctx.smem_bytes = (int)sizeof(scratch);
+    epi.template apply<Acc16, 8, 4, BF_BM, BF_BN>(acc, ctx);
+    if (!has_next) break;
+    // Advance: stages 0..2 of the next tile are in flight (issued in the
+    // last iterations above); await stage 0, then issue stage 3.
+    gb += nk;
+    m0 = nm0;
+    n0 = nn0;
+    rsa = nrsa;
+    rsb = nrsb;
+    tnext += per_xcd;
+    has_next = tnext < hi;
+    if (has_next) {
+      coords(tnext, nm0, nn0);
+      nrsa = panel(A, nm0, M, lda);
+      nrsb = panel(B, nn0, N, ldb);
+    }
+    lof = lane_offs();
+    wait_vmcnt<2 * BF_LPS>();
+    __syncthreads();
+    issue(rsa, rsb, BF_ST - 1, (gb + BF_ST - 1) & (BF_ST - 1));
+    read_frags(gb & (BF_ST - 1), ca, cb);
+  }
+}
+
 // ------------------------------------------------------------ fp32 kernel ---
 
 constexpr int F_BM = 128, F_BN = 128, F_BK = 16;
@@ -690,6 +905,39 @@ hipError_t launch_bf16(const bf16_t* A, int64_t lda, const bf16_t* B, int64_t ld
   return hipGetLastError();
 }
 
+// Compute units of the current device (cached per device).
+int cu_count() {
+  static int cached[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 0;
+  if (cached[dev] == 0) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+      return 0;
+    cached[dev] = n;
+  }
+  return cached[dev];
+}
+
+// Row-major operands (K = lda = ldb columns), one split: the persistent
+// kernel when the K loop has at least BF_ST stages and the device reports
+// its CU count, else the one-tile-per-workgroup kernel.
+template <class Epi>
+hipError_t launch_bf16_rows(const bf16_t* A, int64_t lda, const bf16_t* B, int64_t ldb,
+                            int64_t M, int64_t N, int64_t K, const Epi& epi, hipStream_t s) {
+  const int64_t tm = ceil_div(M, BF_BM), tn = ceil_div(N, BF_BN);
+  const int64_t total = tm * tn;
+  const int cus = cu_count() / 8 * 8;
+  if (total <= 0) return hipSuccess;
+  if (K % BF_BK != 0 || K / BF_BK < BF_ST || cus <= 0 || total > (int64_t)1 << 30)
+    return launch_bf16<false>(A, lda, B, ldb, M, N, K, 1, round_up(K, BF_BK), epi, s);
+  if ((int64_t)BF_BM * std::max(lda, ldb) * 2 >= ((int64_t)1 << 31)) return hipErrorInvalidValue;
+  const int64_t grid = std::min<int64_t>(round_up(total, 8), cus);
+  hipLaunchKernelGGL((gemm_bf16_persist<Epi>), dim3((unsigned)grid), dim3(BF_NT), 0, s,
+                     A, lda, B, ldb, M, N, K, (int)tm, (int)tn, epi);
+  return hipGetLastError();
+}
+
 template <class Epi>
 hipError_t launch_f32(const float* A, int64_t lda, const float* B, int64_t ldb, int64_t M,
                       int64_t N, int64_t K, int splits, int64_t k_split, const Epi& epi,
@@ -720,8 +968,7 @@ hipError_t gemm_fwd(int dtype, const void* W, const void* hc, int64_t V, int64_t
     const T* Wt = static_cast<const T*>(W);
     auto launch = [&](auto epi, const T* A, int64_t M) -> hipError_t {
       if constexpr (sizeof(T) == 2)
-        return launch_bf16<false>(A, H, static_cast<const bf16_t*>(hc), H, M, Tc, H, 1,
-                                  round_up(H, BF_BK), epi, s);
+        return launch_bf16_rows(A, H, static_cast<const bf16_t*>(hc), H, M, Tc, H, epi, s);
       else
         return launch_f32(A, H, static_cast<const float*>(hc), H, M, Tc, H, 1, round_up(H, F_BK),
                           epi, s);

@@ -353,7 +353,9 @@ __global__ void __launch_bounds__(NT) form_g_blocks_kernel(
     const float e = t < Tc ? __expf(m - lse[t]) : 0.0f;
     const float sc = t < Tc ? kap[t] * e : 0.0f;
     float x[8];
-    Elem<bf16_t>::unpack(*reinterpret_cast<const u32x4*>(blk + p * 8), x);
+    // streaming: each element is read and written once here
+    Elem<bf16_t>::unpack(__builtin_nontemporal_load(reinterpret_cast<const u32x4*>(blk + p * 8)),
+                         x);
     if (gs != 0.0f) {
       // entropy bonus: x (sc + sb (m + log x)), 0 where x underflowed
       const float sb = gs * e;
@@ -365,7 +367,7 @@ __global__ void __launch_bounds__(NT) form_g_blocks_kernel(
       for (int k = 0; k < 8; ++k) x[k] = (v + k < V) ? sc * x[k] : 0.0f;
     }
     const u32x4 out = Elem<bf16_t>::pack(x);
-    if (write_g) *reinterpret_cast<u32x4*>(blk + p * 8) = out;
+    if (write_g) __builtin_nontemporal_store(out, reinterpret_cast<u32x4*>(blk + p * 8));
     if (Gt != nullptr) {
       const bf16_t* e = reinterpret_cast<const bf16_t*>(&out);
 #pragma unroll
@@ -385,7 +387,7 @@ __global__ void __launch_bounds__(NT) form_g_blocks_kernel(
     const int lc = pc ^ (int)((row >> 1) & 3);
     const u32x4 val = *reinterpret_cast<const u32x4*>(&tt[rr][g * 32 + lc * 8]);
     bf16_t* dst = Gt + ((vb * KB_gt + tp * 8 + g) * (TILE_ROWS * TILE_K)) + row * TILE_K + pc * 8;
-    *reinterpret_cast<u32x4*>(dst) = val;
+    __builtin_nontemporal_store(val, reinterpret_cast<u32x4*>(dst));
   }
 }
 
