@@ -25,9 +25,8 @@
 // MFMAs are in flight across it.  Out-of-range rows or K columns are given a
 // buffer offset past the descriptor's range, which the hardware reads as zero.
 // In LDS a tile row is 64 bytes (32 bf16 = four 16-byte chunks); chunk c of
-// row r is stored at position c ^ ((r >> 1) & 3), so the 8 lanes of a
-// ds_read_b128 phase that read one chunk of 8 consecutive rows hit disjoint
-// banks.  The backward operands arrive in a tiled layout whose 16 KB blocks
+// row r is stored at position c ^ tile_swz(r) (kernels.h), which keeps the
+// fragment reads free of bank conflicts.  The backward operands arrive in a tiled layout whose 16 KB blocks
 // are exactly this LDS image, so each stage load is one contiguous copy
 // (row-major operands with 300 KB row strides touch 256 pages per stage).
 // Workgroups are remapped so consecutive tiles land on one XCD (dispatch is
@@ -229,7 +228,7 @@ template <typename T, bool FULL_, bool STORE_> struct FwdEpi {
       pl = P +
            ((c.n0 / TILE_ROWS) * ldp + (m_base + c.m0 + c.wm_off) / TILE_K) *
                (TILE_ROWS * TILE_K) +
-           (c.wn_off + l) * TILE_K + ((chunk ^ ((l >> 1) & 3)) << 3);
+           (c.wn_off + l) * TILE_K + ((chunk ^ tile_swz(l)) << 3);
     }
 #pragma unroll
     for (int j = 0; j < NB; ++j) {
@@ -471,11 +470,11 @@ gemm_bf16_kernel(const bf16_t* __restrict__ A, int64_t lda, const bf16_t* __rest
     rsa = make_rsrc(A + tc.m0 * lda, (uint32_t)(rows_a * lda * 2));
     rsb = make_rsrc(B + tc.n0 * ldb, (uint32_t)(rows_b * ldb * 2));
     // Slot p = (wave*2 + i)*64 + lane: tile row p/4, stored chunk p%4 holds
-    // logical chunk (p%4) ^ ((row>>1)&3).
+    // logical chunk (p%4) ^ tile_swz(row).
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
       const int p = (wave * 2 + i) * 64 + lane;
-      const int row = p >> 2, ch = (p & 3) ^ ((row >> 1) & 3);
+      const int row = p >> 2, ch = (p & 3) ^ tile_swz(row);
       kc[i] = 8 * ch;
       offa[i] = row < rows_a ? (int)((row * lda + kb + 8 * ch) * 2) : OOB;
       offb[i] = row < rows_b ? (int)((row * ldb + kb + 8 * ch) * 2) : OOB;
@@ -503,14 +502,14 @@ gemm_bf16_kernel(const bf16_t* __restrict__ A, int64_t lda, const bf16_t* __rest
   };
   // Fragment byte offsets inside a stage: in 16-row block i the lane reads
   // row 16 i + lane % 16, 16-byte chunk lane / 16 (k = 8 (lane / 16) .. +7).
-  // Sixteen rows down keep (row >> 1) & 3, so block i sits at +1 KB * i.
+  // Sixteen rows down keep tile_swz(row), so block i sits at +1 KB * i.
   int fa0, fb0;
   {
     const int ch = lane >> 4;
     int row = wm * 128 + (lane & 15);
-    fa0 = row * 64 + 16 * (ch ^ ((row >> 1) & 3));
+    fa0 = row * 64 + 16 * (ch ^ tile_swz(row));
     row = wn * 64 + (lane & 15);
-    fb0 = BF_STAGE_A + row * 64 + 16 * (ch ^ ((row >> 1) & 3));
+    fb0 = BF_STAGE_A + row * 64 + 16 * (ch ^ tile_swz(row));
   }
 
   f32x4 acc[8][4];
@@ -626,15 +625,15 @@ gemm_bf16_persist(const bf16_t* __restrict__ A, int64_t lda, const bf16_t* __res
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
       const int p = (wave * 2 + i) * 64 + l;
-      const int row = p >> 2, ch = (p & 3) ^ ((row >> 1) & 3);
+      const int row = p >> 2, ch = (p & 3) ^ tile_swz(row);
       o.oa[i] = (int)((row * lda + 8 * ch) * 2);
       o.ob[i] = (int)((row * ldb + 8 * ch) * 2);
     }
     const int ch = l >> 4;
     int row = wm * 128 + (l & 15);
-    o.fa = row * 64 + 16 * (ch ^ ((row >> 1) & 3));
+    o.fa = row * 64 + 16 * (ch ^ tile_swz(row));
     row = wn * 64 + (l & 15);
-    o.fb = BF_STAGE_A + row * 64 + 16 * (ch ^ ((row >> 1) & 3));
+    o.fb = BF_STAGE_A + row * 64 + 16 * (ch ^ tile_swz(row));
     return o;
   };
   LaneOffs lof = lane_offs();

@@ -318,7 +318,7 @@ __global__ void __launch_bounds__(NT) to_tiled_t_kernel(const bf16_t* __restrict
   __syncthreads();
   bf16_t* blk = dst + (rb * KB + kb) * (TILE_ROWS * TILE_K);
   for (int p = threadIdx.x; p < TILE_ROWS * 4; p += NT) {
-    const int r = p >> 2, ch = (p & 3) ^ ((r >> 1) & 3);
+    const int r = p >> 2, ch = (p & 3) ^ tile_swz(r);
     u32x4 out;
     bf16_t* e = reinterpret_cast<bf16_t*>(&out);
 #pragma unroll
@@ -347,7 +347,7 @@ __global__ void __launch_bounds__(NT) form_g_blocks_kernel(
 #pragma unroll
   for (int q = 0; q < 4; ++q) {
     const int p = threadIdx.x + NT * q;  // 16-byte chunk of the block
-    const int r = p >> 2, lc = (p & 3) ^ ((r >> 1) & 3);
+    const int r = p >> 2, lc = (p & 3) ^ tile_swz(r);
     const int64_t t = tp * TILE_ROWS + r, v = kb * TILE_K + lc * 8;
     const float m = t < Tc ? part_m[t * J + jt] : 0.0f;
     const float e = t < Tc ? __expf(m - lse[t]) : 0.0f;
@@ -384,7 +384,7 @@ __global__ void __launch_bounds__(NT) form_g_blocks_kernel(
     const int p = threadIdx.x + NT * q;
     const int g = p >> 7, rr = (p >> 2) & 31, pc = p & 3;
     const int64_t row = rbase + rr;
-    const int lc = pc ^ (int)((row >> 1) & 3);
+    const int lc = pc ^ tile_swz(row);
     const u32x4 val = *reinterpret_cast<const u32x4*>(&tt[rr][g * 32 + lc * 8]);
     bf16_t* dst = Gt + ((vb * KB_gt + tp * 8 + g) * (TILE_ROWS * TILE_K)) + row * TILE_K + pc * 8;
     __builtin_nontemporal_store(val, reinterpret_cast<u32x4*>(dst));

@@ -39,12 +39,20 @@ int gemm_k_tile(int dtype);
 // Tiled block layout of a bf16 operand [R rows, K columns] (the backward
 // GEMM operands): 256 x 32 blocks of 16 KB, block (rb, kb) at index
 // rb * KB + kb (KB = blocks per 256-row panel); inside a block row r holds
-// four 16-byte chunks, logical chunk c stored at position c ^ ((r >> 1) & 3).
-// Rows >= R and columns >= K of a block are zero.
+// four 16-byte chunks, logical chunk c stored at position c ^ tile_swz(r).
+// Rows >= R and columns >= K of a block are zero.  The same swizzle is the
+// LDS image of a GEMM stage.  It keeps both fragment reads of the GEMMs free
+// of LDS bank conflicts (measured with SQ_LDS_BANK_CONFLICT): ds_read_b128 of
+// one chunk of 16 consecutive rows, and ds_read_b64_tr_b16 of two chunks of
+// rows {8g + i, 8g + 4 + i} (g, i < 4), which needs rows r and r + 8 to use
+// disjoint chunk pairs.
 constexpr int TILE_ROWS = 256, TILE_K = 32, TILE_BLOCK_BYTES = TILE_ROWS * TILE_K * 2;
+__host__ __device__ inline int tile_swz(int64_t r) {
+  return (int)(((r >> 1) & 3) ^ (((r >> 3) & 1) * 3));
+}
 __host__ __device__ inline int64_t tiled_offset(int64_t r, int64_t k, int64_t KB) {
   return ((r / TILE_ROWS) * KB + k / TILE_K) * (TILE_ROWS * TILE_K) + (r % TILE_ROWS) * TILE_K +
-         ((((k % TILE_K) >> 3) ^ (((r % TILE_ROWS) >> 1) & 3)) << 3) + (k & 7);
+         ((((k % TILE_K) >> 3) ^ tile_swz(r % TILE_ROWS)) << 3) + (k & 7);
 }
 
 // src [S rows, C cols] row-major (ld_src) -> tiled [C rows, S cols] with KB
