@@ -210,15 +210,13 @@ rl_status make_plan(const rl_loss_cfg* c, bool has_support, bool want_dh, bool w
         !mul_ok(H256, p->Vpad, &hv) || !mul_ok((int64_t)p->splits * p->Tc, p->H, &sth))
       return RL_E_ARG;
     if (p->tiled) {
-      p->o_G = L.take(tv, 2);  // e^(z - m), then G, in the tiled layout
+      // e^(z - m), then G, in the tiled layout; dW reads it transposed
+      p->o_G = L.take(tv, 2);
       if (p->want_dh) {
         p->o_Wt = L.take(hv, 2);
         p->o_dhp = L.take(sth, 4);
       }
-      if (p->want_dW) {
-        p->o_Gt = L.take(vt, 2);
-        p->o_ht = L.take(H256 * p->Tc256, 2);
-      }
+      if (p->want_dW) p->o_ht = L.take(H256 * p->Tc256, 2);
     } else {
       p->o_P = L.take(tv, p->esz);  // e^(z - m) token-major [Tc, Vpad], then G in place
       if (p->want_dW) {
@@ -374,7 +372,7 @@ rl_status rl_loss_fwd_bwd(const void* h, const void* W, const int32_t* labels,
   float *lse = F(p.o_lse), *kap = F(p.o_kap), *stats = F(p.o_stats), *coef = F(p.o_coef);
   void* G = p.tiled ? ws + p.o_G : nullptr;
   void* P = p.tiled ? G : p.dense ? ws + p.o_P : nullptr;
-  void* Gt = (p.dense && p.want_dW) ? ws + p.o_Gt : nullptr;
+  void* Gt = (p.dense && !p.tiled && p.want_dW) ? ws + p.o_Gt : nullptr;
   void* Wt = (p.dense && p.want_dh) ? ws + p.o_Wt : nullptr;
   void* ht = (p.dense && p.want_dW) ? ws + p.o_ht : nullptr;
   float* dhp = (p.dense && p.want_dh) ? F(p.o_dhp) : nullptr;
@@ -453,14 +451,14 @@ rl_status rl_loss_fwd_bwd(const void* h, const void* W, const int32_t* labels,
     ca.o_support_lp = has_support ? out->support_logprobs : nullptr;
     RL_TRY(timed(K_COMBINE, s, [&] { return combine(p.dtype, ca, s); }));
     if (p.tiled) {
+      // G in place only: dh reads it as is, dW with transposed LDS reads.
       RL_TRY(timed(K_FORM_G, s, [&] {
-        return form_g_blocks(static_cast<bf16_t*>(G), p.KB_v, p.want_dh ? 1 : 0,
-                             static_cast<bf16_t*>(Gt), p.KB_t, pm, p.J, p.vtile, lse + c0,
-                             kap + c0, gs, p.V, tc, s);
+        return form_g_blocks(static_cast<bf16_t*>(G), p.KB_v, 1, nullptr, p.KB_t, pm, p.J,
+                             p.vtile, lse + c0, kap + c0, gs, p.V, tc, s);
       }));
       RL_TRY(timed(K_FOLD, s, [&] {
-        return fold_sparse(p.dtype, G, p.want_dh ? 1 : 0, Gt, 1, p.KB_v, p.KB_t, labels, skeys,
-                           perm, rows, coef, p.N, p.nnz, c0, tc, p.V, s);
+        return fold_sparse(p.dtype, G, 1, nullptr, 1, p.KB_v, p.KB_t, labels, skeys, perm, rows,
+                           coef, p.N, p.nnz, c0, tc, p.V, s);
       }));
       if (p.want_dh)
         RL_TRY(timed(K_GEMM_DH, s, [&] {
@@ -474,7 +472,7 @@ rl_status rl_loss_fwd_bwd(const void* h, const void* W, const int32_t* labels,
         }));
         const int acc = (c0 > 0 || cfg->accumulate_dW) ? 1 : 0;
         RL_TRY(timed(K_GEMM_DW, s, [&] {
-          return gemm_dw(p.dtype, Gt, p.KB_t, ht, p.KB_t, p.V, p.H, tc, out->dW, p.H, acc, s);
+          return gemm_dw(p.dtype, G, p.KB_v, ht, p.KB_t, p.V, p.H, tc, out->dW, p.H, acc, s);
         }));
       }
     } else if (p.dense) {

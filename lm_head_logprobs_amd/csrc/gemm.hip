@@ -437,11 +437,23 @@ constexpr int BF_LPS = 4;   // direct-to-LDS loads per thread per stage (2 A + 2
 // refills the buffer of stage kt (whose fragments every wave read before the
 // barrier), reads stage kt+1's fragments and issues the MFMAs of row blocks
 // 4..7.  The refill therefore cannot race with fragment reads.
-template <bool TILED, class Epi>
+//
+// ATR (with TILED): A is given transposed, as the tiled layout of A^T [K, M]
+// with lda = blocks per 256-row panel of A^T (the dense gradient G [tokens,
+// vocabulary] for dW = G^T h).  Stage kt of A then is rows (k0 % 256) .. +31
+// of the eight blocks m0/32 .. +7 of panel k0 / 256: eight 2 KB pieces, one
+// per 32-column group, copied verbatim.  Its fragments are read with
+// ds_read_b64_tr_b16: for row block i (16 columns of A^T, half of a piece)
+// lane j of 16-lane group g reads the 8 bytes at row 8 g + j / 4 (then
+// 8 g + 4 + j / 4), columns 4 (j % 4) .. +3, and receives column j % 16 of
+// rows 8 g .. 8 g + 3 (then + 4 .. 7): exactly the MFMA A fragment (row j,
+// k = 8 g .. 8 g + 7).  The split start must be a multiple of 256.
+template <bool TILED, class Epi, bool ATR = false>
 __global__ void __launch_bounds__(BF_NT) __attribute__((amdgpu_waves_per_eu(2, 2)))
 gemm_bf16_kernel(const bf16_t* __restrict__ A, int64_t lda, const bf16_t* __restrict__ B,
                  int64_t ldb, int64_t M, int64_t N, int64_t K, int64_t k_split, int tiles_m,
                  int tiles_n, int splits, Epi epi) {
+  static_assert(TILED || !ATR, "transposed A comes in the tiled layout");
   __shared__ __attribute__((aligned(1024))) char lds[BF_LDS];
   const TileCoord tc = TILED ? map_tile_blocks(tiles_m, tiles_n, splits, BF_BM, BF_BN)
                               : map_tile(tiles_m, tiles_n, splits, BF_BM, BF_BN);
@@ -454,6 +466,10 @@ gemm_bf16_kernel(const bf16_t* __restrict__ A, int64_t lda, const bf16_t* __rest
   const int nk = (int)ceil_div(max<int64_t>(ke - kb, 0), BF_BK);
   i32x4 rsa, rsb;
   int offa[2], offb[2], kc[2];
+  // ATR: the A blocks of this tile's columns that exist (the rest read zero).
+  const int64_t a_blk0 = tc.m0 / TILE_K;
+  const uint32_t a_bytes =
+      ATR ? (uint32_t)(min<int64_t>(BF_BM / TILE_K, lda - a_blk0) * TILE_BLOCK_BYTES) : 0u;
   if constexpr (TILED) {
     // Panel of this tile: blocks [m0/256 * lda + kb/32, ...), 16 KB each.
     const int64_t ba = (tc.m0 / BF_BM) * lda + kb / BF_BK;
@@ -464,6 +480,11 @@ gemm_bf16_kernel(const bf16_t* __restrict__ A, int64_t lda, const bf16_t* __rest
     for (int i = 0; i < 2; ++i) {
       offa[i] = offb[i] = ((wave * 2 + i) * 64 + lane) * 16;
       kc[i] = 0;
+      if constexpr (ATR) {
+        // wave instruction q copies half q & 1 (16 rows) of piece q >> 1
+        const int q = wave * 2 + i;
+        offa[i] = (q >> 1) * TILE_BLOCK_BYTES + ((q & 1) * 16 + (lane >> 2)) * 64 + (lane & 3) * 16;
+      }
     }
   } else {
     const int64_t rows_a = min<int64_t>(M - tc.m0, BF_BM), rows_b = min<int64_t>(N - tc.n0, BF_BN);
@@ -487,7 +508,14 @@ gemm_bf16_kernel(const bf16_t* __restrict__ A, int64_t lda, const bf16_t* __rest
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
       int oa, ob;
-      if constexpr (TILED) {
+      i32x4 ra = rsa;
+      if constexpr (ATR) {
+        // rows 32 ks .. of panel ks / 8 (ks = the stage's 32-row group of A^T)
+        const int64_t ks = kb / BF_BK + kt;
+        ra = make_rsrc(A + ((ks >> 3) * lda + a_blk0) * (TILE_BLOCK_BYTES / 2), a_bytes);
+        oa = offa[i] + (int)(ks & 7) * (TILE_ROWS / 8 * TILE_K * 2);
+        ob = offb[i] + kt * TILE_BLOCK_BYTES;
+      } else if constexpr (TILED) {
         oa = offa[i] + kt * TILE_BLOCK_BYTES;
         ob = offb[i] + kt * TILE_BLOCK_BYTES;
       } else {
@@ -496,7 +524,7 @@ gemm_bf16_kernel(const bf16_t* __restrict__ A, int64_t lda, const bf16_t* __rest
         oa = kok ? offa[i] + 2 * k0 : OOB;
         ob = kok ? offb[i] + 2 * k0 : OOB;
       }
-      load_lds16(rsa, sa + (uint32_t)((wave * 2 + i) * 1024), oa);
+      load_lds16(ra, sa + (uint32_t)((wave * 2 + i) * 1024), oa);
       load_lds16(rsb, sb + (uint32_t)((wave * 2 + i) * 1024), ob);
     }
   };
@@ -511,6 +539,34 @@ gemm_bf16_kernel(const bf16_t* __restrict__ A, int64_t lda, const bf16_t* __rest
     row = wn * 64 + (lane & 15);
     fb0 = BF_STAGE_A + row * 64 + 16 * (ch ^ tile_swz(row));
   }
+  // ATR: transposed-read offsets ftr[half][second] inside a piece; row
+  // block i of the wave is piece 4 wm + i / 2, half i & 1.
+  int ftr[2][2] = {{0, 0}, {0, 0}};
+  if constexpr (ATR) {
+    const int g = lane >> 4, j = lane & 15;
+#pragma unroll
+    for (int h = 0; h < 2; ++h)
+#pragma unroll
+      for (int sec = 0; sec < 2; ++sec) {
+        const int r = 8 * g + 4 * sec + (j >> 2);
+        const int c = 2 * h + ((j & 3) >> 1);
+        ftr[h][sec] = r * 64 + ((c ^ tile_swz(r)) << 4) + 8 * (j & 1);
+      }
+  }
+  auto read_a = [&](const char* sn, int i) -> bf16x8 {
+    if constexpr (ATR) {
+      typedef short v4s __attribute__((ext_vector_type(4)));
+      typedef v4s __attribute__((address_space(3))) * lds_v4s;
+      const char* pc = sn + (4 * wm + (i >> 1)) * (BF_STAGE_A / 8);
+      const v4s lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s)(pc + ftr[i & 1][0]));
+      const v4s hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s)(pc + ftr[i & 1][1]));
+      typedef short v8s __attribute__((ext_vector_type(8)));
+      const v8s v = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+      return __builtin_bit_cast(bf16x8, v);
+    } else {
+      return *reinterpret_cast<const bf16x8*>(sn + fa0 + 1024 * i);
+    }
+  };
 
   f32x4 acc[8][4];
 #pragma unroll
@@ -529,7 +585,7 @@ gemm_bf16_kernel(const bf16_t* __restrict__ A, int64_t lda, const bf16_t* __rest
     if (BF_ST - 1 < nk) issue(BF_ST - 1);
     bf16x8 ca[8], cb[4];
 #pragma unroll
-    for (int i = 0; i < 8; ++i) ca[i] = *reinterpret_cast<const bf16x8*>(lds + fa0 + 1024 * i);
+    for (int i = 0; i < 8; ++i) ca[i] = read_a(lds, i);
 #pragma unroll
     for (int j = 0; j < 4; ++j) cb[j] = *reinterpret_cast<const bf16x8*>(lds + fb0 + 1024 * j);
     for (int kt = 0; kt < nk; ++kt) {
@@ -547,7 +603,7 @@ gemm_bf16_kernel(const bf16_t* __restrict__ A, int64_t lda, const bf16_t* __rest
         if (kt + BF_ST < nk) issue(kt + BF_ST);  // into the buffer of stage kt
         const char* sn = lds + ((kt + 1) % BF_ST) * BF_STAGE;
 #pragma unroll
-        for (int i = 0; i < 8; ++i) na[i] = *reinterpret_cast<const bf16x8*>(sn + fa0 + 1024 * i);
+        for (int i = 0; i < 8; ++i) na[i] = read_a(sn, i);
 #pragma unroll
         for (int j = 0; j < 4; ++j) nb[j] = *reinterpret_cast<const bf16x8*>(sn + fb0 + 1024 * j);
       }
@@ -886,7 +942,7 @@ __global__ void __launch_bounds__(NT) gemm_f32_kernel(const float* __restrict__ 
   epi.template apply<Acc32, MB, NB, F_BM, F_BN>(acc, ctx);
 }
 
-template <bool TILED, class Epi>
+template <bool TILED, class Epi, bool ATR = false>
 hipError_t launch_bf16(const bf16_t* A, int64_t lda, const bf16_t* B, int64_t ldb, int64_t M,
                        int64_t N, int64_t K, int splits, int64_t k_split, const Epi& epi,
                        hipStream_t s) {
@@ -898,7 +954,8 @@ hipError_t launch_bf16(const bf16_t* A, int64_t lda, const bf16_t* B, int64_t ld
   const int64_t panel = TILED ? ceil_div(k_split, BF_BK) * TILE_BLOCK_BYTES
                               : (int64_t)BF_BM * std::max(lda, ldb) * 2;
   if (panel >= ((int64_t)1 << 31)) return hipErrorInvalidValue;
-  hipLaunchKernelGGL((gemm_bf16_kernel<TILED, Epi>), dim3((unsigned)round_up(total, 8)),
+  if (ATR && (splits > 1 || ceil_div(M, TILE_K) > lda)) return hipErrorInvalidValue;
+  hipLaunchKernelGGL((gemm_bf16_kernel<TILED, Epi, ATR>), dim3((unsigned)round_up(total, 8)),
                      dim3(BF_NT), 0, s, A, lda, B, ldb, M, N, K, k_split, (int)tm, (int)tn, splits,
                      epi);
   return hipGetLastError();
@@ -1007,9 +1064,10 @@ hipError_t gemm_dw(int dtype, const void* A, int64_t lda, const void* B, int64_t
   if (ldc >= ((int64_t)1 << 21)) return hipErrorInvalidValue;
   const int bk = gemm_k_tile(dtype);
   auto run = [&](auto e) {
-    if (dtype == RL_DTYPE_BF16)  // tiled operands
-      return launch_bf16<true>(static_cast<const bf16_t*>(A), lda, static_cast<const bf16_t*>(B),
-                               ldb, M, N, K, 1, round_up(K, bk), e, s);
+    if (dtype == RL_DTYPE_BF16)  // tiled operands, A given as G (transposed reads)
+      return launch_bf16<true, decltype(e), true>(static_cast<const bf16_t*>(A), lda,
+                                                  static_cast<const bf16_t*>(B), ldb, M, N, K, 1,
+                                                  round_up(K, bk), e, s);
     return launch_f32(static_cast<const float*>(A), lda, static_cast<const float*>(B), ldb, M, N,
                       K, 1, round_up(K, bk), e, s);
   };

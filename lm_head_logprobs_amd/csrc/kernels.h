@@ -30,7 +30,9 @@ hipError_t gemm_store(int dtype, const void* A, int64_t lda, const void* B, int6
                       int64_t M, int64_t N, int64_t K, int splits, int64_t k_split, float* C,
                       int64_t ldc, int64_t split_stride, hipStream_t s);
 
-// dW (=|+=) A B^T in fp32.
+// dW (=|+=) A B^T in fp32.  bf16: A is given as A^T = G [K rows, M cols] in
+// the tiled layout (lda = its blocks per 256-row panel) and read transposed;
+// B^T tiled.  fp32: A and B row-major.
 hipError_t gemm_dw(int dtype, const void* A, int64_t lda, const void* B, int64_t ldb, int64_t M,
                    int64_t N, int64_t K, float* C, int64_t ldc, int accumulate, hipStream_t s);
 
