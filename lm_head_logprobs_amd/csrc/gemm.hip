@@ -560,9 +560,7 @@ gemm_bf16_kernel(const bf16_t* __restrict__ A, int64_t lda, const bf16_t* __rest
       const char* pc = sn + (4 * wm + (i >> 1)) * (BF_STAGE_A / 8);
       const v4s lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s)(pc + ftr[i & 1][0]));
       const v4s hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s)(pc + ftr[i & 1][1]));
-      typedef short v8s __attribute__((ext_vector_type(8)));
-      const v8s v = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-      return __builtin_bit_cast(bf16x8, v);
+      return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
     } else {
       return *reinterpret_cast<const bf16x8*>(sn + fa0 + 1024 * i);
     }
