@@ -84,6 +84,90 @@ __global__ void __launch_bounds__(NT) transpose_kernel(const T* __restrict__ src
   }
 }
 
+// Label and support logits (before 1/tau) of every gradient entry (labels,
+// then the CSR entries), computed in the vocabulary-sorted order of
+// csc_build.  Entries of one id are adjacent there, so the id's W row comes
+// from HBM once and then from cache; the token rows h_t that each entry
+// gathers are a few tens of MB and stay in the Infinity Cache.  (Gathering W
+// rows per token instead reads 2H bytes of W per entry, most of them from
+// HBM.)  One wave per 64 sorted entries, 16 at a time: each lane keeps 16
+// partial dot products and a transposing lane-swap butterfly reduces them in
+// a fixed order.  An id outside [0, V) gives NaN.
+template <typename T>
+__global__ void __launch_bounds__(NT) entry_logits_kernel(
+    const T* __restrict__ h, const T* __restrict__ W, int64_t H, int64_t V,
+    const int32_t* __restrict__ skeys, const int32_t* __restrict__ perm,
+    const int32_t* __restrict__ row_of, int64_t N, int64_t E, float* __restrict__ z) {
+  constexpr int VEC = Elem<T>::VEC, G = 16;
+  const int lane = threadIdx.x & 63;
+  const int64_t base = ((int64_t)blockIdx.x * (NT / 64) + (threadIdx.x >> 6)) * 64;
+  const int r = lane >> 4;
+  const int off = ((r & 1) << 1) | (r >> 1);  // row r of the butterfly holds entry 4 j + off
+#pragma unroll 1
+  for (int g = 0; g < 64 / G; ++g) {
+    const int64_t i0 = base + G * g;
+    if (i0 >= E) break;
+    const T* wr[G];
+    const T* hr[G];
+    bool ok[G];
+#pragma unroll
+    for (int k = 0; k < G; ++k) {
+      const int64_t i = i0 + k;
+      const bool in = i < E;
+      const int32_t key = in ? skeys[i] : -1;
+      const int32_t e = in ? perm[i] : 0;
+      // (a support entry before the first CSR row, possible only with bad
+      // offsets, has row -1)
+      const int64_t t = e < N ? e : row_of[e - N];
+      const bool t_ok = t >= 0 && t < N;
+      ok[k] = key >= 0 && key < V && t_ok;
+      wr[k] = W + (ok[k] ? (int64_t)key : 0) * H;  // valid rows; the product is discarded
+      hr[k] = h + (in && t_ok ? t : 0) * H;
+    }
+    float f[G];
+#pragma unroll
+    for (int k = 0; k < G; ++k) f[k] = 0.0f;
+    for (int64_t c = (int64_t)lane * VEC; c < H; c += 64 * VEC) {
+#pragma unroll
+      for (int k = 0; k < G; ++k) {
+        const u32x4 a = *reinterpret_cast<const u32x4*>(wr[k] + c);
+        const u32x4 b = *reinterpret_cast<const u32x4*>(hr[k] + c);
+        float fa[VEC], fb[VEC];
+        Elem<T>::unpack(a, fa);
+        Elem<T>::unpack(b, fb);
+#pragma unroll
+        for (int q = 0; q < VEC; ++q) f[k] = fmaf(fa[q], fb[q], f[k]);
+      }
+    }
+    // permlane32_swap pairs, then permlane16_swap pairs, then a row scan:
+    // lane 15 of row r holds the total of entry 4 j + off.
+    float gsum[G / 2];
+#pragma unroll
+    for (int k = 0; k < G / 2; ++k) {
+      const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(f[2 * k]),
+                                                       __float_as_uint(f[2 * k + 1]), false, false);
+      gsum[k] = __uint_as_float(sw[0]) + __uint_as_float(sw[1]);
+    }
+#pragma unroll
+    for (int j = 0; j < G / 4; ++j) {
+      const auto sw = __builtin_amdgcn_permlane16_swap(__float_as_uint(gsum[2 * j]),
+                                                       __float_as_uint(gsum[2 * j + 1]), false,
+                                                       false);
+      float v = __uint_as_float(sw[0]) + __uint_as_float(sw[1]);
+      v = dpp_add<0x111, 0xf>(v);  // row_shr:1
+      v = dpp_add<0x112, 0xf>(v);  // row_shr:2
+      v = dpp_add<0x114, 0xf>(v);  // row_shr:4
+      v = dpp_add<0x118, 0xf>(v);  // row_shr:8
+      const int k = 4 * j + off;
+      // ok[k] with a lane-dependent k: select it without dynamic register indexing
+      bool okk = false;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) okk = (off == q) ? ok[4 * j + q] : okk;
+      if ((lane & 15) == 15 && i0 + k < E) z[perm[i0 + k]] = okk ? v : NAN;
+    }
+  }
+}
+
 template <typename T>
 __global__ void __launch_bounds__(NT) combine_kernel(CombineArgs a) {
   __shared__ float sh[8];
@@ -118,8 +202,13 @@ __global__ void __launch_bounds__(NT) combine_kernel(CombineArgs a) {
   // yields NaN (such inputs are reported by the validation call).
   const int32_t lab = a.labels[t];
   const bool lab_ok = lab >= 0 && lab < a.V;
-  float za = a.inv_t * block_sum(lab_ok ? dot_row_part<T>(h, W + (int64_t)lab * a.H, a.H, tid, NT)
-                                        : 0.0f, sh);
+  float za;
+  if (a.zent != nullptr) {
+    za = a.inv_t * a.zent[t];
+  } else {
+    za = a.inv_t * block_sum(lab_ok ? dot_row_part<T>(h, W + (int64_t)lab * a.H, a.H, tid, NT)
+                                    : 0.0f, sh);
+  }
   if (!lab_ok) za = NAN;
   const float lp = za - lse;
   const float lq = a.infer_lp[t];
@@ -141,6 +230,33 @@ __global__ void __launch_bounds__(NT) combine_kernel(CombineArgs a) {
     // send a read out of bounds.
     e0 = min(max(a.off[t], (int64_t)0), a.nnz);
     e1 = min(max(a.off[t + 1], e0), a.nnz);
+  }
+  if (a.off != nullptr && a.zent != nullptr) {
+    // entry logits precomputed (entry_logits_kernel): one entry per lane
+    for (int64_t eb = e0 + tid - lane; eb < e1; eb += NT) {
+      const int64_t e = eb + lane;
+      if (e < e1) {
+        const float lpe = a.inv_t * a.zent[a.N + e] - lse;
+        const float ue = a.u[e];
+        const float lqe = a.logq != nullptr ? a.logq[e] : logf(ue);
+        bool ke;
+        const float we = rl_weight(lpe, lqe, a.wp, &ke);
+        const float ce = ue * we;
+        sc += ce;
+        cent += ce * lpe;
+        su += ue;
+        kl += ue * (lqe - lpe);
+        sm += ue * __expf(lpe - lqe);
+        a.coef[a.N + e] = (s * ce - beta * ue) * a.inv_t * a.inv_D;
+        if (a.o_support_lp != nullptr) a.o_support_lp[e] = lpe;
+      }
+    }
+    sc = wave_sum(sc);
+    cent = wave_sum(cent);
+    su = wave_sum(su);
+    kl = wave_sum(kl);
+    sm = wave_sum(sm);
+  } else if (a.off != nullptr) {
     // Wave w takes entries w, w + 4, ... in order; four of them per step so
     // that their row loads are in flight together (the order of every sum is
     // unchanged).
@@ -611,6 +727,22 @@ hipError_t transpose_pad(int dtype, const void* src, int64_t ld_src, int64_t R, 
     hipLaunchKernelGGL(transpose_kernel<float>, grid, dim3(NT), 0, s,
                        static_cast<const float*>(src), ld_src, R, C, static_cast<float*>(dst),
                        Rpad);
+  return hipGetLastError();
+}
+
+hipError_t entry_logits(int dtype, const void* h, const void* W, int64_t H, int64_t V,
+                        const int32_t* skeys, const int32_t* perm, const int32_t* row_of,
+                        int64_t N, int64_t E, float* z, hipStream_t s) {
+  if (E <= 0) return hipSuccess;
+  const dim3 grid((unsigned)ceil_div(E, (int64_t)(NT / 64) * 64));
+  if (dtype == RL_DTYPE_BF16)
+    hipLaunchKernelGGL(entry_logits_kernel<bf16_t>, grid, dim3(NT), 0, s,
+                       static_cast<const bf16_t*>(h), static_cast<const bf16_t*>(W), H, V, skeys,
+                       perm, row_of, N, E, z);
+  else
+    hipLaunchKernelGGL(entry_logits_kernel<float>, grid, dim3(NT), 0, s,
+                       static_cast<const float*>(h), static_cast<const float*>(W), H, V, skeys,
+                       perm, row_of, N, E, z);
   return hipGetLastError();
 }
 

@@ -91,6 +91,8 @@ struct CombineArgs {
   int64_t t0, Tc, N, H, V, J, nnz;
   WeightParams wp;
   float adv_tau, beta, inv_t, inv_D;
+  const float* zent;   // [N + nnz] label then support logits (before 1/tau), or null:
+                       // then combine forms them as dot products itself
   const int32_t* age;  // [N] policy age or null (all 0)
   int staleness;       // rl_kl_staleness: beta_t = beta / sqrt(1 + age_t) when inv_sqrt
   float gamma;         // entropy bonus coefficient
@@ -110,6 +112,14 @@ constexpr int STAT_LOSS = 0, STAT_MASKED = 1, STAT_SMASS = 2, STAT_HAS_SUPPORT =
               STAT_TVFAIL = 4, STAT_KL = 5, STAT_ABS_KAPPA = 6, STAT_ENTROPY = 7, STAT_BETA = 8,
               STAT_KL_AGE0 = 9, STAT_AGE0 = 10, STAT_N = 11;
 hipError_t combine(int dtype, const CombineArgs& a, hipStream_t s);
+
+// z[e] = h[token(e)] . W[id(e)] for the N + nnz gradient entries (labels
+// first, then support entries; token(e) = e for labels, row_of[e - N] after),
+// computed in the vocabulary-sorted order (skeys / perm of csc_build).  h is
+// the whole batch [N, H].  NaN for an id outside [0, V).
+hipError_t entry_logits(int dtype, const void* h, const void* W, int64_t H, int64_t V,
+                        const int32_t* skeys, const int32_t* perm, const int32_t* row_of,
+                        int64_t N, int64_t E, float* z, hipStream_t s);
 
 // G (in place over P, if write_g) and Gt from P = exp(z - m_tile):
 // g[t, v] = exp(m - lse[t]) * P[t, v] * (kappa_s[t] + gs * (m + log P[t, v])),
