@@ -199,6 +199,16 @@ template <typename T, bool FULL_, bool STORE_> struct FwdEpi {
       mx = L::col_max(mx);
       red[c.wave_m * BN + c.wn_off + L::col(j, c.lane)] = mx;
     }
+    // The exponent pass reads the accumulators again from AGPRs: without this
+    // the compiler keeps the max pass's VGPR copies alive across the barrier,
+    // spills other values, and the spill reloads wait for every outstanding
+    // memory operation (the next tile's operand loads, this tile's stores).
+    if constexpr (std::is_same<L, Acc16>::value) {
+#pragma unroll
+      for (int i = 0; i < MB; ++i)
+#pragma unroll
+        for (int j = 0; j < NB; ++j) __asm__ volatile("" : "+a"(acc[i][j]));
+    }
     __syncthreads();
 #pragma unroll
     for (int j = 0; j < NB; ++j) {
