@@ -470,8 +470,8 @@ rl_status rl_loss_fwd_bwd(const void* h, const void* W, const int32_t* labels,
     if (p.tiled) {
       // G in place only: dh reads it as is, dW with transposed LDS reads.
       RL_TRY(timed(K_FORM_G, s, [&] {
-        return form_g_blocks(static_cast<bf16_t*>(G), p.KB_v, 1, nullptr, p.KB_t, pm, p.J,
-                             p.vtile, lse + c0, kap + c0, gs, p.V, tc, s);
+        return form_g_blocks(static_cast<bf16_t*>(G), p.KB_v, pm, p.J, p.vtile, lse + c0,
+                             kap + c0, gs, p.V, tc, s);
       }));
       RL_TRY(timed(K_FOLD, s, [&] {
         return fold_sparse(p.dtype, G, 1, nullptr, 1, p.KB_v, p.KB_t, labels, skeys, perm, rows,

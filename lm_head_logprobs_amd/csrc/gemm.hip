@@ -5,7 +5,8 @@
 // operands are laid out K-contiguous:
 //   forward   S^T[V,Tc]  = W[V,H]      . h_c[Tc,H]^T       (K = H)
 //   dh        dh[Tc,H]   = G[Tc,V]     . (W^T)[H,V]^T      (K = V, split-K)
-//   dW        dW[V,H]    = G^T[V,Tc]   . (h_c^T)[H,Tc]^T   (K = Tc)
+//   dW        dW[V,H]    = G^T[V,Tc]   . (h_c^T)[H,Tc]^T   (K = Tc; G^T read from
+//                                                            G's layout, see ATR)
 // Accumulation is fp32.  The epilogues are written against an accumulator
 // layout (Acc16 / Acc32 below) that maps lane and register to row and column.
 //
@@ -33,8 +34,7 @@
 // round-robin over the 8 XCDs).  The forward GEMM groups 8 tiles along M;
 // the backward GEMMs walk blocks of 4 x 8 tiles with N fastest, so the 32
 // tiles an XCD runs at once cover at most 8 N-tiles and each slice of the
-// large operand (G or G^T) is fetched into that XCD's L2 once for all of
-// them.
+// large operand (G) is fetched into that XCD's L2 once for all of them.
 //
 // fp32 kernel (small problems).  Same tile mapping and epilogues, register
 // staged loads, v_mfma_f32_32x32x2_f32 (layout Acc32).

@@ -444,66 +444,57 @@ __global__ void __launch_bounds__(NT) to_tiled_t_kernel(const bf16_t* __restrict
 }
 
 // Dense-gradient pass over the tiled layout (bf16).  The forward GEMM left
-// e^(z - m_j) in G's tiled blocks; each workgroup takes one 16 KB block
-// (256 tokens x 32 vocabulary entries, one vocabulary tile j), scales every
-// element by kappa_t e^(m_tj - LSE_t) (with the entropy bonus, by
+// e^(z - m_j) in G's tiled blocks (256 tokens x 32 vocabulary entries, each
+// inside one vocabulary tile j).  Every element is scaled in place by
+// kappa_t e^(m_tj - LSE_t) (with the entropy bonus, by
 // e^(m_tj - LSE_t) (kappa_t + gs (m_tj + log x)), kappa_t holding the rest of
-// that term) (zero past Tc and V), writes it back in
-// place when G is wanted, and writes its transpose as eight 2 KB pieces of
-// the Gt blocks (rows = vocabulary, K = tokens) through an LDS transpose.
+// that term), zero past Tc and V.  Both backward GEMMs read this one copy
+// (dW through transposing LDS reads).  A workgroup takes NBLK consecutive
+// blocks of one token panel and issues all their loads first (NBLK = 4: 8%
+// faster than one block per workgroup, measured at the 16k shape).
+template <int NBLK>
 __global__ void __launch_bounds__(NT) form_g_blocks_kernel(
-    bf16_t* __restrict__ G, int64_t KB_g, int write_g, bf16_t* __restrict__ Gt, int64_t KB_gt,
-    const float* __restrict__ part_m, int64_t J, int vtile, const float* __restrict__ lse,
-    const float* __restrict__ kap, float gs, int64_t V, int64_t Tc) {
-  constexpr int PITCH = TILE_ROWS + 8;                                   // 528 bytes
-  __shared__ __attribute__((aligned(16))) bf16_t tt[TILE_K][PITCH];  // [vocab][token]
-  const int64_t tp = blockIdx.x, kb = blockIdx.y;
-  bf16_t* blk = G + (tp * KB_g + kb) * (TILE_ROWS * TILE_K);
-  const int64_t jt = kb * TILE_K / vtile;
+    bf16_t* __restrict__ G, int64_t KB_g, const float* __restrict__ part_m, int64_t J, int vtile,
+    const float* __restrict__ lse, const float* __restrict__ kap, float gs, int64_t V,
+    int64_t Tc) {
+  const int64_t tp = blockIdx.x, kb0 = (int64_t)blockIdx.y * NBLK;
+  bf16_t* blk0 = G + (tp * KB_g + kb0) * (TILE_ROWS * TILE_K);
+  // streaming: each element is read and written once here
+  u32x4 raw[NBLK][4];
+#pragma unroll
+  for (int b = 0; b < NBLK; ++b)
+#pragma unroll
+    for (int q = 0; q < 4; ++q)
+      raw[b][q] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(
+          blk0 + b * (TILE_ROWS * TILE_K) + (threadIdx.x + NT * q) * 8));
 #pragma unroll
   for (int q = 0; q < 4; ++q) {
-    const int p = threadIdx.x + NT * q;  // 16-byte chunk of the block
+    const int p = threadIdx.x + NT * q;  // 16-byte chunk of a block
     const int r = p >> 2, lc = (p & 3) ^ tile_swz(r);
-    const int64_t t = tp * TILE_ROWS + r, v = kb * TILE_K + lc * 8;
-    const float m = t < Tc ? part_m[t * J + jt] : 0.0f;
-    const float e = t < Tc ? __expf(m - lse[t]) : 0.0f;
-    const float sc = t < Tc ? kap[t] * e : 0.0f;
-    float x[8];
-    // streaming: each element is read and written once here
-    Elem<bf16_t>::unpack(__builtin_nontemporal_load(reinterpret_cast<const u32x4*>(blk + p * 8)),
-                         x);
-    if (gs != 0.0f) {
-      // entropy bonus: x (sc + sb (m + log x)), 0 where x underflowed
-      const float sb = gs * e;
+    const int64_t t = tp * TILE_ROWS + r;
+    const bool tok = t < Tc;
+    const float l = tok ? lse[t] : 0.0f, kt = tok ? kap[t] : 0.0f;
 #pragma unroll
-      for (int k = 0; k < 8; ++k)
-        x[k] = (v + k < V && x[k] > 0.0f) ? x[k] * (sc + sb * (m + __logf(x[k]))) : 0.0f;
-    } else {
+    for (int b = 0; b < NBLK; ++b) {
+      const int64_t kb = kb0 + b, v = kb * TILE_K + lc * 8;
+      const float m = tok ? part_m[t * J + kb * TILE_K / vtile] : 0.0f;
+      const float e = tok ? __expf(m - l) : 0.0f;
+      const float sc = kt * e;
+      float x[8];
+      Elem<bf16_t>::unpack(raw[b][q], x);
+      if (gs != 0.0f) {
+        // entropy bonus: x (sc + sb (m + log x)), 0 where x underflowed
+        const float sb = gs * e;
 #pragma unroll
-      for (int k = 0; k < 8; ++k) x[k] = (v + k < V) ? sc * x[k] : 0.0f;
+        for (int k = 0; k < 8; ++k)
+          x[k] = (v + k < V && x[k] > 0.0f) ? x[k] * (sc + sb * (m + __logf(x[k]))) : 0.0f;
+      } else {
+#pragma unroll
+        for (int k = 0; k < 8; ++k) x[k] = (v + k < V) ? sc * x[k] : 0.0f;
+      }
+      __builtin_nontemporal_store(Elem<bf16_t>::pack(x),
+                                  reinterpret_cast<u32x4*>(blk0 + b * (TILE_ROWS * TILE_K) + p * 8));
     }
-    const u32x4 out = Elem<bf16_t>::pack(x);
-    if (write_g) __builtin_nontemporal_store(out, reinterpret_cast<u32x4*>(blk + p * 8));
-    if (Gt != nullptr) {
-      const bf16_t* e = reinterpret_cast<const bf16_t*>(&out);
-#pragma unroll
-      for (int k = 0; k < 8; ++k) tt[lc * 8 + k][r] = e[k];
-    }
-  }
-  if (Gt == nullptr) return;
-  __syncthreads();
-  // Piece g covers tokens 32 g .. 32 g + 31 of this panel: rows
-  // (kb * 32) % 256 + rr of Gt block (vocab panel kb / 8, token block 8 tp + g).
-  const int64_t vb = kb * TILE_K / TILE_ROWS, rbase = (kb * TILE_K) % TILE_ROWS;
-#pragma unroll
-  for (int q = 0; q < 4; ++q) {
-    const int p = threadIdx.x + NT * q;
-    const int g = p >> 7, rr = (p >> 2) & 31, pc = p & 3;
-    const int64_t row = rbase + rr;
-    const int lc = pc ^ tile_swz(row);
-    const u32x4 val = *reinterpret_cast<const u32x4*>(&tt[rr][g * 32 + lc * 8]);
-    bf16_t* dst = Gt + ((vb * KB_gt + tp * 8 + g) * (TILE_ROWS * TILE_K)) + row * TILE_K + pc * 8;
-    __builtin_nontemporal_store(val, reinterpret_cast<u32x4*>(dst));
   }
 }
 
@@ -777,13 +768,17 @@ hipError_t to_tiled_t(const bf16_t* src, int64_t ld_src, int64_t S, int64_t C, b
   return hipGetLastError();
 }
 
-hipError_t form_g_blocks(bf16_t* G, int64_t KB_g, int write_g, bf16_t* Gt, int64_t KB_gt,
-                         const float* part_m, int64_t J, int vtile, const float* lse_c,
-                         const float* kappa_c, float gs, int64_t V, int64_t Tc, hipStream_t s) {
+hipError_t form_g_blocks(bf16_t* G, int64_t KB_g, const float* part_m, int64_t J, int vtile,
+                         const float* lse_c, const float* kappa_c, float gs, int64_t V,
+                         int64_t Tc, hipStream_t s) {
   if (Tc <= 0) return hipSuccess;
-  const dim3 grid((unsigned)ceil_div(Tc, TILE_ROWS), (unsigned)KB_g);
-  hipLaunchKernelGGL(form_g_blocks_kernel, grid, dim3(NT), 0, s, G, KB_g, write_g, Gt, KB_gt,
-                     part_m, J, vtile, lse_c, kappa_c, gs, V, Tc);
+  const unsigned panels = (unsigned)ceil_div(Tc, TILE_ROWS);
+  if (KB_g % 4 == 0)
+    hipLaunchKernelGGL(form_g_blocks_kernel<4>, dim3(panels, (unsigned)(KB_g / 4)), dim3(NT), 0,
+                       s, G, KB_g, part_m, J, vtile, lse_c, kappa_c, gs, V, Tc);
+  else
+    hipLaunchKernelGGL(form_g_blocks_kernel<1>, dim3(panels, (unsigned)KB_g), dim3(NT), 0, s, G,
+                       KB_g, part_m, J, vtile, lse_c, kappa_c, gs, V, Tc);
   return hipGetLastError();
 }
 

@@ -65,12 +65,11 @@ hipError_t to_tiled_t(const bf16_t* src, int64_t ld_src, int64_t S, int64_t C, b
 
 // bf16 dense gradient in the tiled layout: G holds e^(z - m) as left by the
 // forward GEMM (KB_g blocks per 256-token panel, panels covering Tc); every
-// element becomes kappa_t e^(m_tj - LSE_t) e^(z - m_tj) (zero past Tc and V),
-// written back in place when write_g, and transposed into Gt (rows =
-// vocabulary, KB_gt blocks of 32 tokens per panel) when Gt is not null.
-hipError_t form_g_blocks(bf16_t* G, int64_t KB_g, int write_g, bf16_t* Gt, int64_t KB_gt,
-                         const float* part_m, int64_t J, int vtile, const float* lse_c,
-                         const float* kappa_c, float gs, int64_t V, int64_t Tc, hipStream_t s);
+// element becomes kappa_t e^(m_tj - LSE_t) e^(z - m_tj) (with the entropy
+// bonus as in form_g below), zero past Tc and V, in place.
+hipError_t form_g_blocks(bf16_t* G, int64_t KB_g, const float* part_m, int64_t J, int vtile,
+                         const float* lse_c, const float* kappa_c, float gs, int64_t V,
+                         int64_t Tc, hipStream_t s);
 
 // dst[c][r] = src[r][c] for r < R, 0 for R <= r < Rpad; c < C.
 hipError_t transpose_pad(int dtype, const void* src, int64_t ld_src, int64_t R, int64_t C,
