@@ -178,6 +178,34 @@ def test_empty_support_rows_and_duplicates():
     compare_all(wl, got, ref)
 
 
+def test_invalid_ids_give_nan_only_where_used():
+    """Ids outside [0, V) are reported by the validation call; the head itself
+    must not read through them.  The tokens that use one get NaN; every other
+    token's per-token outputs and dh row are bit-identical to the clean run
+    (the label / support logits are formed per entry and G row by row)."""
+    wl = _case("c4_head16k_ipo_topp_replay", N=64, V=900)
+    V = wl.W.shape[0]
+    _, clean = run_head(wl)
+    off = wl.offsets.cpu().numpy()
+    sizes = off[1:] - off[:-1]
+    t_lab = 3
+    t_low, t_high = [int(t) for t in np.nonzero(sizes >= 2)[0] if t != t_lab][:2]
+    e_low, e_high = int(off[t_low]), int(off[t_high]) + 1
+    wl.labels[t_lab] = V + 7
+    wl.ids[e_low] = -2
+    wl.ids[e_high] = V
+    _, got = run_head(wl)
+    bad = [t_lab, t_low, t_high]
+    good = np.setdiff1d(np.arange(wl.N), bad)
+    assert np.isnan(got["logprobs"][t_lab])
+    assert np.all(np.isnan(got["token_loss"][bad]))
+    assert np.isnan(got["support_logprobs"][e_low]) and np.isnan(got["support_logprobs"][e_high])
+    for k in ("logprobs", "entropy", "token_loss", "weight"):
+        assert np.array_equal(got[k][good], clean[k][good]), k
+    assert np.array_equal(got["entropy"], clean["entropy"])
+    assert np.array_equal(got["dh"][good], clean["dh"][good])
+
+
 # ---------------------------------------------------------------- full size --
 
 def _sample(n, k, seed):
