@@ -688,15 +688,17 @@ __global__ void __launch_bounds__(1024) reduce_final_kernel(const float* __restr
   }
 }
 
+// One wave per row; its lanes write the row's entries (coalesced).
 __global__ void csr_rows_kernel(const int64_t* __restrict__ off, int64_t N, int64_t nnz,
                                 int32_t* __restrict__ row_of) {
-  const int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  const int64_t t = (int64_t)blockIdx.x * (blockDim.x / 64) + (threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
   if (t >= N) return;
   if (t == 0)  // entries before the first row keep a marker no bucket reads
-    for (int64_t e = 0; e < min(max(off[0], (int64_t)0), nnz); ++e) row_of[e] = -1;
+    for (int64_t e = lane; e < min(max(off[0], (int64_t)0), nnz); e += 64) row_of[e] = -1;
   const int64_t e0 = min(max(off[t], (int64_t)0), nnz);
   const int64_t e1 = min(max(off[t + 1], e0), nnz);
-  for (int64_t e = e0; e < e1; ++e) row_of[e] = (int32_t)t;
+  for (int64_t e = e0 + lane; e < e1; e += 64) row_of[e] = (int32_t)t;
 }
 
 __global__ void fill_f32_kernel(float* p, int64_t n, float v) {
@@ -832,7 +834,7 @@ hipError_t reduce_final(const float* stats, int64_t N, float inv_D, float beta, 
 }
 
 hipError_t csr_rows(const int64_t* off, int64_t N, int64_t nnz, int32_t* row_of, hipStream_t s) {
-  hipLaunchKernelGGL(csr_rows_kernel, dim3((unsigned)ceil_div(N, 256)), dim3(256), 0, s, off, N,
+  hipLaunchKernelGGL(csr_rows_kernel, dim3((unsigned)ceil_div(N, 4)), dim3(256), 0, s, off, N,
                      nnz, row_of);
   return hipGetLastError();
 }
