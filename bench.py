@@ -272,6 +272,59 @@ def event_overhead(torch, steps):
     return tot / steps
 
 
+def graph_per_call_ms(torch, calls, steps):
+    """Launch-overhead-free time per call: the calls (one step each, on their
+    own input copies) are captured once into a HIP graph, which is replayed
+    until about `steps` calls ran.  Before timing, every replay's outputs are
+    checked bit for bit against an eager run of the same calls, with eager
+    work and synchronisations between the replays.  Returns (ms per call, or
+    None if a replay disagreed)."""
+    outs = [list(c.o.values()) for c in calls]
+
+    def snapshot():
+        return [[t.clone() for t in o] for o in outs]
+
+    for c in calls:
+        c()
+    torch.cuda.synchronize()
+    eager = snapshot()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        for c in calls:
+            c()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for c in calls:
+            c()
+    ok = True
+    for _ in range(3):
+        for o in outs:
+            for t in o:
+                t.zero_()
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        got = snapshot()
+        ok = ok and all(torch.equal(a, b) for ea, ga in zip(eager, got) for a, b in zip(ea, ga))
+        calls[0]()  # eager work between the replays
+        torch.cuda.synchronize()
+    if not ok:
+        return None
+    reps = max(1, -(-steps // len(calls)))
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        g.replay()
+    e1.record()
+    torch.cuda.synchronize()
+    del g
+    return e0.elapsed_time(e1) / (reps * len(calls))
+
+
 def replay_16x(torch, L, ops, r, steps):
     """The same pass over 16 N tokens (the replay input repeated 16 times), two
     rotated copies of 1.24 GB: launch and tail costs amortise at this size."""
@@ -309,6 +362,10 @@ def bench_replay(args, torch):
     for i in range(args.warmup):
         copies[i % 16]()
     torch.cuda.synchronize()
+    # step time: the 16 rotated passes captured in a graph (a pass is two
+    # kernels of a few microseconds; eager launches from Python cost more)
+    ms_graph = graph_per_call_ms(torch, copies, args.steps)
+    # per-kernel times: eager launches with the library's event timing
     L.rl_profile_begin()
     e0 = torch.cuda.Event(enable_timing=True)
     e1 = torch.cuda.Event(enable_timing=True)
@@ -318,7 +375,8 @@ def bench_replay(args, torch):
     e1.record()
     torch.cuda.synchronize()
     prof = L.rl_profile_end()
-    ms = e0.elapsed_time(e1) / args.steps
+    ms_eager = e0.elapsed_time(e1) / args.steps
+    ms = ms_graph if ms_graph is not None else ms_eager
     n, tot = prof["elementwise"]
     avg = tot / n
     nf, totf = prof.get("elementwise_final", (1, 0.0))
@@ -330,6 +388,9 @@ def bench_replay(args, torch):
         "warmup": args.warmup, "ms_per_step": ms, "higher_is_better": True, "scaling": "weak",
         "vs_baseline": None, "dtype": "fp32", "data": "synthetic",
         "config": {"workload": "c2_replay", "tokens": r.N},
+        "step_timing": ("hip graph of the 16 rotated passes, replays checked bit for bit against "
+                        "eager runs" if ms_graph is not None else "eager launches"),
+        "eager_ms_per_step_with_kernel_events": ms_eager,
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": PEAK_HBM_GBS, "unit": "GB/s",
                      "frac": achieved / PEAK_HBM_GBS,
                      "traffic": read_traffic("elementwise", "c2_replay"),
@@ -360,6 +421,7 @@ def bench_mis(args, torch):
     for i in range(args.warmup):
         copies[i % 16]()
     torch.cuda.synchronize()
+    ms_graph = graph_per_call_ms(torch, copies, args.steps)
     L.rl_profile_begin()
     e0 = torch.cuda.Event(enable_timing=True)
     e1 = torch.cuda.Event(enable_timing=True)
@@ -369,7 +431,8 @@ def bench_mis(args, torch):
     e1.record()
     torch.cuda.synchronize()
     prof = L.rl_profile_end()
-    ms = e0.elapsed_time(e1) / args.steps
+    ms_eager = e0.elapsed_time(e1) / args.steps
+    ms = ms_graph if ms_graph is not None else ms_eager
     kern = {k: {"launches": n, "avg_ms": t / n} for k, (n, t) in prof.items()}
     tok = kern["mis_token"]["avg_ms"]
     byt = 17.0 * r.N  # reads lp, lq, A; writes the fp32 weight and the uint8 flags
@@ -385,6 +448,9 @@ def bench_mis(args, torch):
                    "tis": f'{params["tis_level"]}/{params["tis_mode"]}',
                    "rs": params["rs_level"] if params["use_rs"] else "off",
                    "veto": params["veto"], "batch_normalize": params["batch_normalize"]},
+        "step_timing": ("hip graph of the 16 rotated passes, replays checked bit for bit against "
+                        "eager runs" if ms_graph is not None else "eager launches"),
+        "eager_ms_per_step_with_kernel_events": ms_eager,
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": PEAK_HBM_GBS, "unit": "GB/s",
                      "frac": achieved / PEAK_HBM_GBS,
                      "traffic": read_traffic("mis_token", "c2_mis"),
