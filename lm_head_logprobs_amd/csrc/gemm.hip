@@ -38,6 +38,7 @@
 //
 // fp32 kernel (small problems).  Same tile mapping and epilogues, register
 // staged loads, v_mfma_f32_32x32x2_f32 (layout Acc32).
+#include <atomic>
 #include <type_traits>
 
 #include "kernels.h"
@@ -969,18 +970,19 @@ hipError_t launch_bf16(const bf16_t* A, int64_t lda, const bf16_t* B, int64_t ld
   return hipGetLastError();
 }
 
-// Compute units of the current device (cached per device).
+// Compute units of the current device (cached per device; calls from
+// several threads may query concurrently and store the same value).
 int cu_count() {
-  static int cached[64] = {0};
+  static std::atomic<int> cached[64];
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 0;
-  if (cached[dev] == 0) {
-    int n = 0;
+  int n = cached[dev].load(std::memory_order_relaxed);
+  if (n == 0) {
     if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
       return 0;
-    cached[dev] = n;
+    cached[dev].store(n, std::memory_order_relaxed);
   }
-  return cached[dev];
+  return n;
 }
 
 // Row-major operands (K = lda = ldb columns), one split: the persistent
