@@ -467,6 +467,56 @@ def bench_mis(args, torch):
     return out, host
 
 
+def measured_peaks(torch):
+    """What the bf16 matrix pipe and HBM deliver on this device with kernels that
+    do nothing else (the library's calibration calls): a register-only MFMA loop
+    at two waves per SIMD, with all-zero and with random operands (operand
+    toggling costs power, so the sustained clock differs), and a grid-stride
+    copy of 1 GiB, out of place and in place.  Reported beside the published
+    peaks, which the roofline fractions use."""
+    from lm_head_logprobs_amd import _lib as L
+
+    dev = torch.device("cuda:0")
+    nb = 2 * torch.cuda.get_device_properties(0).multi_processor_count
+    sink = torch.empty(nb * 256, device=dev, dtype=torch.float32)
+    stamps = torch.zeros(nb * 4, device=dev, dtype=torch.int64)
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    res = {"mfma_blocks": nb, "published_bf16_tflops": PEAK_BF16_TFLOPS,
+           "published_hbm_gbs": PEAK_HBM_GBS}
+    for name, rnd in (("mfma_bf16_zero_operands", False), ("mfma_bf16_random_operands", True)):
+        L.rl_calib_mfma_bf16(rnd, nb, 2000, sink, stamps)
+        e0.record()
+        flop, khz = L.rl_calib_mfma_bf16(rnd, nb, 100000, sink, stamps)
+        e1.record()
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1)
+        st = stamps.view(nb, 4).cpu().double()
+        ghz = float(((st[:, 1] - st[:, 0]) / (st[:, 3] - st[:, 2])).median()) * khz * 1e3 / 1e9
+        tf = flop / (ms * 1e-3) / 1e12
+        res[name] = {"tflops": tf, "frac_of_published": tf / PEAK_BF16_TFLOPS,
+                     "clock_ghz": ghz, "ms": ms}
+    nbytes = 1 << 30
+    src = torch.empty(nbytes // 4, device=dev, dtype=torch.float32)
+    dst = torch.empty_like(src)
+    src.fill_(1.0)
+    for name, d in (("copy", dst), ("copy_in_place", src)):
+        best = None
+        for blocks in (1024, 2048, 4096, 8192):
+            L.rl_calib_copy(src, d, nbytes, blocks)
+            e0.record()
+            for _ in range(5):
+                L.rl_calib_copy(src, d, nbytes, blocks)
+            e1.record()
+            torch.cuda.synchronize()
+            gbs = 2 * nbytes * 5 / (e0.elapsed_time(e1) * 1e-3) / 1e9
+            if best is None or gbs > best["gbs"]:
+                best = {"gbs": gbs, "frac_of_published": gbs / PEAK_HBM_GBS, "blocks": blocks}
+        res[name] = best
+    del src, dst
+    return res
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -485,6 +535,8 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=15.0,
                     help="target length of the oracle CPU baseline sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-peak-check", action="store_true",
+                    help="skip the measured MFMA and copy peaks")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a plain 1 GiB device copy (counter calibration)")
     args = ap.parse_args()
@@ -509,6 +561,8 @@ def main():
         wl, host = None, ("mis", h)
     else:
         out, wl = bench_head(args, torch)
+    if not args.no_peak_check:
+        out["measured_peaks"] = measured_peaks(torch)
     if args.copy_calibration:
         a = torch.empty(1 << 28, device="cuda:0", dtype=torch.float32)
         b = torch.empty_like(a)

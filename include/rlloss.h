@@ -440,6 +440,40 @@ rl_status rl_profile_begin(void);
  * kernel names seen.  Errors: RL_E_ARG (null), RL_E_HIP. */
 rl_status rl_profile_end(rl_profile_entry* out, int32_t max_entries, int32_t* n_entries);
 
+/* ---------------------------------------------------------------------------
+ * Machine calibration (measurement helpers, not part of the loss path): what
+ * the bf16 matrix pipe and HBM deliver on the current device with kernels
+ * that do nothing else, to set beside the published peaks.
+ * ------------------------------------------------------------------------ */
+
+/*
+ * rl_calib_mfma_bf16 -- enqueue n_blocks 256-thread blocks (use 2 per compute
+ * unit for two waves per SIMD, as the GEMMs run), each wave issuing
+ * iters x 16 v_mfma_f32_16x16x32_bf16 from registers only.  random_operands:
+ * 0 = all-zero operands, otherwise uniform random bf16 in [-2, 2).
+ *   sink_dev    device float [n_blocks * 256], written (keeps the results live)
+ *   stamps_dev  device int64 [n_blocks * 4]; block b writes, before and after
+ *               its loop: [4b] shader-clock counter, [4b+1] the same at the
+ *               end, [4b+2] / [4b+3] the fixed-rate wall clock at start / end.
+ *               Shader clock in Hz = (d[4b+1]-d[4b]) / (d[4b+3]-d[4b+2]) *
+ *               *wall_clock_khz * 1000.
+ *   flop        host: receives the FLOP count of the launch
+ *   wall_clock_khz host: receives the wall-clock counter rate
+ * 1 <= n_blocks <= 2^20, 1 <= iters <= 2^32.  Errors: RL_E_ARG, RL_E_HIP.
+ */
+rl_status rl_calib_mfma_bf16(int32_t random_operands, int32_t n_blocks, int64_t iters,
+                             float* sink_dev, int64_t* stamps_dev, double* flop,
+                             int32_t* wall_clock_khz, void* stream);
+
+/*
+ * rl_calib_copy -- enqueue a grid-stride copy of `bytes` (a multiple of 16,
+ * both pointers 16-byte aligned, device memory) from src to dst with
+ * n_blocks 256-thread blocks.  dst == src reads and writes back every 16-byte
+ * vector in place; any other overlap is RL_E_ARG.  Errors: RL_E_ARG, RL_E_HIP.
+ */
+rl_status rl_calib_copy(const void* src, void* dst, int64_t bytes, int32_t n_blocks,
+                        void* stream);
+
 /* Static description of a status code; never NULL. */
 const char* rl_status_string(rl_status s);
 

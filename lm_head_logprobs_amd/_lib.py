@@ -50,6 +50,8 @@ EXPORTED = (
     "rl_validate_support_sync",
     "rl_profile_begin",
     "rl_profile_end",
+    "rl_calib_mfma_bf16",
+    "rl_calib_copy",
     "rl_status_string",
     "rl_version",
 )
@@ -163,6 +165,11 @@ def lib() -> ctypes.CDLL:
         L.rl_profile_end.argtypes = [ctypes.POINTER(RlProfileEntry), i32,
                                      ctypes.POINTER(ctypes.c_int32)]
         L.rl_profile_end.restype = ctypes.c_int
+        L.rl_calib_mfma_bf16.argtypes = [i32, i32, i64, vp, vp, ctypes.POINTER(ctypes.c_double),
+                                         ctypes.POINTER(i32), vp]
+        L.rl_calib_mfma_bf16.restype = ctypes.c_int
+        L.rl_calib_copy.argtypes = [vp, vp, i64, i32, vp]
+        L.rl_calib_copy.restype = ctypes.c_int
         _lib = L
     return _lib
 
@@ -292,3 +299,22 @@ def rl_profile_end() -> dict:
         raise RlError(st, "rl_profile_end")
     return {arr[i].name.decode(): (int(arr[i].launches), float(arr[i].total_ms))
             for i in range(min(n.value, 64))}
+
+
+def rl_calib_mfma_bf16(random_operands: bool, n_blocks: int, iters: int, sink, stamps,
+                       stream=None):
+    """Enqueue the register-only MFMA loop; returns (FLOP of the launch, wall-clock kHz)."""
+    flop = ctypes.c_double(0.0)
+    khz = ctypes.c_int32(0)
+    st = lib().rl_calib_mfma_bf16(int(bool(random_operands)), int(n_blocks), int(iters),
+                                  _ptr(sink), _ptr(stamps), ctypes.byref(flop), ctypes.byref(khz),
+                                  _stream(stream))
+    if st != RL_OK:
+        raise RlError(st, "rl_calib_mfma_bf16")
+    return flop.value, khz.value
+
+
+def rl_calib_copy(src, dst, nbytes: int, n_blocks: int, stream=None) -> None:
+    st = lib().rl_calib_copy(_ptr(src), _ptr(dst), int(nbytes), int(n_blocks), _stream(stream))
+    if st != RL_OK:
+        raise RlError(st, "rl_calib_copy")

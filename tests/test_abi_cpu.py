@@ -27,7 +27,7 @@ def _declared():
 
 def test_every_declared_symbol_is_exported():
     names = _declared()
-    assert len(names) == 12
+    assert len(names) == 14
     out = subprocess.run(["nm", "-D", "--defined-only", L.LIB_PATH], capture_output=True,
                          text=True, check=True).stdout
     exported = {ln.split()[-1] for ln in out.splitlines() if " T " in ln}
@@ -308,3 +308,24 @@ def test_missing_library_fails_loudly(monkeypatch, tmp_path):
     monkeypatch.setattr(L, "_lib", None)
     with pytest.raises(RuntimeError, match="no fallback"):
         L.lib()
+
+
+def test_calibration_calls_reject_bad_arguments_before_any_launch():
+    """The measurement helpers check their arguments on the host first."""
+    import ctypes
+
+    lib = L.lib()
+    flop, khz = ctypes.c_double(0.0), ctypes.c_int32(0)
+    fake = ctypes.c_void_p(1 << 20)  # never dereferenced: every call below fails its checks
+    assert lib.rl_calib_mfma_bf16(1, 512, 10, None, fake, ctypes.byref(flop), ctypes.byref(khz),
+                                  None) == L.RL_E_ARG
+    assert lib.rl_calib_mfma_bf16(1, 0, 10, fake, fake, ctypes.byref(flop), ctypes.byref(khz),
+                                  None) == L.RL_E_ARG
+    assert lib.rl_calib_mfma_bf16(1, 512, 0, fake, fake, ctypes.byref(flop), ctypes.byref(khz),
+                                  None) == L.RL_E_ARG
+    assert lib.rl_calib_copy(fake, fake, 24, 64, None) == L.RL_E_ARG       # not a multiple of 16
+    assert lib.rl_calib_copy(fake, ctypes.c_void_p((1 << 20) + 16), 64, 64, None) == L.RL_E_ARG
+    assert lib.rl_calib_copy(fake, ctypes.c_void_p((1 << 20) + 8), 64, 64, None) == L.RL_E_ARG
+    assert lib.rl_calib_copy(None, fake, 64, 64, None) == L.RL_E_ARG
+    assert lib.rl_calib_copy(fake, ctypes.c_void_p(1 << 21), 64, 0, None) == L.RL_E_ARG
+
