@@ -219,7 +219,7 @@ def bench_head(args, torch):
                    "kl": wl.params["kl_estimator"], "backward": wl.params["backward"],
                    "kl_staleness": wl.params.get("kl_staleness", "none"),
                    "entropy_coeff": wl.params.get("entropy_coeff", 0.0),
-                   "token_chunk": fh.cfg.token_chunk or min(N, 16384)},
+                   "token_chunk": fh.cfg.token_chunk or min(N, 32768)},
         "mfma_frac_6nhv": flops_6nhv / (ms * 1e-3) / 1e12 / peak,
         "roofline": roof,
         "kernels": kernels,

@@ -103,7 +103,7 @@ typedef struct rl_loss_cfg {
   int64_t H;            /* hidden size, >= 8 and a multiple of 8                */
   int64_t V;            /* vocabulary, 1 .. 2^31-1                              */
   int64_t nnz;          /* support entries (0 without a support)                */
-  int64_t token_chunk;  /* tokens per pass through the head; 0 = default 16384  */
+  int64_t token_chunk;  /* tokens per pass through the head; 0 = default 32768  */
   int32_t dtype;        /* rl_dtype of h and W                                  */
   int32_t grad_dtype;   /* rl_dtype of dh (dW is always fp32)                   */
   int32_t loss_type;    /* rl_loss_type                                         */

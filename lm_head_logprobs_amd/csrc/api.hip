@@ -77,7 +77,7 @@ hipError_t timed(int kind, hipStream_t s, F&& f) {
 }
 
 constexpr size_t WS_ALIGN = 256;
-constexpr int64_t DEFAULT_CHUNK = 16384;
+constexpr int64_t DEFAULT_CHUNK = 32768;
 
 bool mul_ok(int64_t a, int64_t b, int64_t* out) {
   if (a < 0 || b < 0) return false;
