@@ -459,7 +459,8 @@ rl_status rl_profile_end(rl_profile_entry* out, int32_t max_entries, int32_t* n_
  *               *wall_clock_khz * 1000.
  *   flop        host: receives the FLOP count of the launch
  *   wall_clock_khz host: receives the wall-clock counter rate
- * 1 <= n_blocks <= 2^20, 1 <= iters <= 2^32.  Errors: RL_E_ARG, RL_E_HIP.
+ * 1 <= n_blocks <= 2^20, 1 <= iters <= 2^32 and n_blocks * iters <= 2^34 (a
+ * launch of seconds at most).  Errors: RL_E_ARG, RL_E_HIP.
  */
 rl_status rl_calib_mfma_bf16(int32_t random_operands, int32_t n_blocks, int64_t iters,
                              float* sink_dev, int64_t* stamps_dev, double* flop,

@@ -125,9 +125,11 @@ extern "C" {
 rl_status rl_calib_mfma_bf16(int32_t random_operands, int32_t n_blocks, int64_t iters,
                              float* sink_dev, int64_t* stamps_dev, double* flop,
                              int32_t* wall_clock_khz, void* stream) {
+  // n_blocks * iters is bounded so that one launch stays within seconds (about
+  // 9 s at the full matrix rate of 512 blocks).
   if (sink_dev == nullptr || stamps_dev == nullptr || flop == nullptr ||
       wall_clock_khz == nullptr || n_blocks < 1 || n_blocks > (1 << 20) || iters < 1 ||
-      iters > ((int64_t)1 << 32))
+      iters > ((int64_t)1 << 32) || (int64_t)n_blocks * iters > ((int64_t)1 << 34))
     return RL_E_ARG;
   int dev = 0, khz = 0;
   if (hipGetDevice(&dev) != hipSuccess ||

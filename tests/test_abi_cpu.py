@@ -323,6 +323,8 @@ def test_calibration_calls_reject_bad_arguments_before_any_launch():
                                   None) == L.RL_E_ARG
     assert lib.rl_calib_mfma_bf16(1, 512, 0, fake, fake, ctypes.byref(flop), ctypes.byref(khz),
                                   None) == L.RL_E_ARG
+    assert lib.rl_calib_mfma_bf16(1, 1 << 11, 1 << 24, fake, fake, ctypes.byref(flop),
+                                  ctypes.byref(khz), None) == L.RL_E_ARG  # n_blocks * iters > 2^34
     assert lib.rl_calib_copy(fake, fake, 24, 64, None) == L.RL_E_ARG       # not a multiple of 16
     assert lib.rl_calib_copy(fake, ctypes.c_void_p((1 << 20) + 16), 64, 64, None) == L.RL_E_ARG
     assert lib.rl_calib_copy(fake, ctypes.c_void_p((1 << 20) + 8), 64, 64, None) == L.RL_E_ARG
