@@ -701,12 +701,6 @@ __global__ void csr_rows_kernel(const int64_t* __restrict__ off, int64_t N, int6
   for (int64_t e = e0 + lane; e < e1; e += 64) row_of[e] = (int32_t)t;
 }
 
-__global__ void fill_f32_kernel(float* p, int64_t n, float v) {
-  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n;
-       i += (int64_t)gridDim.x * blockDim.x)
-    p[i] = v;
-}
-
 }  // namespace
 
 hipError_t transpose_pad(int dtype, const void* src, int64_t ld_src, int64_t R, int64_t C,
@@ -836,13 +830,6 @@ hipError_t reduce_final(const float* stats, int64_t N, float inv_D, float beta, 
 hipError_t csr_rows(const int64_t* off, int64_t N, int64_t nnz, int32_t* row_of, hipStream_t s) {
   hipLaunchKernelGGL(csr_rows_kernel, dim3((unsigned)ceil_div(N, 4)), dim3(256), 0, s, off, N,
                      nnz, row_of);
-  return hipGetLastError();
-}
-
-hipError_t fill_f32(float* p, int64_t n, float v, hipStream_t s) {
-  if (n <= 0) return hipSuccess;
-  const int64_t blocks = std::min<int64_t>(ceil_div(n, 256), 8192);
-  hipLaunchKernelGGL(fill_f32_kernel, dim3((unsigned)blocks), dim3(256), 0, s, p, n, v);
   return hipGetLastError();
 }
 

@@ -168,8 +168,6 @@ hipError_t sparse_dw(int dtype, const void* h, int64_t H, int64_t N, int64_t V,
                      const int32_t* start, const int32_t* perm, const int32_t* row_of,
                      const float* coef, float* dW, int overwrite, hipStream_t s);
 
-hipError_t fill_f32(float* p, int64_t n, float v, hipStream_t s);
-
 // Loss-only replay.
 int64_t elem_num_blocks(int64_t N);
 hipError_t elementwise(const float* lp, const float* lq, const float* adv, int64_t N,
