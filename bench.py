@@ -542,9 +542,8 @@ def main():
     args = ap.parse_args()
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
-        print("bench.py: this build runs on one GPU only; --gpus N > 1 is not supported "
-              "(how the path would shard across GPUs is described in DESIGN.md)",
-              file=sys.stderr)
+        print("bench.py: measures one GPU only; --gpus N > 1 is not supported (the path "
+              "would shard by tokens, with dW as the one exchange)", file=sys.stderr)
         sys.exit(2)
     import torch
 
