@@ -794,6 +794,16 @@ gemm_bf16_persist(const bf16_t* __restrict__ A, int64_t lda, const bf16_t* __res
 #pragma unroll
         for (int j = 0; j < 4; ++j)
           acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ca[i], cb[j], acc[i][j], 0, 0, 0);
+      // One fragment read of the next stage per MFMA of this half: measured
+      // 0.07 ms faster on the forward shape than all reads first (the same
+      // schedule makes the long-K dh GEMM slower, so that kernel keeps the
+      // compiler's order).
+#pragma unroll
+      for (int q = 0; q < 12; ++q) {
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // one LDS read
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA
+      }
+      __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
 #pragma unroll
       for (int i = 0; i < 8; ++i) ca[i] = na[i];
 #pragma unroll
