@@ -13,3 +13,30 @@ def test_multi_gpu_request_exits_with_message():
     assert r.returncode == 2
     assert "one GPU" in r.stderr
     assert r.stdout == ""
+
+
+def _bench_module():
+    import importlib.util
+
+    spec = importlib.util.spec_from_file_location("bench_under_test", os.path.join(ROOT, "bench.py"))
+    mod = importlib.util.module_from_spec(spec)
+    spec.loader.exec_module(mod)
+    return mod
+
+
+def test_traffic_summary_is_used_only_for_the_sources_it_was_taken_on(tmp_path, monkeypatch):
+    """roofline.traffic comes from a committed counter summary, and only while the
+    kernel's sources hash to the value recorded with it."""
+    b = _bench_module()
+    (tmp_path / "profiles").mkdir()
+    summary = tmp_path / "profiles" / "gemm_fwd_wl_traffic.txt"
+    monkeypatch.setattr(b, "ROOT", str(tmp_path))
+    assert b.read_traffic("gemm_fwd", "wl") is None  # no summary
+    monkeypatch.setattr(b, "ROOT", ROOT)
+    sha = b.kernel_src_sha("gemm_fwd")
+    monkeypatch.setattr(b, "ROOT", str(tmp_path))
+    monkeypatch.setattr(b, "kernel_src_sha", lambda kernel="gemm_fwd": sha)
+    summary.write_text(f"# comment\nkernel_src_sha: {sha}\nhbm_bytes_per_launch: 12345\n")
+    assert b.read_traffic("gemm_fwd", "wl") == 12345.0
+    summary.write_text("kernel_src_sha: 0000000000000000\nhbm_bytes_per_launch: 12345\n")
+    assert b.read_traffic("gemm_fwd", "wl") is None  # taken on other sources
