@@ -1,4 +1,5 @@
-"""bench.py's contract on the host: multi-GPU requests are refused with a message."""
+"""bench.py on the host: multi-GPU requests are refused with a message, and counter
+summaries are used only for the kernel sources they were taken on."""
 
 import os
 import subprocess
