@@ -68,7 +68,13 @@ def kl_beta(params):
 
 
 def beta_per_token(params, age):
-    """beta_t: kl_coeff, divided by sqrt(1 + age_t) under kl_staleness inv_sqrt."""
+    """beta_t: kl_coeff, divided by sqrt(1 + age_t) under kl_staleness inv_sqrt.
+
+    The PR's KL bullet names the inv_sqrt option and the per-token age but
+    gives no formula; 1/sqrt(1 + age) is the plainest reading of the name.
+    Parity unpinned: nothing on the pages fixes this formula, so its test only
+    restates the reading (ages 0, 3, 8 give factors 1, 1/2, 1/3).
+    """
     beta = kl_beta(params)
     age = np.asarray(age, np.float64)
     if params.get("kl_staleness", "none") == "inv_sqrt":

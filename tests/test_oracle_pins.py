@@ -477,3 +477,128 @@ def test_replay_ipo_masked_fraction_monotone_in_eps():
     kept = [res[f"ipo{i}_kept"] for i in range(len(eps))]
     assert all(a <= b for a, b in zip(kept, kept[1:]))
     assert kept[-1] == 5000
+
+
+# ------------------------------------------- head metrics: closed forms ----
+#
+# Three tokens over V = 3 whose training softmax is set by hand: with W = I
+# (H = V) the logits are h_t, and h_t = log p_t makes softmax(h_t) = p_t
+# (the row sums to 1, so its log-sum-exp is 0).  Each metric then has a value
+# computed by hand from the table below (prime-rl PR 4233, "What changes",
+# metrics bullet: support mass is E_q[p/q] from the support; mask_tv is the
+# fraction of label tokens failing the IPO total-variation test).
+#
+#  t  p_t               label  q(label)  |P-Q|  band ratio   support (v, u, q_v)
+#  0  (0.5, 0.3, 0.2)   0      0.4       0.10   1.25         (1, .5, .5), (2, .5, .25)
+#  1  (0.1, 0.6, 0.3)   0      0.9       0.80   0.111        (1, 1., .3)
+#  2  (0.2, 0.2, 0.6)   1      0.05      0.15   4.0          none
+
+def _metric_problem():
+    p = np.array([[0.5, 0.3, 0.2], [0.1, 0.6, 0.3], [0.2, 0.2, 0.6]])
+    h = np.log(p)
+    W = np.eye(3)
+    labels = np.array([0, 0, 1])
+    lq = np.log([0.4, 0.9, 0.05])
+    adv = np.array([1.0, -0.5, 2.0])
+    offsets = np.array([0, 2, 3, 3])
+    ids = np.array([1, 2, 1])
+    u = np.array([0.5, 0.5, 1.0])
+    logq = np.log([0.5, 0.25, 0.3])
+    return p, h, W, labels, lq, adv, offsets, ids, u, logq
+
+
+def test_head_metrics_closed_form():
+    p, h, W, labels, lq, adv, offsets, ids, u, logq = _metric_problem()
+    beta = 0.05
+    for lt, masked_fraction in (("ipo", 1 / 3), ("icepop", 2 / 3), ("reinforce", 0.0)):
+        prm = _params(loss_type=lt, ipo_eps=0.3, icepop_lo=0.5, icepop_hi=2.0, kl_coeff=beta,
+                      kl_estimator="k1", loss_norm=3.0)
+        out = ohead.head_reference(h, W, labels, lq, adv, prm, offsets, ids, u, logq)
+        m = out["metrics"]
+        # per-token softmax reproduced
+        assert np.allclose(out["logprobs"], np.log([0.5, 0.1, 0.2]), rtol=0, atol=1e-14)
+        # masked fraction: IPO masks token 1; the band masks tokens 1 and 2
+        assert m["masked_fraction"] == pytest.approx(masked_fraction, abs=1e-15)
+        # mask_tv: the IPO test at ipo_eps on the label, whatever the loss type
+        assert m["mask_tv"] == pytest.approx(1 / 3, abs=1e-15)
+        # support mass: sum_e u_e p(v_e)/q(v_e) per row with a support
+        # (token 0: .5*.3/.5 + .5*.2/.25 = 0.7; token 1: .6/.3 = 2), mean over
+        # those two rows (token 2 has none)
+        assert m["support_mass"] == pytest.approx((0.7 + 2.0) / 2, rel=1e-13)
+        # kl: sum_e u_e (log q - log p) per token, mean over all three tokens
+        kl0 = 0.5 * math.log(0.5 / 0.3) + 0.5 * math.log(0.25 / 0.2)
+        kl1 = math.log(0.3 / 0.6)
+        assert np.allclose(out["kl"], [kl0, kl1, 0.0], rtol=1e-13, atol=1e-15)
+        assert m["kl"] == pytest.approx((kl0 + kl1) / 3, rel=1e-12)
+        assert m["kl_beta"] == pytest.approx(beta, rel=1e-15)
+        # entropy mean from the table
+        ent = [-(r * np.log(r)).sum() for r in p]
+        assert m["entropy_mean"] == pytest.approx(np.mean(ent), rel=1e-13)
+
+
+def test_head_metric_kappa_closed_form():
+    # kappa_t = s_t (w_t - sum_e u_e w_e) + beta sum_e u_e with reinforce
+    # (every w = 1): token 0: s (1 - 1) + beta = beta; token 1: same; token 2
+    # (no support): s_2 = 2.  max |kappa| = 2.
+    p, h, W, labels, lq, adv, offsets, ids, u, logq = _metric_problem()
+    prm = _params(loss_type="reinforce", kl_coeff=0.05, kl_estimator="k1", loss_norm=3.0)
+    out = ohead.head_reference(h, W, labels, lq, adv, prm, offsets, ids, u, logq)
+    assert np.allclose(out["kappa"], [0.05, 0.05, 2.0], rtol=1e-15, atol=1e-15)
+    assert out["metrics"]["max_abs_kappa"] == pytest.approx(2.0, rel=1e-15)
+
+
+# ------------------------------------- replay: per-variant sums by hand ----
+
+def test_replay_variant_sums_on_worked_examples():
+    # The IPO page's two tokens (0.01 -> 0.06 and 0.90 -> 0.20) with
+    # advantages 1.5 and -2: every per-variant sum is a closed form.
+    rows = _worked_examples()
+    P = np.array([r[0] for r in rows])
+    Q = np.array([r[1] for r in rows])
+    lp, lq = np.log(P), np.log(Q)
+    A = np.array([1.5, -2.0])
+    prm = dict(RP, eps=(0.01, 0.3, 0.8), primary_eps_index=1, icepop_lo=0.2, icepop_hi=2.0)
+    res = oreplay.replay_reference(lp, lq, A, prm)
+    r1 = 0.2 / 0.9
+    # eps 0.01 masks both (moved 0.05 and 0.70)
+    assert res["ipo0_kept"] == 0
+    assert res["ipo0_loss_sum"] == 0.0 and res["ipo0_weight_sum"] == 0.0
+    # eps 0.3 keeps token 0 (w = min(6, 5) = 5), masks token 1
+    assert res["ipo1_kept"] == 1
+    assert res["ipo1_weight_sum"] == pytest.approx(5.0, rel=1e-14)
+    assert res["ipo1_loss_sum"] == pytest.approx(-1.5 * 5.0 * math.log(0.06), rel=1e-14)
+    # eps 0.8 keeps both; token 1's weight is its ratio 0.2/0.9
+    assert res["ipo2_kept"] == 2
+    assert res["ipo2_weight_sum"] == pytest.approx(5.0 + r1, rel=1e-14)
+    assert res["ipo2_loss_sum"] == pytest.approx(
+        -1.5 * 5.0 * math.log(0.06) + 2.0 * r1 * math.log(0.2), rel=1e-14)
+    # band [0.2, 2]: token 0 (ratio 6) above it, token 1 (0.222) inside
+    assert (res["icepop_kept"], res["icepop_low"], res["icepop_high"]) == (1, 0, 1)
+    assert res["icepop_weight_sum"] == pytest.approx(r1, rel=1e-14)
+    assert res["icepop_loss_sum"] == pytest.approx(2.0 * r1 * math.log(0.2), rel=1e-14)
+    # REINFORCE: -sum A lp
+    assert res["reinforce_loss_sum"] == pytest.approx(
+        -(1.5 * math.log(0.06) - 2.0 * math.log(0.2)), rel=1e-14)
+    # ppo_kl sums lq - lp: log(0.01/0.06) + log(0.9/0.2) = log 0.75
+    assert res["ppo_kl_sum"] == pytest.approx(math.log(0.75), rel=1e-13)
+    # the primary weight is eps 0.3's
+    assert np.allclose(res["w_primary"], [5.0, 0.0], rtol=1e-14, atol=0)
+
+
+def test_replay_ppo_kl_estimates_kl_of_rollout_to_trainer():
+    # Tokens drawn from the rollout policy q: the mean of lq - lp is the k1
+    # estimate of KL(q || p) = sum_v q_v log(q_v / p_v) >= 0, so ppo_kl_sum / N
+    # must land on that (positive) divergence within 4 standard errors; the
+    # opposite sign, or lp - lq, lands near -KL(q || p).
+    rng = np.random.default_rng(21)
+    V = 50
+    q = rng.dirichlet(np.ones(V))
+    p = rng.dirichlet(np.ones(V))
+    kl_qp = float(np.sum(q * np.log(q / p)))
+    y = rng.choice(V, size=200_000, p=q)
+    lq, lp = np.log(q[y]), np.log(p[y])
+    res = oreplay.replay_reference(lp, lq, np.zeros(len(y)), RP)
+    est = res["ppo_kl_sum"] / len(y)
+    se = np.std(lq - lp, ddof=1) / math.sqrt(len(y))
+    assert kl_qp > 10 * se
+    assert abs(est - kl_qp) <= 4 * se
