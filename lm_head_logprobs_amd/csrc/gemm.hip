@@ -383,6 +383,86 @@ struct DwEpi {
   }
 };
 
+// One DPP quad permutation (lanes 4q .. 4q+3 exchange values).
+template <int CTRL>
+__device__ __forceinline__ float quad_perm(float v) {
+  return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), CTRL, 0xf, 0xf, false));
+}
+
+// 4 x 4 transpose inside each quad of lanes: lane 4q + b holds x[r] = M[r][b]
+// and receives y[k] = M[b][k].  Two exchange rounds (distance 2, then 1).
+__device__ __forceinline__ f32x4 quad_transpose(f32x4 x, int b) {
+  const bool hi = (b & 2) != 0, odd = (b & 1) != 0;
+  const float r0 = quad_perm<0x4E>(hi ? x[0] : x[2]);  // lanes b ^ 2
+  const float r1 = quad_perm<0x4E>(hi ? x[1] : x[3]);
+  const float z0 = hi ? r0 : x[0], z1 = hi ? r1 : x[1];
+  const float z2 = hi ? x[2] : r0, z3 = hi ? x[3] : r1;
+  const float u0 = quad_perm<0xB1>(odd ? z0 : z1);  // lanes b ^ 1
+  const float u1 = quad_perm<0xB1>(odd ? z2 : z3);
+  f32x4 y;
+  y[0] = odd ? u0 : z0;
+  y[1] = odd ? z1 : u0;
+  y[2] = odd ? u1 : z2;
+  y[3] = odd ? z3 : u1;
+  return y;
+}
+
+// dW (=|+=) acc with 16-byte accesses (layout Acc16): a quad transpose gives
+// lane 16 g + 4 a + b row 16 i + 4 g + b, columns 16 j + 4 a .. + 3 of every
+// block, so each lane writes (and, when accumulating, reads) 32 float4
+// instead of 128 floats.  Elements outside [M, N] get an offset past the
+// descriptor's range (N is a multiple of 4 here).  The accumulate pass reads
+// in two halves of 16 loads, so that at most 64 VGPRs hold loaded values.
+// Returns nothing; every lane issues exactly 32 stores (the persistent kernel
+// counts them in its stage waits).
+template <bool ACC>
+struct DwEpiT {
+  float* C;
+  int64_t ldc, M, N;
+  static constexpr int STORES = 32;
+  template <class L, int MB, int NB, int BM, int BN>
+  __device__ __forceinline__ void apply(typename L::V (&acc)[MB][NB], const EpiCtx& c) const {
+    static_assert(std::is_same<L, Acc16>::value && MB == 8 && NB == 4, "wave tile 128 x 64");
+    const int64_t rows = min<int64_t>(M - c.m0, BM), cols = min<int64_t>(N - c.n0, BN);
+    const uint64_t a = reinterpret_cast<uint64_t>(C + c.m0 * ldc + c.n0);
+    const uint64_t au = ((uint64_t)__builtin_amdgcn_readfirstlane((uint32_t)(a >> 32)) << 32) |
+                        (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)a);
+    const int bytes = __builtin_amdgcn_readfirstlane((int)(((rows - 1) * ldc + cols) * 4));
+    const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+        reinterpret_cast<void*>(au), (short)0, bytes, 0x00020000);
+    const int ld = (int)ldc;
+    const int g = c.lane >> 4, q = (c.lane >> 2) & 3, b = c.lane & 3;
+    auto offset = [&](int i, int j) {
+      const int rl = c.wm_off + 16 * i + 4 * g + b, cl = c.wn_off + 16 * j + 4 * q;
+      return (rl < rows && cl < cols) ? (rl * ld + cl) * 4 : OOB;
+    };
+#pragma unroll
+    for (int half = 0; half < 2; ++half) {
+      u32x4 old[4][4];
+      if constexpr (ACC) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+          for (int j = 0; j < 4; ++j)
+            old[i][j] = __builtin_bit_cast(
+                u32x4, __builtin_amdgcn_raw_buffer_load_b128(rs, offset(4 * half + i, j), 0, 0));
+      }
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          f32x4 y = quad_transpose(acc[4 * half + i][j], b);
+          if constexpr (ACC) {
+#pragma unroll
+            for (int r = 0; r < 4; ++r) y[r] += __uint_as_float(old[i][j][r]);
+          }
+          __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, y), rs,
+                                                 offset(4 * half + i, j), 0, 0);
+        }
+    }
+  }
+};
+
 // ------------------------------------------------------------ bf16 kernel ---
 
 constexpr int BF_BM = 256, BF_BN = 256, BF_BK = 32, BF_ST = 4;
@@ -857,6 +937,236 @@ gemm_bf16_persist(const bf16_t* __restrict__ A, int64_t lda, const bf16_t* __res
   }
 }
 
+// Persistent variant for tiled operands with a long K loop (the dW
+// contraction, K = the chunk's tokens): one workgroup per CU walks its tiles
+// in the blocked order of map_tile_blocks (XCD x takes the logical tiles
+// [x * ceil(T / 8), ...) round-robin), and the stage ring runs on across tile
+// boundaries as in gemm_bf16_persist.  What this buys is the epilogue: its
+// Epi::STORES stores per lane are issued after the first three stages of the
+// next tile and drain while those stages' MFMAs run.  The stage waits of the
+// next tile's first two K-steps count the stores as younger operations (so
+// they do not wait for them); the third waits for them.  With ATR, A is given
+// as A^T in the tiled layout (G for dW) and read transposed, as in
+// gemm_bf16_kernel.  Requires K / BF_BK >= BF_ST stages and one split.
+template <class Epi, bool ATR>
+__global__ void __launch_bounds__(BF_NT) __attribute__((amdgpu_waves_per_eu(2, 2)))
+gemm_bf16_persist_t(const bf16_t* __restrict__ A, int64_t lda, const bf16_t* __restrict__ B,
+                    int64_t ldb, int64_t M, int64_t N, int64_t K, int tiles_m, int tiles_n,
+                    Epi epi) {
+  constexpr int NST = Epi::STORES;
+  static_assert(2 * BF_LPS + NST + BF_LPS < 64, "stage waits must fit vmcnt");
+  __shared__ __attribute__((aligned(1024))) char lds[BF_LDS];
+  const int total = tiles_m * tiles_n;
+  const int per_xcd = gridDim.x >> 3;  // the grid is a multiple of 8
+  const int chunk = (int)ceil_div(total, 8);
+  const int lo = (blockIdx.x & 7) * chunk, hi = min(total, lo + chunk);
+  int t = lo + (blockIdx.x >> 3);
+  if (t >= hi) return;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // 0..7
+  const int wm = wave >> 2, wn = wave & 3;
+  const int nk = (int)ceil_div(K, BF_BK);
+  // Blocks of 4 x 8 tiles (M x N), N fastest inside a block.
+  auto coords = [&](int lt, int64_t& m0, int64_t& n0) {
+    constexpr int BMT = 4, BNT = 8;
+    const int band = lt / (BMT * tiles_n);
+    const int first_m = band * BMT;
+    const int hm = min(BMT, tiles_m - first_m);
+    const int within = lt - band * BMT * tiles_n;
+    const int blk = within / (hm * BNT);
+    const int first_n = blk * BNT;
+    const int wn_ = min(BNT, tiles_n - first_n);
+    const int inb = within - blk * hm * BNT;
+    m0 = (int64_t)(first_m + inb / wn_) * BF_BM;
+    n0 = (int64_t)(first_n + inb % wn_) * BF_BN;
+  };
+  // Per tile: B's panel descriptor; A's first block column (ATR: its
+  // descriptor is rebased at every 256-row panel of A^T) or panel descriptor.
+  struct Tile {
+    int64_t m0, n0;
+    i32x4 ra, rb;
+    uint32_t a_bytes;
+  };
+  auto tile = [&](int lt) {
+    Tile T;
+    coords(lt, T.m0, T.n0);
+    i32x4 rb = make_rsrc(B + (T.n0 / BF_BN) * ldb * (TILE_BLOCK_BYTES / 2),
+                         (uint32_t)(nk * TILE_BLOCK_BYTES));
+    i32x4 ra = make_rsrc(A + (T.m0 / BF_BM) * lda * (TILE_BLOCK_BYTES / 2),
+                         (uint32_t)(nk * TILE_BLOCK_BYTES));
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      T.rb[i] = __builtin_amdgcn_readfirstlane(rb[i]);
+      T.ra[i] = __builtin_amdgcn_readfirstlane(ra[i]);
+    }
+    T.a_bytes = ATR ? (uint32_t)(min<int64_t>(BF_BM / TILE_K, lda - T.m0 / TILE_K) *
+                                 TILE_BLOCK_BYTES)
+                    : 0u;
+    return T;
+  };
+  // Per-lane copy-slot and fragment offsets (tile independent), formed from
+  // an opaque copy of the lane index before the first tile and after every
+  // epilogue.
+  struct LaneOffs {
+    int oa[2], ob[2], fa, fb;
+    int ftr[2][2];
+  };
+  auto lane_offs = [&]() {
+    int l;
+    __asm__ volatile("v_and_b32 %0, 63, %1" : "=v"(l) : "v"(tid));
+    LaneOffs o;
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const int q = wave * 2 + i;
+      o.ob[i] = (q * 64 + l) * 16;
+      // ATR: wave instruction q copies half q & 1 (16 rows) of piece q >> 1
+      o.oa[i] = ATR ? (q >> 1) * TILE_BLOCK_BYTES + ((q & 1) * 16 + (l >> 2)) * 64 + (l & 3) * 16
+                    : o.ob[i];
+    }
+    const int ch = l >> 4;
+    int row = wm * 128 + (l & 15);
+    o.fa = row * 64 + 16 * (ch ^ tile_swz(row));
+    row = wn * 64 + (l & 15);
+    o.fb = BF_STAGE_A + row * 64 + 16 * (ch ^ tile_swz(row));
+    const int g = l >> 4, j = l & 15;
+#pragma unroll
+    for (int h = 0; h < 2; ++h)
+#pragma unroll
+      for (int sec = 0; sec < 2; ++sec) {
+        const int r = 8 * g + 4 * sec + (j >> 2);
+        const int c = 2 * h + ((j & 3) >> 1);
+        o.ftr[h][sec] = r * 64 + ((c ^ tile_swz(r)) << 4) + 8 * (j & 1);
+      }
+    return o;
+  };
+  LaneOffs lof = lane_offs();
+  const uint32_t lds_base = (uint32_t)reinterpret_cast<uintptr_t>(lds);
+  auto issue = [&](const Tile& T, int kt, int slot) {
+    const uint32_t sa = lds_base + (uint32_t)(slot * BF_STAGE);
+    const uint32_t sb = sa + BF_STAGE_A;
+    i32x4 ra = T.ra;
+    int abase = kt * TILE_BLOCK_BYTES;
+    if constexpr (ATR) {
+      // rows 32 (kt % 8) .. of the 256-row panel kt / 8 of A^T
+      ra = make_rsrc(A + ((int64_t)(kt >> 3) * lda + T.m0 / TILE_K) * (TILE_BLOCK_BYTES / 2),
+                     T.a_bytes);
+      abase = (kt & 7) * (TILE_ROWS / 8 * TILE_K * 2);
+    }
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      load_lds16(ra, sa + (uint32_t)((wave * 2 + i) * 1024), lof.oa[i] + abase);
+      load_lds16(T.rb, sb + (uint32_t)((wave * 2 + i) * 1024), lof.ob[i] + kt * TILE_BLOCK_BYTES);
+    }
+  };
+  auto read_frags = [&](int slot, bf16x8 (&fa)[8], bf16x8 (&fb)[4]) {
+    const char* sn = lds + slot * BF_STAGE;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      if constexpr (ATR) {
+        typedef short v4s __attribute__((ext_vector_type(4)));
+        typedef v4s __attribute__((address_space(3))) * lds_v4s;
+        const char* pc = sn + (4 * wm + (i >> 1)) * (BF_STAGE_A / 8);
+        const v4s lo4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s)(pc + lof.ftr[i & 1][0]));
+        const v4s hi4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s)(pc + lof.ftr[i & 1][1]));
+        fa[i] = __builtin_bit_cast(bf16x8,
+                                   __builtin_shufflevector(lo4, hi4, 0, 1, 2, 3, 4, 5, 6, 7));
+      } else {
+        fa[i] = *reinterpret_cast<const bf16x8*>(sn + lof.fa + 1024 * i);
+      }
+    }
+#pragma unroll
+    for (int j = 0; j < 4; ++j) fb[j] = *reinterpret_cast<const bf16x8*>(sn + lof.fb + 1024 * j);
+  };
+  Tile cur = tile(t);
+  int tnext = t + per_xcd;
+  bool has_next = tnext < hi;
+  Tile nxt = cur;
+  if (has_next) nxt = tile(tnext);
+  bf16x8 ca[8], cb[4];
+  int gb = 0;  // ring position of the current tile's stage 0
+#pragma unroll
+  for (int s = 0; s < BF_ST - 1; ++s) issue(cur, s, s);
+  wait_vmcnt<2 * BF_LPS>();
+  __syncthreads();
+  issue(cur, BF_ST - 1, BF_ST - 1);
+  read_frags(0, ca, cb);
+  bool stores_out = false;  // the previous tile's epilogue stores may be in flight
+  for (;;) {
+    f32x4 acc[8][4];
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) acc[i][j][r] = 0.0f;
+    for (int kt = 0; kt + 1 < nk; ++kt) {
+      bf16x8 na[8], nb[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ca[i], cb[j], acc[i][j], 0, 0, 0);
+      // Await stage kt + 1.  Younger than it: two stages, plus (in the first
+      // two K-steps of a tile) the previous epilogue's stores.
+      if (stores_out && kt < 2)
+        wait_vmcnt<2 * BF_LPS + NST>();
+      else
+        wait_stage<BF_LPS>(has_next ? 2 : min(nk - 2 - kt, 2));
+      __syncthreads();
+      const int slot = (gb + kt) & (BF_ST - 1);
+      if (kt + BF_ST < nk) issue(cur, kt + BF_ST, slot);
+      else if (has_next) issue(nxt, kt + BF_ST - nk, slot);
+      read_frags((gb + kt + 1) & (BF_ST - 1), na, nb);
+#pragma unroll
+      for (int i = 4; i < 8; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ca[i], cb[j], acc[i][j], 0, 0, 0);
+#pragma unroll
+      for (int i = 0; i < 8; ++i) ca[i] = na[i];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) cb[j] = nb[j];
+    }
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ca[i], cb[j], acc[i][j], 0, 0, 0);
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) __asm__ volatile("" : "+a"(acc[i][j]));
+    int elane;
+    __asm__ volatile("v_and_b32 %0, 63, %1" : "=v"(elane) : "v"(tid));
+    EpiCtx ctx;
+    ctx.m0 = cur.m0;
+    ctx.n0 = cur.n0;
+    ctx.wm_off = wm * 128;
+    ctx.wn_off = wn * 64;
+    ctx.wave_m = wm;
+    ctx.lane = elane;
+    ctx.split = 0;
+    ctx.smem = nullptr;  // the ring is in use by the next tile's stages
+    ctx.smem_bytes = 0;
+    epi.template apply<Acc16, 8, 4, BF_BM, BF_BN>(acc, ctx);
+    if (!has_next) break;
+    // Advance: stages 0..2 of the next tile were issued before the epilogue's
+    // stores; await stage 0 (younger: stages 1, 2 and the stores), then
+    // issue stage 3.
+    gb += nk;
+    cur = nxt;
+    tnext += per_xcd;
+    has_next = tnext < hi;
+    if (has_next) nxt = tile(tnext);
+    lof = lane_offs();
+    wait_vmcnt<2 * BF_LPS + NST>();
+    __syncthreads();
+    issue(cur, BF_ST - 1, (gb + BF_ST - 1) & (BF_ST - 1));
+    read_frags(gb & (BF_ST - 1), ca, cb);
+    stores_out = true;
+  }
+}
+
 // ------------------------------------------------------------ fp32 kernel ---
 
 constexpr int F_BM = 128, F_BN = 128, F_BK = 16;
@@ -1083,6 +1393,26 @@ hipError_t gemm_dw(int dtype, const void* A, int64_t lda, const void* B, int64_t
                    int64_t N, int64_t K, float* C, int64_t ldc, int accumulate, hipStream_t s) {
   if (ldc >= ((int64_t)1 << 21)) return hipErrorInvalidValue;
   const int bk = gemm_k_tile(dtype);
+  // bf16: the persistent kernel (epilogue stores overlapped with the next
+  // tile) when the K loop has at least BF_ST stages and the CU count is known.
+  if (dtype == RL_DTYPE_BF16 && ceil_div(K, BF_BK) >= BF_ST && N % 4 == 0) {
+    const int64_t tm = ceil_div(M, BF_BM), tn = ceil_div(N, BF_BN);
+    const int64_t total = tm * tn;
+    const int cus = cu_count() / 8 * 8;
+    if (total <= 0) return hipSuccess;
+    if (cus > 0 && total <= ((int64_t)1 << 30)) {
+      if (ceil_div(M, TILE_K) > lda) return hipErrorInvalidValue;
+      if (ceil_div(K, BF_BK) * TILE_BLOCK_BYTES >= ((int64_t)1 << 31)) return hipErrorInvalidValue;
+      const int64_t grid = std::min<int64_t>(round_up(total, 8), cus);
+      auto go = [&](auto e) {
+        hipLaunchKernelGGL((gemm_bf16_persist_t<decltype(e), true>), dim3((unsigned)grid),
+                           dim3(BF_NT), 0, s, static_cast<const bf16_t*>(A), lda,
+                           static_cast<const bf16_t*>(B), ldb, M, N, K, (int)tm, (int)tn, e);
+        return hipGetLastError();
+      };
+      return accumulate ? go(DwEpiT<true>{C, ldc, M, N}) : go(DwEpiT<false>{C, ldc, M, N});
+    }
+  }
   auto run = [&](auto e) {
     if (dtype == RL_DTYPE_BF16)  // tiled operands, A given as G (transposed reads)
       return launch_bf16<true, decltype(e), true>(static_cast<const bf16_t*>(A), lda,
