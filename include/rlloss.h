@@ -265,6 +265,26 @@ rl_status rl_loss_elementwise(const float* lp, const float* lq, const float* adv
                               const rl_elem_cfg* cfg, const rl_elem_out* out,
                               void* workspace, size_t workspace_bytes, void* stream);
 
+/*
+ * rl_loss_elementwise_noalloc -- rl_loss_elementwise for callers that cannot
+ * allocate device memory or own a workspace: code under HIP graph capture,
+ * tight serving loops, harnesses that forbid hipMalloc.  Same passes, limits,
+ * outputs and results (bit for bit) as rl_loss_elementwise; it allocates
+ * nothing and needs no workspace.  Its scratch (the per-block partial sums)
+ * is a fixed array of RL_ELEM_NOALLOC_SCRATCH_BYTES in the library's own
+ * device memory, one per GPU, kept until the process ends; the first call on
+ * a device looks up its address.  Every call overwrites what it reads, so no
+ * state carries over between calls, but all calls on one GPU share that
+ * array: calls that may overlap in time on one GPU (unordered streams) race
+ * and must not be made.  N beyond RL_ELEM_MAX_N is RL_E_ARG (the scratch
+ * does not grow with N beyond 1024 blocks).
+ * Errors: RL_E_ARG, RL_E_CFG, RL_E_HIP.
+ */
+#define RL_ELEM_NOALLOC_SCRATCH_BYTES (RL_ELEM_SUM_COUNT * 1024 * 8)
+rl_status rl_loss_elementwise_noalloc(const float* lp, const float* lq, const float* adv,
+                                      int64_t N, const rl_elem_cfg* cfg, const rl_elem_out* out,
+                                      void* stream);
+
 /* ---------------------------------------------------------------------------
  * Sequence-aware rollout correction over a replay (Rollout Correction Methods
  * page: "Config keys", "Importance Sampling", "Rejection Sampling", "Veto

@@ -44,6 +44,7 @@ EXPORTED = (
     "rl_loss_fwd_bwd",
     "rl_elementwise_workspace_size",
     "rl_loss_elementwise",
+    "rl_loss_elementwise_noalloc",
     "rl_mis_workspace_size",
     "rl_mis_replay",
     "rl_validate_support",
@@ -145,6 +146,9 @@ def lib() -> ctypes.CDLL:
         L.rl_loss_elementwise.argtypes = [vp, vp, vp, i64, ctypes.POINTER(RlElemCfg),
                                           ctypes.POINTER(RlElemOut), vp, sz, vp]
         L.rl_loss_elementwise.restype = ctypes.c_int
+        L.rl_loss_elementwise_noalloc.argtypes = [vp, vp, vp, i64, ctypes.POINTER(RlElemCfg),
+                                                  ctypes.POINTER(RlElemOut), vp]
+        L.rl_loss_elementwise_noalloc.restype = ctypes.c_int
         L.rl_mis_workspace_size.argtypes = [i64, i64, ctypes.POINTER(sz)]
         L.rl_mis_workspace_size.restype = ctypes.c_int
         L.rl_mis_replay.argtypes = [vp, vp, vp, i64, vp, vp, i64, ctypes.POINTER(RlMisCfg),
@@ -236,6 +240,15 @@ def rl_loss_elementwise(lp, lq, adv, N, cfg: RlElemCfg, out: RlElemOut, workspac
                                    _stream(stream))
     if check and st != RL_OK:
         raise RlError(st, "rl_loss_elementwise")
+    return st
+
+
+def rl_loss_elementwise_noalloc(lp, lq, adv, N, cfg: RlElemCfg, out: RlElemOut, stream=None,
+                                check=True) -> int:
+    st = lib().rl_loss_elementwise_noalloc(_ptr(lp), _ptr(lq), _ptr(adv), int(N),
+                                           ctypes.byref(cfg), ctypes.byref(out), _stream(stream))
+    if check and st != RL_OK:
+        raise RlError(st, "rl_loss_elementwise_noalloc")
     return st
 
 

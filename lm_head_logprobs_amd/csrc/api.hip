@@ -544,9 +544,9 @@ rl_status rl_elementwise_workspace_size(int64_t N, size_t* bytes) {
   return RL_OK;
 }
 
-rl_status rl_loss_elementwise(const float* lp, const float* lq, const float* adv, int64_t N,
-                              const rl_elem_cfg* cfg, const rl_elem_out* out, void* workspace,
-                              size_t workspace_bytes, void* stream) {
+namespace {
+rl_status check_elementwise(const float* lp, const float* lq, const float* adv, int64_t N,
+                            const rl_elem_cfg* cfg, const rl_elem_out* out) {
   if (lp == nullptr || lq == nullptr || adv == nullptr || cfg == nullptr || out == nullptr ||
       out->sums == nullptr || N < 1 || N > RL_ELEM_MAX_N)
     return RL_E_ARG;
@@ -563,6 +563,15 @@ rl_status rl_loss_elementwise(const float* lp, const float* lq, const float* adv
       !(cfg->icepop_lo <= cfg->icepop_hi) || !(cfg->clip_low >= 0.0f && cfg->clip_low < 1.0f) ||
       !(cfg->clip_high >= 0.0f) || !(cfg->clip_c > 1.0f) || !(cfg->tis_upper > 0.0f))
     return RL_E_CFG;
+  return RL_OK;
+}
+}  // namespace
+
+rl_status rl_loss_elementwise(const float* lp, const float* lq, const float* adv, int64_t N,
+                              const rl_elem_cfg* cfg, const rl_elem_out* out, void* workspace,
+                              size_t workspace_bytes, void* stream) {
+  const rl_status st = check_elementwise(lp, lq, adv, N, cfg, out);
+  if (st != RL_OK) return st;
   size_t need;
   rl_elementwise_workspace_size(N, &need);
   if (workspace == nullptr || workspace_bytes < need || !aligned(workspace, 16))
@@ -576,6 +585,24 @@ rl_status rl_loss_elementwise(const float* lp, const float* lq, const float* adv
     return rl::elementwise_final(static_cast<const double*>(workspace), N, cfg->n_eps,
                                  out->sums, s);
   }));
+  return RL_OK;
+}
+
+rl_status rl_loss_elementwise_noalloc(const float* lp, const float* lq, const float* adv,
+                                      int64_t N, const rl_elem_cfg* cfg, const rl_elem_out* out,
+                                      void* stream) {
+  const rl_status st = check_elementwise(lp, lq, adv, N, cfg, out);
+  if (st != RL_OK) return st;
+  size_t need;
+  rl_elementwise_workspace_size(N, &need);
+  if (need > (size_t)elem_noalloc_scratch_bytes()) return RL_E_ARG;  // not reached: N is bounded
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  double* part = nullptr;
+  RL_TRY(elem_noalloc_scratch(&part));
+  // no event timing here: this entry point creates nothing
+  RL_TRY(rl::elementwise(lp, lq, adv, N, *cfg, out->mask_word, out->w_primary, part, out->sums,
+                         s));
+  RL_TRY(rl::elementwise_final(part, N, cfg->n_eps, out->sums, s));
   return RL_OK;
 }
 

@@ -27,6 +27,8 @@
 // total-major, and a second launch with one block per output sum combines
 // the raw totals that output needs over the blocks in a fixed order, so the
 // results are deterministic.
+#include <mutex>
+
 #include "kernels.h"
 
 namespace rl {
@@ -384,7 +386,36 @@ void launch_main(int64_t nb, const float* lp, const float* lq, const float* adv,
                        wprim, partials);
 }
 
+// Scratch of rl_loss_elementwise_noalloc: the per-block raw totals of the
+// largest grid, in the library's own device memory (one copy per GPU, held
+// until the process ends).  Every block writes its whole row before the final
+// pass reads it, so nothing in it has to start at zero.  Host code reaches it
+// only through the address hipGetSymbolAddress returns for the current
+// device.
+static __device__ __align__(256) double scratch[(int64_t)NS * kMaxBlocks];
+
 }  // namespace
+
+int64_t elem_noalloc_scratch_bytes() { return (int64_t)sizeof(scratch); }
+
+hipError_t elem_noalloc_scratch(double** out) {
+  static std::mutex mu;
+  static double* ptrs[64] = {};
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= 64) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lk(mu);
+  if (ptrs[dev] == nullptr) {  // set-up, once per device
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    if (p == nullptr) return hipErrorInvalidSymbol;
+    ptrs[dev] = static_cast<double*>(p);
+  }
+  *out = ptrs[dev];
+  return hipSuccess;
+}
 
 int64_t elem_num_blocks(int64_t N) {
   const int64_t nch = (std::max<int64_t>(N, 1) + 255) / 256;  // 64-vector chunks

@@ -176,6 +176,11 @@ hipError_t elementwise(const float* lp, const float* lq, const float* adv, int64
 // partials: the main pass's per-block raw totals; n_eps selects their layout.
 hipError_t elementwise_final(const double* partials, int64_t N, int n_eps, double* sums,
                              hipStream_t s);
+// The library-owned partials of the allocation-free entry point on the
+// current device (its address looked up at the first call there), and their
+// size, enough for the largest grid.
+hipError_t elem_noalloc_scratch(double** partials);
+int64_t elem_noalloc_scratch_bytes();
 
 // Sequence-aware rollout correction over a replay (four launches in order:
 // stage 0 chunk totals, 1 sequences, 2 tokens, 3 raw totals and metrics).

@@ -27,7 +27,7 @@ def _declared():
 
 def test_every_declared_symbol_is_exported():
     names = _declared()
-    assert len(names) == 14
+    assert len(names) == 15
     out = subprocess.run(["nm", "-D", "--defined-only", L.LIB_PATH], capture_output=True,
                          text=True, check=True).stdout
     exported = {ln.split()[-1] for ln in out.splitlines() if " T " in ln}
@@ -244,6 +244,16 @@ def test_elementwise_and_validate_host_errors():
     assert call(good, lpp=lp + 4) == L.RL_E_ARG  # misaligned input
     o2 = L.RlElemOut()
     assert call(good, o=o2) == L.RL_E_ARG  # sums required
+    # the allocation-free variant checks the same arguments before it touches a device
+    na = L.lib().rl_loss_elementwise_noalloc
+    assert na(lp, lq, adv, N, ctypes.byref(good), ctypes.byref(o2), None) == L.RL_E_ARG
+    assert na(lp + 4, lq, adv, N, ctypes.byref(good), ctypes.byref(out), None) == L.RL_E_ARG
+    assert na(lp, lq, adv, 0, ctypes.byref(good), ctypes.byref(out), None) == L.RL_E_ARG
+    assert na(lp, lq, adv, (1 << 38) + 1, ctypes.byref(good), ctypes.byref(out),
+              None) == L.RL_E_ARG
+    c = ops.elem_cfg(REPLAY_PARAMS)
+    c.clip_c = 0.5
+    assert na(lp, lq, adv, N, ctypes.byref(c), ctypes.byref(out), None) == L.RL_E_CFG
     # validation: host offsets are checked before any launch
     lab, ilq, A, flags = hb.buf(4 * 4), hb.buf(16), hb.buf(16), hb.buf(4)
     bad = np.array([0, 3, 2, 5, 6], np.int64)
