@@ -41,6 +41,7 @@ dW = (dL/dz)^T h / tau.  The oracle always forms the dense gradient.
 """
 
 import numpy as np
+import torch
 
 from . import weights as _w
 
@@ -83,7 +84,8 @@ def beta_per_token(params, age):
 
 
 def head_reference(h, W, labels, infer_logprobs, adv, params, offsets=None, ids=None,
-                   u=None, logq=None, tokens=None, want_grads=True, chunk=None, age=None):
+                   u=None, logq=None, tokens=None, want_grads=True, chunk=None, age=None,
+                   progress=None):
     """Dense fp64 forward + backward.
 
     h [N,H], W [V,H] (any float dtype; read exactly), labels [N] ints,
@@ -96,10 +98,13 @@ def head_reference(h, W, labels, infer_logprobs, adv, params, offsets=None, ids=
     per-token outputs and dh rows of those tokens, and dW from those tokens
     only); D stays params["loss_norm"].  ``chunk`` bounds memory by handling
     that many tokens per dense [tokens, V] block; it does not change any
-    per-token arithmetic.
+    per-token arithmetic.  ``progress``, if given, is called with (tokens
+    done, tokens) after each block.
     Returns a dict of numpy arrays (fp64) and scalars.
     """
-    W = np.asarray(W, np.float64)
+    # The [tokens, V] steps run on torch CPU tensors in fp64, which spread the
+    # elementwise work over the host cores; the arithmetic is the same.
+    W = torch.as_tensor(np.asarray(W, np.float64))
     V, H = W.shape
     N = len(labels)
     tok = np.arange(N) if tokens is None else np.asarray(tokens, np.int64)
@@ -125,23 +130,24 @@ def head_reference(h, W, labels, infer_logprobs, adv, params, offsets=None, ids=
     )
     sup_lp = {}  # entry index -> log p(v_e)
     dh = np.zeros((n_tok, H)) if want_grads else None
-    dW = np.zeros((V, H)) if want_grads else None
+    dW = torch.zeros((V, H), dtype=torch.float64) if want_grads else None
     step = n_tok if chunk is None else int(chunk)
     for c0 in range(0, n_tok, max(step, 1)):
         sel = np.arange(c0, min(n_tok, c0 + step))
         rows = tok[sel]
-        hc = np.asarray(h[rows], np.float64)
+        hc = torch.as_tensor(np.asarray(h[rows], np.float64))
         # LM head logits at temperature tau.
         z = inv_t * (hc @ W.T)
         # Log-sum-exp with the max subtracted, then log-softmax and softmax.
-        zmax = z.max(axis=1, keepdims=True)
-        lse = zmax[:, 0] + np.log(np.exp(z - zmax).sum(axis=1))
-        logp = z - lse[:, None]
-        p = np.exp(logp)
+        zmax = z.max(dim=1, keepdim=True).values
+        lse_t = zmax[:, 0] + torch.log(torch.exp(z - zmax).sum(dim=1))
+        logp_t = z - lse_t[:, None]
+        p = torch.exp(logp_t)
         # Shannon entropy of the training softmax.
-        ent = -(p * logp).sum(axis=1)
+        ent = (-(p * logp_t).sum(dim=1)).numpy()
+        lse = lse_t.numpy()
         a = np.asarray(labels, np.int64)[rows]
-        lp = logp[np.arange(len(rows)), a]
+        lp = logp_t[torch.arange(len(rows)), torch.as_tensor(a)].numpy()
         lq = np.asarray(infer_logprobs, np.float64)[rows]
         w, keep = _w.weight(lp, lq, params)
         s = s_all[rows]
@@ -154,7 +160,7 @@ def head_reference(h, W, labels, infer_logprobs, adv, params, offsets=None, ids=
         cnt = np.zeros(len(rows), np.int64)
         G = None
         if want_grads:
-            G = np.zeros_like(z)
+            G = torch.zeros_like(z)
         if has_support:
             for i, t in enumerate(rows):
                 e0, e1 = offsets[t], offsets[t + 1]
@@ -162,7 +168,7 @@ def head_reference(h, W, labels, infer_logprobs, adv, params, offsets=None, ids=
                     continue
                 v = ids[e0:e1]
                 ue = u[e0:e1]
-                lpe = logp[i, v]
+                lpe = logp_t[i, torch.as_tensor(v)].numpy()
                 lqe = lq_e_all[e0:e1]
                 we, _ = _w.weight(lpe, lqe, params)
                 ce = ue * we
@@ -175,17 +181,18 @@ def head_reference(h, W, labels, infer_logprobs, adv, params, offsets=None, ids=
                 for k in range(e0, e1):
                     sup_lp[k] = lpe[k - e0]
                 if want_grads:
-                    np.add.at(G[i], v, s[i] * ce - beta[i] * ue)
+                    # repeated ids add up
+                    G[i].index_add_(0, torch.as_tensor(v), torch.as_tensor(s[i] * ce - beta[i] * ue))
         klterm = kl if kl_beta(params) != 0.0 else np.zeros_like(kl)
         loss = -s * (w * lp - cent) + beta * klterm - gamma * ent
         kappa = s * (w - sum_c) + beta * sum_u
         if want_grads:
-            G += kappa[:, None] * p
+            G += torch.as_tensor(kappa)[:, None] * p
             if gamma != 0.0:
-                G += gamma * p * (logp + ent[:, None])
-            G[np.arange(len(rows)), a] -= s * w
+                G += gamma * p * (logp_t + torch.as_tensor(ent)[:, None])
+            G[torch.arange(len(rows)), torch.as_tensor(a)] -= torch.as_tensor(s * w)
             G /= D
-            dh[sel] = inv_t * (G @ W)
+            dh[sel] = (inv_t * (G @ W)).numpy()
             dW += inv_t * (G.T @ hc)
         out["logprobs"][sel] = lp
         out["entropy"][sel] = ent
@@ -198,10 +205,12 @@ def head_reference(h, W, labels, infer_logprobs, adv, params, offsets=None, ids=
         out["support_mass"][sel] = smass
         out["support_count"][sel] = cnt
         out["beta"][sel] = beta
+        if progress is not None:
+            progress(int(sel[-1]) + 1, n_tok)
     out["loss"] = out["token_loss"].sum() / D
     if want_grads:
         out["dh"] = dh
-        out["dW"] = dW
+        out["dW"] = dW.numpy()
     if has_support:
         e_list = sorted(sup_lp)
         out["support_entries"] = np.array(e_list, np.int64)
