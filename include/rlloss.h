@@ -47,7 +47,15 @@
 extern "C" {
 #endif
 
-typedef enum rl_status {
+/* rl_status travels as a 32-bit int across the ABI; in C++ it is given that
+ * underlying type, so any int a caller passes (e.g. to rl_status_string) is a
+ * valid value of the type. */
+#ifdef __cplusplus
+#define RL_STATUS_BASE : int32_t
+#else
+#define RL_STATUS_BASE
+#endif
+typedef enum rl_status RL_STATUS_BASE {
   RL_OK = 0,
   RL_E_ARG = 1,           /* null pointer, bad size or dtype, size overflow */
   RL_E_CFG = 2,           /* inconsistent or out-of-range configuration     */
@@ -103,7 +111,7 @@ typedef struct rl_loss_cfg {
   int64_t H;            /* hidden size, >= 8 and a multiple of 8                */
   int64_t V;            /* vocabulary, 1 .. 2^31-1                              */
   int64_t nnz;          /* support entries (0 without a support)                */
-  int64_t token_chunk;  /* tokens per pass through the head; 0 = default 32768  */
+  int64_t token_chunk;  /* tokens per pass through the head; 0 = default 8192   */
   int32_t dtype;        /* rl_dtype of h and W                                  */
   int32_t grad_dtype;   /* rl_dtype of dh (dW is always fp32)                   */
   int32_t loss_type;    /* rl_loss_type                                         */

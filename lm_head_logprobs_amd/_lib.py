@@ -13,7 +13,9 @@ import ctypes
 import os
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_HERE, "librlloss.so")
+# RL_LIB_PATH selects another build of the same library (the host-sanitizer
+# build the ABI tests run under); by default the in-tree librlloss.so.
+LIB_PATH = os.environ.get("RL_LIB_PATH") or os.path.join(_HERE, "librlloss.so")
 
 RL_OK, RL_E_ARG, RL_E_CFG, RL_E_CSR, RL_E_WORKSPACE, RL_E_HIP, RL_E_INVALID_INPUT = range(7)
 RL_DTYPE_FP32, RL_DTYPE_BF16 = 0, 1
