@@ -7,8 +7,12 @@
 // support).  The gradient treats every importance weight as a constant:
 //   dL/dz_t = (kappa_t p_t - s_t w_t e_a + sum_e (s_t c_e - beta u_e) e_{v_e}) / D
 //   kappa_t = s_t (w_t - sum_e c_e) + beta sum_e u_e,   c_e = u_e w_e.
-// The kappa_t p_t part is the dense operand G; the label and entry parts are
-// per-entry coefficients applied by gathers (dh) and a bucketed scatter (dW).
+// On the dense backward the whole of dL/dz is one bf16 operand G: the
+// kappa_t p_t part is formed in place over the forward's e^(z - m), then the
+// label and entry coefficients are added into the same elements (fold_sparse,
+// from the vocabulary-sorted entry list).  On the sparse backward (kappa = 0)
+// only the per-entry coefficients exist, applied in fp32 by gathers of W rows
+// (dh) and a bucketed scatter of h rows (dW).
 #include "kernels.h"
 
 namespace rl {
