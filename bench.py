@@ -30,6 +30,7 @@ if ROOT not in sys.path:
 METRIC = "tokens/s fused LM-head+RLLoss fwd+bwd (H=2048,V=152k) + % bf16 MFMA peak"
 PEAK_BF16_TFLOPS = 2500.0  # MI355X dense bf16 MFMA
 PEAK_FP32_TFLOPS = 157.3
+DEFAULT_TOKEN_CHUNK = 8192  # the library's default tokens per pass (rl_loss_cfg.token_chunk = 0)
 PEAK_HBM_GBS = 8000.0
 GEMMS = ("gemm_fwd", "gemm_dh", "gemm_dw")
 # Sources a kernel's counter summary was taken on (a summary is ignored once
@@ -168,6 +169,7 @@ def bench_head(args, torch):
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
+    torch.cuda.reset_peak_memory_stats()
     if int(flags.item()) != 0:
         raise RuntimeError(f"validation flags {int(flags.item()):#x} on the synthetic batch")
     L.rl_profile_begin()
@@ -184,6 +186,18 @@ def bench_head(args, torch):
     prof = L.rl_profile_end()
     ms = e0.elapsed_time(e1) / args.steps
     N, H, V = wl.N, wl.H, wl.V
+    # Device memory of the path: the caller's inputs, outputs and workspace
+    # (the library allocates nothing); torch's allocator peak over the timed
+    # steps is the same set of buffers plus the flag word.
+    def nbytes(*ts):
+        return int(sum(t.numel() * t.element_size() for t in ts if t is not None))
+    mem_in = nbytes(wl.h, wl.W, wl.labels, wl.infer_logprobs, wl.adv, fh.offsets_dev, wl.ids,
+                    wl.u, wl.logq, age)
+    mem_out = nbytes(*fh.o.values())
+    memory = {"peak_device_bytes": mem_in + mem_out + fh.ws_bytes, "inputs_bytes": mem_in,
+              "outputs_bytes": mem_out, "workspace_bytes": int(fh.ws_bytes),
+              "torch_allocator_peak_bytes": int(torch.cuda.max_memory_allocated())}
+    memory["peak_gib"] = memory["peak_device_bytes"] / 2**30
     value = N / (ms * 1e-3)
     flops_6nhv = 6.0 * N * H * V
     peak = PEAK_BF16_TFLOPS if wl.dtype == "bf16" else PEAK_FP32_TFLOPS
@@ -219,8 +233,10 @@ def bench_head(args, torch):
                    "kl": wl.params["kl_estimator"], "backward": wl.params["backward"],
                    "kl_staleness": wl.params.get("kl_staleness", "none"),
                    "entropy_coeff": wl.params.get("entropy_coeff", 0.0),
-                   "token_chunk": fh.cfg.token_chunk or min(N, 32768)},
+                   "token_chunk": fh.cfg.token_chunk or min(N, DEFAULT_TOKEN_CHUNK)},
         "mfma_frac_6nhv": flops_6nhv / (ms * 1e-3) / 1e12 / peak,
+        "peak_device_bytes": memory["peak_device_bytes"],
+        "memory": memory,
         "roofline": roof,
         "kernels": kernels,
         "wall_s_timed": wall,
@@ -517,6 +533,47 @@ def measured_peaks(torch):
     return res
 
 
+def secondary(args, torch):
+    """Compact figures of two more workloads in the same run: the 16k top-p
+    replay with exact KL (head) and the 2.16M-token loss-only replay, each
+    with its step time, roofline fraction, memory and oracle CPU baseline."""
+    from types import SimpleNamespace
+
+    res = {}
+    a4 = SimpleNamespace(**vars(args))
+    a4.workload, a4.steps, a4.warmup = "c4_head16k_ipo_topp_replay", 10, 3
+    a4.kl_staleness, a4.entropy_coeff, a4.token_chunk = "none", 0.0, 0
+    out, wl = bench_head(a4, torch)
+    res[a4.workload] = {
+        "ms_per_step": out["ms_per_step"], "tokens_per_s": out["value"],
+        "mfma_frac_6nhv": out["mfma_frac_6nhv"], "support_nnz": out["config"]["support_nnz"],
+        "token_chunk": out["config"]["token_chunk"],
+        "peak_device_bytes": out["peak_device_bytes"],
+        "roofline": {k: out["roofline"][k] for k in ("kernel", "frac", "avg_launch_ms")},
+        "kernels_ms_per_step": {k: v["ms_per_step"] for k, v in out["kernels"].items()
+                                if v["ms_per_step"] >= 0.05},
+        "cpu_baseline": None if args.no_cpu_baseline else cpu_baseline(wl, 10.0),
+    }
+    del out, wl
+    torch.cuda.empty_cache()
+    a2 = SimpleNamespace(**vars(args))
+    a2.workload, a2.steps, a2.warmup = "c2_replay", 200, 20
+    out, _ = bench_replay(a2, torch)
+    res["c2_replay"] = {
+        "us_per_step": out["ms_per_step"] * 1e3, "tokens_per_s": out["value"],
+        "step_timing": out["step_timing"],
+        "roofline": {"kernel": out["roofline"]["kernel"], "frac": out["roofline"]["frac"],
+                     "avg_launch_us": out["roofline"]["avg_launch_ms"] * 1e3,
+                     "GB/s": out["roofline"]["achieved"]},
+        "kernels_avg_us": {k: v["avg_ms"] * 1e3 for k, v in out["kernels"].items()},
+        "replay_16x_frac": out["replay_16x"]["frac"],
+        "cpu_baseline": (None if args.no_cpu_baseline
+                         else cpu_baseline_replay("replay", wl_replay_host(), 5.0)),
+    }
+    torch.cuda.empty_cache()
+    return res
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -537,6 +594,9 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-peak-check", action="store_true",
                     help="skip the measured MFMA and copy peaks")
+    ap.add_argument("--no-secondary", action="store_true",
+                    help="default workload only: skip the 16k top-p replay and loss-only "
+                         "replay figures")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a plain 1 GiB device copy (counter calibration)")
     args = ap.parse_args()
@@ -572,6 +632,10 @@ def main():
                                else cpu_baseline(wl, args.cpu_seconds))
     elif host is not None and not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline_replay(host[0], host[1], args.cpu_seconds)
+    if args.workload == "c3_head16k_ipo" and not args.no_secondary:
+        del wl
+        torch.cuda.empty_cache()
+        out["secondary"] = secondary(args, torch)
     print(json.dumps(out), flush=True)
 
 

@@ -151,9 +151,14 @@ def test_workspace_size_scales_and_does_not_overflow():
     import torch
     cfg = ops.make_cfg(16384, 2048, 152064, 0, torch.bfloat16, _params(loss_norm=16384.0))
     dense = _ws(cfg)
-    # the one [Tc, V] bf16 operand G dominates (dh reads it as is, dW transposed): no
-    # second [V, Tc] copy
-    assert 2 * 152064 * 16384 < dense < 2 * 2 * 152064 * 16384
+    # the one [Tc, V] bf16 operand G of a chunk dominates (dh reads it as is, dW
+    # transposed): no second [V, Tc] copy, and by default a chunk of 8192 tokens,
+    # not the batch
+    Tc = 8192
+    assert 2 * 152064 * Tc < dense < 2 * 2 * 152064 * Tc
+    cfg.token_chunk = 16384  # the whole batch in one chunk
+    assert 2 * 152064 * 16384 < _ws(cfg) < 2 * 2 * 152064 * 16384
+    cfg.token_chunk = 0
     cfg.backward = L.RL_BWD_NONE
     fwd = _ws(cfg)
     assert fwd < dense // 40

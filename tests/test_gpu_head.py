@@ -4,7 +4,7 @@ import numpy as np
 import pytest
 import torch
 
-from gpu_util import compare_all, compare_forward, rel_fro, run_head, to_np
+from gpu_util import compare_all, compare_forward, record, rel_fro, run_head, to_np
 from oracle import head as ohead
 from synth import make_head, policy_ages
 
@@ -33,7 +33,7 @@ def test_tiny_fp32_full_size(name):
     print(f"[case] {name} full size", flush=True)
     _, got = run_head(wl)
     ref = ohead.from_workload(wl)
-    r = compare_all(wl, got, ref)
+    r = compare_all(wl, got, ref, case=f"{name} full size")
     print(r)
 
 
@@ -45,7 +45,7 @@ def test_small_parity(name):
     wl = _case(name)
     _, got = run_head(wl)
     ref = ohead.from_workload(wl)
-    r = compare_all(wl, got, ref)
+    r = compare_all(wl, got, ref, case=f"{name} small")
     print(r)
 
 
@@ -54,7 +54,7 @@ def test_icepop_and_fp32_grad():
     wl.params.update(loss_type="icepop", icepop_lo=0.5, icepop_hi=2.0)
     _, got = run_head(wl, grad_dtype=torch.float32)
     ref = ohead.from_workload(wl)
-    r = compare_all(wl, got, ref)
+    r = compare_all(wl, got, ref, case="icepop, fp32 dh")
     print(r)
 
 
@@ -63,7 +63,7 @@ def test_temperature_adv_tau_and_accumulate():
     wl.params.update(inv_temperature=1.25, adv_tau=0.5, loss_norm=77.0)
     fh, got = run_head(wl, accumulate_dW=True)
     ref = ohead.from_workload(wl)
-    compare_all(wl, got, ref)
+    compare_all(wl, got, ref, case="temperature, adv_tau, D, accumulate")
     fh()  # dW accumulates a second copy of the gradient
     torch.cuda.synchronize()
     assert rel_fro(to_np(fh.o["dW"]), 2.0 * ref["dW"]) <= 1e-2
@@ -80,8 +80,17 @@ def test_dense_and_sparse_backward_agree_when_kappa_vanishes():
     # the dense softmax part is zero; the dense path carries the label and
     # support coefficients inside the bf16 operand G (relative rounding 2^-9
     # per element) while the sparse path keeps them in fp32
-    assert rel_fro(sp["dh"], de["dh"]) <= 2.0**-8
-    assert rel_fro(sp["dW"], de["dW"]) <= 2.0**-8
+    ref = ohead.from_workload(wl)
+    rep = {"dense_vs_sparse_dh": rel_fro(de["dh"], sp["dh"]),
+           "dense_vs_sparse_dW": rel_fro(de["dW"], sp["dW"]),
+           "dense_dh_vs_oracle": rel_fro(de["dh"], ref["dh"]),
+           "dense_dW_vs_oracle": rel_fro(de["dW"], ref["dW"]),
+           "sparse_dh_vs_oracle": rel_fro(sp["dh"], ref["dh"]),
+           "sparse_dW_vs_oracle": rel_fro(sp["dW"], ref["dW"])}
+    record("c5b small: dense vs sparse backward", rep)
+    print(rep)
+    assert rep["dense_vs_sparse_dh"] <= 2.0**-8
+    assert rep["dense_vs_sparse_dW"] <= 2.0**-8
 
 
 def _ref(wl, **kw):
@@ -98,7 +107,7 @@ def test_kl_staleness_and_entropy_bonus(name):
     _, got = run_head(wl)
     ref = _ref(wl)
     assert 0 < np.count_nonzero(to_np(wl.age)) < wl.N
-    r = compare_all(wl, got, ref)
+    r = compare_all(wl, got, ref, case=f"{name} small, inv_sqrt staleness, entropy bonus")
     print(r)
 
 
@@ -107,7 +116,7 @@ def test_entropy_bonus_fp32_and_negative():
     print("[case] c1 fp32 with an entropy penalty", flush=True)
     wl.params.update(entropy_coeff=-0.2)
     _, got = run_head(wl)
-    r = compare_all(wl, got, _ref(wl))
+    r = compare_all(wl, got, _ref(wl), case="c1 fp32, entropy penalty")
     print(r)
 
 
@@ -118,7 +127,7 @@ def test_entropy_bonus_makes_reinforce_dense():
     wl.params.update(entropy_coeff=0.03, backward="auto")
     _, got = run_head(wl)
     assert np.abs(got["dW"]).sum() > 0
-    r = compare_all(wl, got, _ref(wl))
+    r = compare_all(wl, got, _ref(wl), case="c5b small, entropy bonus (dense)")
     print(r)
 
 
@@ -160,7 +169,7 @@ def test_degenerate_shapes(shape):
     wl = _case("c5a_head64k_draws_ipo_k1", **shape)
     _, got = run_head(wl)
     ref = ohead.from_workload(wl)
-    compare_all(wl, got, ref)
+    compare_all(wl, got, ref, case=f"degenerate {shape}")
 
 
 def test_empty_support_rows_and_duplicates():
@@ -175,7 +184,7 @@ def test_empty_support_rows_and_duplicates():
     wl.ids[1] = wl.ids[0]  # a repeated id inside one row
     _, got = run_head(wl)
     ref = ohead.from_workload(wl)
-    compare_all(wl, got, ref)
+    compare_all(wl, got, ref, case="empty support rows, repeated id")
 
 
 def test_invalid_ids_give_nan_only_where_used():
@@ -237,9 +246,12 @@ def test_full_size_sampled_tokens(name):
     _, got = run_head(wl)
     tok = _sample(wl.N, 24, 1)
     ref = _ref(wl, tokens=tok, want_grads=True)
-    near, _ = compare_forward(wl, got, ref, tokens=tok)
+    rep = {}
+    near, _ = compare_forward(wl, got, ref, tokens=tok, report=rep)
     ok = ~near
     dh_err = rel_fro(got["dh"][tok][ok], ref["dh"][ok])
+    rep["dh_rel_sampled_rows"] = dh_err
+    record(f"{name} full size, 24 sampled tokens", rep)
     assert dh_err <= 1e-2, dh_err
     total = got["token_loss"].sum() / wl.params["loss_norm"]
     assert abs(got["loss"][0] - total) <= 1e-5 * abs(total) + 1e-7
@@ -269,7 +281,10 @@ def test_full_size_dW_on_token_sample(name):
     print(f"[case] {name} full size, advantage on {len(tok)} tokens", flush=True)
     _, got = run_head(wl)
     ref = ohead.from_workload(wl, tokens=tok, want_grads=True)
-    compare_forward(wl, got, ref, tokens=tok)
-    assert rel_fro(got["dW"], ref["dW"]) <= 1e-2
+    rep = {}
+    compare_forward(wl, got, ref, tokens=tok, report=rep)
+    rep["dW_rel"] = rel_fro(got["dW"], ref["dW"])
+    record(f"{name} full size, advantage on 16 tokens", rep)
+    assert rep["dW_rel"] <= 1e-2
     other = np.setdiff1d(np.arange(n), tok)
     assert np.all(got["dh"][other] == 0.0)
