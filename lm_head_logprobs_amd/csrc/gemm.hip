@@ -17,11 +17,11 @@
 // the other issues its loads or waits at the barrier.  With random
 // operands this shape sustains a higher MFMA rate than 32x32x16 (measured
 // about 84% against 72% of the dense peak in a loop without memory traffic).
-// K advances 32 at a time through a 4-stage ring of LDS buffers (32 KB each:
-// A then B).
+// K advances 32 at a time through a 5-stage ring of LDS buffers (32 KB each:
+// A then B; the whole 160 KB).
 // Operand tiles are copied global -> LDS by buffer_load_dwordx4 ... lds: each
 // wave instruction fills 1 KB of LDS (16 bytes per lane, consecutive), no
-// VGPR staging.  Loads run three stages ahead; a stage is waited for with an
+// VGPR staging.  Loads run four stages ahead; a stage is waited for with an
 // explicit vmcnt and one barrier, placed between the two K-steps of a stage so
 // MFMAs are in flight across it.  Out-of-range rows or K columns are given a
 // buffer offset past the descriptor's range, which the hardware reads as zero.
@@ -465,10 +465,12 @@ struct DwEpiT {
 
 // ------------------------------------------------------------ bf16 kernel ---
 
+// K advances 32 at a time through a ring of BF_ST = 4 stages of 32 KB (a ring
+// of five, filling the 160 KB of LDS, timed the same on the head step).
 constexpr int BF_BM = 256, BF_BN = 256, BF_BK = 32, BF_ST = 4;
 constexpr int BF_STAGE_A = BF_BM * BF_BK * 2;  // bytes
 constexpr int BF_STAGE = (BF_BM + BF_BN) * BF_BK * 2;
-constexpr int BF_LDS = BF_ST * BF_STAGE;  // the ring; the epilogues reuse it (128 KB)
+constexpr int BF_LDS = BF_ST * BF_STAGE;  // the ring; the epilogues reuse it (160 KB)
 static_assert(BF_LDS >= 6 * BF_BN * 4, "forward epilogue reductions");
 static_assert(BF_STAGE_A == TILE_BLOCK_BYTES, "a stage of one operand is one tiled block");
 
@@ -483,16 +485,24 @@ __device__ __forceinline__ i32x4 make_rsrc(const void* base, uint32_t bytes) {
   return r;
 }
 
-// 16 bytes per lane from `rsrc` + voffset into LDS at lds_addr + 16 * lane
-// (lds_addr wave-uniform).  Issued as inline asm so the compiler adds no
-// vmcnt waits of its own; the main loop waits explicitly.  Offsets past the
-// descriptor's range read zeros.
-__device__ __forceinline__ void load_lds16(i32x4 rsrc, uint32_t lds_addr, int voffset) {
+// 16 bytes per lane from `rsrc` + voffset + soffset into LDS at lds_addr +
+// 16 * lane (lds_addr and soffset wave-uniform).  Issued as inline asm so the
+// compiler adds no vmcnt waits of its own; the main loop waits explicitly.
+// Offsets past the descriptor's range read zeros.
+__device__ __forceinline__ void load_lds16(i32x4 rsrc, uint32_t lds_addr, int voffset,
+                                           int soffset = 0) {
 #pragma unroll
   for (int i = 0; i < 4; ++i) rsrc[i] = __builtin_amdgcn_readfirstlane(rsrc[i]);
   lds_addr = __builtin_amdgcn_readfirstlane(lds_addr);
-  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
-               :: "s"(lds_addr), "v"(voffset), "s"(rsrc) : "memory");
+  soffset = __builtin_amdgcn_readfirstlane(soffset);
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, %3 offen lds"
+               :: "s"(lds_addr), "v"(voffset), "s"(rsrc), "s"(soffset) : "memory");
+}
+
+// ATR pieces: wave instruction q copies half q & 1 (16 rows) of piece q >> 1;
+// the byte offset of a copying wave's piece i from its first (q even).
+__host__ __device__ constexpr int atr_piece_step(int i) {
+  return (i >> 1) * TILE_BLOCK_BYTES + (i & 1) * 1024;
 }
 
 // s_waitcnt vmcnt(n) with the other counters left alone (gfx9 encoding).
@@ -503,16 +513,31 @@ __device__ __forceinline__ void wait_vmcnt() {
 }
 
 // Wait until the oldest stage not yet waited for has landed, given how many
-// younger stages (LPS loads per thread each) were issued after it.
-template <int LPS>
-__device__ __forceinline__ void wait_stage(int younger) {
-  if (younger >= 2)
+// younger stages (LPS loads per thread each) were issued after it, and
+// whether NST stores (an epilogue's) were issued after it as well.
+template <int LPS, int NST = 0>
+__device__ __forceinline__ void wait_stage(int younger, bool stores = false) {
+  static_assert(3 * LPS + NST < 64, "vmcnt");
+  if (NST > 0 && stores) {
+    if (younger >= 3)
+      wait_vmcnt<3 * LPS + NST>();
+    else if (younger == 2)
+      wait_vmcnt<2 * LPS + NST>();
+    else if (younger == 1)
+      wait_vmcnt<LPS + NST>();
+    else
+      wait_vmcnt<NST>();
+  } else if (younger >= 3) {
+    wait_vmcnt<3 * LPS>();
+  } else if (younger == 2) {
     wait_vmcnt<2 * LPS>();
-  else if (younger == 1)
+  } else if (younger == 1) {
     wait_vmcnt<LPS>();
-  else
+  } else {
     wait_vmcnt<0>();
+  }
 }
+static_assert(BF_ST - 2 <= 3, "wait_stage covers up to three younger stages");
 
 // TILED = false: A [M, lda] and B [N, ldb] row-major, any K (multiple of 8).
 // TILED = true: A and B in the tiled block layout (tiled_offset in
@@ -520,7 +545,19 @@ __device__ __forceinline__ void wait_stage(int younger) {
 // or the blocks are zero past K.
 //
 constexpr int BF_NT = 512;  // 8 waves
-constexpr int BF_LPS = 4;   // direct-to-LDS loads per thread per stage (2 A + 2 B)
+// A stage is 32 wave instructions of 1 KB (16 per operand).  Only the first
+// BF_DMAW waves issue them, BF_PER per operand each; the other waves only
+// read fragments and issue MFMAs, so on every SIMD one wave keeps the matrix
+// pipe fed while the other waits on the copy path.
+constexpr int BF_DMAW = 4;
+constexpr int BF_PER = 16 / BF_DMAW;  // 1 KB pieces per operand per copying wave
+constexpr int BF_LPS = 2 * BF_PER;    // direct-to-LDS loads per copying wave per stage
+static_assert(BF_DMAW * BF_PER == 16 && BF_PER % 2 == 0, "copy split");
+// The persistent dW kernel's split (its waits also count 32 epilogue stores).
+constexpr int BT_DMAW = 4;
+constexpr int BT_PER = 16 / BT_DMAW;
+constexpr int BT_LPS = 2 * BT_PER;
+static_assert(BT_DMAW * BT_PER == 16 && BT_PER % 2 == 0, "copy split");
 
 // Software pipeline per stage kt (one K-step of 32): the MFMAs of row blocks
 // 0..3 issue from fragments read during the previous stage, then the wave
@@ -556,7 +593,10 @@ gemm_bf16_kernel(const bf16_t* __restrict__ A, int64_t lda, const bf16_t* __rest
   const int64_t ke = min(K, kb + k_split);
   const int nk = (int)ceil_div(max<int64_t>(ke - kb, 0), BF_BK);
   i32x4 rsa, rsb;
-  int offa[2], offb[2], kc[2];
+  // Copy slots of a copying wave: its piece i of each operand sits at the
+  // lane's base offset plus a uniform step (sa_step / sb_step).
+  int offa, offb, kc = 0;
+  int sa_step = 1024, sb_step = 1024;
   // ATR: the A blocks of this tile's columns that exist (the rest read zero).
   const int64_t a_blk0 = tc.m0 / TILE_K;
   const uint32_t a_bytes =
@@ -567,56 +607,55 @@ gemm_bf16_kernel(const bf16_t* __restrict__ A, int64_t lda, const bf16_t* __rest
     const int64_t bb = (tc.n0 / BF_BN) * ldb + kb / BF_BK;
     rsa = make_rsrc(A + ba * (TILE_BLOCK_BYTES / 2), (uint32_t)(nk * TILE_BLOCK_BYTES));
     rsb = make_rsrc(B + bb * (TILE_BLOCK_BYTES / 2), (uint32_t)(nk * TILE_BLOCK_BYTES));
-#pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      offa[i] = offb[i] = ((wave * 2 + i) * 64 + lane) * 16;
-      kc[i] = 0;
-      if constexpr (ATR) {
-        // wave instruction q copies half q & 1 (16 rows) of piece q >> 1
-        const int q = wave * 2 + i;
-        offa[i] = (q >> 1) * TILE_BLOCK_BYTES + ((q & 1) * 16 + (lane >> 2)) * 64 + (lane & 3) * 16;
-      }
+    offa = offb = (wave * BF_PER * 64 + lane) * 16;
+    if constexpr (ATR) {
+      const int q = wave * BF_PER;  // even
+      offa = (q >> 1) * TILE_BLOCK_BYTES + (lane >> 2) * 64 + (lane & 3) * 16;
     }
   } else {
     const int64_t rows_a = min<int64_t>(M - tc.m0, BF_BM), rows_b = min<int64_t>(N - tc.n0, BF_BN);
     rsa = make_rsrc(A + tc.m0 * lda, (uint32_t)(rows_a * lda * 2));
     rsb = make_rsrc(B + tc.n0 * ldb, (uint32_t)(rows_b * ldb * 2));
-    // Slot p = (wave*2 + i)*64 + lane: tile row p/4, stored chunk p%4 holds
-    // logical chunk (p%4) ^ tile_swz(row).
-#pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      const int p = (wave * 2 + i) * 64 + lane;
-      const int row = p >> 2, ch = (p & 3) ^ tile_swz(row);
-      kc[i] = 8 * ch;
-      offa[i] = row < rows_a ? (int)((row * lda + kb + 8 * ch) * 2) : OOB;
-      offb[i] = row < rows_b ? (int)((row * ldb + kb + 8 * ch) * 2) : OOB;
-    }
+    // Slot p = (wave * BF_PER + i) * 64 + lane: tile row p/4, stored chunk p%4
+    // holds logical chunk (p%4) ^ tile_swz(row).  Piece i is 16 rows further
+    // down, which keeps tile_swz(row); rows past the tile's extent lie past
+    // the descriptor's range and read zero.
+    const int p = wave * BF_PER * 64 + lane;
+    const int row = p >> 2, ch = (p & 3) ^ tile_swz(row);
+    kc = 8 * ch;
+    offa = (int)((row * lda + kb + 8 * ch) * 2);
+    offb = (int)((row * ldb + kb + 8 * ch) * 2);
+    sa_step = (int)(16 * lda * 2);
+    sb_step = (int)(16 * ldb * 2);
   }
+  const bool copier = wave < BF_DMAW;
   const uint32_t lds_base = (uint32_t)reinterpret_cast<uintptr_t>(lds);
   auto issue = [&](int kt) {
+    if (!copier) return;
     const uint32_t sa = lds_base + (uint32_t)((kt % BF_ST) * BF_STAGE);
     const uint32_t sb = sa + BF_STAGE_A;
+    int oa, ob;
+    i32x4 ra = rsa;
+    if constexpr (ATR) {
+      // rows 32 ks .. of panel ks / 8 (ks = the stage's 32-row group of A^T)
+      const int64_t ks = kb / BF_BK + kt;
+      ra = make_rsrc(A + ((ks >> 3) * lda + a_blk0) * (TILE_BLOCK_BYTES / 2), a_bytes);
+      oa = offa + (int)(ks & 7) * (TILE_ROWS / 8 * TILE_K * 2);
+      ob = offb + kt * TILE_BLOCK_BYTES;
+    } else if constexpr (TILED) {
+      oa = offa + kt * TILE_BLOCK_BYTES;
+      ob = offb + kt * TILE_BLOCK_BYTES;
+    } else {
+      const int k0 = kt * BF_BK;
+      const bool kok = kb + k0 + kc < ke;
+      oa = kok ? offa + 2 * k0 : OOB;
+      ob = kok ? offb + 2 * k0 : OOB;
+    }
 #pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      int oa, ob;
-      i32x4 ra = rsa;
-      if constexpr (ATR) {
-        // rows 32 ks .. of panel ks / 8 (ks = the stage's 32-row group of A^T)
-        const int64_t ks = kb / BF_BK + kt;
-        ra = make_rsrc(A + ((ks >> 3) * lda + a_blk0) * (TILE_BLOCK_BYTES / 2), a_bytes);
-        oa = offa[i] + (int)(ks & 7) * (TILE_ROWS / 8 * TILE_K * 2);
-        ob = offb[i] + kt * TILE_BLOCK_BYTES;
-      } else if constexpr (TILED) {
-        oa = offa[i] + kt * TILE_BLOCK_BYTES;
-        ob = offb[i] + kt * TILE_BLOCK_BYTES;
-      } else {
-        const int k0 = kt * BF_BK;
-        const bool kok = kb + k0 + kc[i] < ke;
-        oa = kok ? offa[i] + 2 * k0 : OOB;
-        ob = kok ? offb[i] + 2 * k0 : OOB;
-      }
-      load_lds16(ra, sa + (uint32_t)((wave * 2 + i) * 1024), oa);
-      load_lds16(rsb, sb + (uint32_t)((wave * 2 + i) * 1024), ob);
+    for (int i = 0; i < BF_PER; ++i) {
+      const uint32_t dst = (uint32_t)((wave * BF_PER + i) * 1024);
+      load_lds16(ra, sa + dst, oa, ATR ? atr_piece_step(i) : i * sa_step);
+      load_lds16(rsb, sb + dst, ob, i * sb_step);
     }
   };
   // Fragment byte offsets inside a stage: in 16-row block i the lane reads
@@ -669,7 +708,7 @@ gemm_bf16_kernel(const bf16_t* __restrict__ A, int64_t lda, const bf16_t* __rest
 #pragma unroll
     for (int s = 0; s < BF_ST - 1; ++s)
       if (s < nk) issue(s);
-    wait_stage<BF_LPS>(min(nk - 1, BF_ST - 2));
+    if (copier) wait_stage<BF_LPS>(min(nk - 1, BF_ST - 2));
     __syncthreads();
     if (BF_ST - 1 < nk) issue(BF_ST - 1);
     bf16x8 ca[8], cb[4];
@@ -687,7 +726,7 @@ gemm_bf16_kernel(const bf16_t* __restrict__ A, int64_t lda, const bf16_t* __rest
       if (kt + 1 < nk) {
         // Stage kt+1 has landed once at most the stages issued after it
         // (kt+2, kt+3) are outstanding.
-        wait_stage<BF_LPS>(min(nk - 2 - kt, BF_ST - 2));
+        if (copier) wait_stage<BF_LPS>(min(nk - 2 - kt, BF_ST - 2));
         __syncthreads();
         if (kt + BF_ST < nk) issue(kt + BF_ST);  // into the buffer of stage kt
         const char* sn = lds + ((kt + 1) % BF_ST) * BF_STAGE;
@@ -744,7 +783,7 @@ gemm_bf16_persist(const bf16_t* __restrict__ A, int64_t lda, const bf16_t* __res
                   int64_t ldb, int64_t M, int64_t N, int64_t K, int tiles_m, int tiles_n,
                   Epi epi) {
   __shared__ __attribute__((aligned(1024))) char lds[BF_LDS];
-  __shared__ __attribute__((aligned(16))) char scratch[6 * BF_BN * 4];
+  static_assert(BF_STAGE >= 6 * BF_BN * 4, "the epilogue's reductions fit one stage");
   const int total = tiles_m * tiles_n;
   const int per_xcd = gridDim.x >> 3;  // the grid is a multiple of 8
   const int chunk = (int)ceil_div(total, 8);
@@ -761,18 +800,20 @@ gemm_bf16_persist(const bf16_t* __restrict__ A, int64_t lda, const bf16_t* __res
   // copy of the lane index before the first tile and again after every
   // epilogue, so they are not live (and not spilled) across the epilogue.
   struct LaneOffs {
-    int oa[2], ob[2], fa, fb;
+    int oa, ob, fa, fb;
   };
+  const bool copier = wave < BF_DMAW;
+  // A copying wave's piece i is 16 rows below its piece 0 (same swizzle).
+  const int sa_step = (int)(16 * lda * 2), sb_step = (int)(16 * ldb * 2);
   auto lane_offs = [&]() {
     int l;
     __asm__ volatile("v_and_b32 %0, 63, %1" : "=v"(l) : "v"(tid));
     LaneOffs o;
-#pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      const int p = (wave * 2 + i) * 64 + l;
+    {
+      const int p = wave * BF_PER * 64 + l;
       const int row = p >> 2, ch = (p & 3) ^ tile_swz(row);
-      o.oa[i] = (int)((row * lda + 8 * ch) * 2);
-      o.ob[i] = (int)((row * ldb + 8 * ch) * 2);
+      o.oa = (int)((row * lda + 8 * ch) * 2);
+      o.ob = (int)((row * ldb + 8 * ch) * 2);
     }
     const int ch = l >> 4;
     int row = wm * 128 + (l & 15);
@@ -815,14 +856,16 @@ gemm_bf16_persist(const bf16_t* __restrict__ A, int64_t lda, const bf16_t* __res
   // per-lane offsets are formed at each issue instead of being kept as
   // induction variables (registers are short in the K loop).
   auto issue = [&](i32x4 ra, i32x4 rb, int kt, int slot) {
+    if (!copier) return;
     const uint32_t sa = lds_base + (uint32_t)(slot * BF_STAGE);
     const uint32_t sb = sa + BF_STAGE_A;
     int kbytes;
     __asm__ volatile("s_lshl_b32 %0, %1, 6" : "=s"(kbytes) : "s"(kt));  // kt * BF_BK * 2
 #pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      load_lds16(ra, sa + (uint32_t)((wave * 2 + i) * 1024), lof.oa[i] + kbytes);
-      load_lds16(rb, sb + (uint32_t)((wave * 2 + i) * 1024), lof.ob[i] + kbytes);
+    for (int i = 0; i < BF_PER; ++i) {
+      const uint32_t dst = (uint32_t)((wave * BF_PER + i) * 1024);
+      load_lds16(ra, sa + dst, lof.oa, kbytes + i * sa_step);
+      load_lds16(rb, sb + dst, lof.ob, kbytes + i * sb_step);
     }
   };
   bf16x8 ca[8], cb[4];
@@ -833,11 +876,12 @@ gemm_bf16_persist(const bf16_t* __restrict__ A, int64_t lda, const bf16_t* __res
 #pragma unroll
     for (int j = 0; j < 4; ++j) fb[j] = *reinterpret_cast<const bf16x8*>(sn + lof.fb + 1024 * j);
   };
-  // First tile: stages 0..2, then stage 0 awaited, stage 3 issued.
+  // First tile: stages 0 .. BF_ST-2, then stage 0 awaited, stage BF_ST-1
+  // issued.
   int gb = 0;  // ring position of the current tile's stage 0
 #pragma unroll
   for (int s = 0; s < BF_ST - 1; ++s) issue(rsa, rsb, s, s);
-  wait_vmcnt<2 * BF_LPS>();
+  if (copier) wait_stage<BF_LPS>(BF_ST - 2);
   __syncthreads();
   issue(rsa, rsb, BF_ST - 1, BF_ST - 1);
   read_frags(0, ca, cb);
@@ -860,15 +904,15 @@ gemm_bf16_persist(const bf16_t* __restrict__ A, int64_t lda, const bf16_t* __res
         for (int j = 0; j < 4; ++j)
           acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ca[i], cb[j], acc[i][j], 0, 0, 0);
       // Stage kt+1 has landed once at most the stages issued after it are
-      // outstanding (two, except at the end of the last tile).
-      wait_stage<BF_LPS>(has_next ? 2 : min(nk - 2 - kt, 2));
+      // outstanding (BF_ST - 2, except at the end of the last tile).
+      if (copier) wait_stage<BF_LPS>(has_next ? BF_ST - 2 : min(nk - 2 - kt, BF_ST - 2));
       __syncthreads();
-      // Refill the buffer of stage kt with stage kt + 4 of this tile or,
+      // Refill the buffer of stage kt with stage kt + BF_ST of this tile or,
       // past its end, with the first stages of the next tile.
-      const int slot = (gb + kt) & (BF_ST - 1);
+      const int slot = (gb + kt) % BF_ST;
       if (kt + BF_ST < nk) issue(rsa, rsb, kt + BF_ST, slot);
       else if (has_next) issue(nrsa, nrsb, kt + BF_ST - nk, slot);
-      read_frags((gb + kt + 1) & (BF_ST - 1), na, nb);
+      read_frags((gb + kt + 1) % BF_ST, na, nb);
 #pragma unroll
       for (int i = 4; i < 8; ++i)
 #pragma unroll
@@ -911,12 +955,16 @@ gemm_bf16_persist(const bf16_t* __restrict__ A, int64_t lda, const bf16_t* __res
     ctx.wave_m = wm;
     ctx.lane = elane;
     ctx.split = 0;
-    ctx.smem = scratch;
-    ctx.smem_bytes = (int)sizeof(scratch);
+    // The epilogue's LDS is the ring slot of this tile's last stage: the next
+    // tile's first BF_ST - 1 stages fill the other slots, and the epilogue's
+    // opening barrier follows every wave's last fragment read from this one.
+    ctx.smem = lds + ((gb + nk - 1) % BF_ST) * BF_STAGE;
+    ctx.smem_bytes = BF_STAGE;
     epi.template apply<Acc16, 8, 4, BF_BM, BF_BN>(acc, ctx);
     if (!has_next) break;
-    // Advance: stages 0..2 of the next tile are in flight (issued in the
-    // last iterations above); await stage 0, then issue stage 3.
+    // Advance: stages 0 .. BF_ST-2 of the next tile are in flight (issued in
+    // the last iterations above); await stage 0, then, past a barrier that
+    // ends the epilogue's use of its slot, issue stage BF_ST-1 there.
     gb += nk;
     m0 = nm0;
     n0 = nn0;
@@ -930,10 +978,10 @@ gemm_bf16_persist(const bf16_t* __restrict__ A, int64_t lda, const bf16_t* __res
       nrsb = panel(B, nn0, N, ldb);
     }
     lof = lane_offs();
-    wait_vmcnt<2 * BF_LPS>();
+    if (copier) wait_stage<BF_LPS>(BF_ST - 2);
     __syncthreads();
-    issue(rsa, rsb, BF_ST - 1, (gb + BF_ST - 1) & (BF_ST - 1));
-    read_frags(gb & (BF_ST - 1), ca, cb);
+    issue(rsa, rsb, BF_ST - 1, (gb + BF_ST - 1) % BF_ST);
+    read_frags(gb % BF_ST, ca, cb);
   }
 }
 
@@ -942,10 +990,11 @@ gemm_bf16_persist(const bf16_t* __restrict__ A, int64_t lda, const bf16_t* __res
 // in the blocked order of map_tile_blocks (XCD x takes the logical tiles
 // [x * ceil(T / 8), ...) round-robin), and the stage ring runs on across tile
 // boundaries as in gemm_bf16_persist.  What this buys is the epilogue: its
-// Epi::STORES stores per lane are issued after the first three stages of the
-// next tile and drain while those stages' MFMAs run.  The stage waits of the
-// next tile's first two K-steps count the stores as younger operations (so
-// they do not wait for them); the third waits for them.  With ATR, A is given
+// Epi::STORES stores per lane are issued after the first BF_ST - 1 stages of
+// the next tile and drain while those stages' MFMAs run.  The stage waits of
+// the next tile's first BF_ST - 2 K-steps count the stores as younger
+// operations (so they do not wait for them); the next one waits for them.
+// With ATR, A is given
 // as A^T in the tiled layout (G for dW) and read transposed, as in
 // gemm_bf16_kernel.  Requires K / BF_BK >= BF_ST stages and one split.
 template <class Epi, bool ATR>
@@ -954,7 +1003,7 @@ gemm_bf16_persist_t(const bf16_t* __restrict__ A, int64_t lda, const bf16_t* __r
                     int64_t ldb, int64_t M, int64_t N, int64_t K, int tiles_m, int tiles_n,
                     Epi epi) {
   constexpr int NST = Epi::STORES;
-  static_assert(2 * BF_LPS + NST + BF_LPS < 64, "stage waits must fit vmcnt");
+  static_assert((BF_ST - 2) * BT_LPS + NST < 64, "stage waits must fit vmcnt");
   __shared__ __attribute__((aligned(1024))) char lds[BF_LDS];
   const int total = tiles_m * tiles_n;
   const int per_xcd = gridDim.x >> 3;  // the grid is a multiple of 8
@@ -1008,20 +1057,18 @@ gemm_bf16_persist_t(const bf16_t* __restrict__ A, int64_t lda, const bf16_t* __r
   // an opaque copy of the lane index before the first tile and after every
   // epilogue.
   struct LaneOffs {
-    int oa[2], ob[2], fa, fb;
+    int oa, ob, fa, fb;
     int ftr[2][2];
   };
+  const bool copier = wave < BT_DMAW;
   auto lane_offs = [&]() {
     int l;
     __asm__ volatile("v_and_b32 %0, 63, %1" : "=v"(l) : "v"(tid));
     LaneOffs o;
-#pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      const int q = wave * 2 + i;
-      o.ob[i] = (q * 64 + l) * 16;
-      // ATR: wave instruction q copies half q & 1 (16 rows) of piece q >> 1
-      o.oa[i] = ATR ? (q >> 1) * TILE_BLOCK_BYTES + ((q & 1) * 16 + (l >> 2)) * 64 + (l & 3) * 16
-                    : o.ob[i];
+    {
+      const int q = wave * BT_PER;  // the copying wave's first piece (even)
+      o.ob = (q * 64 + l) * 16;
+      o.oa = ATR ? (q >> 1) * TILE_BLOCK_BYTES + (l >> 2) * 64 + (l & 3) * 16 : o.ob;
     }
     const int ch = l >> 4;
     int row = wm * 128 + (l & 15);
@@ -1042,6 +1089,7 @@ gemm_bf16_persist_t(const bf16_t* __restrict__ A, int64_t lda, const bf16_t* __r
   LaneOffs lof = lane_offs();
   const uint32_t lds_base = (uint32_t)reinterpret_cast<uintptr_t>(lds);
   auto issue = [&](const Tile& T, int kt, int slot) {
+    if (!copier) return;
     const uint32_t sa = lds_base + (uint32_t)(slot * BF_STAGE);
     const uint32_t sb = sa + BF_STAGE_A;
     i32x4 ra = T.ra;
@@ -1053,9 +1101,10 @@ gemm_bf16_persist_t(const bf16_t* __restrict__ A, int64_t lda, const bf16_t* __r
       abase = (kt & 7) * (TILE_ROWS / 8 * TILE_K * 2);
     }
 #pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      load_lds16(ra, sa + (uint32_t)((wave * 2 + i) * 1024), lof.oa[i] + abase);
-      load_lds16(T.rb, sb + (uint32_t)((wave * 2 + i) * 1024), lof.ob[i] + kt * TILE_BLOCK_BYTES);
+    for (int i = 0; i < BT_PER; ++i) {
+      const uint32_t dst = (uint32_t)((wave * BT_PER + i) * 1024);
+      load_lds16(ra, sa + dst, lof.oa, abase + (ATR ? atr_piece_step(i) : i * 1024));
+      load_lds16(T.rb, sb + dst, lof.ob, kt * TILE_BLOCK_BYTES + i * 1024);
     }
   };
   auto read_frags = [&](int slot, bf16x8 (&fa)[8], bf16x8 (&fb)[4]) {
@@ -1086,7 +1135,7 @@ gemm_bf16_persist_t(const bf16_t* __restrict__ A, int64_t lda, const bf16_t* __r
   int gb = 0;  // ring position of the current tile's stage 0
 #pragma unroll
   for (int s = 0; s < BF_ST - 1; ++s) issue(cur, s, s);
-  wait_vmcnt<2 * BF_LPS>();
+  if (copier) wait_stage<BT_LPS>(BF_ST - 2);
   __syncthreads();
   issue(cur, BF_ST - 1, BF_ST - 1);
   read_frags(0, ca, cb);
@@ -1106,17 +1155,17 @@ gemm_bf16_persist_t(const bf16_t* __restrict__ A, int64_t lda, const bf16_t* __r
 #pragma unroll
         for (int j = 0; j < 4; ++j)
           acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ca[i], cb[j], acc[i][j], 0, 0, 0);
-      // Await stage kt + 1.  Younger than it: two stages, plus (in the first
-      // two K-steps of a tile) the previous epilogue's stores.
-      if (stores_out && kt < 2)
-        wait_vmcnt<2 * BF_LPS + NST>();
-      else
-        wait_stage<BF_LPS>(has_next ? 2 : min(nk - 2 - kt, 2));
+      // Await stage kt + 1.  Younger than it: up to BF_ST - 2 stages (fewer
+      // at the end of the last tile), plus the previous epilogue's stores
+      // when stage kt + 1 was issued before them (stages 0 .. BF_ST-2).
+      if (copier)
+        wait_stage<BT_LPS, NST>(has_next ? BF_ST - 2 : min(nk - 2 - kt, BF_ST - 2),
+                                stores_out && kt + 1 <= BF_ST - 2);
       __syncthreads();
-      const int slot = (gb + kt) & (BF_ST - 1);
+      const int slot = (gb + kt) % BF_ST;
       if (kt + BF_ST < nk) issue(cur, kt + BF_ST, slot);
       else if (has_next) issue(nxt, kt + BF_ST - nk, slot);
-      read_frags((gb + kt + 1) & (BF_ST - 1), na, nb);
+      read_frags((gb + kt + 1) % BF_ST, na, nb);
 #pragma unroll
       for (int i = 4; i < 8; ++i)
 #pragma unroll
@@ -1150,19 +1199,19 @@ gemm_bf16_persist_t(const bf16_t* __restrict__ A, int64_t lda, const bf16_t* __r
     ctx.smem_bytes = 0;
     epi.template apply<Acc16, 8, 4, BF_BM, BF_BN>(acc, ctx);
     if (!has_next) break;
-    // Advance: stages 0..2 of the next tile were issued before the epilogue's
-    // stores; await stage 0 (younger: stages 1, 2 and the stores), then
-    // issue stage 3.
+    // Advance: stages 0 .. BF_ST-2 of the next tile were issued before the
+    // epilogue's stores; await stage 0 (younger: the other stages and the
+    // stores), then issue stage BF_ST-1.
     gb += nk;
     cur = nxt;
     tnext += per_xcd;
     has_next = tnext < hi;
     if (has_next) nxt = tile(tnext);
     lof = lane_offs();
-    wait_vmcnt<2 * BF_LPS + NST>();
+    if (copier) wait_stage<BT_LPS, NST>(BF_ST - 2, true);
     __syncthreads();
-    issue(cur, BF_ST - 1, (gb + BF_ST - 1) & (BF_ST - 1));
-    read_frags(gb & (BF_ST - 1), ca, cb);
+    issue(cur, BF_ST - 1, (gb + BF_ST - 1) % BF_ST);
+    read_frags(gb % BF_ST, ca, cb);
     stores_out = true;
   }
 }

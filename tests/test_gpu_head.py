@@ -141,6 +141,18 @@ def test_token_chunking_invariance():
     assert rel_fro(b["dW"], a["dW"]) <= 1e-5
 
 
+@pytest.mark.parametrize("chunk", [160, 129])
+def test_short_token_chunks_through_the_persistent_dW(chunk):
+    # dW's persistent kernel needs at least five 32-token K-steps: chunks of
+    # 129..160 tokens give exactly five (and the tail chunk fewer, which takes
+    # the one-tile kernel); V = 70000, H = 512 give more tiles than workgroups,
+    # so the epilogue stores of one tile overlap the next tile's first stages.
+    wl = _case("c5a_head64k_draws_ipo_k1", N=300, H=512, V=70000)
+    _, got = run_head(wl, token_chunk=chunk)
+    ref = ohead.from_workload(wl)
+    compare_all(wl, got, ref, case=f"token chunk {chunk}, V=70000, H=512")
+
+
 def test_bitwise_deterministic():
     wl = _case("c5a_head64k_draws_ipo_k1", N=260)
     fh, a = run_head(wl)
