@@ -125,7 +125,7 @@ def head_reference(h, W, labels, infer_logprobs, adv, params, offsets=None, ids=
         logprobs=np.zeros(n_tok), entropy=np.zeros(n_tok), lse=np.zeros(n_tok),
         weight=np.zeros(n_tok), keep=np.zeros(n_tok, bool), token_loss=np.zeros(n_tok),
         kappa=np.zeros(n_tok), kl=np.zeros(n_tok), support_mass=np.zeros(n_tok),
-        beta=np.zeros(n_tok),
+        beta=np.zeros(n_tok), zmax_abs=np.zeros(n_tok),
         support_count=np.zeros(n_tok, np.int64),
     )
     sup_lp = {}  # entry index -> log p(v_e)
@@ -205,6 +205,9 @@ def head_reference(h, W, labels, infer_logprobs, adv, params, offsets=None, ids=
         out["support_mass"][sel] = smass
         out["support_count"][sel] = cnt
         out["beta"][sel] = beta
+        # largest logit magnitude of the token (the scale of fp32 rounding in
+        # an implementation's logits, used by the tests' decision bands)
+        out["zmax_abs"][sel] = z.abs().max(dim=1).values.numpy()
         if progress is not None:
             progress(int(sel[-1]) + 1, n_tok)
     out["loss"] = out["token_loss"].sum() / D
