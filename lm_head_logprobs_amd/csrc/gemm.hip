@@ -422,7 +422,7 @@ struct DwEpiT {
   static constexpr int STORES = 32;
   template <class L, int MB, int NB, int BM, int BN>
   __device__ __forceinline__ void apply(typename L::V (&acc)[MB][NB], const EpiCtx& c) const {
-    static_assert(std::is_same<L, Acc16>::value && MB == 8 && NB == 4, "wave tile 128 x 64");
+    static_assert(std::is_same<L, Acc16>::value && MB * NB == 32, "32 blocks of 16 x 16");
     const int64_t rows = min<int64_t>(M - c.m0, BM), cols = min<int64_t>(N - c.n0, BN);
     const uint64_t a = reinterpret_cast<uint64_t>(C + c.m0 * ldc + c.n0);
     const uint64_t au = ((uint64_t)__builtin_amdgcn_readfirstlane((uint32_t)(a >> 32)) << 32) |
@@ -436,29 +436,29 @@ struct DwEpiT {
       const int rl = c.wm_off + 16 * i + 4 * g + b, cl = c.wn_off + 16 * j + 4 * q;
       return (rl < rows && cl < cols) ? (rl * ld + cl) * 4 : OOB;
     };
+    // Blocks in two batches of 16 (block q = (i, j) with i = q / NB, j = q % NB).
 #pragma unroll
     for (int half = 0; half < 2; ++half) {
-      u32x4 old[4][4];
+      u32x4 old[16];
       if constexpr (ACC) {
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
-#pragma unroll
-          for (int j = 0; j < 4; ++j)
-            old[i][j] = __builtin_bit_cast(
-                u32x4, __builtin_amdgcn_raw_buffer_load_b128(rs, offset(4 * half + i, j), 0, 0));
+        for (int e = 0; e < 16; ++e) {
+          const int q = 16 * half + e;
+          old[e] = __builtin_bit_cast(
+              u32x4, __builtin_amdgcn_raw_buffer_load_b128(rs, offset(q / NB, q % NB), 0, 0));
+        }
       }
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
+      for (int e = 0; e < 16; ++e) {
+        const int q = 16 * half + e;
+        f32x4 y = quad_transpose(acc[q / NB][q % NB], b);
+        if constexpr (ACC) {
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          f32x4 y = quad_transpose(acc[4 * half + i][j], b);
-          if constexpr (ACC) {
-#pragma unroll
-            for (int r = 0; r < 4; ++r) y[r] += __uint_as_float(old[i][j][r]);
-          }
-          __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, y), rs,
-                                                 offset(4 * half + i, j), 0, 0);
+          for (int r = 0; r < 4; ++r) y[r] += __uint_as_float(old[e][r]);
         }
+        __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, y), rs,
+                                               offset(q / NB, q % NB), 0, 0);
+      }
     }
   }
 };
@@ -554,6 +554,9 @@ constexpr int BF_PER = 16 / BF_DMAW;  // 1 KB pieces per operand per copying wav
 constexpr int BF_LPS = 2 * BF_PER;    // direct-to-LDS loads per copying wave per stage
 static_assert(BF_DMAW * BF_PER == 16 && BF_PER % 2 == 0, "copy split");
 // The persistent dW kernel's split (its waits also count 32 epilogue stores).
+// dW's wave layout: row blocks per wave (8: 2 x 4 waves of 128 x 64; 4: 4 x 2
+// waves of 64 x 128, which halves the transposing reads of G per wave).
+constexpr int DW_MB = 4;
 constexpr int BT_DMAW = 4;
 constexpr int BT_PER = 16 / BT_DMAW;
 constexpr int BT_LPS = 2 * BT_PER;
@@ -997,7 +1000,7 @@ gemm_bf16_persist(const bf16_t* __restrict__ A, int64_t lda, const bf16_t* __res
 // With ATR, A is given
 // as A^T in the tiled layout (G for dW) and read transposed, as in
 // gemm_bf16_kernel.  Requires K / BF_BK >= BF_ST stages and one split.
-template <class Epi, bool ATR>
+template <class Epi, bool ATR, int MB = 8>
 __global__ void __launch_bounds__(BF_NT) __attribute__((amdgpu_waves_per_eu(2, 2)))
 gemm_bf16_persist_t(const bf16_t* __restrict__ A, int64_t lda, const bf16_t* __restrict__ B,
                     int64_t ldb, int64_t M, int64_t N, int64_t K, int tiles_m, int tiles_n,
@@ -1013,7 +1016,11 @@ gemm_bf16_persist_t(const bf16_t* __restrict__ A, int64_t lda, const bf16_t* __r
   if (t >= hi) return;
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // 0..7
-  const int wm = wave >> 2, wn = wave & 3;
+  // Wave tiles of 16 MB x 16 NB (MB row blocks, NB column blocks of 16): 8 x 4
+  // blocks as 2 x 4 waves, or 4 x 8 blocks as 4 x 2 waves.
+  constexpr int NB = 32 / MB, WN = 16 / NB;
+  static_assert(MB == 8 || MB == 4, "wave layouts 2 x 4 and 4 x 2");
+  const int wm = wave / WN, wn = wave % WN;
   const int nk = (int)ceil_div(K, BF_BK);
   // Blocks of 4 x 8 tiles (M x N), N fastest inside a block.
   auto coords = [&](int lt, int64_t& m0, int64_t& n0) {
@@ -1071,9 +1078,9 @@ gemm_bf16_persist_t(const bf16_t* __restrict__ A, int64_t lda, const bf16_t* __r
       o.oa = ATR ? (q >> 1) * TILE_BLOCK_BYTES + (l >> 2) * 64 + (l & 3) * 16 : o.ob;
     }
     const int ch = l >> 4;
-    int row = wm * 128 + (l & 15);
+    int row = wm * 16 * MB + (l & 15);
     o.fa = row * 64 + 16 * (ch ^ tile_swz(row));
-    row = wn * 64 + (l & 15);
+    row = wn * 16 * NB + (l & 15);
     o.fb = BF_STAGE_A + row * 64 + 16 * (ch ^ tile_swz(row));
     const int g = l >> 4, j = l & 15;
 #pragma unroll
@@ -1107,14 +1114,15 @@ gemm_bf16_persist_t(const bf16_t* __restrict__ A, int64_t lda, const bf16_t* __r
       load_lds16(T.rb, sb + dst, lof.ob, kt * TILE_BLOCK_BYTES + i * 1024);
     }
   };
-  auto read_frags = [&](int slot, bf16x8 (&fa)[8], bf16x8 (&fb)[4]) {
+  auto read_frags = [&](int slot, bf16x8 (&fa)[MB], bf16x8 (&fb)[NB]) {
     const char* sn = lds + slot * BF_STAGE;
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
+    for (int i = 0; i < MB; ++i) {
       if constexpr (ATR) {
         typedef short v4s __attribute__((ext_vector_type(4)));
         typedef v4s __attribute__((address_space(3))) * lds_v4s;
-        const char* pc = sn + (4 * wm + (i >> 1)) * (BF_STAGE_A / 8);
+        // row block i of the wave is piece (wm MB + i) / 2 (32 rows each), half i & 1
+        const char* pc = sn + ((MB / 2) * wm + (i >> 1)) * (BF_STAGE_A / 8);
         const v4s lo4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s)(pc + lof.ftr[i & 1][0]));
         const v4s hi4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s)(pc + lof.ftr[i & 1][1]));
         fa[i] = __builtin_bit_cast(bf16x8,
@@ -1124,14 +1132,14 @@ gemm_bf16_persist_t(const bf16_t* __restrict__ A, int64_t lda, const bf16_t* __r
       }
     }
 #pragma unroll
-    for (int j = 0; j < 4; ++j) fb[j] = *reinterpret_cast<const bf16x8*>(sn + lof.fb + 1024 * j);
+    for (int j = 0; j < NB; ++j) fb[j] = *reinterpret_cast<const bf16x8*>(sn + lof.fb + 1024 * j);
   };
   Tile cur = tile(t);
   int tnext = t + per_xcd;
   bool has_next = tnext < hi;
   Tile nxt = cur;
   if (has_next) nxt = tile(tnext);
-  bf16x8 ca[8], cb[4];
+  bf16x8 ca[MB], cb[NB];
   int gb = 0;  // ring position of the current tile's stage 0
 #pragma unroll
   for (int s = 0; s < BF_ST - 1; ++s) issue(cur, s, s);
@@ -1141,20 +1149,20 @@ gemm_bf16_persist_t(const bf16_t* __restrict__ A, int64_t lda, const bf16_t* __r
   read_frags(0, ca, cb);
   bool stores_out = false;  // the previous tile's epilogue stores may be in flight
   for (;;) {
-    f32x4 acc[8][4];
+    f32x4 acc[MB][NB];
 #pragma unroll
-    for (int i = 0; i < 8; ++i)
+    for (int i = 0; i < MB; ++i)
 #pragma unroll
-      for (int j = 0; j < 4; ++j)
+      for (int j = 0; j < NB; ++j)
 #pragma unroll
         for (int r = 0; r < 4; ++r) acc[i][j][r] = 0.0f;
     for (int kt = 0; kt + 1 < nk; ++kt) {
-      bf16x8 na[8], nb[4];
+      bf16x8 na[MB], nb[NB];
+      // first half of the stage's MFMAs: blocks 0 .. 15 (block q = (q / NB, q % NB))
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
-#pragma unroll
-        for (int j = 0; j < 4; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ca[i], cb[j], acc[i][j], 0, 0, 0);
+      for (int q = 0; q < 16; ++q)
+        acc[q / NB][q % NB] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+            ca[q / NB], cb[q % NB], acc[q / NB][q % NB], 0, 0, 0);
       // Await stage kt + 1.  Younger than it: up to BF_ST - 2 stages (fewer
       // at the end of the last tile), plus the previous epilogue's stores
       // when stage kt + 1 was issued before them (stages 0 .. BF_ST-2).
@@ -1167,37 +1175,36 @@ gemm_bf16_persist_t(const bf16_t* __restrict__ A, int64_t lda, const bf16_t* __r
       else if (has_next) issue(nxt, kt + BF_ST - nk, slot);
       read_frags((gb + kt + 1) % BF_ST, na, nb);
 #pragma unroll
-      for (int i = 4; i < 8; ++i)
+      for (int q = 16; q < 32; ++q)
+        acc[q / NB][q % NB] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+            ca[q / NB], cb[q % NB], acc[q / NB][q % NB], 0, 0, 0);
 #pragma unroll
-        for (int j = 0; j < 4; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ca[i], cb[j], acc[i][j], 0, 0, 0);
+      for (int i = 0; i < MB; ++i) ca[i] = na[i];
 #pragma unroll
-      for (int i = 0; i < 8; ++i) ca[i] = na[i];
-#pragma unroll
-      for (int j = 0; j < 4; ++j) cb[j] = nb[j];
+      for (int j = 0; j < NB; ++j) cb[j] = nb[j];
     }
 #pragma unroll
-    for (int i = 0; i < 8; ++i)
+    for (int i = 0; i < MB; ++i)
 #pragma unroll
-      for (int j = 0; j < 4; ++j)
+      for (int j = 0; j < NB; ++j)
         acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ca[i], cb[j], acc[i][j], 0, 0, 0);
 #pragma unroll
-    for (int i = 0; i < 8; ++i)
+    for (int i = 0; i < MB; ++i)
 #pragma unroll
-      for (int j = 0; j < 4; ++j) __asm__ volatile("" : "+a"(acc[i][j]));
+      for (int j = 0; j < NB; ++j) __asm__ volatile("" : "+a"(acc[i][j]));
     int elane;
     __asm__ volatile("v_and_b32 %0, 63, %1" : "=v"(elane) : "v"(tid));
     EpiCtx ctx;
     ctx.m0 = cur.m0;
     ctx.n0 = cur.n0;
-    ctx.wm_off = wm * 128;
-    ctx.wn_off = wn * 64;
+    ctx.wm_off = wm * 16 * MB;
+    ctx.wn_off = wn * 16 * NB;
     ctx.wave_m = wm;
     ctx.lane = elane;
     ctx.split = 0;
     ctx.smem = nullptr;  // the ring is in use by the next tile's stages
     ctx.smem_bytes = 0;
-    epi.template apply<Acc16, 8, 4, BF_BM, BF_BN>(acc, ctx);
+    epi.template apply<Acc16, MB, NB, BF_BM, BF_BN>(acc, ctx);
     if (!has_next) break;
     // Advance: stages 0 .. BF_ST-2 of the next tile were issued before the
     // epilogue's stores; await stage 0 (younger: the other stages and the
@@ -1454,7 +1461,7 @@ hipError_t gemm_dw(int dtype, const void* A, int64_t lda, const void* B, int64_t
       if (ceil_div(K, BF_BK) * TILE_BLOCK_BYTES >= ((int64_t)1 << 31)) return hipErrorInvalidValue;
       const int64_t grid = std::min<int64_t>(round_up(total, 8), cus);
       auto go = [&](auto e) {
-        hipLaunchKernelGGL((gemm_bf16_persist_t<decltype(e), true>), dim3((unsigned)grid),
+        hipLaunchKernelGGL((gemm_bf16_persist_t<decltype(e), true, DW_MB>), dim3((unsigned)grid),
                            dim3(BF_NT), 0, s, static_cast<const bf16_t*>(A), lda,
                            static_cast<const bf16_t*>(B), ldb, M, N, K, (int)tm, (int)tn, e);
         return hipGetLastError();
