@@ -20,8 +20,8 @@ tokens whose logits stay below 4 in magnitude, wider on sharp ones.
 Decisions with a margin of at most 1e-6 (the stated band) and those in
 (1e-6, band] are counted separately, with how many of each actually differ;
 every decision beyond its band must agree.  Every comparison appends its
-figures to a JSON-lines report (RL_PARITY_REPORT, default
-gpurun_out/parity_report.jsonl).
+figures to a JSON-lines report: the file RL_PARITY_REPORT names, by default
+parity_report.jsonl in the folder whose contents a remote run hands back.
 """
 
 from __future__ import annotations
