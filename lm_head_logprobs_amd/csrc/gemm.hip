@@ -12,16 +12,17 @@
 //
 // bf16 kernel (the hot path).  A 512-thread workgroup (8 waves as 2x4, two
 // per SIMD) owns a 256 x 256 output tile; each wave owns 128 x 64 as 8 x 4
-// blocks of v_mfma_f32_16x16x32_bf16 with its 128 accumulators in AGPRs.
+// blocks of v_mfma_f32_16x16x32_bf16 with its 128 accumulators in AGPRs
+// (VGPRs in the persistent forward, whose epilogue reads each one twice).
 // With two waves per SIMD one wave's MFMAs keep the matrix pipe busy while
 // the other issues its loads or waits at the barrier.  With random
 // operands this shape sustains a higher MFMA rate than 32x32x16 (measured
 // about 84% against 72% of the dense peak in a loop without memory traffic).
-// K advances 32 at a time through a 5-stage ring of LDS buffers (32 KB each:
-// A then B; the whole 160 KB).
+// K advances 32 at a time through a 4-stage ring of LDS buffers (32 KB each:
+// A then B; 128 KB).
 // Operand tiles are copied global -> LDS by buffer_load_dwordx4 ... lds: each
 // wave instruction fills 1 KB of LDS (16 bytes per lane, consecutive), no
-// VGPR staging.  Loads run four stages ahead; a stage is waited for with an
+// VGPR staging.  Loads run three stages ahead; a stage is waited for with an
 // explicit vmcnt and one barrier, placed between the two K-steps of a stage so
 // MFMAs are in flight across it.  Out-of-range rows or K columns are given a
 // buffer offset past the descriptor's range, which the hardware reads as zero.
@@ -150,6 +151,13 @@ struct Acc16 {  // v_mfma_f32_16x16x32_bf16 : 16 x 16 blocks, 4 registers per la
     return x + __shfl_xor(x, 32, 64);
   }
   static __device__ __forceinline__ bool col_owner(int lane) { return lane < 16; }
+  static constexpr bool IN_VGPR = false;  // the accumulators live in AGPRs
+};
+// The same layout with the accumulators in VGPRs (the MFMAs' VGPR form): an
+// epilogue that reads every accumulator more than once then needs no AGPR
+// copies (v_accvgpr_read) for it.
+struct Acc16V : Acc16 {
+  static constexpr bool IN_VGPR = true;
 };
 
 // ------------------------------------------------------------- epilogues ---
@@ -209,6 +217,11 @@ template <typename T, bool FULL_, bool STORE_> struct FwdEpi {
       for (int i = 0; i < MB; ++i)
 #pragma unroll
         for (int j = 0; j < NB; ++j) __asm__ volatile("" : "+a"(acc[i][j]));
+    } else if constexpr (std::is_same<L, Acc16V>::value) {
+#pragma unroll
+      for (int i = 0; i < MB; ++i)
+#pragma unroll
+        for (int j = 0; j < NB; ++j) __asm__ volatile("" : "+v"(acc[i][j]));
     }
     __syncthreads();
 #pragma unroll
@@ -232,7 +245,7 @@ template <typename T, bool FULL_, bool STORE_> struct FwdEpi {
     // swizzle of a row depends on lane % 16 alone).
     T* pl = nullptr;
     if constexpr (TILED_P && STORE) {
-      static_assert(std::is_same<L, Acc16>::value, "tiled P store assumes the 16x16 layout");
+      static_assert(std::is_base_of<Acc16, L>::value, "tiled P store assumes the 16x16 layout");
       static_assert(MB % 2 == 0, "row blocks pair up into 32-row groups");
       const int g = c.lane >> 4, l = c.lane & 15;
       const int chunk = ((g & 1) << 1) | (g >> 1);
@@ -470,7 +483,7 @@ struct DwEpiT {
 constexpr int BF_BM = 256, BF_BN = 256, BF_BK = 32, BF_ST = 4;
 constexpr int BF_STAGE_A = BF_BM * BF_BK * 2;  // bytes
 constexpr int BF_STAGE = (BF_BM + BF_BN) * BF_BK * 2;
-constexpr int BF_LDS = BF_ST * BF_STAGE;  // the ring; the epilogues reuse it (160 KB)
+constexpr int BF_LDS = BF_ST * BF_STAGE;  // the ring; the epilogues reuse it (128 KB)
 static_assert(BF_LDS >= 6 * BF_BN * 4, "forward epilogue reductions");
 static_assert(BF_STAGE_A == TILE_BLOCK_BYTES, "a stage of one operand is one tiled block");
 
@@ -944,7 +957,7 @@ gemm_bf16_persist(const bf16_t* __restrict__ A, int64_t lda, const bf16_t* __res
 #pragma unroll
     for (int i = 0; i < 8; ++i)
 #pragma unroll
-      for (int j = 0; j < 4; ++j) __asm__ volatile("" : "+a"(acc[i][j]));
+      for (int j = 0; j < 4; ++j) __asm__ volatile("" : "+v"(acc[i][j]));
     // The lane index enters the epilogue through an opaque copy, so that
     // nothing the epilogue derives from it is hoisted out of the tile loop
     // (where it would hold registers through the K loop).
@@ -963,7 +976,7 @@ gemm_bf16_persist(const bf16_t* __restrict__ A, int64_t lda, const bf16_t* __res
     // opening barrier follows every wave's last fragment read from this one.
     ctx.smem = lds + ((gb + nk - 1) % BF_ST) * BF_STAGE;
     ctx.smem_bytes = BF_STAGE;
-    epi.template apply<Acc16, 8, 4, BF_BM, BF_BN>(acc, ctx);
+    epi.template apply<Acc16V, 8, 4, BF_BM, BF_BN>(acc, ctx);
     if (!has_next) break;
     // Advance: stages 0 .. BF_ST-2 of the next tile are in flight (issued in
     // the last iterations above); await stage 0, then, past a barrier that
