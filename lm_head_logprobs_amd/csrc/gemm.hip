@@ -1191,6 +1191,11 @@ gemm_bf16_persist_t(const bf16_t* __restrict__ A, int64_t lda, const bf16_t* __r
       for (int q = 16; q < 32; ++q)
         acc[q / NB][q % NB] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
             ca[q / NB], cb[q % NB], acc[q / NB][q % NB], 0, 0, 0);
+      // Keep the register moves that assemble the next A fragments (the two
+      // halves of a transposing read do not always land in adjacent
+      // registers) below these MFMAs: hoisted between them, their wait for
+      // the LDS reads stalled the wave's MFMA issue right after the barrier.
+      __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
       for (int i = 0; i < MB; ++i) ca[i] = na[i];
 #pragma unroll
