@@ -785,15 +785,16 @@ gemm_bf16_kernel(const bf16_t* __restrict__ A, int64_t lda, const bf16_t* __rest
 // forward, K = H): one workgroup per CU walks its tiles in order and the
 // stage ring runs on across tile boundaries, so the first stages of the next
 // tile are in flight while the epilogue of the current one runs (the
-// epilogue gets LDS of its own).  Tiles of XCD x are the logical tiles
+// epilogue's LDS is the ring slot of the tile's last stage).  Tiles of XCD x are the logical tiles
 // [x * ceil(T / 8), ...) of map_tile's order, taken round-robin by its
 // workgroups, so the tiles an XCD runs at once are consecutive as before.
 // Requires K to be a multiple of BF_BK with at least BF_ST stages.  The
 // epilogue's stores count in vmcnt like the loads, in issue order; a wait
 // that ignores them (counts only younger stages) also waits for the stores
 // issued after the awaited stage, which is correct and measured to cost
-// nothing here.
-template <class Epi>
+// nothing here.  EVEN_NK: the stage count K / BF_BK is even (fixed per
+// launch; it decides which fragment set holds the last stage).
+template <class Epi, bool EVEN_NK>
 __global__ void __launch_bounds__(BF_NT) __attribute__((amdgpu_waves_per_eu(2, 2)))
 gemm_bf16_persist(const bf16_t* __restrict__ A, int64_t lda, const bf16_t* __restrict__ B,
                   int64_t ldb, int64_t M, int64_t N, int64_t K, int tiles_m, int tiles_n,
@@ -884,7 +885,7 @@ gemm_bf16_persist(const bf16_t* __restrict__ A, int64_t lda, const bf16_t* __res
       load_lds16(rb, sb + dst, lof.ob, kbytes + i * sb_step);
     }
   };
-  bf16x8 ca[8], cb[4];
+  bf16x8 ca[8], cb[4], da[8], db[4];  // two fragment sets, used in turn
   auto read_frags = [&](int slot, bf16x8 (&fa)[8], bf16x8 (&fb)[4]) {
     const char* sn = lds + slot * BF_STAGE;
 #pragma unroll
@@ -900,7 +901,8 @@ gemm_bf16_persist(const bf16_t* __restrict__ A, int64_t lda, const bf16_t* __res
   if (copier) wait_stage<BF_LPS>(BF_ST - 2);
   __syncthreads();
   issue(rsa, rsb, BF_ST - 1, BF_ST - 1);
-  read_frags(0, ca, cb);
+  if constexpr (EVEN_NK) read_frags(0, da, db);
+  else read_frags(0, ca, cb);
   for (;;) {
     f32x4 acc[8][4];
 #pragma unroll
@@ -909,16 +911,15 @@ gemm_bf16_persist(const bf16_t* __restrict__ A, int64_t lda, const bf16_t* __res
       for (int j = 0; j < 4; ++j)
 #pragma unroll
         for (int r = 0; r < 4; ++r) acc[i][j][r] = 0.0f;
-    // Stages 0 .. nk-2 (each also refills and reads the next stage); the last
-    // stage is peeled off below, so no fragment register is undefined on
-    // the way out of the loop.
-    for (int kt = 0; kt + 1 < nk; ++kt) {
-      bf16x8 na[8], nb[4];
+    // Stage kt's MFMAs from fragments xa/xb, with stage kt+1 awaited, the
+    // buffer of stage kt refilled and stage kt+1's fragments read into ya/yb.
+    auto kstep = [&](int kt, bf16x8 (&xa)[8], bf16x8 (&xb)[4], bf16x8 (&ya)[8],
+                     bf16x8 (&yb)[4]) {
 #pragma unroll
       for (int i = 0; i < 4; ++i)
 #pragma unroll
         for (int j = 0; j < 4; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ca[i], cb[j], acc[i][j], 0, 0, 0);
+          acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xa[i], xb[j], acc[i][j], 0, 0, 0);
       // Stage kt+1 has landed once at most the stages issued after it are
       // outstanding (BF_ST - 2, except at the end of the last tile).
       if (copier) wait_stage<BF_LPS>(has_next ? BF_ST - 2 : min(nk - 2 - kt, BF_ST - 2));
@@ -928,12 +929,12 @@ gemm_bf16_persist(const bf16_t* __restrict__ A, int64_t lda, const bf16_t* __res
       const int slot = (gb + kt) % BF_ST;
       if (kt + BF_ST < nk) issue(rsa, rsb, kt + BF_ST, slot);
       else if (has_next) issue(nrsa, nrsb, kt + BF_ST - nk, slot);
-      read_frags((gb + kt + 1) % BF_ST, na, nb);
+      read_frags((gb + kt + 1) % BF_ST, ya, yb);
 #pragma unroll
       for (int i = 4; i < 8; ++i)
 #pragma unroll
         for (int j = 0; j < 4; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ca[i], cb[j], acc[i][j], 0, 0, 0);
+          acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xa[i], xb[j], acc[i][j], 0, 0, 0);
       // One fragment read of the next stage per MFMA of this half: measured
       // 0.07 ms faster on the forward shape than all reads first (the same
       // schedule makes the long-K dh GEMM slower, so that kernel keeps the
@@ -944,16 +945,31 @@ gemm_bf16_persist(const bf16_t* __restrict__ A, int64_t lda, const bf16_t* __res
         __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA
       }
       __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
+    };
+    auto last = [&](bf16x8 (&xa)[8], bf16x8 (&xb)[4]) {
 #pragma unroll
-      for (int i = 0; i < 8; ++i) ca[i] = na[i];
+      for (int i = 0; i < 8; ++i)
 #pragma unroll
-      for (int j = 0; j < 4; ++j) cb[j] = nb[j];
+        for (int j = 0; j < 4; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xa[i], xb[j], acc[i][j], 0, 0, 0);
+    };
+    // Stages 0 .. nk-2 in pairs, the two fragment sets swapping roles, so
+    // no register moves carry fragments from one stage to the next; the last
+    // stage is peeled off (no fragment register is undefined on the way out).
+    // With an even stage count, stage 0's fragments are in da/db and one step
+    // runs before the pairs, so the last stage always ends up in ca/cb: the
+    // parity is a template parameter, and no branch with live accumulators
+    // surrounds the loop.
+    int kt = 0;
+    if constexpr (EVEN_NK) {
+      kstep(0, da, db, ca, cb);
+      kt = 1;
     }
-#pragma unroll
-    for (int i = 0; i < 8; ++i)
-#pragma unroll
-      for (int j = 0; j < 4; ++j)
-        acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ca[i], cb[j], acc[i][j], 0, 0, 0);
+    for (; kt + 2 < nk; kt += 2) {
+      kstep(kt, ca, cb, da, db);
+      kstep(kt + 1, da, db, ca, cb);
+    }
+    last(ca, cb);  // kt = nk - 1
 #pragma unroll
     for (int i = 0; i < 8; ++i)
 #pragma unroll
@@ -997,7 +1013,8 @@ gemm_bf16_persist(const bf16_t* __restrict__ A, int64_t lda, const bf16_t* __res
     if (copier) wait_stage<BF_LPS>(BF_ST - 2);
     __syncthreads();
     issue(rsa, rsb, BF_ST - 1, (gb + BF_ST - 1) % BF_ST);
-    read_frags(gb % BF_ST, ca, cb);
+    if constexpr (EVEN_NK) read_frags(gb % BF_ST, da, db);
+    else read_frags(gb % BF_ST, ca, cb);
   }
 }
 
@@ -1393,8 +1410,12 @@ hipError_t launch_bf16_rows(const bf16_t* A, int64_t lda, const bf16_t* B, int64
     return launch_bf16<false>(A, lda, B, ldb, M, N, K, 1, round_up(K, BF_BK), epi, s);
   if ((int64_t)BF_BM * std::max(lda, ldb) * 2 >= ((int64_t)1 << 31)) return hipErrorInvalidValue;
   const int64_t grid = std::min<int64_t>(round_up(total, 8), cus);
-  hipLaunchKernelGGL((gemm_bf16_persist<Epi>), dim3((unsigned)grid), dim3(BF_NT), 0, s,
-                     A, lda, B, ldb, M, N, K, (int)tm, (int)tn, epi);
+  if ((K / BF_BK) % 2 == 0)
+    hipLaunchKernelGGL((gemm_bf16_persist<Epi, true>), dim3((unsigned)grid), dim3(BF_NT), 0, s,
+                       A, lda, B, ldb, M, N, K, (int)tm, (int)tn, epi);
+  else
+    hipLaunchKernelGGL((gemm_bf16_persist<Epi, false>), dim3((unsigned)grid), dim3(BF_NT), 0, s,
+                       A, lda, B, ldb, M, N, K, (int)tm, (int)tn, epi);
   return hipGetLastError();
 }
 
