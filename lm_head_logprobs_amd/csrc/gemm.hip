@@ -567,8 +567,9 @@ constexpr int BF_PER = 16 / BF_DMAW;  // 1 KB pieces per operand per copying wav
 constexpr int BF_LPS = 2 * BF_PER;    // direct-to-LDS loads per copying wave per stage
 static_assert(BF_DMAW * BF_PER == 16 && BF_PER % 2 == 0, "copy split");
 // The persistent dW kernel's split (its waits also count 32 epilogue stores).
-// dW's wave layout: row blocks per wave (8: 2 x 4 waves of 128 x 64; 4: 4 x 2
-// waves of 64 x 128, which halves the transposing reads of G per wave).
+// dW's wave layout: row blocks per wave (4: 4 x 2 waves of 64 x 128, which
+// halves the transposing reads of G per wave against 8, 2 x 4 waves of
+// 128 x 64; the main loop's read schedule assumes 4).
 constexpr int DW_MB = 4;
 constexpr int BT_DMAW = 4;
 constexpr int BT_PER = 16 / BT_DMAW;
@@ -727,40 +728,72 @@ gemm_bf16_kernel(const bf16_t* __restrict__ A, int64_t lda, const bf16_t* __rest
     if (copier) wait_stage<BF_LPS>(min(nk - 1, BF_ST - 2));
     __syncthreads();
     if (BF_ST - 1 < nk) issue(BF_ST - 1);
-    bf16x8 ca[8], cb[4];
+    // Two fragment sets used in turn (no register moves carry fragments from
+    // one stage to the next).  kstep: stage kt's MFMAs from x, with stage
+    // kt+1 awaited, the buffer of stage kt refilled and stage kt+1's
+    // fragments read into y.
+    bf16x8 ca[8], cb[4], da[8], db[4];
+    auto read_stage = [&](const char* sn, bf16x8 (&ya)[8], bf16x8 (&yb)[4]) {
 #pragma unroll
-    for (int i = 0; i < 8; ++i) ca[i] = read_a(lds, i);
+      for (int i = 0; i < 8; ++i) ya[i] = read_a(sn, i);
 #pragma unroll
-    for (int j = 0; j < 4; ++j) cb[j] = *reinterpret_cast<const bf16x8*>(lds + fb0 + 1024 * j);
-    for (int kt = 0; kt < nk; ++kt) {
-      bf16x8 na[8], nb[4];
+      for (int j = 0; j < 4; ++j) yb[j] = *reinterpret_cast<const bf16x8*>(sn + fb0 + 1024 * j);
+    };
+    auto kstep = [&](int kt, bf16x8 (&xa)[8], bf16x8 (&xb)[4], bf16x8 (&ya)[8],
+                     bf16x8 (&yb)[4]) {
 #pragma unroll
       for (int i = 0; i < 4; ++i)
 #pragma unroll
         for (int j = 0; j < 4; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ca[i], cb[j], acc[i][j], 0, 0, 0);
-      if (kt + 1 < nk) {
-        // Stage kt+1 has landed once at most the stages issued after it
-        // (kt+2, kt+3) are outstanding.
-        if (copier) wait_stage<BF_LPS>(min(nk - 2 - kt, BF_ST - 2));
-        __syncthreads();
-        if (kt + BF_ST < nk) issue(kt + BF_ST);  // into the buffer of stage kt
-        const char* sn = lds + ((kt + 1) % BF_ST) * BF_STAGE;
-#pragma unroll
-        for (int i = 0; i < 8; ++i) na[i] = read_a(sn, i);
-#pragma unroll
-        for (int j = 0; j < 4; ++j) nb[j] = *reinterpret_cast<const bf16x8*>(sn + fb0 + 1024 * j);
-      }
+          acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xa[i], xb[j], acc[i][j], 0, 0, 0);
+      // Stage kt+1 has landed once at most the stages issued after it
+      // (kt+2, kt+3) are outstanding.
+      if (copier) wait_stage<BF_LPS>(min(nk - 2 - kt, BF_ST - 2));
+      __syncthreads();
+      if (kt + BF_ST < nk) issue(kt + BF_ST);  // into the buffer of stage kt
+      read_stage(lds + ((kt + 1) % BF_ST) * BF_STAGE, ya, yb);
 #pragma unroll
       for (int i = 4; i < 8; ++i)
 #pragma unroll
         for (int j = 0; j < 4; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ca[i], cb[j], acc[i][j], 0, 0, 0);
+          acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xa[i], xb[j], acc[i][j], 0, 0, 0);
+      // One fragment read of the next stage per MFMA of this half (dh, the
+      // long-K contraction: 7.21 -> 6.79 ms on the 16k step against all
+      // reads first); the next step's MFMAs, which need those fragments,
+      // stay out of this half.  The transposed-A variant (20 reads; dW of
+      // short chunks) keeps all reads first.
+      if constexpr (ATR) {
+        __builtin_amdgcn_sched_group_barrier(0x100, 20, 0);  // LDS reads
+        __builtin_amdgcn_sched_group_barrier(0x008, 16, 0);  // MFMAs
+      } else {
 #pragma unroll
-      for (int i = 0; i < 8; ++i) ca[i] = na[i];
-#pragma unroll
-      for (int j = 0; j < 4; ++j) cb[j] = nb[j];
+        for (int q = 0; q < 12; ++q) {
+          __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // one LDS read
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA
+        }
+        __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    };
+    // With an even stage count one step runs before the pairs, so the last
+    // stage always ends up in ca/cb and no branch follows the loop.
+    int kt = 0;
+    if (nk % 2 == 0) {
+      read_stage(lds, da, db);
+      kstep(0, da, db, ca, cb);
+      kt = 1;
+    } else {
+      read_stage(lds, ca, cb);
     }
+    for (; kt + 2 < nk; kt += 2) {
+      kstep(kt, ca, cb, da, db);
+      kstep(kt + 1, da, db, ca, cb);
+    }
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ca[i], cb[j], acc[i][j], 0, 0, 0);
   }
   // Hand the accumulators to the epilogue as AGPR blocks: this keeps the
   // register allocator from rotating them through the main loop.
@@ -935,10 +968,8 @@ gemm_bf16_persist(const bf16_t* __restrict__ A, int64_t lda, const bf16_t* __res
 #pragma unroll
         for (int j = 0; j < 4; ++j)
           acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xa[i], xb[j], acc[i][j], 0, 0, 0);
-      // One fragment read of the next stage per MFMA of this half: measured
-      // 0.07 ms faster on the forward shape than all reads first (the same
-      // schedule makes the long-K dh GEMM slower, so that kernel keeps the
-      // compiler's order).
+      // One fragment read of the next stage per MFMA of this half: 8.65 ->
+      // 8.34 ms on the 16k step against all reads first.
 #pragma unroll
       for (int q = 0; q < 12; ++q) {
         __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // one LDS read
@@ -1030,7 +1061,7 @@ gemm_bf16_persist(const bf16_t* __restrict__ A, int64_t lda, const bf16_t* __res
 // With ATR, A is given
 // as A^T in the tiled layout (G for dW) and read transposed, as in
 // gemm_bf16_kernel.  Requires K / BF_BK >= BF_ST stages and one split.
-template <class Epi, bool ATR, int MB = 8>
+template <class Epi, bool ATR, int MB, bool EVEN_NK>
 __global__ void __launch_bounds__(BF_NT) __attribute__((amdgpu_waves_per_eu(2, 2)))
 gemm_bf16_persist_t(const bf16_t* __restrict__ A, int64_t lda, const bf16_t* __restrict__ B,
                     int64_t ldb, int64_t M, int64_t N, int64_t K, int tiles_m, int tiles_n,
@@ -1169,14 +1200,15 @@ gemm_bf16_persist_t(const bf16_t* __restrict__ A, int64_t lda, const bf16_t* __r
   bool has_next = tnext < hi;
   Tile nxt = cur;
   if (has_next) nxt = tile(tnext);
-  bf16x8 ca[MB], cb[NB];
+  bf16x8 ca[MB], cb[NB], da[MB], db[NB];  // two fragment sets, used in turn
   int gb = 0;  // ring position of the current tile's stage 0
 #pragma unroll
   for (int s = 0; s < BF_ST - 1; ++s) issue(cur, s, s);
   if (copier) wait_stage<BT_LPS>(BF_ST - 2);
   __syncthreads();
   issue(cur, BF_ST - 1, BF_ST - 1);
-  read_frags(0, ca, cb);
+  if constexpr (EVEN_NK) read_frags(0, da, db);
+  else read_frags(0, ca, cb);
   bool stores_out = false;  // the previous tile's epilogue stores may be in flight
   for (;;) {
     f32x4 acc[MB][NB];
@@ -1186,13 +1218,15 @@ gemm_bf16_persist_t(const bf16_t* __restrict__ A, int64_t lda, const bf16_t* __r
       for (int j = 0; j < NB; ++j)
 #pragma unroll
         for (int r = 0; r < 4; ++r) acc[i][j][r] = 0.0f;
-    for (int kt = 0; kt + 1 < nk; ++kt) {
-      bf16x8 na[MB], nb[NB];
+    // Stage kt's MFMAs from x, with stage kt+1 awaited, the buffer of stage
+    // kt refilled and stage kt+1's fragments read into y.
+    auto kstep = [&](int kt, bf16x8 (&xa)[MB], bf16x8 (&xb)[NB], bf16x8 (&ya)[MB],
+                     bf16x8 (&yb)[NB]) {
       // first half of the stage's MFMAs: blocks 0 .. 15 (block q = (q / NB, q % NB))
 #pragma unroll
       for (int q = 0; q < 16; ++q)
         acc[q / NB][q % NB] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-            ca[q / NB], cb[q % NB], acc[q / NB][q % NB], 0, 0, 0);
+            xa[q / NB], xb[q % NB], acc[q / NB][q % NB], 0, 0, 0);
       // Await stage kt + 1.  Younger than it: up to BF_ST - 2 stages (fewer
       // at the end of the last tile), plus the previous epilogue's stores
       // when stage kt + 1 was issued before them (stages 0 .. BF_ST-2).
@@ -1203,20 +1237,36 @@ gemm_bf16_persist_t(const bf16_t* __restrict__ A, int64_t lda, const bf16_t* __r
       const int slot = (gb + kt) % BF_ST;
       if (kt + BF_ST < nk) issue(cur, kt + BF_ST, slot);
       else if (has_next) issue(nxt, kt + BF_ST - nk, slot);
-      read_frags((gb + kt + 1) % BF_ST, na, nb);
+      read_frags((gb + kt + 1) % BF_ST, ya, yb);
 #pragma unroll
       for (int q = 16; q < 32; ++q)
         acc[q / NB][q % NB] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-            ca[q / NB], cb[q % NB], acc[q / NB][q % NB], 0, 0, 0);
-      // Keep the register moves that assemble the next A fragments (the two
-      // halves of a transposing read do not always land in adjacent
-      // registers) below these MFMAs: hoisted between them, their wait for
-      // the LDS reads stalled the wave's MFMA issue right after the barrier.
+            xa[q / NB], xb[q % NB], acc[q / NB][q % NB], 0, 0, 0);
+      // One fragment read of the next stage per MFMA of this half (16 reads
+      // with MB = 4: 8 transposing, 8 plain): 8.61 -> 8.20 ms on the 16k
+      // step against all reads first, and all reads first timed the same as
+      // the compiler's order.  The next step's MFMAs, which need those
+      // fragments (and, where the two halves of a transposing read did not
+      // land in adjacent registers, the moves that join them), stay below
+      // this half.
+      static_assert(!ATR || 2 * MB + NB == 16, "one fragment read per MFMA (the 4 x 2 layout)");
+#pragma unroll
+      for (int q = 0; q < 16; ++q) {
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // one LDS read
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA
+      }
       __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-      for (int i = 0; i < MB; ++i) ca[i] = na[i];
-#pragma unroll
-      for (int j = 0; j < NB; ++j) cb[j] = nb[j];
+    };
+    // With an even stage count one step runs before the pairs, so the last
+    // stage always ends up in ca/cb (the parity is fixed per launch).
+    int kt = 0;
+    if constexpr (EVEN_NK) {
+      kstep(0, da, db, ca, cb);
+      kt = 1;
+    }
+    for (; kt + 2 < nk; kt += 2) {
+      kstep(kt, ca, cb, da, db);
+      kstep(kt + 1, da, db, ca, cb);
     }
 #pragma unroll
     for (int i = 0; i < MB; ++i)
@@ -1253,7 +1303,8 @@ gemm_bf16_persist_t(const bf16_t* __restrict__ A, int64_t lda, const bf16_t* __r
     if (copier) wait_stage<BT_LPS, NST>(BF_ST - 2, true);
     __syncthreads();
     issue(cur, BF_ST - 1, (gb + BF_ST - 1) % BF_ST);
-    read_frags(gb % BF_ST, ca, cb);
+    if constexpr (EVEN_NK) read_frags(gb % BF_ST, da, db);
+    else read_frags(gb % BF_ST, ca, cb);
     stores_out = true;
   }
 }
@@ -1500,9 +1551,16 @@ hipError_t gemm_dw(int dtype, const void* A, int64_t lda, const void* B, int64_t
       if (ceil_div(K, BF_BK) * TILE_BLOCK_BYTES >= ((int64_t)1 << 31)) return hipErrorInvalidValue;
       const int64_t grid = std::min<int64_t>(round_up(total, 8), cus);
       auto go = [&](auto e) {
-        hipLaunchKernelGGL((gemm_bf16_persist_t<decltype(e), true, DW_MB>), dim3((unsigned)grid),
-                           dim3(BF_NT), 0, s, static_cast<const bf16_t*>(A), lda,
-                           static_cast<const bf16_t*>(B), ldb, M, N, K, (int)tm, (int)tn, e);
+        if (ceil_div(K, BF_BK) % 2 == 0)
+          hipLaunchKernelGGL((gemm_bf16_persist_t<decltype(e), true, DW_MB, true>),
+                             dim3((unsigned)grid), dim3(BF_NT), 0, s,
+                             static_cast<const bf16_t*>(A), lda, static_cast<const bf16_t*>(B),
+                             ldb, M, N, K, (int)tm, (int)tn, e);
+        else
+          hipLaunchKernelGGL((gemm_bf16_persist_t<decltype(e), true, DW_MB, false>),
+                             dim3((unsigned)grid), dim3(BF_NT), 0, s,
+                             static_cast<const bf16_t*>(A), lda, static_cast<const bf16_t*>(B),
+                             ldb, M, N, K, (int)tm, (int)tn, e);
         return hipGetLastError();
       };
       return accumulate ? go(DwEpiT<true>{C, ldc, M, N}) : go(DwEpiT<false>{C, ldc, M, N});
