@@ -552,6 +552,22 @@ __device__ __forceinline__ void wait_stage(int younger, bool stores = false) {
 }
 static_assert(BF_ST - 2 <= 3, "wait_stage covers up to three younger stages");
 
+// Of a stage's 32 MFMAs per wave, BF_PRE issue before the stage barrier and
+// the rest after it, interleaved with the next stage's fragment reads (one
+// read per MFMA while both last).
+constexpr int BF_PRE = 16;
+template <int NR, int NM>
+__device__ __forceinline__ void reads_between_mfmas() {
+  constexpr int P = NR < NM ? NR : NM;
+#pragma unroll
+  for (int q = 0; q < P; ++q) {
+    __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // one LDS read
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA
+  }
+  if constexpr (NR > P) __builtin_amdgcn_sched_group_barrier(0x100, NR - P, 0);
+  if constexpr (NM > P) __builtin_amdgcn_sched_group_barrier(0x008, NM - P, 0);
+}
+
 // TILED = false: A [M, lda] and B [N, ldb] row-major, any K (multiple of 8).
 // TILED = true: A and B in the tiled block layout (tiled_offset in
 // kernels.h) with lda / ldb = blocks per 256-row panel; K is a multiple of 32
@@ -569,7 +585,7 @@ static_assert(BF_DMAW * BF_PER == 16 && BF_PER % 2 == 0, "copy split");
 // The persistent dW kernel's split (its waits also count 32 epilogue stores).
 // dW's wave layout: row blocks per wave (4: 4 x 2 waves of 64 x 128, which
 // halves the transposing reads of G per wave against 8, 2 x 4 waves of
-// 128 x 64; the main loop's read schedule assumes 4).
+// 128 x 64).
 constexpr int DW_MB = 4;
 constexpr int BT_DMAW = 4;
 constexpr int BT_PER = 16 / BT_DMAW;
@@ -742,10 +758,9 @@ gemm_bf16_kernel(const bf16_t* __restrict__ A, int64_t lda, const bf16_t* __rest
     auto kstep = [&](int kt, bf16x8 (&xa)[8], bf16x8 (&xb)[4], bf16x8 (&ya)[8],
                      bf16x8 (&yb)[4]) {
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
-#pragma unroll
-        for (int j = 0; j < 4; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xa[i], xb[j], acc[i][j], 0, 0, 0);
+      for (int q = 0; q < BF_PRE; ++q)
+        acc[q / 4][q % 4] =
+            __builtin_amdgcn_mfma_f32_16x16x32_bf16(xa[q / 4], xb[q % 4], acc[q / 4][q % 4], 0, 0, 0);
       // Stage kt+1 has landed once at most the stages issued after it
       // (kt+2, kt+3) are outstanding.
       if (copier) wait_stage<BF_LPS>(min(nk - 2 - kt, BF_ST - 2));
@@ -753,25 +768,19 @@ gemm_bf16_kernel(const bf16_t* __restrict__ A, int64_t lda, const bf16_t* __rest
       if (kt + BF_ST < nk) issue(kt + BF_ST);  // into the buffer of stage kt
       read_stage(lds + ((kt + 1) % BF_ST) * BF_STAGE, ya, yb);
 #pragma unroll
-      for (int i = 4; i < 8; ++i)
-#pragma unroll
-        for (int j = 0; j < 4; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xa[i], xb[j], acc[i][j], 0, 0, 0);
-      // One fragment read of the next stage per MFMA of this half (dh, the
-      // long-K contraction: 7.21 -> 6.79 ms on the 16k step against all
+      for (int q = BF_PRE; q < 32; ++q)
+        acc[q / 4][q % 4] =
+            __builtin_amdgcn_mfma_f32_16x16x32_bf16(xa[q / 4], xb[q % 4], acc[q / 4][q % 4], 0, 0, 0);
+      // One fragment read of the next stage per MFMA after the barrier (dh,
+      // the long-K contraction: 7.21 -> 6.79 ms on the 16k step against all
       // reads first); the next step's MFMAs, which need those fragments,
-      // stay out of this half.  The transposed-A variant (20 reads; dW of
+      // stay out of this part.  The transposed-A variant (20 reads; dW of
       // short chunks) keeps all reads first.
       if constexpr (ATR) {
-        __builtin_amdgcn_sched_group_barrier(0x100, 20, 0);  // LDS reads
-        __builtin_amdgcn_sched_group_barrier(0x008, 16, 0);  // MFMAs
+        __builtin_amdgcn_sched_group_barrier(0x100, 20, 0);           // LDS reads
+        __builtin_amdgcn_sched_group_barrier(0x008, 32 - BF_PRE, 0);  // MFMAs
       } else {
-#pragma unroll
-        for (int q = 0; q < 12; ++q) {
-          __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // one LDS read
-          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA
-        }
-        __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
+        reads_between_mfmas<12, 32 - BF_PRE>();
       }
       __builtin_amdgcn_sched_barrier(0);
     };
@@ -949,10 +958,9 @@ gemm_bf16_persist(const bf16_t* __restrict__ A, int64_t lda, const bf16_t* __res
     auto kstep = [&](int kt, bf16x8 (&xa)[8], bf16x8 (&xb)[4], bf16x8 (&ya)[8],
                      bf16x8 (&yb)[4]) {
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
-#pragma unroll
-        for (int j = 0; j < 4; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xa[i], xb[j], acc[i][j], 0, 0, 0);
+      for (int q = 0; q < BF_PRE; ++q)
+        acc[q / 4][q % 4] =
+            __builtin_amdgcn_mfma_f32_16x16x32_bf16(xa[q / 4], xb[q % 4], acc[q / 4][q % 4], 0, 0, 0);
       // Stage kt+1 has landed once at most the stages issued after it are
       // outstanding (BF_ST - 2, except at the end of the last tile).
       if (copier) wait_stage<BF_LPS>(has_next ? BF_ST - 2 : min(nk - 2 - kt, BF_ST - 2));
@@ -964,18 +972,12 @@ gemm_bf16_persist(const bf16_t* __restrict__ A, int64_t lda, const bf16_t* __res
       else if (has_next) issue(nrsa, nrsb, kt + BF_ST - nk, slot);
       read_frags((gb + kt + 1) % BF_ST, ya, yb);
 #pragma unroll
-      for (int i = 4; i < 8; ++i)
-#pragma unroll
-        for (int j = 0; j < 4; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xa[i], xb[j], acc[i][j], 0, 0, 0);
-      // One fragment read of the next stage per MFMA of this half: 8.65 ->
-      // 8.34 ms on the 16k step against all reads first.
-#pragma unroll
-      for (int q = 0; q < 12; ++q) {
-        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // one LDS read
-        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA
-      }
-      __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
+      for (int q = BF_PRE; q < 32; ++q)
+        acc[q / 4][q % 4] =
+            __builtin_amdgcn_mfma_f32_16x16x32_bf16(xa[q / 4], xb[q % 4], acc[q / 4][q % 4], 0, 0, 0);
+      // One fragment read of the next stage per MFMA after the barrier: 8.65
+      // -> 8.34 ms on the 16k step against all reads first.
+      reads_between_mfmas<12, 32 - BF_PRE>();
     };
     auto last = [&](bf16x8 (&xa)[8], bf16x8 (&xb)[4]) {
 #pragma unroll
@@ -1224,7 +1226,7 @@ gemm_bf16_persist_t(const bf16_t* __restrict__ A, int64_t lda, const bf16_t* __r
                      bf16x8 (&yb)[NB]) {
       // first half of the stage's MFMAs: blocks 0 .. 15 (block q = (q / NB, q % NB))
 #pragma unroll
-      for (int q = 0; q < 16; ++q)
+      for (int q = 0; q < BF_PRE; ++q)
         acc[q / NB][q % NB] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
             xa[q / NB], xb[q % NB], acc[q / NB][q % NB], 0, 0, 0);
       // Await stage kt + 1.  Younger than it: up to BF_ST - 2 stages (fewer
@@ -1239,22 +1241,17 @@ gemm_bf16_persist_t(const bf16_t* __restrict__ A, int64_t lda, const bf16_t* __r
       else if (has_next) issue(nxt, kt + BF_ST - nk, slot);
       read_frags((gb + kt + 1) % BF_ST, ya, yb);
 #pragma unroll
-      for (int q = 16; q < 32; ++q)
+      for (int q = BF_PRE; q < 32; ++q)
         acc[q / NB][q % NB] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
             xa[q / NB], xb[q % NB], acc[q / NB][q % NB], 0, 0, 0);
-      // One fragment read of the next stage per MFMA of this half (16 reads
-      // with MB = 4: 8 transposing, 8 plain): 8.61 -> 8.20 ms on the 16k
-      // step against all reads first, and all reads first timed the same as
-      // the compiler's order.  The next step's MFMAs, which need those
-      // fragments (and, where the two halves of a transposing read did not
-      // land in adjacent registers, the moves that join them), stay below
-      // this half.
-      static_assert(!ATR || 2 * MB + NB == 16, "one fragment read per MFMA (the 4 x 2 layout)");
-#pragma unroll
-      for (int q = 0; q < 16; ++q) {
-        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // one LDS read
-        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA
-      }
+      // One fragment read of the next stage per MFMA after the barrier (16
+      // reads with MB = 4: 8 transposing, 8 plain): 8.61 -> 8.20 ms on the
+      // 16k step against all reads first, and all reads first timed the
+      // same as the compiler's order.  The next step's MFMAs, which need
+      // those fragments (and, where the two halves of a transposing read did
+      // not land in adjacent registers, the moves that join them), stay
+      // below this part.
+      reads_between_mfmas<(ATR ? 2 * MB : MB) + NB, 32 - BF_PRE>();
       __builtin_amdgcn_sched_barrier(0);
     };
     // With an even stage count one step runs before the pairs, so the last
