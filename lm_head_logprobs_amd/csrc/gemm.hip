@@ -928,12 +928,16 @@ gemm_bf16_persist(const bf16_t* __restrict__ A, int64_t lda, const bf16_t* __res
     }
   };
   bf16x8 ca[8], cb[4], da[8], db[4];  // two fragment sets, used in turn
+  // In the order the MFMAs consume them: row block 0, the column blocks, the
+  // other row blocks (the forward 0.04 ms faster per 16k step; dh and dW keep
+  // row blocks first, 0.01 and 0.05 ms faster that way).
   auto read_frags = [&](int slot, bf16x8 (&fa)[8], bf16x8 (&fb)[4]) {
     const char* sn = lds + slot * BF_STAGE;
-#pragma unroll
-    for (int i = 0; i < 8; ++i) fa[i] = *reinterpret_cast<const bf16x8*>(sn + lof.fa + 1024 * i);
+    fa[0] = *reinterpret_cast<const bf16x8*>(sn + lof.fa);
 #pragma unroll
     for (int j = 0; j < 4; ++j) fb[j] = *reinterpret_cast<const bf16x8*>(sn + lof.fb + 1024 * j);
+#pragma unroll
+    for (int i = 1; i < 8; ++i) fa[i] = *reinterpret_cast<const bf16x8*>(sn + lof.fa + 1024 * i);
   };
   // First tile: stages 0 .. BF_ST-2, then stage 0 awaited, stage BF_ST-1
   // issued.
