@@ -1226,8 +1226,14 @@ gemm_bf16_persist_t(const bf16_t* __restrict__ A, int64_t lda, const bf16_t* __r
         for (int r = 0; r < 4; ++r) acc[i][j][r] = 0.0f;
     // Stage kt's MFMAs from x, with stage kt+1 awaited, the buffer of stage
     // kt refilled and stage kt+1's fragments read into y.
-    auto kstep = [&](int kt, bf16x8 (&xa)[MB], bf16x8 (&xb)[NB], bf16x8 (&ya)[MB],
-                     bf16x8 (&yb)[NB]) {
+    // STEADY (a compile-time flag) marks the steps with kt >= BF_ST - 2 and
+    // kt + BF_ST < nk: no previous stores are younger than stage kt + 1,
+    // BF_ST - 2 stages are, and the refill is this tile's stage kt + BF_ST,
+    // so the wait and the refill need no run-time choice (which otherwise
+    // costs a cascade of scalar branches per step).
+    auto kstep = [&](auto steady, int kt, bf16x8 (&xa)[MB], bf16x8 (&xb)[NB],
+                     bf16x8 (&ya)[MB], bf16x8 (&yb)[NB]) {
+      constexpr bool STEADY = decltype(steady)::value;
       // first half of the stage's MFMAs: blocks 0 .. 15 (block q = (q / NB, q % NB))
 #pragma unroll
       for (int q = 0; q < BF_PRE; ++q)
@@ -1236,14 +1242,22 @@ gemm_bf16_persist_t(const bf16_t* __restrict__ A, int64_t lda, const bf16_t* __r
       // Await stage kt + 1.  Younger than it: up to BF_ST - 2 stages (fewer
       // at the end of the last tile), plus the previous epilogue's stores
       // when stage kt + 1 was issued before them (stages 0 .. BF_ST-2).
-      if (copier)
-        wait_stage<BT_LPS, NST>(has_next ? BF_ST - 2 : min(nk - 2 - kt, BF_ST - 2),
-                                stores_out && kt + 1 <= BF_ST - 2);
+      if constexpr (STEADY) {
+        if (copier) wait_vmcnt<(BF_ST - 2) * BT_LPS>();
+      } else {
+        if (copier)
+          wait_stage<BT_LPS, NST>(has_next ? BF_ST - 2 : min(nk - 2 - kt, BF_ST - 2),
+                                  stores_out && kt + 1 <= BF_ST - 2);
+      }
       __syncthreads();
-      const int slot = (gb + kt) % BF_ST;
-      if (kt + BF_ST < nk) issue(cur, kt + BF_ST, slot);
-      else if (has_next) issue(nxt, kt + BF_ST - nk, slot);
-      read_frags((gb + kt + 1) % BF_ST, ya, yb);
+      const int slot = (unsigned)(gb + kt) % BF_ST;
+      if constexpr (STEADY) {
+        issue(cur, kt + BF_ST, slot);
+      } else {
+        if (kt + BF_ST < nk) issue(cur, kt + BF_ST, slot);
+        else if (has_next) issue(nxt, kt + BF_ST - nk, slot);
+      }
+      read_frags((unsigned)(gb + kt + 1) % BF_ST, ya, yb);
 #pragma unroll
       for (int q = BF_PRE; q < 32; ++q)
         acc[q / NB][q % NB] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
@@ -1259,15 +1273,30 @@ gemm_bf16_persist_t(const bf16_t* __restrict__ A, int64_t lda, const bf16_t* __r
       __builtin_amdgcn_sched_barrier(0);
     };
     // With an even stage count one step runs before the pairs, so the last
-    // stage always ends up in ca/cb (the parity is fixed per launch).
+    // stage always ends up in ca/cb (the parity is fixed per launch).  With
+    // an even count (the default chunk) the pairs run in three loops: the
+    // first steps (previous stores may be younger), the steady middle, the
+    // last steps (the refill switches to the next tile, and at the end of the
+    // last tile fewer stages follow).  An odd count takes the general steps
+    // throughout (the split made the compiler spill in that variant).
+    const std::false_type gen;
+    const std::true_type std_;
     int kt = 0;
     if constexpr (EVEN_NK) {
-      kstep(0, da, db, ca, cb);
+      kstep(gen, 0, da, db, ca, cb);
       kt = 1;
+      for (; kt < BF_ST - 2 && kt + 2 < nk; kt += 2) {
+        kstep(gen, kt, ca, cb, da, db);
+        kstep(gen, kt + 1, da, db, ca, cb);
+      }
+      for (; kt + 1 + BF_ST < nk; kt += 2) {
+        kstep(std_, kt, ca, cb, da, db);
+        kstep(std_, kt + 1, da, db, ca, cb);
+      }
     }
     for (; kt + 2 < nk; kt += 2) {
-      kstep(kt, ca, cb, da, db);
-      kstep(kt + 1, da, db, ca, cb);
+      kstep(gen, kt, ca, cb, da, db);
+      kstep(gen, kt + 1, da, db, ca, cb);
     }
 #pragma unroll
     for (int i = 0; i < MB; ++i)
