@@ -755,18 +755,25 @@ gemm_bf16_kernel(const bf16_t* __restrict__ A, int64_t lda, const bf16_t* __rest
 #pragma unroll
       for (int j = 0; j < 4; ++j) yb[j] = *reinterpret_cast<const bf16x8*>(sn + fb0 + 1024 * j);
     };
-    auto kstep = [&](int kt, bf16x8 (&xa)[8], bf16x8 (&xb)[4], bf16x8 (&ya)[8],
+    // STEADY (compile time): kt + BF_ST < nk, so BF_ST - 2 stages are
+    // younger than stage kt + 1 and stage kt + BF_ST is refilled.
+    auto kstep = [&](auto steady, int kt, bf16x8 (&xa)[8], bf16x8 (&xb)[4], bf16x8 (&ya)[8],
                      bf16x8 (&yb)[4]) {
+      constexpr bool STEADY = decltype(steady)::value;
 #pragma unroll
       for (int q = 0; q < BF_PRE; ++q)
         acc[q / 4][q % 4] =
             __builtin_amdgcn_mfma_f32_16x16x32_bf16(xa[q / 4], xb[q % 4], acc[q / 4][q % 4], 0, 0, 0);
       // Stage kt+1 has landed once at most the stages issued after it
       // (kt+2, kt+3) are outstanding.
-      if (copier) wait_stage<BF_LPS>(min(nk - 2 - kt, BF_ST - 2));
+      if constexpr (STEADY) {
+        if (copier) wait_vmcnt<(BF_ST - 2) * BF_LPS>();
+      } else {
+        if (copier) wait_stage<BF_LPS>(min(nk - 2 - kt, BF_ST - 2));
+      }
       __syncthreads();
-      if (kt + BF_ST < nk) issue(kt + BF_ST);  // into the buffer of stage kt
-      read_stage(lds + ((kt + 1) % BF_ST) * BF_STAGE, ya, yb);
+      if (STEADY || kt + BF_ST < nk) issue(kt + BF_ST);  // into the buffer of stage kt
+      read_stage(lds + ((unsigned)(kt + 1) % BF_ST) * BF_STAGE, ya, yb);
 #pragma unroll
       for (int q = BF_PRE; q < 32; ++q)
         acc[q / 4][q % 4] =
@@ -786,17 +793,23 @@ gemm_bf16_kernel(const bf16_t* __restrict__ A, int64_t lda, const bf16_t* __rest
     };
     // With an even stage count one step runs before the pairs, so the last
     // stage always ends up in ca/cb and no branch follows the loop.
+    const std::false_type gen;
+    const std::true_type std_;
     int kt = 0;
     if (nk % 2 == 0) {
       read_stage(lds, da, db);
-      kstep(0, da, db, ca, cb);
+      kstep(gen, 0, da, db, ca, cb);
       kt = 1;
     } else {
       read_stage(lds, ca, cb);
     }
+    for (; kt + 1 + BF_ST < nk; kt += 2) {
+      kstep(std_, kt, ca, cb, da, db);
+      kstep(std_, kt + 1, da, db, ca, cb);
+    }
     for (; kt + 2 < nk; kt += 2) {
-      kstep(kt, ca, cb, da, db);
-      kstep(kt + 1, da, db, ca, cb);
+      kstep(gen, kt, ca, cb, da, db);
+      kstep(gen, kt + 1, da, db, ca, cb);
     }
 #pragma unroll
     for (int i = 0; i < 8; ++i)
@@ -959,22 +972,34 @@ gemm_bf16_persist(const bf16_t* __restrict__ A, int64_t lda, const bf16_t* __res
         for (int r = 0; r < 4; ++r) acc[i][j][r] = 0.0f;
     // Stage kt's MFMAs from fragments xa/xb, with stage kt+1 awaited, the
     // buffer of stage kt refilled and stage kt+1's fragments read into ya/yb.
-    auto kstep = [&](int kt, bf16x8 (&xa)[8], bf16x8 (&xb)[4], bf16x8 (&ya)[8],
+    // STEADY (compile time) marks the steps with kt + BF_ST < nk: BF_ST - 2
+    // stages are younger than stage kt + 1 and the refill is this tile's
+    // stage kt + BF_ST, so the wait and the refill need no run-time choice.
+    auto kstep = [&](auto steady, int kt, bf16x8 (&xa)[8], bf16x8 (&xb)[4], bf16x8 (&ya)[8],
                      bf16x8 (&yb)[4]) {
+      constexpr bool STEADY = decltype(steady)::value;
 #pragma unroll
       for (int q = 0; q < BF_PRE; ++q)
         acc[q / 4][q % 4] =
             __builtin_amdgcn_mfma_f32_16x16x32_bf16(xa[q / 4], xb[q % 4], acc[q / 4][q % 4], 0, 0, 0);
       // Stage kt+1 has landed once at most the stages issued after it are
       // outstanding (BF_ST - 2, except at the end of the last tile).
-      if (copier) wait_stage<BF_LPS>(has_next ? BF_ST - 2 : min(nk - 2 - kt, BF_ST - 2));
+      if constexpr (STEADY) {
+        if (copier) wait_vmcnt<(BF_ST - 2) * BF_LPS>();
+      } else {
+        if (copier) wait_stage<BF_LPS>(has_next ? BF_ST - 2 : min(nk - 2 - kt, BF_ST - 2));
+      }
       __syncthreads();
       // Refill the buffer of stage kt with stage kt + BF_ST of this tile or,
       // past its end, with the first stages of the next tile.
-      const int slot = (gb + kt) % BF_ST;
-      if (kt + BF_ST < nk) issue(rsa, rsb, kt + BF_ST, slot);
-      else if (has_next) issue(nrsa, nrsb, kt + BF_ST - nk, slot);
-      read_frags((gb + kt + 1) % BF_ST, ya, yb);
+      const int slot = (unsigned)(gb + kt) % BF_ST;
+      if constexpr (STEADY) {
+        issue(rsa, rsb, kt + BF_ST, slot);
+      } else {
+        if (kt + BF_ST < nk) issue(rsa, rsb, kt + BF_ST, slot);
+        else if (has_next) issue(nrsa, nrsb, kt + BF_ST - nk, slot);
+      }
+      read_frags((unsigned)(gb + kt + 1) % BF_ST, ya, yb);
 #pragma unroll
       for (int q = BF_PRE; q < 32; ++q)
         acc[q / 4][q % 4] =
@@ -997,14 +1022,23 @@ gemm_bf16_persist(const bf16_t* __restrict__ A, int64_t lda, const bf16_t* __res
     // runs before the pairs, so the last stage always ends up in ca/cb: the
     // parity is a template parameter, and no branch with live accumulators
     // surrounds the loop.
+    // The pairs run in two loops: the steady ones, then the last steps
+    // (whose refill switches to the next tile, and at the end of the last
+    // tile fewer stages follow).
+    const std::false_type gen;
+    const std::true_type std_;
     int kt = 0;
     if constexpr (EVEN_NK) {
-      kstep(0, da, db, ca, cb);
+      kstep(gen, 0, da, db, ca, cb);
       kt = 1;
     }
+    for (; kt + 1 + BF_ST < nk; kt += 2) {
+      kstep(std_, kt, ca, cb, da, db);
+      kstep(std_, kt + 1, da, db, ca, cb);
+    }
     for (; kt + 2 < nk; kt += 2) {
-      kstep(kt, ca, cb, da, db);
-      kstep(kt + 1, da, db, ca, cb);
+      kstep(gen, kt, ca, cb, da, db);
+      kstep(gen, kt + 1, da, db, ca, cb);
     }
     last(ca, cb);  // kt = nk - 1
 #pragma unroll
