@@ -511,6 +511,23 @@ __device__ __forceinline__ void load_lds16(i32x4 rsrc, uint32_t lds_addr, int vo
   asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, %3 offen lds"
                :: "s"(lds_addr), "v"(voffset), "s"(rsrc), "s"(soffset) : "memory");
 }
+// Four such loads of consecutive 1 KB pieces (source and destination both
+// step by 1 KB) under one M0: the instruction's immediate offset moves the
+// LDS destination as well as the source (checked on the GPU).
+__device__ __forceinline__ void load_lds16_x4(i32x4 rsrc, uint32_t lds_addr, int voffset,
+                                              int soffset = 0) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i) rsrc[i] = __builtin_amdgcn_readfirstlane(rsrc[i]);
+  lds_addr = __builtin_amdgcn_readfirstlane(lds_addr);
+  soffset = __builtin_amdgcn_readfirstlane(soffset);
+  asm volatile(
+      "s_mov_b32 m0, %0\n\ts_nop 0\n\t"
+      "buffer_load_dwordx4 %1, %2, %3 offen lds\n\t"
+      "buffer_load_dwordx4 %1, %2, %3 offen offset:1024 lds\n\t"
+      "buffer_load_dwordx4 %1, %2, %3 offen offset:2048 lds\n\t"
+      "buffer_load_dwordx4 %1, %2, %3 offen offset:3072 lds"
+      :: "s"(lds_addr), "v"(voffset), "s"(rsrc), "s"(soffset) : "memory");
+}
 
 // ATR pieces: wave instruction q copies half q & 1 (16 rows) of piece q >> 1;
 // the byte offset of a copying wave's piece i from its first (q even).
@@ -684,11 +701,25 @@ gemm_bf16_kernel(const bf16_t* __restrict__ A, int64_t lda, const bf16_t* __rest
       oa = kok ? offa + 2 * k0 : OOB;
       ob = kok ? offb + 2 * k0 : OOB;
     }
+    if constexpr (TILED && BF_PER == 4) {
+      // tiled operands: a copying wave's four pieces are consecutive 1 KB
+      // runs of one block (A only without ATR)
+      const uint32_t dst = (uint32_t)(wave * BF_PER * 1024);
+      if constexpr (ATR) {
 #pragma unroll
-    for (int i = 0; i < BF_PER; ++i) {
-      const uint32_t dst = (uint32_t)((wave * BF_PER + i) * 1024);
-      load_lds16(ra, sa + dst, oa, ATR ? atr_piece_step(i) : i * sa_step);
-      load_lds16(rsb, sb + dst, ob, i * sb_step);
+        for (int i = 0; i < BF_PER; ++i)
+          load_lds16(ra, sa + dst + i * 1024, oa, atr_piece_step(i));
+      } else {
+        load_lds16_x4(ra, sa + dst, oa);
+      }
+      load_lds16_x4(rsb, sb + dst, ob);
+    } else {
+#pragma unroll
+      for (int i = 0; i < BF_PER; ++i) {
+        const uint32_t dst = (uint32_t)((wave * BF_PER + i) * 1024);
+        load_lds16(ra, sa + dst, oa, ATR ? atr_piece_step(i) : i * sa_step);
+        load_lds16(rsb, sb + dst, ob, i * sb_step);
+      }
     }
   };
   // Fragment byte offsets inside a stage: in 16-row block i the lane reads
@@ -1208,12 +1239,13 @@ gemm_bf16_persist_t(const bf16_t* __restrict__ A, int64_t lda, const bf16_t* __r
                      T.a_bytes);
       abase = (kt & 7) * (TILE_ROWS / 8 * TILE_K * 2);
     }
+    static_assert(BT_PER == 4, "four 1 KB pieces per operand and copying wave");
 #pragma unroll
     for (int i = 0; i < BT_PER; ++i) {
       const uint32_t dst = (uint32_t)((wave * BT_PER + i) * 1024);
       load_lds16(ra, sa + dst, lof.oa, abase + (ATR ? atr_piece_step(i) : i * 1024));
-      load_lds16(T.rb, sb + dst, lof.ob, kt * TILE_BLOCK_BYTES + i * 1024);
     }
+    load_lds16_x4(T.rb, sb + (uint32_t)(wave * BT_PER * 1024), lof.ob, kt * TILE_BLOCK_BYTES);
   };
   auto read_frags = [&](int slot, bf16x8 (&fa)[MB], bf16x8 (&fb)[NB]) {
     const char* sn = lds + slot * BF_STAGE;
