@@ -511,6 +511,24 @@ __device__ __forceinline__ void load_lds16(i32x4 rsrc, uint32_t lds_addr, int vo
   asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, %3 offen lds"
                :: "s"(lds_addr), "v"(voffset), "s"(rsrc), "s"(soffset) : "memory");
 }
+// Four loads into consecutive 1 KB of LDS under one M0, from four per-lane
+// source offsets: load i adds the immediate offset i KB to both its source
+// and its destination, so v_i must hold the piece's source offset less i KB.
+__device__ __forceinline__ void load_lds16_4v(i32x4 rsrc, uint32_t lds_addr, int v0, int v1,
+                                              int v2, int v3, int soffset) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i) rsrc[i] = __builtin_amdgcn_readfirstlane(rsrc[i]);
+  lds_addr = __builtin_amdgcn_readfirstlane(lds_addr);
+  soffset = __builtin_amdgcn_readfirstlane(soffset);
+  asm volatile(
+      "s_mov_b32 m0, %0\n\ts_nop 0\n\t"
+      "buffer_load_dwordx4 %1, %5, %6 offen lds\n\t"
+      "buffer_load_dwordx4 %2, %5, %6 offen offset:1024 lds\n\t"
+      "buffer_load_dwordx4 %3, %5, %6 offen offset:2048 lds\n\t"
+      "buffer_load_dwordx4 %4, %5, %6 offen offset:3072 lds"
+      :: "s"(lds_addr), "v"(v0), "v"(v1), "v"(v2), "v"(v3), "s"(rsrc), "s"(soffset)
+      : "memory");
+}
 // Four such loads of consecutive 1 KB pieces (source and destination both
 // step by 1 KB) under one M0: the instruction's immediate offset moves the
 // LDS destination as well as the source (checked on the GPU).
@@ -902,11 +920,13 @@ gemm_bf16_persist(const bf16_t* __restrict__ A, int64_t lda, const bf16_t* __res
   // of BF_BK here) and the fragment reads.  They are formed from an opaque
   // copy of the lane index before the first tile and again after every
   // epilogue, so they are not live (and not spilled) across the epilogue.
+  static_assert(BF_PER == 4, "four pieces per operand and copying wave");
   struct LaneOffs {
-    int oa, ob, fa, fb;
+    int oa[4], ob[4], fa, fb;
   };
   const bool copier = wave < BF_DMAW;
-  // A copying wave's piece i is 16 rows below its piece 0 (same swizzle).
+  // A copying wave's piece i is 16 rows below its piece 0 (same swizzle);
+  // its source offset is stored less i KB (the loads' immediate offsets).
   const int sa_step = (int)(16 * lda * 2), sb_step = (int)(16 * ldb * 2);
   auto lane_offs = [&]() {
     int l;
@@ -915,8 +935,11 @@ gemm_bf16_persist(const bf16_t* __restrict__ A, int64_t lda, const bf16_t* __res
     {
       const int p = wave * BF_PER * 64 + l;
       const int row = p >> 2, ch = (p & 3) ^ tile_swz(row);
-      o.oa = (int)((row * lda + 8 * ch) * 2);
-      o.ob = (int)((row * ldb + 8 * ch) * 2);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        o.oa[i] = (int)((row * lda + 8 * ch) * 2) + i * (sa_step - 1024);
+        o.ob[i] = (int)((row * ldb + 8 * ch) * 2) + i * (sb_step - 1024);
+      }
     }
     const int ch = l >> 4;
     int row = wm * 128 + (l & 15);
@@ -964,12 +987,9 @@ gemm_bf16_persist(const bf16_t* __restrict__ A, int64_t lda, const bf16_t* __res
     const uint32_t sb = sa + BF_STAGE_A;
     int kbytes;
     __asm__ volatile("s_lshl_b32 %0, %1, 6" : "=s"(kbytes) : "s"(kt));  // kt * BF_BK * 2
-#pragma unroll
-    for (int i = 0; i < BF_PER; ++i) {
-      const uint32_t dst = (uint32_t)((wave * BF_PER + i) * 1024);
-      load_lds16(ra, sa + dst, lof.oa, kbytes + i * sa_step);
-      load_lds16(rb, sb + dst, lof.ob, kbytes + i * sb_step);
-    }
+    const uint32_t dst = (uint32_t)(wave * BF_PER * 1024);
+    load_lds16_4v(ra, sa + dst, lof.oa[0], lof.oa[1], lof.oa[2], lof.oa[3], kbytes);
+    load_lds16_4v(rb, sb + dst, lof.ob[0], lof.ob[1], lof.ob[2], lof.ob[3], kbytes);
   };
   bf16x8 ca[8], cb[4], da[8], db[4];  // two fragment sets, used in turn
   // In the order the MFMAs consume them: row block 0, the column blocks, the
