@@ -1216,7 +1216,7 @@ gemm_bf16_persist_t(const bf16_t* __restrict__ A, int64_t lda, const bf16_t* __r
   // an opaque copy of the lane index before the first tile and after every
   // epilogue.
   struct LaneOffs {
-    int oa, ob, fa, fb;
+    int oa, oa2, ob, fa, fb;  // oa2: the source of pieces 2, 3 less their 2 and 3 KB steps
     int ftr[2][2];
   };
   const bool copier = wave < BT_DMAW;
@@ -1228,6 +1228,7 @@ gemm_bf16_persist_t(const bf16_t* __restrict__ A, int64_t lda, const bf16_t* __r
       const int q = wave * BT_PER;  // the copying wave's first piece (even)
       o.ob = (q * 64 + l) * 16;
       o.oa = ATR ? (q >> 1) * TILE_BLOCK_BYTES + (l >> 2) * 64 + (l & 3) * 16 : o.ob;
+      o.oa2 = o.oa + (ATR ? atr_piece_step(2) - 2048 : 0);
     }
     const int ch = l >> 4;
     int row = wm * 16 * MB + (l & 15);
@@ -1259,13 +1260,16 @@ gemm_bf16_persist_t(const bf16_t* __restrict__ A, int64_t lda, const bf16_t* __r
                      T.a_bytes);
       abase = (kt & 7) * (TILE_ROWS / 8 * TILE_K * 2);
     }
-    static_assert(BT_PER == 4, "four 1 KB pieces per operand and copying wave");
-#pragma unroll
-    for (int i = 0; i < BT_PER; ++i) {
-      const uint32_t dst = (uint32_t)((wave * BT_PER + i) * 1024);
-      load_lds16(ra, sa + dst, lof.oa, abase + (ATR ? atr_piece_step(i) : i * 1024));
-    }
-    load_lds16_x4(T.rb, sb + (uint32_t)(wave * BT_PER * 1024), lof.ob, kt * TILE_BLOCK_BYTES);
+    // Four 1 KB pieces per operand and copying wave, each operand's under one
+    // M0 write: A's pieces i sit at atr_piece_step(i) (two 2 KB runs 16 KB
+    // apart with ATR), which the per-lane offsets oa (pieces 0, 1) and oa2
+    // (pieces 2, 3) absorb less the loads' own 1 KB steps.
+    static_assert(BT_PER == 4 && (!ATR || (atr_piece_step(1) == 1024 &&
+                                           atr_piece_step(3) - atr_piece_step(2) == 1024)),
+                  "piece layout");
+    const uint32_t dst = (uint32_t)(wave * BT_PER * 1024);
+    load_lds16_4v(ra, sa + dst, lof.oa, lof.oa, lof.oa2, lof.oa2, abase);
+    load_lds16_x4(T.rb, sb + dst, lof.ob, kt * TILE_BLOCK_BYTES);
   };
   auto read_frags = [&](int slot, bf16x8 (&fa)[MB], bf16x8 (&fb)[NB]) {
     const char* sn = lds + slot * BF_STAGE;
