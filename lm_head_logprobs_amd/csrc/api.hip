@@ -116,7 +116,9 @@ struct Plan {
   size_t o_P, o_G, o_Gt, o_Wt, o_ht, o_dhp;
   int vtile;
   bool tiled;             // bf16 dense backward: operands in the tiled block layout
-  int64_t Tc256, KB_v, KB_t;
+  bool tfwd;              // bf16 forward from tiled copies of W and h_c (o_Wf, o_hf)
+  int64_t Tc256, KB_v, KB_t, KB_h;
+  size_t o_Wf, o_hf;
   size_t o_ka, o_kb, o_ia, o_ib, o_hist, o_start, o_rows, o_zent;
   bool entry_pass;  // label/support logits by the vocabulary-ordered pass
   size_t total;
@@ -209,6 +211,19 @@ rl_status make_plan(const rl_loss_cfg* c, bool has_support, bool want_dh, bool w
   p->Tc256 = round_up(p->Tc, TILE_ROWS);
   p->KB_v = p->Vpad / TILE_K;
   p->KB_t = p->Tc256 / TILE_K;
+  // The persistent forward reads tiled copies of W and h_c (consecutive 1 KB
+  // pieces per stage; 5% faster than the row-major operands at the 16k
+  // shape): made once per call for W, per chunk for h_c.
+  p->KB_h = ceil_div(p->H, TILE_K);
+  p->tfwd = p->dtype == RL_DTYPE_BF16 && gemm_fwd_tiled_ok(p->H);
+  p->o_Wf = p->o_hf = 0;
+  if (p->tfwd) {
+    int64_t wf, hf;
+    if (!mul_ok(p->Vpad, p->KB_h * TILE_K, &wf) || !mul_ok(p->Tc256, p->KB_h * TILE_K, &hf))
+      return RL_E_ARG;
+    p->o_Wf = L.take(wf, 2);
+    p->o_hf = L.take(hf, 2);
+  }
   if (p->dense) {
     int64_t vt, tv, hv, sth;
     const int64_t H256 = round_up(p->H, TILE_ROWS);
@@ -418,11 +433,19 @@ rl_status rl_loss_fwd_bwd(const void* h, const void* W, const int32_t* labels,
       return entry_logits(p.dtype, h, W, p.H, p.V, skeys, perm, rows, p.N, p.E, zent, s);
     }));
 
-  if (p.dense && p.want_dh)
+  // W^T for dh (tiled or padded) and the forward's tiled copy of W, from one
+  // read of W where both are needed.
+  bf16_t* Wf = p.tfwd ? reinterpret_cast<bf16_t*>(ws + p.o_Wf) : nullptr;
+  bf16_t* hf = p.tfwd ? reinterpret_cast<bf16_t*>(ws + p.o_hf) : nullptr;
+  const bool want_wt = p.dense && p.want_dh;
+  if (want_wt || p.tfwd)
     RL_TRY(timed(K_TRANSPOSE_W, s, [&] {
-      return p.tiled ? to_tiled_t(static_cast<const bf16_t*>(W), p.H, p.V, p.H,
-                                  static_cast<bf16_t*>(Wt), p.KB_v, p.KB_v, s)
-                     : transpose_pad(p.dtype, W, p.H, p.V, p.H, Wt, p.Vpad, s);
+      // bf16 dense is always tiled, so an untiled W^T is only ever fp32
+      return p.tiled || p.tfwd
+                 ? to_tiled_t(static_cast<const bf16_t*>(W), p.H, p.V, p.H,
+                              want_wt ? static_cast<bf16_t*>(Wt) : nullptr, p.KB_v, p.KB_v, s,
+                              Wf, p.KB_h)
+                 : transpose_pad(p.dtype, W, p.H, p.V, p.H, Wt, p.Vpad, s);
     }));
 
   for (int64_t c0 = 0; c0 < p.N; c0 += p.Tc) {
@@ -430,7 +453,18 @@ rl_status rl_loss_fwd_bwd(const void* h, const void* W, const int32_t* labels,
     const int64_t tck = round_up(tc, 64);
     const void* hc = hb + c0 * p.H * p.esz;
     FwdEpiArgs fa{cfg->inv_temperature, p.V, tc, p.J, pm, ps, pt, P, p.tiled ? p.KB_v : p.Vpad};
-    RL_TRY(timed(K_GEMM_FWD, s, [&] { return gemm_fwd(p.dtype, W, hc, p.V, tc, p.H, fa, s); }));
+    // h_c tiled for the forward and, on the tiled dense path, h_c^T for dW
+    // (its panels to the 256-token boundary, zeros past tc)
+    const bool ht_now = p.tfwd && p.tiled && p.want_dW;
+    if (p.tfwd)
+      RL_TRY(timed(K_TRANSPOSE_H, s, [&] {
+        return to_tiled_t(static_cast<const bf16_t*>(hc), p.H, tc, p.H,
+                          ht_now ? static_cast<bf16_t*>(ht) : nullptr, p.KB_t,
+                          round_up(tc, TILE_ROWS) / TILE_K, s, hf, p.KB_h);
+      }));
+    RL_TRY(timed(K_GEMM_FWD, s, [&] {
+      return gemm_fwd(p.dtype, W, hc, p.V, tc, p.H, fa, s, Wf, hf, p.KB_h);
+    }));
     CombineArgs ca{};
     ca.h = h;
     ca.W = W;
@@ -487,10 +521,11 @@ rl_status rl_loss_fwd_bwd(const void* h, const void* W, const int32_t* labels,
                             dhp, p.H, p.Tc * p.H, s);
         }));
       if (p.want_dW) {
-        RL_TRY(timed(K_TRANSPOSE_H, s, [&] {
-          return to_tiled_t(static_cast<const bf16_t*>(hc), p.H, tc, p.H,
-                            static_cast<bf16_t*>(ht), p.KB_t, ceil_div(tc, TILE_K), s);
-        }));
+        if (!ht_now)
+          RL_TRY(timed(K_TRANSPOSE_H, s, [&] {
+            return to_tiled_t(static_cast<const bf16_t*>(hc), p.H, tc, p.H,
+                              static_cast<bf16_t*>(ht), p.KB_t, ceil_div(tc, TILE_K), s);
+          }));
         const int acc = (c0 > 0 || cfg->accumulate_dW) ? 1 : 0;
         RL_TRY(timed(K_GEMM_DW, s, [&] {
           return gemm_dw(p.dtype, G, p.KB_v, ht, p.KB_t, p.V, p.H, tc, out->dW, p.H, acc, s);

@@ -897,8 +897,11 @@ gemm_bf16_kernel(const bf16_t* __restrict__ A, int64_t lda, const bf16_t* __rest
 // that ignores them (counts only younger stages) also waits for the stores
 // issued after the awaited stage, which is correct and measured to cost
 // nothing here.  EVEN_NK: the stage count K / BF_BK is even (fixed per
-// launch; it decides which fragment set holds the last stage).
-template <class Epi, bool EVEN_NK>
+// launch; it decides which fragment set holds the last stage).  TOPS: both
+// operands come in the tiled block layout (lda / ldb = blocks per 256-row
+// panel, zero past K), so a copying wave's pieces are consecutive 1 KB runs;
+// otherwise they are row-major (K = lda = ldb, a multiple of BF_BK).
+template <class Epi, bool EVEN_NK, bool TOPS>
 __global__ void __launch_bounds__(BF_NT) __attribute__((amdgpu_waves_per_eu(2, 2)))
 gemm_bf16_persist(const bf16_t* __restrict__ A, int64_t lda, const bf16_t* __restrict__ B,
                   int64_t ldb, int64_t M, int64_t N, int64_t K, int tiles_m, int tiles_n,
@@ -932,7 +935,11 @@ gemm_bf16_persist(const bf16_t* __restrict__ A, int64_t lda, const bf16_t* __res
     int l;
     __asm__ volatile("v_and_b32 %0, 63, %1" : "=v"(l) : "v"(tid));
     LaneOffs o;
-    {
+    if constexpr (TOPS) {
+      // the wave's pieces: 1 KB runs wave * BF_PER .. of the stage's block
+#pragma unroll
+      for (int i = 0; i < 4; ++i) o.oa[i] = o.ob[i] = (wave * BF_PER * 64 + l) * 16;
+    } else {
       const int p = wave * BF_PER * 64 + l;
       const int row = p >> 2, ch = (p & 3) ^ tile_swz(row);
 #pragma unroll
@@ -960,8 +967,16 @@ gemm_bf16_persist(const bf16_t* __restrict__ A, int64_t lda, const bf16_t* __res
   // Descriptors are uniform; readfirstlane keeps them in SGPRs across the
   // tile loop.
   auto panel = [&](const bf16_t* X, int64_t r0, int64_t R, int64_t ld) {
-    const int64_t rows = R - r0 < BF_BM ? R - r0 : BF_BM;
-    i32x4 r = make_rsrc(X + r0 * ld, (uint32_t)(rows * ld * 2));
+    i32x4 r;
+    if constexpr (TOPS) {
+      // the panel's blocks; rows past R are zero in the layout
+      (void)R;
+      r = make_rsrc(X + (r0 / BF_BM) * ld * (TILE_BLOCK_BYTES / 2),
+                    (uint32_t)(nk * TILE_BLOCK_BYTES));
+    } else {
+      const int64_t rows = R - r0 < BF_BM ? R - r0 : BF_BM;
+      r = make_rsrc(X + r0 * ld, (uint32_t)(rows * ld * 2));
+    }
 #pragma unroll
     for (int i = 0; i < 4; ++i) r[i] = __builtin_amdgcn_readfirstlane(r[i]);
     return r;
@@ -986,10 +1001,18 @@ gemm_bf16_persist(const bf16_t* __restrict__ A, int64_t lda, const bf16_t* __res
     const uint32_t sa = lds_base + (uint32_t)(slot * BF_STAGE);
     const uint32_t sb = sa + BF_STAGE_A;
     int kbytes;
-    __asm__ volatile("s_lshl_b32 %0, %1, 6" : "=s"(kbytes) : "s"(kt));  // kt * BF_BK * 2
+    __asm__ volatile("s_lshl_b32 %0, %1, 6"
+                     : "=s"(kbytes)
+                     : "s"(__builtin_amdgcn_readfirstlane(kt)));  // kt * BF_BK * 2
     const uint32_t dst = (uint32_t)(wave * BF_PER * 1024);
-    load_lds16_4v(ra, sa + dst, lof.oa[0], lof.oa[1], lof.oa[2], lof.oa[3], kbytes);
-    load_lds16_4v(rb, sb + dst, lof.ob[0], lof.ob[1], lof.ob[2], lof.ob[3], kbytes);
+    if constexpr (TOPS) {
+      const int kblk = kbytes << 8;  // kt * TILE_BLOCK_BYTES
+      load_lds16_x4(ra, sa + dst, lof.oa[0], kblk);
+      load_lds16_x4(rb, sb + dst, lof.ob[0], kblk);
+    } else {
+      load_lds16_4v(ra, sa + dst, lof.oa[0], lof.oa[1], lof.oa[2], lof.oa[3], kbytes);
+      load_lds16_4v(rb, sb + dst, lof.ob[0], lof.ob[1], lof.ob[2], lof.ob[3], kbytes);
+    }
   };
   bf16x8 ca[8], cb[4], da[8], db[4];  // two fragment sets, used in turn
   // In the order the MFMAs consume them: row block 0, the column blocks, the
@@ -1582,11 +1605,35 @@ hipError_t launch_bf16_rows(const bf16_t* A, int64_t lda, const bf16_t* B, int64
   if ((int64_t)BF_BM * std::max(lda, ldb) * 2 >= ((int64_t)1 << 31)) return hipErrorInvalidValue;
   const int64_t grid = std::min<int64_t>(round_up(total, 8), cus);
   if ((K / BF_BK) % 2 == 0)
-    hipLaunchKernelGGL((gemm_bf16_persist<Epi, true>), dim3((unsigned)grid), dim3(BF_NT), 0, s,
-                       A, lda, B, ldb, M, N, K, (int)tm, (int)tn, epi);
+    hipLaunchKernelGGL((gemm_bf16_persist<Epi, true, false>), dim3((unsigned)grid), dim3(BF_NT),
+                       0, s, A, lda, B, ldb, M, N, K, (int)tm, (int)tn, epi);
   else
-    hipLaunchKernelGGL((gemm_bf16_persist<Epi, false>), dim3((unsigned)grid), dim3(BF_NT), 0, s,
-                       A, lda, B, ldb, M, N, K, (int)tm, (int)tn, epi);
+    hipLaunchKernelGGL((gemm_bf16_persist<Epi, false, false>), dim3((unsigned)grid),
+                       dim3(BF_NT), 0, s, A, lda, B, ldb, M, N, K, (int)tm, (int)tn, epi);
+  return hipGetLastError();
+}
+
+// Both operands in the tiled block layout (kb = blocks per 256-row panel,
+// at least ceil(K / BF_BK)): the persistent kernel, which needs at least
+// BF_ST stages and the device's CU count; returns hipErrorNotSupported
+// otherwise (the caller then takes the row-major operands).
+template <class Epi>
+hipError_t launch_bf16_tiled_persist(const bf16_t* A, const bf16_t* B, int64_t kb, int64_t M,
+                                     int64_t N, int64_t K, const Epi& epi, hipStream_t s) {
+  const int64_t tm = ceil_div(M, BF_BM), tn = ceil_div(N, BF_BN);
+  const int64_t total = tm * tn;
+  const int64_t nk = ceil_div(K, BF_BK);
+  const int cus = cu_count() / 8 * 8;
+  if (total <= 0) return hipSuccess;
+  if (nk < BF_ST || kb < nk || cus <= 0 || total > (int64_t)1 << 30) return hipErrorNotSupported;
+  if (nk * TILE_BLOCK_BYTES >= ((int64_t)1 << 31)) return hipErrorInvalidValue;
+  const int64_t grid = std::min<int64_t>(round_up(total, 8), cus);
+  if (nk % 2 == 0)
+    hipLaunchKernelGGL((gemm_bf16_persist<Epi, true, true>), dim3((unsigned)grid), dim3(BF_NT),
+                       0, s, A, kb, B, kb, M, N, K, (int)tm, (int)tn, epi);
+  else
+    hipLaunchKernelGGL((gemm_bf16_persist<Epi, false, true>), dim3((unsigned)grid), dim3(BF_NT),
+                       0, s, A, kb, B, kb, M, N, K, (int)tm, (int)tn, epi);
   return hipGetLastError();
 }
 
@@ -1608,33 +1655,45 @@ hipError_t launch_f32(const float* A, int64_t lda, const float* B, int64_t ldb, 
 int gemm_k_tile(int dtype) { return dtype == RL_DTYPE_BF16 ? BF_BK : F_BK; }
 int fwd_vtile(int dtype) { return dtype == RL_DTYPE_BF16 ? BF_BM : F_BM; }
 
+bool gemm_fwd_tiled_ok(int64_t H) { return ceil_div(H, BF_BK) >= BF_ST; }
+
 hipError_t gemm_fwd(int dtype, const void* W, const void* hc, int64_t V, int64_t Tc, int64_t H,
-                    const FwdEpiArgs& a, hipStream_t s) {
+                    const FwdEpiArgs& a, hipStream_t s, const void* Wf, const void* hf,
+                    int64_t kbf) {
   // Full tiles, then the edge row of tiles (if V is not a multiple of the
-  // tile height) in a launch of its own.
+  // tile height) in a launch of its own.  With tiled copies of W and h_c
+  // (Wf, hf: kbf blocks per panel) the persistent kernel reads those.
   auto run = [&](auto tag_t, auto store) -> hipError_t {
     using T = decltype(tag_t);
     constexpr bool STORE = decltype(store)::value;
     const int BM = sizeof(T) == 2 ? BF_BM : F_BM;
     const int64_t Vfull = V / BM * BM;
     const T* Wt = static_cast<const T*>(W);
-    auto launch = [&](auto epi, const T* A, int64_t M) -> hipError_t {
-      if constexpr (sizeof(T) == 2)
-        return launch_bf16_rows(A, H, static_cast<const bf16_t*>(hc), H, M, Tc, H, epi, s);
-      else
-        return launch_f32(A, H, static_cast<const float*>(hc), H, M, Tc, H, 1, round_up(H, F_BK),
-                          epi, s);
+    auto launch = [&](auto epi, int64_t m0, int64_t M) -> hipError_t {
+      if constexpr (sizeof(T) == 2) {
+        if (Wf != nullptr && hf != nullptr) {
+          const hipError_t e = launch_bf16_tiled_persist(
+              static_cast<const bf16_t*>(Wf) + (m0 / BF_BM) * kbf * (TILE_BLOCK_BYTES / 2),
+              static_cast<const bf16_t*>(hf), kbf, M, Tc, H, epi, s);
+          if (e != hipErrorNotSupported) return e;
+        }
+        return launch_bf16_rows(Wt + m0 * H, H, static_cast<const bf16_t*>(hc), H, M, Tc, H,
+                                epi, s);
+      } else {
+        return launch_f32(Wt + m0 * H, H, static_cast<const float*>(hc), H, M, Tc, H, 1,
+                          round_up(H, F_BK), epi, s);
+      }
     };
     if (Vfull > 0) {
       FwdEpi<T, true, STORE> e{a.inv_t, a.V, a.Tc, a.J, a.part_m, a.part_s, a.part_t,
                                static_cast<T*>(a.P), a.ldp, 0};
-      const hipError_t err = launch(e, Wt, Vfull);
+      const hipError_t err = launch(e, 0, Vfull);
       if (err != hipSuccess) return err;
     }
     if (V > Vfull) {
       FwdEpi<T, false, STORE> e{a.inv_t, a.V, a.Tc, a.J, a.part_m, a.part_s, a.part_t,
                                 static_cast<T*>(a.P), a.ldp, Vfull};
-      return launch(e, Wt + Vfull * H, V - Vfull);
+      return launch(e, Vfull, V - Vfull);
     }
     return hipSuccess;
   };

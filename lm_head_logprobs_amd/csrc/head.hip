@@ -421,9 +421,12 @@ __global__ void __launch_bounds__(NT) form_g_kernel(T* __restrict__ P, int64_t l
 // One workgroup writes one 16 KB block (256 tiled rows x 32 tiled columns):
 // it reads the 32 x 256 source patch with 16-byte loads into LDS, then writes
 // the block contiguously in its swizzled order.  Out-of-range entries are 0.
+// With dst2 the same patch also goes, untransposed, into 32 rows of the eight
+// blocks of dst2's layout that it spans (2 KB contiguous per block).
 __global__ void __launch_bounds__(NT) to_tiled_t_kernel(const bf16_t* __restrict__ src,
                                                         int64_t ld_src, int64_t S, int64_t C,
-                                                        bf16_t* __restrict__ dst, int64_t KB) {
+                                                        bf16_t* __restrict__ dst, int64_t KB,
+                                                        bf16_t* __restrict__ dst2, int64_t KB2) {
   constexpr int PITCH = TILE_ROWS + 8;
   __shared__ __attribute__((aligned(16))) bf16_t tile[TILE_K][PITCH];  // [k][row]
   const int64_t rb = blockIdx.x, kb = blockIdx.y;
@@ -436,14 +439,31 @@ __global__ void __launch_bounds__(NT) to_tiled_t_kernel(const bf16_t* __restrict
     *reinterpret_cast<u32x4*>(&tile[sl][cl]) = v;
   }
   __syncthreads();
-  bf16_t* blk = dst + (rb * KB + kb) * (TILE_ROWS * TILE_K);
-  for (int p = threadIdx.x; p < TILE_ROWS * 4; p += NT) {
-    const int r = p >> 2, ch = (p & 3) ^ tile_swz(r);
-    u32x4 out;
-    bf16_t* e = reinterpret_cast<bf16_t*>(&out);
+  if (dst != nullptr && kb < KB) {
+    bf16_t* blk = dst + (rb * KB + kb) * (TILE_ROWS * TILE_K);
+    for (int p = threadIdx.x; p < TILE_ROWS * 4; p += NT) {
+      const int r = p >> 2, ch = (p & 3) ^ tile_swz(r);
+      u32x4 out;
+      bf16_t* e = reinterpret_cast<bf16_t*>(&out);
 #pragma unroll
-    for (int k = 0; k < 8; ++k) e[k] = tile[8 * ch + k][r];
-    *reinterpret_cast<u32x4*>(blk + p * 8) = out;
+      for (int k = 0; k < 8; ++k) e[k] = tile[8 * ch + k][r];
+      *reinterpret_cast<u32x4*>(blk + p * 8) = out;
+    }
+  }
+  if (dst2 != nullptr) {
+    // rows s0 % 256 + sl of panel s0 / 256; block c0 / 32 + b holds columns
+    // c0 + 32 b ..; thread q: chunk q % 4 of row (q / 4) % 32 of block q / 128
+    const int64_t pr = s0 / TILE_ROWS;
+    const int r0 = (int)(s0 % TILE_ROWS);
+    for (int q = threadIdx.x; q < TILE_K * 4 * (TILE_ROWS / TILE_K); q += NT) {
+      const int c = q & 3, sl = (q >> 2) & (TILE_K - 1), b = q >> 7;
+      const int64_t kb2 = c0 / TILE_K + b;
+      if (kb2 >= KB2) continue;
+      const int r = r0 + sl;
+      const u32x4 v = *reinterpret_cast<const u32x4*>(&tile[sl][TILE_K * b + 8 * c]);
+      *reinterpret_cast<u32x4*>(dst2 + ((pr * KB2 + kb2) * TILE_ROWS + r) * TILE_K +
+                                ((c ^ tile_swz(r)) << 3)) = v;
+    }
   }
 }
 
@@ -762,9 +782,11 @@ hipError_t form_g(int dtype, void* P, int64_t ldp, void* Gt, int64_t ldgt, const
 }
 
 hipError_t to_tiled_t(const bf16_t* src, int64_t ld_src, int64_t S, int64_t C, bf16_t* dst,
-                      int64_t KB, int64_t kb_write, hipStream_t s) {
+                      int64_t KB, int64_t kb_write, hipStream_t s, bf16_t* dst2, int64_t KB2) {
+  if (dst2 != nullptr && KB2 < ceil_div(C, TILE_K)) return hipErrorInvalidValue;
   const dim3 grid((unsigned)ceil_div(C, TILE_ROWS), (unsigned)kb_write);
-  hipLaunchKernelGGL(to_tiled_t_kernel, grid, dim3(NT), 0, s, src, ld_src, S, C, dst, KB);
+  hipLaunchKernelGGL(to_tiled_t_kernel, grid, dim3(NT), 0, s, src, ld_src, S, C, dst, KB, dst2,
+                     KB2);
   return hipGetLastError();
 }
 

@@ -21,8 +21,15 @@ struct FwdEpiArgs {
 };
 
 // S^T = W h_c^T with the online-softmax epilogue.  W [V,H], h_c [Tc,H].
+// Wf, hf (bf16, optional): the same operands in the tiled block layout,
+// kbf >= ceil(H / 32) blocks per 256-row panel (Wf's panels covering V, hf's
+// Tc), which the persistent kernel reads instead when it applies.
 hipError_t gemm_fwd(int dtype, const void* W, const void* hc, int64_t V, int64_t Tc, int64_t H,
-                    const FwdEpiArgs& a, hipStream_t s);
+                    const FwdEpiArgs& a, hipStream_t s, const void* Wf = nullptr,
+                    const void* hf = nullptr, int64_t kbf = 0);
+// Whether the bf16 forward can read tiled operands at this H (it needs at
+// least as many K stages as its LDS ring holds).
+bool gemm_fwd_tiled_ok(int64_t H);
 
 // C[split] = A[:, ks] B[:, ks]^T (fp32 out), split-K over K in `splits` slices
 // of k_split elements (a multiple of the K tile).  A [M,K] lda, B [N,K] ldb.
@@ -58,10 +65,13 @@ __host__ __device__ inline int64_t tiled_offset(int64_t r, int64_t k, int64_t KB
 }
 
 // src [S rows, C cols] row-major (ld_src) -> tiled [C rows, S cols] with KB
-// blocks per panel; the blocks kb < kb_write of every panel are written (zeros
-// past S and C).
+// blocks per panel (dst; the blocks kb < min(kb_write, KB) of every panel are
+// written, zeros past S and C) and, when dst2 is given, the untransposed
+// tiled copy [S rows, C cols] with KB2 >= ceil(C / 32) blocks per panel (its
+// rows below 32 kb_write, zeros past S and C).  Either output may be null.
 hipError_t to_tiled_t(const bf16_t* src, int64_t ld_src, int64_t S, int64_t C, bf16_t* dst,
-                      int64_t KB, int64_t kb_write, hipStream_t s);
+                      int64_t KB, int64_t kb_write, hipStream_t s, bf16_t* dst2 = nullptr,
+                      int64_t KB2 = 0);
 
 // bf16 dense gradient in the tiled layout: G holds e^(z - m) as left by the
 // forward GEMM (KB_g blocks per 256-token panel, panels covering Tc); every
