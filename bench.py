@@ -18,6 +18,7 @@ from __future__ import annotations
 
 import argparse
 import hashlib
+import re
 import json
 import os
 import sys
@@ -42,12 +43,24 @@ KERNEL_SOURCES = {
 }
 
 
+_CODE_TOKENS = re.compile(r'"(?:\\.|[^"\\\n])*"|\'(?:\\.|[^\'\\\n])*\'|//[^\n]*|/\*.*?\*/', re.S)
+
+
+def strip_comments(src: str) -> str:
+    """C++ source with its comments removed (string and character literals
+    kept) and every run of whitespace made one space."""
+    code = _CODE_TOKENS.sub(lambda m: " " if m.group(0)[0] == "/" else m.group(0), src)
+    return " ".join(code.split())
+
+
 def kernel_src_sha(kernel: str = "gemm_fwd") -> str:
+    """Hash of the code (comments and layout stripped) of the sources a kernel
+    is built from: a counter summary stays valid across comment-only edits."""
     files = KERNEL_SOURCES["gemm" if kernel.startswith("gemm") else kernel]
     h = hashlib.sha256()
     for f in files:
-        with open(os.path.join(ROOT, "lm_head_logprobs_amd", "csrc", f), "rb") as fh:
-            h.update(fh.read())
+        with open(os.path.join(ROOT, "lm_head_logprobs_amd", "csrc", f), encoding="utf-8") as fh:
+            h.update(strip_comments(fh.read()).encode())
     return h.hexdigest()[:16]
 
 

@@ -28,9 +28,11 @@
 // buffer offset past the descriptor's range, which the hardware reads as zero.
 // In LDS a tile row is 64 bytes (32 bf16 = four 16-byte chunks); chunk c of
 // row r is stored at position c ^ tile_swz(r) (kernels.h), which keeps the
-// fragment reads free of bank conflicts.  The backward operands arrive in a tiled layout whose 16 KB blocks
-// are exactly this LDS image, so each stage load is one contiguous copy
-// (row-major operands with 300 KB row strides touch 256 pages per stage).
+// fragment reads free of bank conflicts.  The backward operands, and the
+// bf16 forward's tiled copies of W and h_c, arrive in a tiled layout whose
+// 16 KB blocks are exactly this LDS image, so each stage load is one
+// contiguous copy (row-major operands with 300 KB row strides touch 256
+// pages per stage).
 // Workgroups are remapped so consecutive tiles land on one XCD (dispatch is
 // round-robin over the 8 XCDs).  The forward GEMM groups 8 tiles along M;
 // the backward GEMMs walk blocks of 4 x 8 tiles with N fastest, so the 32
@@ -885,8 +887,8 @@ gemm_bf16_kernel(const bf16_t* __restrict__ A, int64_t lda, const bf16_t* __rest
   epi.template apply<Acc16, 8, 4, BF_BM, BF_BN>(acc, ctx);
 }
 
-// Persistent variant for row-major operands with a short K loop (the
-// forward, K = H): one workgroup per CU walks its tiles in order and the
+// Persistent variant for a short K loop (the forward, K = H), on tiled or
+// row-major operands: one workgroup per CU walks its tiles in order and the
 // stage ring runs on across tile boundaries, so the first stages of the next
 // tile are in flight while the epilogue of the current one runs (the
 // epilogue's LDS is the ring slot of the tile's last stage).  Tiles of XCD x are the logical tiles

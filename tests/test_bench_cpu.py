@@ -41,3 +41,15 @@ def test_traffic_summary_is_used_only_for_the_sources_it_was_taken_on(tmp_path, 
     assert b.read_traffic("gemm_fwd", "wl") == 12345.0
     summary.write_text("kernel_src_sha: 0000000000000000\nhbm_bytes_per_launch: 12345\n")
     assert b.read_traffic("gemm_fwd", "wl") is None  # taken on other sources
+
+
+def test_source_hash_ignores_comments_and_layout_only():
+    """The hash a counter summary is tied to changes with the code and not with
+    comments or whitespace; comment markers inside string literals are code."""
+    b = _bench_module()
+    base = 'int a = 1; // one\nconst char* s = "x // y";\n/* block\n comment */ float f(float x) { return x; }\n'
+    same = 'int a = 1;\n// another comment\n  const char* s = "x // y"; float f(float x)\n{ return x; }  /* c */\n'
+    assert b.strip_comments(base) == b.strip_comments(same)
+    for changed in (base.replace("= 1", "= 2"), base.replace('"x // y"', '"x / y"'),
+                    base.replace("return x", "return -x")):
+        assert b.strip_comments(changed) != b.strip_comments(base)
