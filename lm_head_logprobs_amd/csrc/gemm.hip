@@ -1176,8 +1176,13 @@ gemm_bf16_persist(const bf16_t* __restrict__ A, int64_t lda, const bf16_t* __res
 // operations (so they do not wait for them); the next one waits for them.
 // With ATR, A is given
 // as A^T in the tiled layout (G for dW) and read transposed, as in
-// gemm_bf16_kernel.  Requires K / BF_BK >= BF_ST stages and one split.
-template <class Epi, bool ATR, int MB, bool EVEN_NK>
+// gemm_bf16_kernel.  A stage of A^T is 32 rows of one 256-row panel; with
+// AFLAT (every byte of A^T a stage can reach lies within 4 GB of the tile's
+// first block column) one descriptor per tile serves all panels and a stage's
+// panel and row offset is a 32-bit scalar offset, else the descriptor is
+// rebuilt at each stage (64-bit address arithmetic: about 12 scalar
+// instructions per K-step).  Requires K / BF_BK >= BF_ST stages and one split.
+template <class Epi, bool ATR, int MB, bool EVEN_NK, bool AFLAT>
 __global__ void __launch_bounds__(BF_NT) __attribute__((amdgpu_waves_per_eu(2, 2)))
 gemm_bf16_persist_t(const bf16_t* __restrict__ A, int64_t lda, const bf16_t* __restrict__ B,
                     int64_t ldb, int64_t M, int64_t N, int64_t K, int tiles_m, int tiles_n,
@@ -1214,27 +1219,34 @@ gemm_bf16_persist_t(const bf16_t* __restrict__ A, int64_t lda, const bf16_t* __r
     n0 = (int64_t)(first_n + inb % wn_) * BF_BN;
   };
   // Per tile: B's panel descriptor; A's first block column (ATR: its
-  // descriptor is rebased at every 256-row panel of A^T) or panel descriptor.
+  // descriptor spans every panel of A^T with AFLAT, else it is rebased at
+  // every 256-row panel) or panel descriptor.
   struct Tile {
     int64_t m0, n0;
     i32x4 ra, rb;
     uint32_t a_bytes;
   };
+  // ATR: bytes of one 256-row panel of A^T, and the blocks of a tile's
+  // column range (8, fewer only at the right edge of A^T)
+  const uint32_t lda_bytes = (uint32_t)(lda * TILE_BLOCK_BYTES);
   auto tile = [&](int lt) {
     Tile T;
     coords(lt, T.m0, T.n0);
     i32x4 rb = make_rsrc(B + (T.n0 / BF_BN) * ldb * (TILE_BLOCK_BYTES / 2),
                          (uint32_t)(nk * TILE_BLOCK_BYTES));
-    i32x4 ra = make_rsrc(A + (T.m0 / BF_BM) * lda * (TILE_BLOCK_BYTES / 2),
-                         (uint32_t)(nk * TILE_BLOCK_BYTES));
+    const int64_t cols = min<int64_t>(BF_BM / TILE_K, lda - T.m0 / TILE_K);
+    i32x4 ra = ATR && AFLAT
+                   ? make_rsrc(A + (T.m0 / TILE_K) * (TILE_BLOCK_BYTES / 2),
+                               (uint32_t)((ceil_div(nk, 8) - 1) * lda_bytes +
+                                          cols * TILE_BLOCK_BYTES))
+                   : make_rsrc(A + (T.m0 / BF_BM) * lda * (TILE_BLOCK_BYTES / 2),
+                               (uint32_t)(nk * TILE_BLOCK_BYTES));
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       T.rb[i] = __builtin_amdgcn_readfirstlane(rb[i]);
       T.ra[i] = __builtin_amdgcn_readfirstlane(ra[i]);
     }
-    T.a_bytes = ATR ? (uint32_t)(min<int64_t>(BF_BM / TILE_K, lda - T.m0 / TILE_K) *
-                                 TILE_BLOCK_BYTES)
-                    : 0u;
+    T.a_bytes = ATR ? (uint32_t)(cols * TILE_BLOCK_BYTES) : 0u;
     return T;
   };
   // Per-lane copy-slot and fragment offsets (tile independent), formed from
@@ -1279,8 +1291,10 @@ gemm_bf16_persist_t(const bf16_t* __restrict__ A, int64_t lda, const bf16_t* __r
     const uint32_t sb = sa + BF_STAGE_A;
     i32x4 ra = T.ra;
     int abase = kt * TILE_BLOCK_BYTES;
-    if constexpr (ATR) {
+    if constexpr (ATR && AFLAT) {
       // rows 32 (kt % 8) .. of the 256-row panel kt / 8 of A^T
+      abase = (int)((uint32_t)(kt >> 3) * lda_bytes + (uint32_t)(kt & 7) * (TILE_ROWS / 8 * TILE_K * 2));
+    } else if constexpr (ATR) {
       ra = make_rsrc(A + ((int64_t)(kt >> 3) * lda + T.m0 / TILE_K) * (TILE_BLOCK_BYTES / 2),
                      T.a_bytes);
       abase = (kt & 7) * (TILE_ROWS / 8 * TILE_K * 2);
@@ -1731,17 +1745,25 @@ hipError_t gemm_dw(int dtype, const void* A, int64_t lda, const void* B, int64_t
       if (ceil_div(M, TILE_K) > lda) return hipErrorInvalidValue;
       if (ceil_div(K, BF_BK) * TILE_BLOCK_BYTES >= ((int64_t)1 << 31)) return hipErrorInvalidValue;
       const int64_t grid = std::min<int64_t>(round_up(total, 8), cus);
+      // one descriptor per tile when the stages' reach into G (the last
+      // panel's 8 block columns included) stays below 4 GB
+      const int64_t nk = ceil_div(K, BF_BK);
+      const bool flat = (ceil_div(nk, 8) - 1) * lda * TILE_BLOCK_BYTES +
+                            (BF_BM / TILE_K) * TILE_BLOCK_BYTES <= (int64_t)UINT32_MAX;
       auto go = [&](auto e) {
-        if (ceil_div(K, BF_BK) % 2 == 0)
-          hipLaunchKernelGGL((gemm_bf16_persist_t<decltype(e), true, DW_MB, true>),
+        auto launch = [&](auto even, auto aflat) {
+          hipLaunchKernelGGL((gemm_bf16_persist_t<decltype(e), true, DW_MB, decltype(even)::value,
+                                                  decltype(aflat)::value>),
                              dim3((unsigned)grid), dim3(BF_NT), 0, s,
                              static_cast<const bf16_t*>(A), lda, static_cast<const bf16_t*>(B),
                              ldb, M, N, K, (int)tm, (int)tn, e);
+        };
+        using T_ = std::true_type;
+        using F_ = std::false_type;
+        if (nk % 2 == 0)
+          flat ? launch(T_{}, T_{}) : launch(T_{}, F_{});
         else
-          hipLaunchKernelGGL((gemm_bf16_persist_t<decltype(e), true, DW_MB, false>),
-                             dim3((unsigned)grid), dim3(BF_NT), 0, s,
-                             static_cast<const bf16_t*>(A), lda, static_cast<const bf16_t*>(B),
-                             ldb, M, N, K, (int)tm, (int)tn, e);
+          flat ? launch(F_{}, T_{}) : launch(F_{}, F_{});
         return hipGetLastError();
       };
       return accumulate ? go(DwEpiT<true>{C, ldc, M, N}) : go(DwEpiT<false>{C, ldc, M, N});

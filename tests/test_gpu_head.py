@@ -141,6 +141,24 @@ def test_token_chunking_invariance():
     assert rel_fro(b["dW"], a["dW"]) <= 1e-5
 
 
+def test_full_size_one_chunk_matches_two():
+    """The 16k workload as one 16384-token chunk against the default two of
+    8192.  With one chunk G spans 4.98 GB, so the persistent dW reaches its
+    panels through a descriptor rebuilt at each stage; with two (2.49 GB each)
+    one descriptor per tile and 32-bit offsets serve every panel.  Per-token
+    outputs must agree bit for bit, dh and dW to fp32 rounding."""
+    wl = make_head("c3_head16k_ipo", device="cuda:0")
+    print("[case] c3 full size, token chunk 16384 against 8192", flush=True)
+    _, a = run_head(wl)
+    _, b = run_head(wl, token_chunk=16384)
+    for k in ("logprobs", "entropy", "token_loss", "weight", "keep"):
+        assert np.array_equal(a[k], b[k]), k
+    assert rel_fro(b["dh"], a["dh"]) <= 1e-5
+    e = rel_fro(b["dW"], a["dW"])
+    print(f"dW rel fro {e:.3g}")
+    assert e <= 1e-5
+
+
 @pytest.mark.parametrize("chunk", [160, 129])
 def test_short_token_chunks_through_the_persistent_dW(chunk):
     # dW's persistent kernel needs at least five 32-token K-steps: chunks of
