@@ -1165,14 +1165,21 @@ gemm_bf16_persist(const bf16_t* __restrict__ A, int64_t lda, const bf16_t* __res
   }
 }
 
+// The persistent dW runs a ring of five stages (the whole 160 KB of LDS; its
+// epilogue uses none): one stage more lookahead for G, whose stages come from
+// HBM (16k step against four stages: dW 8.01 -> 7.86 ms on one box, 7.88 ->
+// 7.81 ms on another).
+constexpr int DW_ST = 5;
+static_assert(DW_ST - 2 <= 3, "wait_stage covers up to three younger stages");
+
 // Persistent variant for tiled operands with a long K loop (the dW
 // contraction, K = the chunk's tokens): one workgroup per CU walks its tiles
 // in the blocked order of map_tile_blocks (XCD x takes the logical tiles
 // [x * ceil(T / 8), ...) round-robin), and the stage ring runs on across tile
 // boundaries as in gemm_bf16_persist.  What this buys is the epilogue: its
-// Epi::STORES stores per lane are issued after the first BF_ST - 1 stages of
+// Epi::STORES stores per lane are issued after the first DW_ST - 1 stages of
 // the next tile and drain while those stages' MFMAs run.  The stage waits of
-// the next tile's first BF_ST - 2 K-steps count the stores as younger
+// the next tile's first DW_ST - 2 K-steps count the stores as younger
 // operations (so they do not wait for them); the next one waits for them.
 // With ATR, A is given
 // as A^T in the tiled layout (G for dW) and read transposed, as in
@@ -1181,15 +1188,15 @@ gemm_bf16_persist(const bf16_t* __restrict__ A, int64_t lda, const bf16_t* __res
 // first block column) one descriptor per tile serves all panels and a stage's
 // panel and row offset is a 32-bit scalar offset, else the descriptor is
 // rebuilt at each stage (64-bit address arithmetic: about 12 scalar
-// instructions per K-step).  Requires K / BF_BK >= BF_ST stages and one split.
+// instructions per K-step).  Requires K / BF_BK >= DW_ST stages and one split.
 template <class Epi, bool ATR, int MB, bool EVEN_NK, bool AFLAT>
 __global__ void __launch_bounds__(BF_NT) __attribute__((amdgpu_waves_per_eu(2, 2)))
 gemm_bf16_persist_t(const bf16_t* __restrict__ A, int64_t lda, const bf16_t* __restrict__ B,
                     int64_t ldb, int64_t M, int64_t N, int64_t K, int tiles_m, int tiles_n,
                     Epi epi) {
   constexpr int NST = Epi::STORES;
-  static_assert((BF_ST - 2) * BT_LPS + NST < 64, "stage waits must fit vmcnt");
-  __shared__ __attribute__((aligned(1024))) char lds[BF_LDS];
+  static_assert((DW_ST - 2) * BT_LPS + NST < 64, "stage waits must fit vmcnt");
+  __shared__ __attribute__((aligned(1024))) char lds[DW_ST * BF_STAGE];
   const int total = tiles_m * tiles_n;
   const int per_xcd = gridDim.x >> 3;  // the grid is a multiple of 8
   const int chunk = (int)ceil_div(total, 8);
@@ -1338,13 +1345,16 @@ gemm_bf16_persist_t(const bf16_t* __restrict__ A, int64_t lda, const bf16_t* __r
   bf16x8 ca[MB], cb[NB], da[MB], db[NB];  // two fragment sets, used in turn
   int gb = 0;  // ring position of the current tile's stage 0
 #pragma unroll
-  for (int s = 0; s < BF_ST - 1; ++s) issue(cur, s, s);
-  if (copier) wait_stage<BT_LPS>(BF_ST - 2);
+  for (int s = 0; s < DW_ST - 1; ++s) issue(cur, s, s);
+  if (copier) wait_stage<BT_LPS>(DW_ST - 2);
   __syncthreads();
-  issue(cur, BF_ST - 1, BF_ST - 1);
+  issue(cur, DW_ST - 1, DW_ST - 1);
   if constexpr (EVEN_NK) read_frags(0, da, db);
   else read_frags(0, ca, cb);
   bool stores_out = false;  // the previous tile's epilogue stores may be in flight
+  // Ring slot of the current stage, (gb + kt) % DW_ST, carried from step to
+  // step (a modulo by 5 per use cost about 15 scalar instructions per K-step).
+  int sl = 0;
   for (;;) {
     f32x4 acc[MB][NB];
 #pragma unroll
@@ -1355,9 +1365,9 @@ gemm_bf16_persist_t(const bf16_t* __restrict__ A, int64_t lda, const bf16_t* __r
         for (int r = 0; r < 4; ++r) acc[i][j][r] = 0.0f;
     // Stage kt's MFMAs from x, with stage kt+1 awaited, the buffer of stage
     // kt refilled and stage kt+1's fragments read into y.
-    // STEADY (a compile-time flag) marks the steps with kt >= BF_ST - 2 and
-    // kt + BF_ST < nk: no previous stores are younger than stage kt + 1,
-    // BF_ST - 2 stages are, and the refill is this tile's stage kt + BF_ST,
+    // STEADY (a compile-time flag) marks the steps with kt >= DW_ST - 2 and
+    // kt + DW_ST < nk: no previous stores are younger than stage kt + 1,
+    // DW_ST - 2 stages are, and the refill is this tile's stage kt + DW_ST,
     // so the wait and the refill need no run-time choice (which otherwise
     // costs a cascade of scalar branches per step).
     auto kstep = [&](auto steady, int kt, bf16x8 (&xa)[MB], bf16x8 (&xb)[NB],
@@ -1368,25 +1378,28 @@ gemm_bf16_persist_t(const bf16_t* __restrict__ A, int64_t lda, const bf16_t* __r
       for (int q = 0; q < BF_PRE; ++q)
         acc[q / NB][q % NB] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
             xa[q / NB], xb[q % NB], acc[q / NB][q % NB], 0, 0, 0);
-      // Await stage kt + 1.  Younger than it: up to BF_ST - 2 stages (fewer
+      // Await stage kt + 1.  Younger than it: up to DW_ST - 2 stages (fewer
       // at the end of the last tile), plus the previous epilogue's stores
-      // when stage kt + 1 was issued before them (stages 0 .. BF_ST-2).
+      // when stage kt + 1 was issued before them (stages 0 .. DW_ST-2).
       if constexpr (STEADY) {
-        if (copier) wait_vmcnt<(BF_ST - 2) * BT_LPS>();
+        if (copier) wait_vmcnt<(DW_ST - 2) * BT_LPS>();
       } else {
         if (copier)
-          wait_stage<BT_LPS, NST>(has_next ? BF_ST - 2 : min(nk - 2 - kt, BF_ST - 2),
-                                  stores_out && kt + 1 <= BF_ST - 2);
+          wait_stage<BT_LPS, NST>(has_next ? DW_ST - 2 : min(nk - 2 - kt, DW_ST - 2),
+                                  stores_out && kt + 1 <= DW_ST - 2);
       }
       __syncthreads();
-      const int slot = (unsigned)(gb + kt) % BF_ST;
+      const int slot = sl;  // stage kt's, refilled with stage kt + DW_ST
+      int sn = sl + 1;      // stage kt + 1's
+      sn = sn == DW_ST ? 0 : sn;
       if constexpr (STEADY) {
-        issue(cur, kt + BF_ST, slot);
+        issue(cur, kt + DW_ST, slot);
       } else {
-        if (kt + BF_ST < nk) issue(cur, kt + BF_ST, slot);
-        else if (has_next) issue(nxt, kt + BF_ST - nk, slot);
+        if (kt + DW_ST < nk) issue(cur, kt + DW_ST, slot);
+        else if (has_next) issue(nxt, kt + DW_ST - nk, slot);
       }
-      read_frags((unsigned)(gb + kt + 1) % BF_ST, ya, yb);
+      read_frags(sn, ya, yb);
+      sl = sn;
 #pragma unroll
       for (int q = BF_PRE; q < 32; ++q)
         acc[q / NB][q % NB] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
@@ -1414,11 +1427,11 @@ gemm_bf16_persist_t(const bf16_t* __restrict__ A, int64_t lda, const bf16_t* __r
     if constexpr (EVEN_NK) {
       kstep(gen, 0, da, db, ca, cb);
       kt = 1;
-      for (; kt < BF_ST - 2 && kt + 2 < nk; kt += 2) {
+      for (; kt < DW_ST - 2 && kt + 2 < nk; kt += 2) {
         kstep(gen, kt, ca, cb, da, db);
         kstep(gen, kt + 1, da, db, ca, cb);
       }
-      for (; kt + 1 + BF_ST < nk; kt += 2) {
+      for (; kt + 1 + DW_ST < nk; kt += 2) {
         kstep(std_, kt, ca, cb, da, db);
         kstep(std_, kt + 1, da, db, ca, cb);
       }
@@ -1450,20 +1463,21 @@ gemm_bf16_persist_t(const bf16_t* __restrict__ A, int64_t lda, const bf16_t* __r
     ctx.smem_bytes = 0;
     epi.template apply<Acc16, MB, NB, BF_BM, BF_BN>(acc, ctx);
     if (!has_next) break;
-    // Advance: stages 0 .. BF_ST-2 of the next tile were issued before the
+    // Advance: stages 0 .. DW_ST-2 of the next tile were issued before the
     // epilogue's stores; await stage 0 (younger: the other stages and the
-    // stores), then issue stage BF_ST-1.
+    // stores), then issue stage DW_ST-1.
     gb += nk;
+    sl = gb % DW_ST;
     cur = nxt;
     tnext += per_xcd;
     has_next = tnext < hi;
     if (has_next) nxt = tile(tnext);
     lof = lane_offs();
-    if (copier) wait_stage<BT_LPS, NST>(BF_ST - 2, true);
+    if (copier) wait_stage<BT_LPS, NST>(DW_ST - 2, true);
     __syncthreads();
-    issue(cur, BF_ST - 1, (gb + BF_ST - 1) % BF_ST);
-    if constexpr (EVEN_NK) read_frags(gb % BF_ST, da, db);
-    else read_frags(gb % BF_ST, ca, cb);
+    issue(cur, DW_ST - 1, (gb + DW_ST - 1) % DW_ST);
+    if constexpr (EVEN_NK) read_frags(gb % DW_ST, da, db);
+    else read_frags(gb % DW_ST, ca, cb);
     stores_out = true;
   }
 }
@@ -1735,8 +1749,8 @@ hipError_t gemm_dw(int dtype, const void* A, int64_t lda, const void* B, int64_t
   if (ldc >= ((int64_t)1 << 21)) return hipErrorInvalidValue;
   const int bk = gemm_k_tile(dtype);
   // bf16: the persistent kernel (epilogue stores overlapped with the next
-  // tile) when the K loop has at least BF_ST stages and the CU count is known.
-  if (dtype == RL_DTYPE_BF16 && ceil_div(K, BF_BK) >= BF_ST && N % 4 == 0) {
+  // tile) when the K loop has at least DW_ST stages and the CU count is known.
+  if (dtype == RL_DTYPE_BF16 && ceil_div(K, BF_BK) >= DW_ST && N % 4 == 0) {
     const int64_t tm = ceil_div(M, BF_BM), tn = ceil_div(N, BF_BN);
     const int64_t total = tm * tn;
     const int cus = cu_count() / 8 * 8;
