@@ -34,7 +34,9 @@
 // contiguous copy (row-major operands with 300 KB row strides touch 256
 // pages per stage).
 // Workgroups are remapped so consecutive tiles land on one XCD (dispatch is
-// round-robin over the 8 XCDs).  The forward GEMM groups 8 tiles along M;
+// round-robin over the 8 XCDs).  The forward GEMM groups 4 tiles along M
+// (with its tiled operands 4 and 6 timed 0.03-0.06 ms faster per 16k step
+// than 8; 2, 3 and 16 slower);
 // the backward GEMMs walk blocks of 4 x 8 tiles with N fastest, so the 32
 // tiles an XCD runs at once cover at most 8 N-tiles and each slice of the
 // large operand (G) is fetched into that XCD's L2 once for all of them.
@@ -50,7 +52,7 @@ namespace rl {
 namespace {
 
 constexpr int NT = 256;
-constexpr int GROUP_M = 8;
+constexpr int GROUP_M = 4;
 constexpr int OOB = (int)0x80000000;  // a buffer offset past any descriptor's range
 
 struct TileCoord {
