@@ -474,8 +474,10 @@ __global__ void __launch_bounds__(NT) to_tiled_t_kernel(const bf16_t* __restrict
 // e^(m_tj - LSE_t) (kappa_t + gs (m_tj + log x)), kappa_t holding the rest of
 // that term), zero past Tc and V.  Both backward GEMMs read this one copy
 // (dW through transposing LDS reads).  A workgroup takes NBLK consecutive
-// blocks of one token panel and issues all their loads first (NBLK = 4: 8%
-// faster than one block per workgroup, measured at the 16k shape).
+// blocks of one token panel and issues all their loads first (NBLK = 2, at
+// the 16k shape: 4 was 8% faster than one block per workgroup and 2 another
+// 1.7%; an in-place streaming probe ran 5.87 TB/s with two blocks per
+// workgroup against 5.54 with four).
 template <int NBLK>
 __global__ void __launch_bounds__(NT) form_g_blocks_kernel(
     bf16_t* __restrict__ G, int64_t KB_g, const float* __restrict__ part_m, int64_t J, int vtile,
@@ -795,8 +797,8 @@ hipError_t form_g_blocks(bf16_t* G, int64_t KB_g, const float* part_m, int64_t J
                          int64_t Tc, hipStream_t s) {
   if (Tc <= 0) return hipSuccess;
   const unsigned panels = (unsigned)ceil_div(Tc, TILE_ROWS);
-  if (KB_g % 4 == 0)
-    hipLaunchKernelGGL(form_g_blocks_kernel<4>, dim3(panels, (unsigned)(KB_g / 4)), dim3(NT), 0,
+  if (KB_g % 2 == 0)
+    hipLaunchKernelGGL(form_g_blocks_kernel<2>, dim3(panels, (unsigned)(KB_g / 2)), dim3(NT), 0,
                        s, G, KB_g, part_m, J, vtile, lse_c, kappa_c, gs, V, Tc);
   else
     hipLaunchKernelGGL(form_g_blocks_kernel<1>, dim3(panels, (unsigned)KB_g), dim3(NT), 0, s, G,
