@@ -889,8 +889,8 @@ gemm_bf16_kernel(const bf16_t* __restrict__ A, int64_t lda, const bf16_t* __rest
   epi.template apply<Acc16, 8, 4, BF_BM, BF_BN>(acc, ctx);
 }
 
-// Persistent variant for a short K loop (the forward, K = H), on tiled or
-// row-major operands: one workgroup per CU walks its tiles in order and the
+// Persistent variant for a short K loop (the forward, K = H), on tiled
+// operands: one workgroup per CU walks its tiles in order and the
 // stage ring runs on across tile boundaries, so the first stages of the next
 // tile are in flight while the epilogue of the current one runs (the
 // epilogue's LDS is the ring slot of the tile's last stage).  Tiles of XCD x are the logical tiles
@@ -901,11 +901,12 @@ gemm_bf16_kernel(const bf16_t* __restrict__ A, int64_t lda, const bf16_t* __rest
 // that ignores them (counts only younger stages) also waits for the stores
 // issued after the awaited stage, which is correct and measured to cost
 // nothing here.  EVEN_NK: the stage count K / BF_BK is even (fixed per
-// launch; it decides which fragment set holds the last stage).  TOPS: both
+// launch; it decides which fragment set holds the last stage).  Both
 // operands come in the tiled block layout (lda / ldb = blocks per 256-row
-// panel, zero past K), so a copying wave's pieces are consecutive 1 KB runs;
-// otherwise they are row-major (K = lda = ldb, a multiple of BF_BK).
-template <class Epi, bool EVEN_NK, bool TOPS>
+// panel, zero past K), so a copying wave's pieces are consecutive 1 KB runs
+// (8.00 -> 7.55 ms per 16k step against row-major operands with 4 KB row
+// strides, whose pieces came from 16-row-apart runs).
+template <class Epi, bool EVEN_NK>
 __global__ void __launch_bounds__(BF_NT) __attribute__((amdgpu_waves_per_eu(2, 2)))
 gemm_bf16_persist(const bf16_t* __restrict__ A, int64_t lda, const bf16_t* __restrict__ B,
                   int64_t ldb, int64_t M, int64_t N, int64_t K, int tiles_m, int tiles_n,
@@ -929,29 +930,15 @@ gemm_bf16_persist(const bf16_t* __restrict__ A, int64_t lda, const bf16_t* __res
   // epilogue, so they are not live (and not spilled) across the epilogue.
   static_assert(BF_PER == 4, "four pieces per operand and copying wave");
   struct LaneOffs {
-    int oa[4], ob[4], fa, fb;
+    int oc, fa, fb;
   };
   const bool copier = wave < BF_DMAW;
-  // A copying wave's piece i is 16 rows below its piece 0 (same swizzle);
-  // its source offset is stored less i KB (the loads' immediate offsets).
-  const int sa_step = (int)(16 * lda * 2), sb_step = (int)(16 * ldb * 2);
   auto lane_offs = [&]() {
     int l;
     __asm__ volatile("v_and_b32 %0, 63, %1" : "=v"(l) : "v"(tid));
     LaneOffs o;
-    if constexpr (TOPS) {
-      // the wave's pieces: 1 KB runs wave * BF_PER .. of the stage's block
-#pragma unroll
-      for (int i = 0; i < 4; ++i) o.oa[i] = o.ob[i] = (wave * BF_PER * 64 + l) * 16;
-    } else {
-      const int p = wave * BF_PER * 64 + l;
-      const int row = p >> 2, ch = (p & 3) ^ tile_swz(row);
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        o.oa[i] = (int)((row * lda + 8 * ch) * 2) + i * (sa_step - 1024);
-        o.ob[i] = (int)((row * ldb + 8 * ch) * 2) + i * (sb_step - 1024);
-      }
-    }
+    // the wave's pieces: 1 KB runs wave * BF_PER .. of each operand's block
+    o.oc = (wave * BF_PER * 64 + l) * 16;
     const int ch = l >> 4;
     int row = wm * 128 + (l & 15);
     o.fa = row * 64 + 16 * (ch ^ tile_swz(row));
@@ -970,31 +957,24 @@ gemm_bf16_persist(const bf16_t* __restrict__ A, int64_t lda, const bf16_t* __res
   };
   // Descriptors are uniform; readfirstlane keeps them in SGPRs across the
   // tile loop.
-  auto panel = [&](const bf16_t* X, int64_t r0, int64_t R, int64_t ld) {
-    i32x4 r;
-    if constexpr (TOPS) {
-      // the panel's blocks; rows past R are zero in the layout
-      (void)R;
-      r = make_rsrc(X + (r0 / BF_BM) * ld * (TILE_BLOCK_BYTES / 2),
-                    (uint32_t)(nk * TILE_BLOCK_BYTES));
-    } else {
-      const int64_t rows = R - r0 < BF_BM ? R - r0 : BF_BM;
-      r = make_rsrc(X + r0 * ld, (uint32_t)(rows * ld * 2));
-    }
+  // The panel's blocks; rows past the matrix are zero in the layout.
+  auto panel = [&](const bf16_t* X, int64_t r0, int64_t ld) {
+    i32x4 r = make_rsrc(X + (r0 / BF_BM) * ld * (TILE_BLOCK_BYTES / 2),
+                        (uint32_t)(nk * TILE_BLOCK_BYTES));
 #pragma unroll
     for (int i = 0; i < 4; ++i) r[i] = __builtin_amdgcn_readfirstlane(r[i]);
     return r;
   };
   int64_t m0, n0;
   coords(t, m0, n0);
-  i32x4 rsa = panel(A, m0, M, lda), rsb = panel(B, n0, N, ldb), nrsa = rsa, nrsb = rsb;
+  i32x4 rsa = panel(A, m0, lda), rsb = panel(B, n0, ldb), nrsa = rsa, nrsb = rsb;
   int tnext = t + per_xcd;
   bool has_next = tnext < hi;
   int64_t nm0 = 0, nn0 = 0;
   if (has_next) {
     coords(tnext, nm0, nn0);
-    nrsa = panel(A, nm0, M, lda);
-    nrsb = panel(B, nn0, N, ldb);
+    nrsa = panel(A, nm0, lda);
+    nrsb = panel(B, nn0, ldb);
   }
   const uint32_t lds_base = (uint32_t)reinterpret_cast<uintptr_t>(lds);
   // The byte offset of stage kt passes through an opaque SGPR copy, so the
@@ -1004,19 +984,13 @@ gemm_bf16_persist(const bf16_t* __restrict__ A, int64_t lda, const bf16_t* __res
     if (!copier) return;
     const uint32_t sa = lds_base + (uint32_t)(slot * BF_STAGE);
     const uint32_t sb = sa + BF_STAGE_A;
-    int kbytes;
-    __asm__ volatile("s_lshl_b32 %0, %1, 6"
-                     : "=s"(kbytes)
-                     : "s"(__builtin_amdgcn_readfirstlane(kt)));  // kt * BF_BK * 2
+    int kblk;
+    __asm__ volatile("s_lshl_b32 %0, %1, 14"
+                     : "=s"(kblk)
+                     : "s"(__builtin_amdgcn_readfirstlane(kt)));  // kt * TILE_BLOCK_BYTES
     const uint32_t dst = (uint32_t)(wave * BF_PER * 1024);
-    if constexpr (TOPS) {
-      const int kblk = kbytes << 8;  // kt * TILE_BLOCK_BYTES
-      load_lds16_x4(ra, sa + dst, lof.oa[0], kblk);
-      load_lds16_x4(rb, sb + dst, lof.ob[0], kblk);
-    } else {
-      load_lds16_4v(ra, sa + dst, lof.oa[0], lof.oa[1], lof.oa[2], lof.oa[3], kbytes);
-      load_lds16_4v(rb, sb + dst, lof.ob[0], lof.ob[1], lof.ob[2], lof.ob[3], kbytes);
-    }
+    load_lds16_x4(ra, sa + dst, lof.oc, kblk);
+    load_lds16_x4(rb, sb + dst, lof.oc, kblk);
   };
   bf16x8 ca[8], cb[4], da[8], db[4];  // two fragment sets, used in turn
   // In the order the MFMAs consume them: row block 0, the column blocks, the
@@ -1155,8 +1129,8 @@ gemm_bf16_persist(const bf16_t* __restrict__ A, int64_t lda, const bf16_t* __res
     has_next = tnext < hi;
     if (has_next) {
       coords(tnext, nm0, nn0);
-      nrsa = panel(A, nm0, M, lda);
-      nrsb = panel(B, nn0, N, ldb);
+      nrsa = panel(A, nm0, lda);
+      nrsb = panel(B, nn0, ldb);
     }
     lof = lane_offs();
     if (copier) wait_stage<BF_LPS>(BF_ST - 2);
@@ -1622,27 +1596,14 @@ int cu_count() {
   return n;
 }
 
-// Row-major operands (K = lda = ldb columns), one split: the persistent
-// kernel when the K loop has at least BF_ST stages and the device reports
-// its CU count, else the one-tile-per-workgroup kernel.
+// Row-major operands (K = lda = ldb columns), one split: the
+// one-tile-per-workgroup kernel.  The bf16 forward comes here only when H
+// has fewer K blocks than the persistent kernel's ring (it reads tiled
+// copies otherwise).
 template <class Epi>
 hipError_t launch_bf16_rows(const bf16_t* A, int64_t lda, const bf16_t* B, int64_t ldb,
                             int64_t M, int64_t N, int64_t K, const Epi& epi, hipStream_t s) {
-  const int64_t tm = ceil_div(M, BF_BM), tn = ceil_div(N, BF_BN);
-  const int64_t total = tm * tn;
-  const int cus = cu_count() / 8 * 8;
-  if (total <= 0) return hipSuccess;
-  if (K % BF_BK != 0 || K / BF_BK < BF_ST || cus <= 0 || total > (int64_t)1 << 30)
-    return launch_bf16<false>(A, lda, B, ldb, M, N, K, 1, round_up(K, BF_BK), epi, s);
-  if ((int64_t)BF_BM * std::max(lda, ldb) * 2 >= ((int64_t)1 << 31)) return hipErrorInvalidValue;
-  const int64_t grid = std::min<int64_t>(round_up(total, 8), cus);
-  if ((K / BF_BK) % 2 == 0)
-    hipLaunchKernelGGL((gemm_bf16_persist<Epi, true, false>), dim3((unsigned)grid), dim3(BF_NT),
-                       0, s, A, lda, B, ldb, M, N, K, (int)tm, (int)tn, epi);
-  else
-    hipLaunchKernelGGL((gemm_bf16_persist<Epi, false, false>), dim3((unsigned)grid),
-                       dim3(BF_NT), 0, s, A, lda, B, ldb, M, N, K, (int)tm, (int)tn, epi);
-  return hipGetLastError();
+  return launch_bf16<false>(A, lda, B, ldb, M, N, K, 1, round_up(K, BF_BK), epi, s);
 }
 
 // Both operands in the tiled block layout (kb = blocks per 256-row panel,
@@ -1661,11 +1622,11 @@ hipError_t launch_bf16_tiled_persist(const bf16_t* A, const bf16_t* B, int64_t k
   if (nk * TILE_BLOCK_BYTES >= ((int64_t)1 << 31)) return hipErrorInvalidValue;
   const int64_t grid = std::min<int64_t>(round_up(total, 8), cus);
   if (nk % 2 == 0)
-    hipLaunchKernelGGL((gemm_bf16_persist<Epi, true, true>), dim3((unsigned)grid), dim3(BF_NT),
-                       0, s, A, kb, B, kb, M, N, K, (int)tm, (int)tn, epi);
+    hipLaunchKernelGGL((gemm_bf16_persist<Epi, true>), dim3((unsigned)grid), dim3(BF_NT), 0, s,
+                       A, kb, B, kb, M, N, K, (int)tm, (int)tn, epi);
   else
-    hipLaunchKernelGGL((gemm_bf16_persist<Epi, false, true>), dim3((unsigned)grid), dim3(BF_NT),
-                       0, s, A, kb, B, kb, M, N, K, (int)tm, (int)tn, epi);
+    hipLaunchKernelGGL((gemm_bf16_persist<Epi, false>), dim3((unsigned)grid), dim3(BF_NT), 0, s,
+                       A, kb, B, kb, M, N, K, (int)tm, (int)tn, epi);
   return hipGetLastError();
 }
 
