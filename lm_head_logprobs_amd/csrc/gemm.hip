@@ -18,13 +18,14 @@
 // the other issues its loads or waits at the barrier.  With random
 // operands this shape sustains a higher MFMA rate than 32x32x16 (measured
 // about 84% against 72% of the dense peak in a loop without memory traffic).
-// K advances 32 at a time through a 4-stage ring of LDS buffers (32 KB each:
-// A then B; 128 KB).
+// K advances 32 at a time through a ring of LDS buffers (32 KB each: A then
+// B), four stages (128 KB) in the forward and dh, five (160 KB) in the
+// persistent dW, whose G stages come from HBM.
 // Operand tiles are copied global -> LDS by buffer_load_dwordx4 ... lds: each
 // wave instruction fills 1 KB of LDS (16 bytes per lane, consecutive), no
-// VGPR staging.  Loads run three stages ahead; a stage is waited for with an
-// explicit vmcnt and one barrier, placed between the two K-steps of a stage so
-// MFMAs are in flight across it.  Out-of-range rows or K columns are given a
+// VGPR staging.  Loads run one stage less than the ring ahead; a stage is
+// waited for with an explicit vmcnt and one barrier, placed among the stage's
+// MFMAs so that MFMAs are in flight across it.  Out-of-range rows or K columns are given a
 // buffer offset past the descriptor's range, which the hardware reads as zero.
 // In LDS a tile row is 64 bytes (32 bf16 = four 16-byte chunks); chunk c of
 // row r is stored at position c ^ tile_swz(r) (kernels.h), which keeps the
@@ -482,8 +483,9 @@ struct DwEpiT {
 
 // ------------------------------------------------------------ bf16 kernel ---
 
-// K advances 32 at a time through a ring of BF_ST = 4 stages of 32 KB (a ring
-// of five, filling the 160 KB of LDS, timed the same on the head step).
+// K advances 32 at a time through a ring of BF_ST = 4 stages of 32 KB (the
+// forward and dh: a ring of five, filling the 160 KB of LDS, was slightly
+// slower for both; the persistent dW has its own, DW_ST).
 constexpr int BF_BM = 256, BF_BN = 256, BF_BK = 32, BF_ST = 4;
 constexpr int BF_STAGE_A = BF_BM * BF_BK * 2;  // bytes
 constexpr int BF_STAGE = (BF_BM + BF_BN) * BF_BK * 2;
