@@ -171,13 +171,14 @@ def test_short_token_chunks_through_the_persistent_dW(chunk):
     compare_all(wl, got, ref, case=f"token chunk {chunk}, V=70000, H=512")
 
 
-@pytest.mark.parametrize("H,chunk", [(224, 0), (224, 160), (160, 96)])
+@pytest.mark.parametrize("H,chunk", [(224, 0), (224, 160), (224, 128), (160, 96)])
 def test_odd_stage_counts(H, chunk):
     # The persistent forward (K = H) and dW (K = the chunk's tokens) pick the
     # fragment set that holds stage 0 by the parity of their stage count:
     # H = 224 and 160 give 7 and 5 stages of 32 (odd; the workloads' H are
-    # even multiples), chunks of 160 tokens 5 dW stages, the default chunk 10,
-    # and 96-token chunks 3 (too few for the persistent dW).
+    # even multiples), chunks of 160 tokens 5 dW stages, the default chunk 10;
+    # 128- and 96-token chunks give 4 and 3, too few for the persistent dW's
+    # five-stage ring (the one-tile dW kernel takes them).
     wl = _case("c4_head16k_ipo_topp_replay", N=300, H=H, V=5000)
     _, got = run_head(wl, token_chunk=chunk)
     ref = ohead.from_workload(wl)
