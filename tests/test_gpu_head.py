@@ -216,6 +216,17 @@ def test_degenerate_shapes(shape):
     compare_all(wl, got, ref, case=f"degenerate {shape}")
 
 
+@pytest.mark.parametrize("shape", [dict(N=1, H=8, V=1), dict(N=5, H=8, V=3),
+                                   dict(N=129, H=136, V=129)])
+def test_degenerate_shapes_fp32(shape):
+    # the fp32 path (its own GEMM tiles and partial tile height) at the same
+    # edge shapes
+    wl = _case("c1_tiny_fp32_ipo", **shape)
+    _, got = run_head(wl)
+    ref = ohead.from_workload(wl)
+    compare_all(wl, got, ref, case=f"fp32 degenerate {shape}")
+
+
 def test_empty_support_rows_and_duplicates():
     wl = _case("c5a_head64k_draws_ipo_k1", N=64, V=900)
     off = wl.offsets.clone()
