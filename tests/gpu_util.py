@@ -21,13 +21,15 @@ Decisions with a margin of at most 1e-6 (the stated band) and those in
 (1e-6, band] are counted separately, with how many of each actually differ;
 every decision beyond its band must agree.  Every comparison appends its
 figures to a JSON-lines report: the file RL_PARITY_REPORT names, by default
-parity_report.jsonl in the folder whose contents a remote run hands back.
+rl_parity_report.jsonl in the temp directory; tests/parity_summary.py turns
+it into a table.
 """
 
 from __future__ import annotations
 
 import json
 import os
+import tempfile
 
 import numpy as np
 import torch
@@ -43,8 +45,10 @@ C_BAND = 32.0    # decision band: max(NS_BAND, C_BAND u (max|z| + 2) max(P, r))
 U32 = 2.0**-24
 
 _ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+# Where the parity tests append their per-case figures (JSON lines): set
+# RL_PARITY_REPORT to keep them; by default they go to the temp directory.
 REPORT = os.environ.get("RL_PARITY_REPORT",
-                        os.path.join(_ROOT, "gpurun_out", "parity_report.jsonl"))
+                        os.path.join(tempfile.gettempdir(), "rl_parity_report.jsonl"))
 
 
 def record(case, rep):
