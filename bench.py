@@ -212,7 +212,11 @@ def bench_head(args, torch):
               "torch_allocator_peak_bytes": int(torch.cuda.max_memory_allocated())}
     memory["peak_gib"] = memory["peak_device_bytes"] / 2**30
     value = N / (ms * 1e-3)
-    flops_6nhv = 6.0 * N * H * V
+    # MFMA work per step: the forward, dh and dW GEMMs (6NHV) on the dense
+    # backward; the forward alone (2NHV) on the sparse one, whose gradients
+    # are gathers and a scatter
+    dense_bwd = wl.params["backward"] != "sparse"
+    gemm_flops = (6.0 if dense_bwd else 2.0) * N * H * V
     peak = PEAK_BF16_TFLOPS if wl.dtype == "bf16" else PEAK_FP32_TFLOPS
     kernels = {k: {"launches": n, "avg_ms": t / n, "ms_per_step": t / args.steps}
                for k, (n, t) in sorted(prof.items(), key=lambda kv: -kv[1][1])}
@@ -247,7 +251,8 @@ def bench_head(args, torch):
                    "kl_staleness": wl.params.get("kl_staleness", "none"),
                    "entropy_coeff": wl.params.get("entropy_coeff", 0.0),
                    "token_chunk": fh.cfg.token_chunk or min(N, DEFAULT_TOKEN_CHUNK)},
-        "mfma_frac_6nhv": flops_6nhv / (ms * 1e-3) / 1e12 / peak,
+        ("mfma_frac_6nhv" if dense_bwd else "mfma_frac_2nhv"):
+            gemm_flops / (ms * 1e-3) / 1e12 / peak,
         "peak_device_bytes": memory["peak_device_bytes"],
         "memory": memory,
         "roofline": roof,
@@ -547,28 +552,38 @@ def measured_peaks(torch):
 
 
 def secondary(args, torch):
-    """Compact figures of two more workloads in the same run: the 16k top-p
-    replay with exact KL (head) and the 2.16M-token loss-only replay, each
-    with its step time, roofline fraction, memory and oracle CPU baseline."""
+    """Compact figures of the other workloads in the same run: the 16k top-p
+    replay with exact KL, the two 64k-token draw workloads (IPO with k1 KL on
+    the dense backward, reinforce on the sparse one), the 2.16M-token
+    loss-only replay and the sequence-aware correction over it, each with its
+    step time, roofline fraction and memory; the 16k top-p replay and the
+    loss-only replay also with their oracle CPU baselines (the 64k workloads'
+    per-token oracle work is that of the 16k ones)."""
     from types import SimpleNamespace
 
     res = {}
-    a4 = SimpleNamespace(**vars(args))
-    a4.workload, a4.steps, a4.warmup = "c4_head16k_ipo_topp_replay", 10, 3
-    a4.kl_staleness, a4.entropy_coeff, a4.token_chunk = "none", 0.0, 0
-    out, wl = bench_head(a4, torch)
-    res[a4.workload] = {
-        "ms_per_step": out["ms_per_step"], "tokens_per_s": out["value"],
-        "mfma_frac_6nhv": out["mfma_frac_6nhv"], "support_nnz": out["config"]["support_nnz"],
-        "token_chunk": out["config"]["token_chunk"],
-        "peak_device_bytes": out["peak_device_bytes"],
-        "roofline": {k: out["roofline"][k] for k in ("kernel", "frac", "avg_launch_ms")},
-        "kernels_ms_per_step": {k: v["ms_per_step"] for k, v in out["kernels"].items()
-                                if v["ms_per_step"] >= 0.05},
-        "cpu_baseline": None if args.no_cpu_baseline else cpu_baseline(wl, 10.0),
-    }
-    del out, wl
-    torch.cuda.empty_cache()
+    for name, steps, warmup, cpu_s in (("c4_head16k_ipo_topp_replay", 10, 3, 10.0),
+                                       ("c5a_head64k_draws_ipo_k1", 5, 2, None),
+                                       ("c5b_head64k_draws_reinforce", 5, 2, None)):
+        a = SimpleNamespace(**vars(args))
+        a.workload, a.steps, a.warmup = name, steps, warmup
+        a.kl_staleness, a.entropy_coeff, a.token_chunk = "none", 0.0, 0
+        out, wl = bench_head(a, torch)
+        res[name] = {
+            "ms_per_step": out["ms_per_step"], "tokens_per_s": out["value"],
+            "steps": steps,
+            **{k: out[k] for k in ("mfma_frac_6nhv", "mfma_frac_2nhv") if k in out},
+            "support_nnz": out["config"]["support_nnz"],
+            "backward": out["config"]["backward"], "token_chunk": out["config"]["token_chunk"],
+            "peak_device_bytes": out["peak_device_bytes"],
+            "roofline": {k: out["roofline"][k] for k in ("kernel", "frac", "avg_launch_ms")},
+            "kernels_ms_per_step": {k: v["ms_per_step"] for k, v in out["kernels"].items()
+                                    if v["ms_per_step"] >= 0.05},
+            "cpu_baseline": (None if args.no_cpu_baseline or cpu_s is None
+                             else cpu_baseline(wl, cpu_s)),
+        }
+        del out, wl
+        torch.cuda.empty_cache()
     a2 = SimpleNamespace(**vars(args))
     a2.workload, a2.steps, a2.warmup = "c2_replay", 200, 20
     out, _ = bench_replay(a2, torch)
@@ -583,6 +598,19 @@ def secondary(args, torch):
         "cpu_baseline": (None if args.no_cpu_baseline
                          else cpu_baseline_replay("replay", wl_replay_host(), 5.0)),
     }
+    torch.cuda.empty_cache()
+    am = SimpleNamespace(**vars(args))
+    am.workload, am.steps, am.warmup = "c2_mis", 200, 20
+    out, _ = bench_mis(am, torch)
+    res["c2_mis"] = {
+        "us_per_step": out["ms_per_step"] * 1e3, "tokens_per_s": out["value"],
+        "sequences": out["config"]["sequences"], "step_timing": out["step_timing"],
+        "roofline": {"kernel": out["roofline"]["kernel"], "frac": out["roofline"]["frac"],
+                     "avg_launch_us": out["roofline"]["avg_launch_ms"] * 1e3,
+                     "GB/s": out["roofline"]["achieved"]},
+        "kernels_avg_us": {k: v["avg_ms"] * 1e3 for k, v in out["kernels"].items()},
+    }
+    del out
     torch.cuda.empty_cache()
     return res
 
@@ -608,8 +636,9 @@ def main():
     ap.add_argument("--no-peak-check", action="store_true",
                     help="skip the measured MFMA and copy peaks")
     ap.add_argument("--no-secondary", action="store_true",
-                    help="default workload only: skip the 16k top-p replay and loss-only "
-                         "replay figures")
+                    help="default workload only: skip the figures of the other workloads "
+                         "(16k top-p replay, 64k draws, loss-only replay, sequence-aware "
+                         "correction)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a plain 1 GiB device copy (counter calibration)")
     args = ap.parse_args()
