@@ -493,17 +493,41 @@ __global__ void __launch_bounds__(NT) form_g_blocks_kernel(
     for (int q = 0; q < 4; ++q)
       raw[b][q] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(
           blk0 + b * (TILE_ROWS * TILE_K) + (threadIdx.x + NT * q) * 8));
+  // The per-token values of all four rows, loaded before the first store:
+  // loaded after it, each would wait for that store too (one in-order
+  // counter for loads and stores).
+  float lq[4], kq[4], mq[4][NBLK];
+  int jt[NBLK];  // vocabulary tile of each block (uniform)
+#pragma unroll
+  for (int b = 0; b < NBLK; ++b)
+    jt[b] = __builtin_amdgcn_readfirstlane((int)(((int)kb0 + b) * TILE_K / vtile));
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    // rows past Tc read row Tc - 1 (Tc > 0) and drop the values: no branches
+    const int r = (threadIdx.x + NT * q) >> 2;
+    const int64_t t = tp * TILE_ROWS + r;
+    const bool tok = t < Tc;
+    const int64_t tr = tok ? t : Tc - 1;
+    const float l = lse[tr], k = kap[tr];
+    lq[q] = tok ? l : 0.0f;
+    kq[q] = tok ? k : 0.0f;
+#pragma unroll
+    for (int b = 0; b < NBLK; ++b) {
+      const float m = part_m[tr * J + jt[b]];
+      mq[q][b] = tok ? m : 0.0f;
+    }
+  }
 #pragma unroll
   for (int q = 0; q < 4; ++q) {
     const int p = threadIdx.x + NT * q;  // 16-byte chunk of a block
     const int r = p >> 2, lc = (p & 3) ^ tile_swz(r);
     const int64_t t = tp * TILE_ROWS + r;
     const bool tok = t < Tc;
-    const float l = tok ? lse[t] : 0.0f, kt = tok ? kap[t] : 0.0f;
+    const float l = lq[q], kt = kq[q];
 #pragma unroll
     for (int b = 0; b < NBLK; ++b) {
       const int64_t kb = kb0 + b, v = kb * TILE_K + lc * 8;
-      const float m = tok ? part_m[t * J + kb * TILE_K / vtile] : 0.0f;
+      const float m = mq[q][b];
       const float e = tok ? __expf(m - l) : 0.0f;
       const float sc = kt * e;
       float x[8];
