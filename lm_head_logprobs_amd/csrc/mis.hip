@@ -302,44 +302,76 @@ mis_token_kernel(const float* __restrict__ lp, const float* __restrict__ lq,
   // counts (exact in fp32 per thread) and weight sums
   float f[8] = {0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f};
   float wmin = __builtin_inff(), wmax = -__builtin_inff();
-  for (int c = wv * (int)gridDim.x + (int)blockIdx.x; c < nch; c += stride) {
-    const Tok4 t = load_tok4(lp, lq, N, c, lane);
-    const int64_t t0 = (int64_t)c * kChunk + 4 * lane;
+  // A chunk's vector inputs: the lane's four tokens and their advantages.
+  struct In {
+    Tok4 t;
     float A[4];
+  };
+  auto load_in = [&](int c) {
+    In x;
+    x.t = load_tok4(lp, lq, N, c, lane);
+    const int64_t t0 = (int64_t)c * kChunk + 4 * lane;
     if (t0 + 4 <= N) {
       const f32x4 a = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(adv + t0));
 #pragma unroll
-      for (int j = 0; j < 4; ++j) A[j] = a[j];
+      for (int j = 0; j < 4; ++j) x.A[j] = a[j];
     } else {
 #pragma unroll
-      for (int j = 0; j < 4; ++j) A[j] = t.in[j] ? adv[t0 + j] : 0.0f;
+      for (int j = 0; j < 4; ++j) x.A[j] = x.t.in[j] ? adv[t0 + j] : 0.0f;
     }
+    return x;
+  };
+  // Each wave loads its next chunk's inputs before it works on the current
+  // one, and the four tokens' sequence values are gathered together ahead of
+  // that prefetch (loads and stores share one in-order counter: a gather
+  // issued token by token, after the previous chunk's stores, waited for
+  // each of them in turn).
+  const int cfirst = wv * (int)gridDim.x + (int)blockIdx.x;
+  In cur;
+  if (cfirst < nch) cur = load_in(cfirst);
+  for (int c = cfirst; c < nch; c += stride) {
+    const int64_t t0 = (int64_t)c * kChunk + 4 * lane;
     // sequence of each token: the chunk's first sequence plus the starts in
     // (chunk start, token]
     const int s0 = std::min(std::max(firstseq[c], 0), S - 1);
+    // the chunk's eight start-bit words are wave-uniform (scalar loads); the
+    // lane's own word is selected from them rather than loaded per lane
     const uint32_t* bw = bitmap + (int64_t)c * 8;
     const int k = lane >> 3;  // word of the lane's 4 tokens
     int before = 0;
+    uint32_t mk = 0;
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
-      const uint32_t m = i == 0 ? (bw[0] & ~1u) : bw[i];
+      uint32_t m = __builtin_amdgcn_readfirstlane(bw[i]);
+      m = i == 0 ? (m & ~1u) : m;
       before += i < k ? __builtin_popcount(m) : 0;
+      mk = i == k ? m : mk;
     }
-    const uint32_t mk = k == 0 ? (bw[0] & ~1u) : bw[k];
     const int bit0 = (4 * lane) & 31;
     // starts at or before the lane's first token within its word
     int cnt = before + __builtin_popcount(mk & (bit0 == 31 ? ~0u : ((2u << bit0) - 1u)));
+    uint32_t sf[4];
+    float swv[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      if (j > 0) cnt += (mk >> (bit0 + j)) & 1u;
+      const int sj = std::min(s0 + cnt, S - 1);  // in range even for inconsistent offsets
+      sf[j] = seq_flags[sj];
+      swv[j] = p.tis_level != RL_LEVEL_TOKEN ? seq_w[sj] : 0.0f;
+    }
+    In nxt;  // read only when the loop goes on
+    if (c + stride < nch) nxt = load_in(c + stride);
+    const Tok4& t = cur.t;
+    const float* A = cur.A;
     float wout[4];
     uint32_t fw = 0;
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      if (j > 0) cnt += (mk >> (bit0 + j)) & 1u;
-      const int s = std::min(s0 + cnt, S - 1);  // in range even for inconsistent offsets
       const double d = (double)t.lp[j] - (double)t.lq[j];
       uint32_t fl = 0;
       float w_b = 0.0f;
       if (t.in[j]) {
-        const uint32_t sf = seq_flags[s];
+        const uint32_t sfj = sf[j];
         if (p.tis_level == RL_LEVEL_TOKEN) {
           const bool low = p.tis_mode != RL_TIS_TRUNCATE && d < p.lL;
           const bool high = d > p.lU;
@@ -348,16 +380,16 @@ mis_token_kernel(const float* __restrict__ lp, const float* __restrict__ lq,
           else w_b = (low || high) ? 0.0f : __expf((float)d);
           fl |= (low ? RL_MIS_F_TIS_LOW : 0u) | (high ? RL_MIS_F_TIS_HIGH : 0u);
         } else {
-          w_b = seq_w[s];
-          fl |= sf & (RL_MIS_F_TIS_LOW | RL_MIS_F_TIS_HIGH);
+          w_b = swv[j];
+          fl |= sfj & (RL_MIS_F_TIS_LOW | RL_MIS_F_TIS_HIGH);
         }
         if (p.use_rs) {
           if (p.rs_level == RL_LEVEL_TOKEN)
             fl |= (d < p.rlL ? RL_MIS_F_RS_LOW : 0u) | (d > p.rlU ? RL_MIS_F_RS_HIGH : 0u);
           else
-            fl |= sf & (RL_MIS_F_RS_LOW | RL_MIS_F_RS_HIGH);
+            fl |= sfj & (RL_MIS_F_RS_LOW | RL_MIS_F_RS_HIGH);
         }
-        fl |= sf & RL_MIS_F_VETO;
+        fl |= sfj & RL_MIS_F_VETO;
         fl |= (p.veto_on && d < p.lC) ? RL_MIS_F_CATASTROPHIC : 0u;
         const bool rej = (fl & (RL_MIS_F_RS_LOW | RL_MIS_F_RS_HIGH | RL_MIS_F_VETO)) != 0u;
         fl |= rej ? RL_MIS_F_REJECTED : 0u;
@@ -391,6 +423,7 @@ mis_token_kernel(const float* __restrict__ lp, const float* __restrict__ lq,
           if (flags) flags[t0 + j] = (uint8_t)(fw >> (8 * j));
         }
     }
+    cur = nxt;
   }
   wave_totals<8>(f, wt[wv], lane);
   wmin = wave_min_f(wmin);
