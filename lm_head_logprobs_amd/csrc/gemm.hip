@@ -156,14 +156,11 @@ struct Acc16 {  // v_mfma_f32_16x16x32_bf16 : 16 x 16 blocks, 4 registers per la
     return x + __shfl_xor(x, 32, 64);
   }
   static __device__ __forceinline__ bool col_owner(int lane) { return lane < 16; }
-  static constexpr bool IN_VGPR = false;  // the accumulators live in AGPRs
 };
 // The same layout with the accumulators in VGPRs (the MFMAs' VGPR form): an
 // epilogue that reads every accumulator more than once then needs no AGPR
-// copies (v_accvgpr_read) for it.
-struct Acc16V : Acc16 {
-  static constexpr bool IN_VGPR = true;
-};
+// copies (v_accvgpr_read) for it.  Acc16 keeps them in AGPRs.
+struct Acc16V : Acc16 {};
 
 // ------------------------------------------------------------- epilogues ---
 
@@ -911,8 +908,8 @@ gemm_bf16_kernel(const bf16_t* __restrict__ A, int64_t lda, const bf16_t* __rest
 template <class Epi, bool EVEN_NK>
 __global__ void __launch_bounds__(BF_NT) __attribute__((amdgpu_waves_per_eu(2, 2)))
 gemm_bf16_persist(const bf16_t* __restrict__ A, int64_t lda, const bf16_t* __restrict__ B,
-                  int64_t ldb, int64_t M, int64_t N, int64_t K, int tiles_m, int tiles_n,
-                  Epi epi) {
+                  int64_t ldb, [[maybe_unused]] int64_t M, [[maybe_unused]] int64_t N, int64_t K,
+                  int tiles_m, int tiles_n, Epi epi) {
   __shared__ __attribute__((aligned(1024))) char lds[BF_LDS];
   static_assert(BF_STAGE >= 6 * BF_BN * 4, "the epilogue's reductions fit one stage");
   const int total = tiles_m * tiles_n;
@@ -1170,8 +1167,8 @@ static_assert(DW_ST - 2 <= 3, "wait_stage covers up to three younger stages");
 template <class Epi, bool ATR, int MB, bool EVEN_NK, bool AFLAT>
 __global__ void __launch_bounds__(BF_NT) __attribute__((amdgpu_waves_per_eu(2, 2)))
 gemm_bf16_persist_t(const bf16_t* __restrict__ A, int64_t lda, const bf16_t* __restrict__ B,
-                    int64_t ldb, int64_t M, int64_t N, int64_t K, int tiles_m, int tiles_n,
-                    Epi epi) {
+                    int64_t ldb, [[maybe_unused]] int64_t M, [[maybe_unused]] int64_t N,
+                    int64_t K, int tiles_m, int tiles_n, Epi epi) {
   constexpr int NST = Epi::STORES;
   static_assert((DW_ST - 2) * BT_LPS + NST < 64, "stage waits must fit vmcnt");
   __shared__ __attribute__((aligned(1024))) char lds[DW_ST * BF_STAGE];
@@ -1181,7 +1178,7 @@ gemm_bf16_persist_t(const bf16_t* __restrict__ A, int64_t lda, const bf16_t* __r
   const int lo = (blockIdx.x & 7) * chunk, hi = min(total, lo + chunk);
   int t = lo + (blockIdx.x >> 3);
   if (t >= hi) return;
-  const int tid = threadIdx.x, lane = tid & 63;
+  const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // 0..7
   // Wave tiles of 16 MB x 16 NB (MB row blocks, NB column blocks of 16): 8 x 4
   // blocks as 2 x 4 waves, or 4 x 8 blocks as 4 x 2 waves.

@@ -684,8 +684,8 @@ __global__ void __launch_bounds__(NT) finalize_dh_kernel(
 }
 
 __global__ void __launch_bounds__(1024) reduce_final_kernel(const float* __restrict__ stats,
-                                                            int64_t N, float inv_D, float beta,
-                                                            float* loss, float* metrics) {
+                                                            int64_t N, float inv_D, float* loss,
+                                                            float* metrics) {
   __shared__ double sh[STAT_N][16];
   double acc[STAT_N];
 #pragma unroll
@@ -872,9 +872,11 @@ hipError_t fold_sparse(int dtype, void* G, int write_g, void* Gt, int tiled, int
   return hipGetLastError();
 }
 
-hipError_t reduce_final(const float* stats, int64_t N, float inv_D, float beta, float* loss,
+// beta is not needed here: each token's KL coefficient (beta, or its
+// staleness-scaled value) is applied in combine, before the per-token stats.
+hipError_t reduce_final(const float* stats, int64_t N, float inv_D, float /*beta*/, float* loss,
                         float* metrics, hipStream_t s) {
-  hipLaunchKernelGGL(reduce_final_kernel, dim3(1), dim3(1024), 0, s, stats, N, inv_D, beta, loss,
+  hipLaunchKernelGGL(reduce_final_kernel, dim3(1), dim3(1024), 0, s, stats, N, inv_D, loss,
                      metrics);
   return hipGetLastError();
 }
