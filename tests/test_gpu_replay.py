@@ -28,6 +28,14 @@ def test_replay_parity(N):
     r = make_replay(N=N, device="cuda:0")
     print(f"[case] replay N={N}", flush=True)
     _, got = _run(r)
+    check_replay(r, got)
+
+
+def check_replay(r, got):
+    """Every output of one replay call against the oracle: mask words bit for
+    bit outside the near-threshold band, the primary weight to rounding, the
+    counts exactly up to the near-threshold decisions, the sums to 1e-4
+    relative plus what the near-threshold tokens can move."""
     ref = orp.replay_reference(r.lp.cpu().numpy(), r.lq.cpu().numpy(), r.adv.cpu().numpy(),
                                r.params)
     near = orp.near_threshold_bits(ref, BAND)
